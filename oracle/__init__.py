@@ -1,0 +1,166 @@
+"""CPU oracle of the W4A16 sigmoid-routed MoE layer (FP64, plain C).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the CPU-baseline leg of the benchmark, never by the product package.  This
+wrapper only marshals numpy arrays into ``oracle.c``; the arithmetic and its
+page citations live there.
+
+A layer is a dict of numpy arrays with these keys (the convention the input
+generator in ``synth`` writes):
+  hidden, inter, shared_inter, n_experts, top_k, wtype ('bf16' | 'nvfp4'),
+  eps (float), residual (0/1),
+  norm_gain  uint16 [H] bf16 bits or None,
+  router_w   uint16 [E, H], router_b float32 [E] or None,
+  w_gate/w_up  NVFP4: uint8 [E, I, H/16*9] (GGUF-like blocks) | BF16: uint16 [E, I, H]
+  w_down       NVFP4: uint8 [E, H, I/16*9]                    | BF16: uint16 [E, H, I]
+  w_scale    float32 [E, 3] (NVFP4 tensor scales: gate, up, down) or None
+  sh_gate/sh_up/sh_down (shared expert, same layouts without E), sh_scale float32 [3]
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build():
+    """Compile oracle.c with gcc into oracle/liboracle.so (always rebuilds)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-shared", "-fPIC",
+                           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wtype", ctypes.c_int32),
+        ("norm_eps", ctypes.c_double), ("residual", ctypes.c_int32),
+        ("norm_gain", ctypes.c_void_p), ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("w_scale", ctypes.c_void_p),
+        ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+        ("sh_scale", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int32]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int32]
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_round.restype = ctypes.c_uint16
+        L.oracle_bf16_round.argtypes = [ctypes.c_double]
+        L.oracle_decode_nvfp4.restype = ctypes.c_int64
+        L.oracle_decode_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_double, ctypes.c_void_p]
+        L.oracle_moe_tokens.restype = ctypes.c_int32
+        L.oracle_moe_tokens.argtypes = [ctypes.POINTER(_Layer), ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def e2m1_value(code):
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e4m3_value(code):
+    return lib().oracle_e4m3_value(int(code))
+
+
+def bf16_value(bits):
+    return lib().oracle_bf16_value(int(bits))
+
+
+def bf16_round(v):
+    """FP64 -> BF16 bits, one round-to-nearest-even."""
+    return lib().oracle_bf16_round(float(v))
+
+
+def bf16_to_f64(bits):
+    """Vector form of bf16_value (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode_nvfp4(src, rows, cols, tensor_scale):
+    """GGUF-like NVFP4 bytes -> (FP64 [rows, cols], number of NaN scale bytes)."""
+    src = np.ascontiguousarray(src, dtype=np.uint8)
+    assert src.size == rows * (cols // 16) * 9
+    out = np.empty((rows, cols), dtype=np.float64)
+    nan = lib().oracle_decode_nvfp4(src.ctypes.data, rows, cols, float(tensor_scale), out.ctypes.data)
+    return out, int(nan)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_layer(layer, keep):
+    def arr(key, dtype):
+        v = layer.get(key)
+        if v is None:
+            return None
+        a = np.ascontiguousarray(v, dtype=dtype)
+        keep.append(a)
+        return a
+
+    wdt = np.uint16 if layer["wtype"] == "bf16" else np.uint8
+    s = _Layer()
+    s.hidden, s.inter, s.shared_inter = layer["hidden"], layer["inter"], layer["shared_inter"]
+    s.n_experts, s.top_k = layer["n_experts"], layer["top_k"]
+    s.wtype = 0 if layer["wtype"] == "bf16" else 1
+    s.norm_eps = float(layer.get("eps", 0.0))
+    s.residual = int(layer.get("residual", 0))
+    s.norm_gain = _ptr(arr("norm_gain", np.uint16))
+    s.router_w = _ptr(arr("router_w", np.uint16))
+    s.router_b = _ptr(arr("router_b", np.float32))
+    s.w_gate = _ptr(arr("w_gate", wdt))
+    s.w_up = _ptr(arr("w_up", wdt))
+    s.w_down = _ptr(arr("w_down", wdt))
+    s.w_scale = _ptr(arr("w_scale", np.float32))
+    s.sh_gate = _ptr(arr("sh_gate", wdt))
+    s.sh_up = _ptr(arr("sh_up", wdt))
+    s.sh_down = _ptr(arr("sh_down", wdt))
+    s.sh_scale = _ptr(arr("sh_scale", np.float32))
+    return s
+
+
+def moe_tokens(layer, x, forced_idx=None):
+    """Run T tokens x [T, H] (bf16 bits) through the layer.
+
+    Returns dict(out [T,H] uint16, idx [T,k] int32, w [T,k] f64, flag [T] int32,
+    logits [T,E] f64, nan_tokens int).  forced_idx [T,k] replaces the selection.
+    """
+    keep = []
+    s = _as_layer(layer, keep)
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1, layer["hidden"])
+    T = x.shape[0]
+    E = layer["n_experts"]
+    k = layer["top_k"] if E > 0 else 0
+    out = np.empty((T, layer["hidden"]), dtype=np.uint16)
+    idx = np.empty((T, max(k, 1)), dtype=np.int32)
+    w = np.empty((T, max(k, 1)), dtype=np.float64)
+    flag = np.zeros((T,), dtype=np.int32)
+    logits = np.empty((T, max(E, 1)), dtype=np.float64)
+    fp = None
+    if forced_idx is not None:
+        fp = np.ascontiguousarray(forced_idx, dtype=np.int32).reshape(T, k)
+        keep.append(fp)
+    bad = lib().oracle_moe_tokens(ctypes.byref(s), x.ctypes.data, T, _ptr(fp), out.ctypes.data,
+                                  idx.ctypes.data, w.ctypes.data, flag.ctypes.data, logits.ctypes.data)
+    return dict(out=out, idx=idx[:, :k], w=w[:, :k], flag=flag, logits=logits[:, :E], nan_tokens=int(bad))
