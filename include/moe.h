@@ -1,0 +1,175 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) small-batch W4A16 sigmoid-routed
+ * mixture-of-experts layer.
+ *
+ * The layer (pages: "Day-0 Support for Flint on vLLM", section "Model
+ * architecture"; "vLLM Flint" commentary, section "Only 14 of 49 layers
+ * retain full-history KV"): a pre-norm MoE block of hidden size H whose
+ * router scores 256 routed experts with a sigmoid and keeps the top 6,
+ * plus one shared expert; experts are SwiGLU MLPs.  Weights are NVFP4
+ * (E2M1 values, one E4M3 scale per 16 elements along K, one FP32 scale
+ * per tensor) executed weight-only with BF16 activations (W4A16), or BF16.
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are caller-owned device memory (hipMalloc or
+ *    torch tensors); the library allocates nothing, keeps no state between
+ *    calls and never synchronises.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    stream-ordered and asynchronous and may be captured into a HIP graph.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    on an error nothing is launched and the return value says why.  Faults
+ *    during kernel execution surface at the caller's next synchronisation.
+ *  - Activations are BF16 (raw 16-bit patterns), row-major [tokens][H].
+ *    Device pointers must be 16-byte aligned.  Inputs and outputs must not
+ *    alias.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or shape */
+  MOE_ERR_UNSUPPORTED = -2, /* valid request outside the fast path's shapes:
+                               the caller should use another implementation
+                               (the pages' dispatch falls back to standard
+                               layers off its fast path) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace too small */
+  MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_wtype {
+  MOE_W_BF16 = 0,  /* BF16 weights, row-major [out][in] */
+  MOE_W_NVFP4 = 1  /* NVFP4 weights in the runtime layout written by moe_repack_nvfp4 */
+} moe_wtype;
+
+/* Shape of one layer.  Routed and shared experts are SwiGLU MLPs:
+ *   y = W_down (SiLU(W_gate x) * (W_up x)),  W_gate, W_up: [inter][hidden],
+ *   W_down: [hidden][inter].
+ * n_experts == 0 describes a dense SwiGLU layer: only the "shared" expert,
+ * of width shared_inter, with no router (the first two layers of the model
+ * use a dense MLP). */
+typedef struct moe_layer_desc {
+  int32_t hidden;       /* H */
+  int32_t inter;        /* I, intermediate width of each routed expert */
+  int32_t shared_inter; /* Is, width of the shared expert; 0 = none */
+  int32_t n_experts;    /* E routed experts; 0 = dense layer */
+  int32_t top_k;        /* k experts kept per token, 1..8, <= E */
+  int32_t wtype;        /* moe_wtype of routed and shared expert weights */
+  float norm_eps;       /* RMSNorm epsilon, used when norm_gain != NULL */
+} moe_layer_desc;
+
+/* Weights of one layer (all device pointers). */
+typedef struct moe_layer_weights {
+  const void *router_w;  /* [E][H] BF16 (the router stays BF16 in both modes) */
+  const float *router_b; /* [E] FP32 logit offset, or NULL for zero */
+  const void *w_gate;    /* E matrices [I][H], back to back */
+  const void *w_up;      /* E matrices [I][H] */
+  const void *w_down;    /* E matrices [H][I] */
+  const float *w_scale;  /* [E][3] FP32 tensor scales (gate, up, down); NVFP4 only */
+  const void *sh_gate;   /* [Is][H] */
+  const void *sh_up;     /* [Is][H] */
+  const void *sh_down;   /* [H][Is] */
+  const float *sh_scale; /* [3] FP32 tensor scales; NVFP4 only */
+  const void *norm_gain; /* [H] BF16 RMSNorm gain, or NULL: no pre-norm */
+} moe_layer_weights;
+
+/* Bytes of one NVFP4 matrix [rows][cols], in either the GGUF-like source
+ * layout or the runtime layout (both hold rows*cols/2 nibble bytes plus
+ * rows*cols/16 scale bytes).  Returns 0 if rows % 8 or cols % 32 != 0. */
+size_t moe_nvfp4_matrix_bytes(int64_t rows, int64_t cols);
+
+/* Load-time lossless repack of NVFP4 matrices ("Day-0 Support for Flint on
+ * vLLM", section "Model architecture": the GGUF checkpoint holds NVIDIA
+ * NVFP4 blocks in a different byte order and is repacked without loss at
+ * load time).
+ *  src: device, n_mats matrices [rows][cols] back to back, each row-major
+ *       over rows, each row cols/16 blocks of 9 bytes: [E4M3 scale][8 bytes
+ *       of nibbles], nibble byte j holding element j (low nibble) and
+ *       element j+8 (high nibble) of the block.
+ *  dst: device, same size, runtime layout: per matrix a nibble plane
+ *       [rows][cols/2] with element 2i
+ *       in the low and 2i+1 in the high nibble of byte i, followed by a
+ *       scale plane of 16-byte tiles [rows/8][cols/32][8 rows][2 blocks].
+ *  nan_scale_count: device int32 or NULL; when given, the number of NaN
+ *       E4M3 scale bytes (0x7F, 0xFF) met is ADDED to it.
+ * Errors: INVALID_ARG for null src/dst, src == dst, rows % 8, cols % 32,
+ * non-positive sizes or misaligned pointers. */
+moe_status moe_repack_nvfp4(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                            int32_t *nan_scale_count, void *stream);
+
+/* Inverse of moe_repack_nvfp4 (runtime layout -> GGUF-like blocks); used to
+ * prove the repack lossless.  Same arguments and errors, no NaN count. */
+moe_status moe_unpack_nvfp4(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                            void *stream);
+
+/* Runtime-layout NVFP4 matrices -> FP32 [n_mats][rows][cols], element =
+ * E2M1 * E4M3 block scale * tensor_scale[m] (tensor_scale: device [n_mats]
+ * FP32, or NULL for 1), through the same per-element conversions the GEMV
+ * kernels use.  For inspection and tests; not on the decode path.
+ * Errors: INVALID_ARG as for moe_repack_nvfp4 (dst 16-byte aligned). */
+moe_status moe_dequant_nvfp4(const void *src, float *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                             const float *tensor_scale, void *stream);
+
+/* Workspace bytes moe_decode_layer needs for batches up to max_batch, or 0
+ * if the description is invalid. */
+size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch);
+
+/* One decode step of the layer for `batch` independent tokens, 1..8 (the
+ * low-latency path the pages describe for up to eight requests: "Day-0
+ * Support for Flint on vLLM", section "Optimizations").
+ *  x [batch][H] BF16 in; y [batch][H] BF16 out.
+ *  Per token: xn = x, or BF16(RMSNorm(x) * gain) when norm_gain is given;
+ *  logits l = W_r xn + b (FP32); the top_k experts by logit (ties: lower
+ *  index) are kept with weights s_j / sum s, s = sigmoid(l); each selected
+ *  expert and the shared expert run as SwiGLU with FP32 accumulation and a
+ *  BF16 rounding after each GEMV and after SiLU*up; the outputs are
+ *  combined in FP32 as sum_j w_j y_j + y_shared and rounded to BF16; with
+ *  `residual` != 0 the result is BF16(x + that).  Only the selected
+ *  experts' weights are read.
+ *  topk_idx [batch][k] int32, topk_w [batch][k] FP32: optional (NULL)
+ *  outputs, in descending score order.
+ *  ws: device workspace of ws_bytes >= moe_decode_workspace_bytes(desc,
+ *  batch).  It must be zero-filled before its first use; every call leaves
+ *  its internal counter at zero again, so it can be reused without
+ *  clearing.  Concurrent calls must not share a workspace.
+ * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
+ * for shapes the kernels do not tile (H/32 and I/32 must each be a power of
+ * two or a multiple of 64, E a multiple of 8 and at most 1024, Is == I when
+ * both routed and shared experts exist); INVALID_ARG for null required
+ * pointers, misalignment, top_k outside 1..8 or above E, H or I not a
+ * multiple of 32; WORKSPACE; HIP. */
+moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                            int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes moe_prefill_layer needs for up to n_tokens tokens. */
+size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
+
+/* The same layer over n_tokens >= 1 prompt tokens (prefill; the pages
+ * measure 8192-token prefill: "Day-0 Support for Flint on vLLM", section
+ * "Optimizations").  Same per-token definition and arguments as
+ * moe_decode_layer.  Tokens are grouped by expert and each expert runs as
+ * a matrix product on the matrix cores. */
+moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                             int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
+                             float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(moe_status s);
+
+/* The HIP runtime's description of the last HIP failure reported as
+ * MOE_ERR_HIP on the calling thread ("no HIP error" if none). */
+const char *moe_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,163 @@
+"""Python binding of libmoe.so, the MI355X small-batch W4A16 sigmoid-routed
+MoE layer.
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  PyTorch provides device memory and streams.  The entry points
+keep the C names (include/moe.h) and take device pointers as integers (or
+tensors, whose data_ptr() is used); `stream` defaults to torch's current
+stream.  A failing call raises MoeError with the library's status.
+
+The library must have been built (``python -m w4a16_routed_expert_sigmoid_amd.build``
+or ``__graft_entry__.build()``); importing fails loudly otherwise.
+"""
+import ctypes
+import os
+
+# PyTorch ships its own HIP runtime.  Load it first so that libmoe.so binds to
+# that same runtime instance (matched by soname) instead of a second copy
+# from the system ROCm, which would not share devices or memory with torch.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_W_BF16, MOE_W_NVFP4 = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        msg = f"{what}: {status_string(status)} ({status})"
+        if status == MOE_ERR_HIP:
+            msg += ": " + _lib.moe_last_error_detail().decode()
+        super().__init__(msg)
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("wtype", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
+
+
+class moe_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "router_b", "w_gate", "w_up", "w_down", "w_scale",
+        "sh_gate", "sh_up", "sh_down", "sh_scale", "norm_gain")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                      "(python -m w4a16_routed_expert_sigmoid_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_status_string.argtypes = [_i32]
+_lib.moe_last_error_detail.restype = ctypes.c_char_p
+_lib.moe_last_error_detail.argtypes = []
+_lib.moe_nvfp4_matrix_bytes.restype = _sz
+_lib.moe_nvfp4_matrix_bytes.argtypes = [_i64, _i64]
+_lib.moe_repack_nvfp4.restype = _i32
+_lib.moe_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
+_lib.moe_unpack_nvfp4.restype = _i32
+_lib.moe_unpack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp]
+_lib.moe_dequant_nvfp4.restype = _i32
+_lib.moe_dequant_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp]
+_lib.moe_decode_workspace_bytes.restype = _sz
+_lib.moe_decode_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32]
+_lib.moe_decode_layer.restype = _i32
+_lib.moe_decode_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
+                                  _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_prefill_workspace_bytes.restype = _sz
+_lib.moe_prefill_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32]
+_lib.moe_prefill_layer.restype = _i32
+_lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
+                                   _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+
+EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4", "moe_unpack_nvfp4",
+           "moe_dequant_nvfp4",
+           "moe_decode_workspace_bytes", "moe_decode_layer", "moe_prefill_workspace_bytes",
+           "moe_prefill_layer")
+
+
+def lib():
+    return _lib
+
+
+def _ptr(p):
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p
+    return p.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(st, what):
+    if st != MOE_OK:
+        raise MoeError(st, what)
+
+
+def status_string(st):
+    return _lib.moe_status_string(st).decode()
+
+
+def moe_status_string(st):
+    return status_string(st)
+
+
+def moe_last_error_detail():
+    return _lib.moe_last_error_detail().decode()
+
+
+def moe_nvfp4_matrix_bytes(rows, cols):
+    return _lib.moe_nvfp4_matrix_bytes(rows, cols)
+
+
+def moe_repack_nvfp4(src, dst, rows, cols, n_mats, nan_scale_count=None, stream=None):
+    _check(_lib.moe_repack_nvfp4(_ptr(src), _ptr(dst), rows, cols, n_mats, _ptr(nan_scale_count),
+                                 _stream(stream)), "moe_repack_nvfp4")
+
+
+def moe_unpack_nvfp4(src, dst, rows, cols, n_mats, stream=None):
+    _check(_lib.moe_unpack_nvfp4(_ptr(src), _ptr(dst), rows, cols, n_mats, _stream(stream)),
+           "moe_unpack_nvfp4")
+
+
+def moe_dequant_nvfp4(src, dst, rows, cols, n_mats, tensor_scale=None, stream=None):
+    _check(_lib.moe_dequant_nvfp4(_ptr(src), _ptr(dst), rows, cols, n_mats, _ptr(tensor_scale), _stream(stream)),
+           "moe_dequant_nvfp4")
+
+
+def moe_decode_workspace_bytes(desc, max_batch):
+    return _lib.moe_decode_workspace_bytes(ctypes.byref(desc), max_batch)
+
+
+def moe_decode_layer(desc, weights, x, batch, residual, y, topk_idx=None, topk_w=None, ws=None, ws_bytes=0,
+                     stream=None):
+    _check(_lib.moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, int(residual),
+                                 _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_decode_layer")
+
+
+def moe_prefill_workspace_bytes(desc, n_tokens):
+    return _lib.moe_prefill_workspace_bytes(ctypes.byref(desc), n_tokens)
+
+
+def moe_prefill_layer(desc, weights, x, n_tokens, residual, y, topk_idx=None, topk_w=None, ws=None,
+                      ws_bytes=0, stream=None):
+    _check(_lib.moe_prefill_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), n_tokens, int(residual),
+                                  _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_prefill_layer")
+
+
+from .layer import DeviceLayer  # noqa: E402  (device memory holder for one layer)

@@ -1,0 +1,245 @@
+// C ABI of the library: argument validation, workspace layout and dispatch.
+// Every check runs on the host before anything is enqueued, so each error
+// path can be exercised without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// The last failing HIP call of this thread, for moe_last_error_detail().
+thread_local hipError_t g_last_hip = hipSuccess;
+
+inline moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = e;
+  return MOE_ERR_HIP;
+}
+
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct WsLayout {
+  size_t counter, logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, bytes;
+};
+
+inline int max_routed_of(const moe_layer_desc &d, int B) {
+  if (d.n_experts <= 0) return 0;
+  int m = B * d.top_k;
+  return m < d.n_experts ? m : d.n_experts;
+}
+
+WsLayout decode_layout(const moe_layer_desc &d, int B) {
+  WsLayout L;
+  const size_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = d.n_experts > 0 ? d.top_k : 0;
+  const size_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  const size_t R = max_routed_of(d, B);
+  size_t o = 0;
+  L.counter = o; o += up(4);
+  L.logits = o; o += up(B * E * 4);
+  L.xn = o; o += up(B * H * 2);
+  L.n_routed = o; o += up(4);
+  L.entry_expert = o; o += up(R * 4);
+  L.entry_mask = o; o += up(R * 4);
+  L.entry_w = o; o += up(R * kMaxBatch * 4);
+  L.topk_idx = o; o += up(B * k * 4);
+  L.topk_w = o; o += up(B * k * 4);
+  L.h = o; o += up((R + 1) * B * Imax * 2);
+  L.bytes = o;
+  return L;
+}
+
+// Shape checks shared by the decode calls.  Returns MOE_OK or the error.
+moe_status check_desc(const moe_layer_desc *d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->hidden % 32) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts < 0 || d->inter < 0 || d->shared_inter < 0) return MOE_ERR_INVALID_ARG;
+  if (d->wtype != MOE_W_BF16 && d->wtype != MOE_W_NVFP4) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts == 0 && d->shared_inter == 0) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts > 0) {
+    if (d->inter <= 0 || d->inter % 32) return MOE_ERR_INVALID_ARG;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->shared_inter % 32) return MOE_ERR_INVALID_ARG;
+  if (!(d->norm_eps >= 0.0f) || isinf(d->norm_eps)) return MOE_ERR_INVALID_ARG;
+  // Shapes the kernels tile.
+  if (d->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!k_tileable(d->hidden)) return MOE_ERR_UNSUPPORTED;
+  if (d->n_experts > 0 && !k_tileable(d->inter)) return MOE_ERR_UNSUPPORTED;
+  if (d->shared_inter > 0 && !k_tileable(d->shared_inter)) return MOE_ERR_UNSUPPORTED;
+  if (d->n_experts > 0 && d->shared_inter > 0 && d->shared_inter != d->inter) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_layer_desc *d, const moe_layer_weights *w) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  const bool fp4 = d->wtype == MOE_W_NVFP4;
+  if (d->n_experts > 0) {
+    if (!w->router_w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+    if (fp4 && !w->w_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->router_w, 16) || !aligned(w->w_gate, 16) || !aligned(w->w_up, 16) ||
+        !aligned(w->w_down, 16))
+      return MOE_ERR_INVALID_ARG;
+    if ((w->router_b && !aligned(w->router_b, 4)) || (w->w_scale && !aligned(w->w_scale, 4)))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (d->shared_inter > 0) {
+    if (!w->sh_gate || !w->sh_up || !w->sh_down) return MOE_ERR_INVALID_ARG;
+    if (fp4 && !w->sh_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->sh_gate, 16) || !aligned(w->sh_up, 16) || !aligned(w->sh_down, 16))
+      return MOE_ERR_INVALID_ARG;
+    if (w->sh_scale && !aligned(w->sh_scale, 4)) return MOE_ERR_INVALID_ARG;
+  }
+  if (w->norm_gain && !aligned(w->norm_gain, 2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_nvfp4_matrix_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 8 || cols % 32) return 0;
+  return (size_t)nvfp4_matrix_bytes(rows, cols);
+}
+
+static moe_status check_repack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
+  if (!src || !dst || src == dst) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+  // The two ranges must not overlap.
+  const uintptr_t s = (uintptr_t)src, t = (uintptr_t)dst;
+  const uintptr_t n = (uintptr_t)(n_mats * nvfp4_matrix_bytes(rows, cols));
+  if (s < t + n && t < s + n) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status moe_repack_nvfp4(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                            int32_t *nan_scale_count, void *stream) {
+  moe_status st = check_repack(src, dst, rows, cols, n_mats);
+  if (st != MOE_OK) return st;
+  if (nan_scale_count && !aligned(nan_scale_count, 4)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_repack(src, dst, rows, cols, n_mats, nan_scale_count, (hipStream_t)stream));
+}
+
+moe_status moe_unpack_nvfp4(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                            void *stream) {
+  moe_status st = check_repack(src, dst, rows, cols, n_mats);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_unpack(src, dst, rows, cols, n_mats, (hipStream_t)stream));
+}
+
+moe_status moe_dequant_nvfp4(const void *src, float *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                             const float *tensor_scale, void *stream) {
+  if (!src || !dst || (const void *)dst == src) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+  if (tensor_scale && !aligned(tensor_scale, 4)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t s = (uintptr_t)src, t = (uintptr_t)dst;
+  const uintptr_t ns = (uintptr_t)(n_mats * nvfp4_matrix_bytes(rows, cols)), nt = (uintptr_t)(n_mats * rows * cols * 4);
+  if (s < t + nt && t < s + ns) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dequant(src, dst, rows, cols, n_mats, tensor_scale, (hipStream_t)stream));
+}
+
+size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch) {
+  if (check_desc(desc) != MOE_OK || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  return decode_layout(*desc, max_batch).bytes;
+}
+
+moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                            int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  // The router stages the batch's activations in 64 KiB of LDS.
+  if ((size_t)batch * desc->hidden * 2 > 65536) return MOE_ERR_UNSUPPORTED;
+  st = check_weights(desc, w);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !ws || x == y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID_ARG;
+  const WsLayout L = decode_layout(*desc, batch);
+  if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+
+  uint8_t *base = (uint8_t *)ws;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.H = desc->hidden;
+  a.I = desc->n_experts > 0 ? desc->inter : 0;
+  a.Is = desc->shared_inter;
+  a.E = desc->n_experts;
+  a.k = desc->n_experts > 0 ? desc->top_k : 0;
+  a.B = batch;
+  a.residual = residual ? 1 : 0;
+  a.use_norm = w->norm_gain ? 1 : 0;
+  a.max_routed = max_routed_of(*desc, batch);
+  a.wtype = desc->wtype;
+  a.eps = desc->norm_eps;
+  a.x = (const uint16_t *)x;
+  a.y = (uint16_t *)y;
+  a.router_w = (const uint16_t *)w->router_w;
+  a.router_b = w->router_b;
+  a.w_gate = (const uint8_t *)w->w_gate;
+  a.w_up = (const uint8_t *)w->w_up;
+  a.w_down = (const uint8_t *)w->w_down;
+  a.w_scale = w->w_scale;
+  a.sh_gate = (const uint8_t *)w->sh_gate;
+  a.sh_up = (const uint8_t *)w->sh_up;
+  a.sh_down = (const uint8_t *)w->sh_down;
+  a.sh_scale = w->sh_scale;
+  a.norm_gain = (const uint16_t *)w->norm_gain;
+  a.ws.counter = (uint32_t *)(base + L.counter);
+  a.ws.logits = (float *)(base + L.logits);
+  a.ws.xn = (uint16_t *)(base + L.xn);
+  a.ws.n_routed = (int32_t *)(base + L.n_routed);
+  a.ws.entry_expert = (int32_t *)(base + L.entry_expert);
+  a.ws.entry_mask = (uint32_t *)(base + L.entry_mask);
+  a.ws.entry_w = (float *)(base + L.entry_w);
+  a.ws.topk_idx = (int32_t *)(base + L.topk_idx);
+  a.ws.topk_w = (float *)(base + L.topk_w);
+  a.ws.h = (uint16_t *)(base + L.h);
+  a.ws.bytes = L.bytes;
+  a.out_idx = topk_idx ? topk_idx : a.ws.topk_idx;
+  a.out_w = topk_w ? topk_w : a.ws.topk_w;
+  return hip_status(launch_decode(a, (hipStream_t)stream));
+}
+
+size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {
+  (void)desc;
+  (void)n_tokens;
+  return 0;
+}
+
+moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                             int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
+                             float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  (void)desc; (void)w; (void)x; (void)n_tokens; (void)residual; (void)y;
+  (void)topk_idx; (void)topk_w; (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+const char *moe_last_error_detail(void) {
+  return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
+}
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or batch for this path";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
