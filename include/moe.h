@@ -140,9 +140,9 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  *  its internal counter at zero again, so it can be reused without
  *  clearing.  Concurrent calls must not share a workspace.
  * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
- * for shapes the kernels do not tile (H/32 and I/32 must each be a power of
- * two or a multiple of 64, E a multiple of 8 and at most 1024, Is == I when
- * both routed and shared experts exist); INVALID_ARG for null required
+ * for shapes the kernels do not tile (H/32, I/32 and Is/32 must each be at
+ * least 2 and either a power of two or at least 64; E at most 1024; Is == I
+ * when both routed and shared experts exist; batch * H * 2 <= 64 KiB); INVALID_ARG for null required
  * pointers, misalignment, top_k outside 1..8 or above E, H or I not a
  * multiple of 32; WORKSPACE; HIP. */
 moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
@@ -163,6 +163,15 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
 
 /* Static description of a status code. */
 const char *moe_status_string(moe_status s);
+
+/* Measurement hook.  With 6 hipEvent_t handles set, every later
+ * moe_decode_layer call on this thread records events[0]/[1] before/after
+ * its router stage, [2]/[3] around the gate/up stage and [4]/[5] around the
+ * down-and-combine stage, on the call's stream (also under graph capture).
+ * events == NULL or n_events == 0 turns it off.  The events stay owned by
+ * the caller.  Errors: INVALID_ARG for n_events other than 0 or 6 or a
+ * null handle. */
+moe_status moe_set_stage_events(void *const *events, int32_t n_events);
 
 /* The HIP runtime's description of the last HIP failure reported as
  * MOE_ERR_HIP on the calling thread ("no HIP error" if none). */

@@ -102,6 +102,7 @@ def test_decode_call_errors(kw, want):
     (dict(norm_eps=float("nan")), m.MOE_ERR_INVALID_ARG),
     (dict(n_experts=-1), m.MOE_ERR_INVALID_ARG),
     (dict(hidden=96), m.MOE_ERR_UNSUPPORTED),        # 3 chunks per row: not tiled
+    (dict(inter=32, shared_inter=32), m.MOE_ERR_UNSUPPORTED),  # one chunk per row: not tiled
     (dict(inter=96, shared_inter=96), m.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=2048), m.MOE_ERR_UNSUPPORTED),
     (dict(shared_inter=1024), m.MOE_ERR_UNSUPPORTED),  # shared width != routed width

@@ -111,7 +111,7 @@ def test_decode_small_norm_residual(B):
 
 
 def test_decode_all_experts_selected():
-    L = synth.make_layer(13, hidden=128, inter=32, shared_inter=32, n_experts=8, top_k=8)
+    L = synth.make_layer(13, hidden=128, inter=64, shared_inter=64, n_experts=8, top_k=8)
     x = synth.tokens(3, 128, stream=5)
     out, idx, w = run(L, x)
     assert all(sorted(r) == list(range(8)) for r in idx.tolist())

@@ -56,6 +56,8 @@ _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [_i32]
 _lib.moe_last_error_detail.restype = ctypes.c_char_p
 _lib.moe_last_error_detail.argtypes = []
+_lib.moe_set_stage_events.restype = _i32
+_lib.moe_set_stage_events.argtypes = [ctypes.POINTER(_vp), _i32]
 _lib.moe_nvfp4_matrix_bytes.restype = _sz
 _lib.moe_nvfp4_matrix_bytes.argtypes = [_i64, _i64]
 _lib.moe_repack_nvfp4.restype = _i32
@@ -75,7 +77,7 @@ _lib.moe_prefill_layer.restype = _i32
 _lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
                                    _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 
-EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4", "moe_unpack_nvfp4",
+EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_set_stage_events", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4", "moe_unpack_nvfp4",
            "moe_dequant_nvfp4",
            "moe_decode_workspace_bytes", "moe_decode_layer", "moe_prefill_workspace_bytes",
            "moe_prefill_layer")
@@ -117,6 +119,15 @@ def moe_status_string(st):
 
 def moe_last_error_detail():
     return _lib.moe_last_error_detail().decode()
+
+
+def moe_set_stage_events(events):
+    """events: None, or 6 torch.cuda.Event (created with enable_timing=True)."""
+    if not events:
+        _check(_lib.moe_set_stage_events(None, 0), "moe_set_stage_events")
+        return
+    arr = (_vp * len(events))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
+    _check(_lib.moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
 
 
 def moe_nvfp4_matrix_bytes(rows, cols):

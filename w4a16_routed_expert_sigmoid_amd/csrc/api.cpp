@@ -17,6 +17,10 @@ constexpr size_t kAlign = 256;
 // The last failing HIP call of this thread, for moe_last_error_detail().
 thread_local hipError_t g_last_hip = hipSuccess;
 
+// Stage events set by moe_set_stage_events (per thread).
+thread_local hipEvent_t g_stage_events[6];
+thread_local bool g_stage_events_on = false;
+
 inline moe_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   g_last_hip = e;
@@ -210,7 +214,7 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
   a.ws.bytes = L.bytes;
   a.out_idx = topk_idx ? topk_idx : a.ws.topk_idx;
   a.out_w = topk_w ? topk_w : a.ws.topk_w;
-  return hip_status(launch_decode(a, (hipStream_t)stream));
+  return hip_status(launch_decode(a, (hipStream_t)stream, g_stage_events_on ? g_stage_events : nullptr));
 }
 
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {
@@ -225,6 +229,19 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
   (void)desc; (void)w; (void)x; (void)n_tokens; (void)residual; (void)y;
   (void)topk_idx; (void)topk_w; (void)ws; (void)ws_bytes; (void)stream;
   return MOE_ERR_UNSUPPORTED;
+}
+
+moe_status moe_set_stage_events(void *const *events, int32_t n_events) {
+  if (!events || n_events == 0) {
+    g_stage_events_on = false;
+    return MOE_OK;
+  }
+  if (n_events != 6) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i) g_stage_events[i] = (hipEvent_t)events[i];
+  g_stage_events_on = true;
+  return MOE_OK;
 }
 
 const char *moe_last_error_detail(void) {

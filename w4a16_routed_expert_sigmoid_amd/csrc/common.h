@@ -17,6 +17,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -38,8 +40,10 @@ __host__ __device__ inline int lanes_per_row(int k) {
   return c >= kWave ? kWave : c;
 }
 
+// A reduction dimension the GEMV kernels tile: at least two 32-element
+// chunks, and either a power of two of them or at least one per lane.
 __host__ inline bool k_tileable(int64_t k) {
-  if (k <= 0 || k % 32) return false;
+  if (k < 64 || k % 32) return false;
   int64_t c = k / 32;
   return c >= kWave || (c & (c - 1)) == 0;
 }
@@ -57,14 +61,10 @@ __device__ inline uint32_t f32_to_bf16(float f) {
 
 __device__ inline float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
-// E4M3FN byte -> FP32: exponent field e (bias 7), mantissa m; e == 0 is
-// subnormal m * 2^-9; S.1111.111 is NaN.
-__device__ inline float e4m3_to_f32(uint32_t c) {
-  uint32_t em = c & 0x7fu;
-  float v = (em >= 8u) ? __uint_as_float((em << 20) + 0x3c000000u) : (float)em * 0x1p-9f;
-  if (em == 0x7fu) v = __uint_as_float(0x7fc00000u);
-  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
-}
+// E4M3FN byte (low 8 bits of c) -> FP32 with the hardware conversion; on
+// gfx950 it decodes the OCP E4M3FN format (bias 7, subnormals, S.1111.111 =
+// NaN), which the exhaustive code test checks against the format table.
+__device__ inline float e4m3_to_f32(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // Two FP4 (E2M1) values of byte `sel` of w -> two BF16 (exact).
 #define MOE_FP4X2_TO_BF16X2(w, sel) __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((w), 1.0f, (sel))
@@ -90,9 +90,74 @@ __device__ inline float dot8_fp4_bf16(uint32_t w, uint32_t x0, uint32_t x1, uint
   return acc;
 }
 
+// value of lane ^ O for a compile-time O: DPP within 16-lane rows (xor 1,
+// 2, 4, 8), the gfx950 cross-row swaps for 16 and 32.  No LDS round trip.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int O, typename T>
+__device__ inline T xor_lane(T v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "xor offset");
+  if constexpr (O == 1) return dpp<0xB1>(v);                   // quad_perm [1,0,3,2]
+  else if constexpr (O == 2) return dpp<0x4E>(v);              // quad_perm [2,3,0,1]
+  else if constexpr (O == 4) return dpp<0x1B>(dpp<0x141>(v));  // row_half_mirror, quad_perm [3,2,1,0]
+  else if constexpr (O == 8) return dpp<0x128>(v);             // row_ror:8
+  else {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const bool hi = (threadIdx.x & O) != 0;
+    if constexpr (O == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      return __builtin_bit_cast(T, hi ? (uint32_t)r[0] : (uint32_t)r[1]);
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      return __builtin_bit_cast(T, hi ? (uint32_t)r[0] : (uint32_t)r[1]);
+    }
+  }
+}
+
+// xor_lane with an offset that is a compile-time constant after unrolling.
+template <typename T>
+__device__ inline T xor_lane_n(T v, int o) {
+  switch (o) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
+  }
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled at
+// compile time (so register arrays indexed by I stay in registers).
+template <int I, int N>
+struct StaticFor {
+  template <typename F>
+  __device__ static __forceinline__ void run(F &&f) {
+    f(std::integral_constant<int, I>());
+    StaticFor<I + 1, N>::run(f);
+  }
+};
+template <int N>
+struct StaticFor<N, N> {
+  template <typename F>
+  __device__ static __forceinline__ void run(F &&) {}
+};
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ inline float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (width > 1) v += xor_lane<1>(v);
+  if (width > 2) v += xor_lane<2>(v);
+  if (width > 4) v += xor_lane<4>(v);
+  if (width > 8) v += xor_lane<8>(v);
+  if (width > 16) v += xor_lane<16>(v);
+  if (width > 32) v += xor_lane<32>(v);
   return v;
 }
 
@@ -129,7 +194,7 @@ struct DecodeArgs {
   DecodeWs ws;
 };
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
 hipError_t launch_repack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
                          int32_t *nan_count, hipStream_t stream);
 hipError_t launch_unpack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,

@@ -1,17 +1,25 @@
 // Small-batch (1..8 tokens) decode path of the sigmoid-routed W4A16 MoE
-// layer: three kernels per layer.
+// layer: three kernels per layer and no cross-block synchronisation inside a
+// kernel (on this GPU a device-scope atomic on one address serialises across
+// blocks and an agent-scope fence writes back the L2, so the stages are
+// separated by kernel boundaries instead).
 //
-//   k_router_topk  pre-norm (optional), router GEMV (BF16 weights, FP32
-//                  accumulation), then -- in the last workgroup to finish --
-//                  sigmoid top-k, renormalisation and the list of distinct
-//                  selected experts with their token masks and weights.
-//   k_gateup       for every (selected or shared expert, 8-row group):
-//                  gate and up GEMVs on NVFP4 (or BF16) weights decoded in
-//                  registers, BF16 rounding of g and u, h = BF16(SiLU(g) u).
-//   k_down         for every 8-row group of the output: the down GEMV of
-//                  every selected expert and the shared expert, BF16
-//                  rounding per expert, weighted FP32 combine, BF16 output
-//                  (plus the residual when asked).
+//   k_router   pre-norm (optional, in registers) and router GEMV: logits
+//              l = W_r xn + b in FP32, one row per lane group.
+//   k_route    (batches of 2..8 tokens) one block: sigmoid top-k of every
+//              token, the sorted list of distinct selected experts with
+//              token masks, the renormalised combine weights.
+//   k_gateup   (one token: every block first recomputes the top-k from the
+//              1 KB of logits, which is cheaper than another launch, and
+//              block 0 publishes the list) then runs its share of the gate
+//              and up GEMVs of one selected (or the shared) expert: FP4
+//              decoded to BF16 in registers once and reused for every token
+//              routed to the expert, FP32 accumulation, BF16 rounding of g
+//              and u, h = BF16(SiLU(g) u).
+//   k_down     for every 4-row group of the output: the down GEMV of every
+//              selected expert and of the shared expert, BF16 rounding per
+//              expert, weighted FP32 combine in a fixed order, BF16 output
+//              (plus the residual when asked).
 //
 // What is computed follows "Day-0 Support for Flint on vLLM" (sections
 // "Model architecture" and "Optimizations"): 256 experts, sigmoid top-6
@@ -21,310 +29,459 @@
 
 namespace moe {
 
-constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
-
 // ---------------------------------------------------------------------------
-// Router: logits, then top-k and the expert work list in the last block.
+// Wave-level helpers
 // ---------------------------------------------------------------------------
 
-// Better candidate: larger logit, then lower expert index.
-__device__ inline bool cand_better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-__global__ __launch_bounds__(kBlock) void k_router_topk(DecodeArgs a) {
-  extern __shared__ uint16_t s_x[];  // [B][H] BF16: x or its pre-norm
-  __shared__ uint32_t s_mark[kMaxExperts];
-  __shared__ int32_t s_sel[kMaxBatch][kMaxTopK];
-  __shared__ float s_selw[kMaxBatch][kMaxTopK];
-  __shared__ float s_red[kWavesPerBlock][kMaxBatch];
-  __shared__ float s_inv[kMaxBatch];
-  __shared__ int s_last;
-
-  const int H = a.H, E = a.E, B = a.B;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-
-  // Stage x (or BF16(RMSNorm(x) * gain)) in LDS.
-  if (a.use_norm) {
-    float ss[kMaxBatch];
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.f;
-    for (int t = 0; t < B; ++t)
-      for (int i = tid; i < H; i += kBlock) {
-        float v = bf16_to_f32(a.x[(int64_t)t * H + i]);
-        ss[t] += v * v;
-      }
-    for (int t = 0; t < B; ++t) {
-      float v = group_sum(ss[t], kWave);
-      if (lane == 0) s_red[wave][t] = v;
-    }
-    __syncthreads();
-    if (tid < B) {
-      float v = 0.f;
-      for (int w = 0; w < kWavesPerBlock; ++w) v += s_red[w][tid];
-      s_inv[tid] = 1.0f / sqrtf(v / (float)H + a.eps);
-    }
-    __syncthreads();
-    for (int t = 0; t < B; ++t)
-      for (int i = tid; i < H; i += kBlock) {
-        float v = bf16_to_f32(a.x[(int64_t)t * H + i]) * s_inv[t] * bf16_to_f32(a.norm_gain[i]);
-        uint16_t r = (uint16_t)f32_to_bf16(v);
-        s_x[t * H + i] = r;
-        if (blockIdx.x == 0) a.ws.xn[(int64_t)t * H + i] = r;
-      }
-  } else {
-    for (int i = tid; i < B * H; i += kBlock) s_x[i] = a.x[i];
+// Fold-reduce 4 values over aligned groups of W lanes (W a power of two,
+// 2..64): step 1 exchanges two of them with lane ^ 1, step 2 one with
+// lane ^ 2, then plain sums over the remaining lane bits; 2 + 1 + (log2(W)
+// - 2) lane exchanges instead of 4 * log2(W).  Returns the group total of
+// value index `row` = 2*(lane bit 0) + (lane bit 1) (with W == 2 the lane
+// also keeps row + 1's total in *second).  Written on scalars so that no
+// register array gets a runtime index.
+__device__ __forceinline__ float fold4(float v0, float v1, float v2, float v3, int W, int &row, float *second) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool u1 = (lane & 1) != 0, u2 = (lane & 2) != 0;
+  // step o = 1: lower lanes keep values 0,1; upper lanes keep 2,3
+  const float n0 = (u1 ? v2 : v0) + xor_lane<1>(u1 ? v0 : v2);
+  const float n1 = (u1 ? v3 : v1) + xor_lane<1>(u1 ? v1 : v3);
+  row = u1 ? 2 : 0;
+  if (W <= 2) {
+    if (second) *second = n1;
+    return n0;
   }
-  __syncthreads();
-  if (E == 0) return;  // dense layer: only the pre-norm was wanted
-
-  // One expert row per lane group; a lane owns 32-element chunks.
-  const int LPR = lanes_per_row(H), C = H / 32;
-  const int groups = kBlock / LPR;
-  const int row = blockIdx.x * groups + tid / LPR;
-  const int lg = tid % LPR;
-  if (row < E) {
-    float acc[kMaxBatch];
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(a.router_w + (int64_t)row * H);
-    for (int c = lg; c < C; c += LPR) {
-      uint4 w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = wrow[c * 4 + q];
-      for (int t = 0; t < B; ++t) {
-        const uint4 *xr = reinterpret_cast<const uint4 *>(s_x + t * H) + c * 4;
-        float s = acc[t];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint4 xv = xr[q];
-          s = dot2_bf16(w[q].x, xv.x, s);
-          s = dot2_bf16(w[q].y, xv.y, s);
-          s = dot2_bf16(w[q].z, xv.z, s);
-          s = dot2_bf16(w[q].w, xv.w, s);
-        }
-        acc[t] = s;
-      }
-    }
-    const float bias = a.router_b ? a.router_b[row] : 0.f;
-    for (int t = 0; t < B; ++t) {
-      float v = group_sum(acc[t], LPR);
-      if (lg == 0) a.ws.logits[t * E + row] = v + bias;
-    }
-  } else {
-    // Rows past E: the shuffles above are group-local, nothing to do.
-  }
-
-  // Completion count: the last block to finish selects the experts.
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    unsigned prev = atomicAdd(a.ws.counter, 1u);
-    s_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  for (int e = tid; e < E; e += kBlock) s_mark[e] = 0u;
-  __syncthreads();
-
-  // Top-k per token, one wave per token.
-  for (int t = wave; t < B; t += kWavesPerBlock) {
-    const float *lt = a.ws.logits + t * E;
-    float v[kMaxExperts / kWave];
-    const int per = (E + kWave - 1) / kWave;
-#pragma unroll
-    for (int j = 0; j < kMaxExperts / kWave; ++j) {
-      int e = lane + j * kWave;
-      float lv = (j < per && e < E) ? lt[e] : -INFINITY;
-      v[j] = (lv != lv) ? -INFINITY : lv;  // NaN never wins over a number
-    }
-    uint32_t taken = 0;  // bit j: candidate j of this lane already selected
-    float selv[kMaxTopK];
-    int seli[kMaxTopK];
-    for (int r = 0; r < a.k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < kMaxExperts / kWave; ++j) {
-        int e = lane + j * kWave;
-        if (j < per && e < E && !((taken >> j) & 1u) && cand_better(v[j], e, bv, bi)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o, kWave);
-        int oi = __shfl_xor(bi, o, kWave);
-        if (cand_better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-      selv[r] = bv;
-      seli[r] = bi;
-    }
-    if (lane == 0) {
-      float s[kMaxTopK], sum = 0.f;
-      for (int r = 0; r < a.k; ++r) {
-        // The logit of a selected expert: re-read it (the reduction kept
-        // -inf for NaN, which only matters for NaN input).
-        float l = lt[seli[r]];
-        s[r] = 1.0f / (1.0f + expf(-l));
-        sum += s[r];
-      }
-      for (int r = 0; r < a.k; ++r) {
-        float w = s[r] / sum;
-        s_sel[t][r] = seli[r];
-        s_selw[t][r] = w;
-        a.out_idx[t * a.k + r] = seli[r];
-        a.out_w[t * a.k + r] = w;
-        atomicOr(&s_mark[seli[r]], 1u << t);
-      }
-      (void)selv;
-    }
-  }
-  __syncthreads();
-
-  // Distinct experts in ascending order with token masks and weights.
-  if (wave == 0) {
-    int count = 0;
-    for (int base = 0; base < E; base += kWave) {
-      int e = base + lane;
-      uint32_t m = (e < E) ? s_mark[e] : 0u;
-      unsigned long long ball = __ballot(m != 0u);
-      int pre = __popcll(ball & ((1ull << lane) - 1ull));
-      if (m) {
-        int slot = count + pre;
-        a.ws.entry_expert[slot] = e;
-        a.ws.entry_mask[slot] = m;
-        for (int t = 0; t < kMaxBatch; ++t) {
-          float w = 0.f;
-          if (t < B)
-            for (int r = 0; r < a.k; ++r)
-              if (s_sel[t][r] == e) w = s_selw[t][r];
-          a.ws.entry_w[slot * kMaxBatch + t] = w;
-        }
-      }
-      count += __popcll(ball);
-    }
-    if (lane == 0) {
-      *a.ws.n_routed = count;
-      __hip_atomic_store(a.ws.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Expert GEMV building blocks
-// ---------------------------------------------------------------------------
-
-// One lane's share of 8 rows x one 32-element chunk of an NVFP4 matrix:
-// acc[r] += sum over the chunk of W[row0 + r][.] * x[.], before the tensor
-// scale.  nib: 8 nibble loads (one per row), sc: the chunk's scale tile.
-__device__ inline void nvfp4_chunk8(const uint4 (&nib)[8], const uint4 &sc, const uint4 (&xv)[4],
-                                    float (&acc)[8]) {
-  const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
-  const uint32_t xw[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
-                           xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const uint32_t nw[4] = {nib[r].x, nib[r].y, nib[r].z, nib[r].w};
-    float p0 = 0.f, p1 = 0.f;
-    p0 = dot8_fp4_bf16(nw[0], xw[0], xw[1], xw[2], xw[3], p0);
-    p0 = dot8_fp4_bf16(nw[1], xw[4], xw[5], xw[6], xw[7], p0);
-    p1 = dot8_fp4_bf16(nw[2], xw[8], xw[9], xw[10], xw[11], p1);
-    p1 = dot8_fp4_bf16(nw[3], xw[12], xw[13], xw[14], xw[15], p1);
-    // scale bytes of row r: 2r (block 2c) and 2r+1 (block 2c+1)
-    uint32_t sword = scw[r >> 1] >> ((r & 1) * 16);
-    float s0 = e4m3_to_f32(sword & 0xffu), s1 = e4m3_to_f32((sword >> 8) & 0xffu);
-    acc[r] = fmaf(s0, p0, fmaf(s1, p1, acc[r]));
-  }
-}
-
-__device__ inline void load_chunk8_nvfp4(const uint8_t *m, int64_t N, int64_t K, int rg, int c,
-                                         uint4 (&nib)[8], uint4 &sc) {
-  const int64_t rowb = K / 2;
-  const uint8_t *p = m + (int64_t)(rg * 8) * rowb + (int64_t)c * 16;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) nib[r] = *reinterpret_cast<const uint4 *>(p + r * rowb);
-  sc = *reinterpret_cast<const uint4 *>(m + N * K / 2 + ((int64_t)rg * (K / 32) + c) * 16);
-}
-
-__device__ inline void load_x_chunk(const uint16_t *xrow, int c, uint4 (&xv)[4]) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(xrow) + c * 4;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) xv[q] = p[q];
-}
-
-// BF16 weights: acc[r] += W[row0 + r][32c .. 32c+31] . x chunk, 8 rows.
-__device__ inline void bf16_chunk8(const uint16_t *m, int64_t K, int rg, int c, const uint4 (&xv)[4],
-                                   float (&acc)[8]) {
-  const uint32_t xw[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
-                           xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(m + (int64_t)(rg * 8 + r) * K) + c * 4;
-    float s = acc[r];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 w = p[q];
-      s = dot2_bf16(w.x, xw[q * 4 + 0], s);
-      s = dot2_bf16(w.y, xw[q * 4 + 1], s);
-      s = dot2_bf16(w.z, xw[q * 4 + 2], s);
-      s = dot2_bf16(w.w, xw[q * 4 + 3], s);
-    }
-    acc[r] = s;
-  }
-}
-
-// Value of register-array element i for lane-dependent i without dynamic
-// register indexing.
-__device__ inline float pick8(const float (&v)[8], int i) {
-  float r = 0.f;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) r = (i == q) ? v[q] : r;
+  // step o = 2
+  float r = (u2 ? n1 : n0) + xor_lane<2>(u2 ? n0 : n1);
+  row += u2 ? 1 : 0;
+  if (W > 4) r += xor_lane<4>(r);
+  if (W > 8) r += xor_lane<8>(r);
+  if (W > 16) r += xor_lane<16>(r);
+  if (W > 32) r += xor_lane<32>(r);
   return r;
 }
 
+// Orderable 32-bit image of a logit: larger logit -> larger key; NaN ranks
+// as -inf; 0 is below every real key and marks "taken / absent".
+__device__ __forceinline__ uint32_t topk_key(float l) {
+  if (l != l) l = -INFINITY;
+  const uint32_t u = __float_as_uint(l);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float topk_key_logit(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = max(m, xor_lane<1>(m));
+  m = max(m, xor_lane<2>(m));
+  m = max(m, xor_lane<4>(m));
+  m = max(m, xor_lane<8>(m));
+  m = max(m, xor_lane<16>(m));
+  m = max(m, xor_lane<32>(m));
+  return m;
+}
+
+// Top-k experts of one token's logits by one wave: sel[0..k) in descending
+// logit order, ties to the lower expert index; selv = their logits.  Lane l
+// holds experts l, l+64, ... (J per lane, E <= 64*J).  Each round: a wave
+// max of the 32-bit keys, then ballots find the lowest expert index holding
+// it.  Results are wave-uniform.
+template <int J>
+__device__ __forceinline__ void wave_topk(const float *lt, int E, int k, int (&sel)[kMaxTopK],
+                                          float (&selv)[kMaxTopK]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + j * kWave;
+    key[j] = (e < E) ? topk_key(lt[e]) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    if (r < k) {
+      uint32_t m = key[0];
+#pragma unroll
+      for (int j = 1; j < J; ++j) m = max(m, key[j]);
+      m = wave_max_u32(m);
+      // lowest expert index with key m: first j with a match, lowest lane
+      int e = 0x7fffffff;
+#pragma unroll
+      for (int j = J - 1; j >= 0; --j) {
+        const unsigned long long b = __ballot(key[j] == m);
+        if (b) e = j * kWave + (int)__builtin_ctzll(b);
+      }
+      sel[r] = e;
+      selv[r] = topk_key_logit(m);
+#pragma unroll
+      for (int j = 0; j < J; ++j) key[j] = (lane + j * kWave == e) ? 0u : key[j];
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_topk_any(const float *lt, int E, int k, int (&sel)[kMaxTopK],
+                                              float (&selv)[kMaxTopK]) {
+  if (E <= 4 * kWave) wave_topk<4>(lt, E, k, sel, selv);
+  else wave_topk<kMaxExperts / kWave>(lt, E, k, sel, selv);
+}
+
 // ---------------------------------------------------------------------------
-// Gate/up + SiLU*up
+// Chunk math: one lane's 32-element chunk of kRows rows
 // ---------------------------------------------------------------------------
+
+constexpr int kRows = 4;  // rows per lane in the expert GEMVs
+
+__device__ __forceinline__ void load16(const uint16_t *p, uint32_t (&x)[16]) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = q[i];
+    x[i * 4 + 0] = v.x;
+    x[i * 4 + 1] = v.y;
+    x[i * 4 + 2] = v.z;
+    x[i * 4 + 3] = v.w;
+  }
+}
+
+// Raw weights of kRows rows x one chunk as loaded from memory.
+struct ChunkRaw {
+  uint4 q[kRows][4];    // FP4 uses q[r][0] (16 bytes of nibbles); BF16 all four
+  uint32_t scale[kRows];  // FP4: block scales of the row (byte 0: block 2c, byte 1: block 2c+1)
+};
+
+// Rows [r0, r0 + kRows) of matrix m (N x K), chunk c; r0 % 4 == 0.
+template <int WT>
+__device__ __forceinline__ void load_rows(const uint8_t *m, int64_t N, int64_t K, int r0, int c, ChunkRaw &cr) {
+  if (WT == 1) {
+    const int64_t rowb = K / 2;
+    const uint8_t *p = m + (int64_t)r0 * rowb + (int64_t)c * 16;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) cr.q[r][0] = *reinterpret_cast<const uint4 *>(p + r * rowb);
+    // 16-byte tile of rows 8g..8g+7: this lane's rows are its first or second half
+    const uint4 t = *reinterpret_cast<const uint4 *>(m + N * K / 2 + ((int64_t)(r0 >> 3) * (K / 32) + c) * 16);
+    const bool second = (r0 & 4) != 0;
+    const uint32_t w0 = second ? t.z : t.x, w1 = second ? t.w : t.y;
+    cr.scale[0] = w0 & 0xffffu;
+    cr.scale[1] = w0 >> 16;
+    cr.scale[2] = w1 & 0xffffu;
+    cr.scale[3] = w1 >> 16;
+  } else {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(m) + (int64_t)r0 * K + (int64_t)c * 32;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const uint4 *q = reinterpret_cast<const uint4 *>(p + r * K);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cr.q[r][i] = q[i];
+    }
+  }
+}
+
+// Weights as 16 BF16 pairs per row plus FP32 block scales.
+struct ChunkBF {
+  uint32_t w[kRows][16];
+  float s0[kRows], s1[kRows];
+};
 
 template <int WT>
-__global__ __launch_bounds__(kBlock) void k_gateup(DecodeArgs a) {
+__device__ __forceinline__ void convert_rows(const ChunkRaw &cr, ChunkBF &cb) {
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    if (WT == 1) {
+      const uint32_t nw[4] = {cr.q[r][0].x, cr.q[r][0].y, cr.q[r][0].z, cr.q[r][0].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        cb.w[r][d * 4 + 0] = __builtin_bit_cast(uint32_t, MOE_FP4X2_TO_BF16X2(nw[d], 0));
+        cb.w[r][d * 4 + 1] = __builtin_bit_cast(uint32_t, MOE_FP4X2_TO_BF16X2(nw[d], 1));
+        cb.w[r][d * 4 + 2] = __builtin_bit_cast(uint32_t, MOE_FP4X2_TO_BF16X2(nw[d], 2));
+        cb.w[r][d * 4 + 3] = __builtin_bit_cast(uint32_t, MOE_FP4X2_TO_BF16X2(nw[d], 3));
+      }
+      cb.s0[r] = e4m3_to_f32(cr.scale[r] & 0xffu);
+      cb.s1[r] = e4m3_to_f32(cr.scale[r] >> 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cb.w[r][i * 4 + 0] = cr.q[r][i].x;
+        cb.w[r][i * 4 + 1] = cr.q[r][i].y;
+        cb.w[r][i * 4 + 2] = cr.q[r][i].z;
+        cb.w[r][i * 4 + 3] = cr.q[r][i].w;
+      }
+      cb.s0[r] = 1.f;
+      cb.s1[r] = 1.f;
+    }
+  }
+}
+
+// acc[r] += sum over the chunk of W[r][.] * x[.] (block scales applied).
+template <int WT>
+__device__ __forceinline__ void dot_rows(const ChunkBF &cb, const uint32_t (&x)[16], float (&acc)[kRows]) {
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p0 = dot2_bf16(cb.w[r][i], x[i], p0);
+#pragma unroll
+    for (int i = 8; i < 16; ++i) p1 = dot2_bf16(cb.w[r][i], x[i], p1);
+    acc[r] = (WT == 1) ? fmaf(cb.s0[r], p0, fmaf(cb.s1[r], p1, acc[r])) : acc[r] + (p0 + p1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_router: logits (and the pre-norm)
+// ---------------------------------------------------------------------------
+
+// One wave per block, one router row per lane group.  With a pre-norm each
+// lane group computes mean(x^2) over the whole row from its own chunks and
+// normalises the chunks it uses; block 0 also stores xn for the expert
+// kernels (the same code, hence the same bits, in every block).
+__global__ __launch_bounds__(kWave) void k_router(DecodeArgs a) {
+  const int H = a.H, E = a.E, B = a.B;
+  const int LPR = lanes_per_row(H), C = H / 32;
+  const int lane = threadIdx.x, lg = lane % LPR;
+  const int row = blockIdx.x * (kWave / LPR) + lane / LPR;
+  const bool store_xn = a.use_norm && blockIdx.x == 0 && lane < LPR;
+
+  float acc[kMaxBatch];
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
+  for (int t = 0; t < B; ++t) {
+    float inv = 1.f;
+    if (a.use_norm) {
+      float ss = 0.f;
+      for (int c = lg; c < C; c += LPR) {
+        uint32_t x[16];
+        load16(a.x + (int64_t)t * H + c * 32, x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float lo = bf16_to_f32(x[i] & 0xffffu), hi = bf16_to_f32(x[i] >> 16);
+          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+        }
+      }
+      ss = group_sum(ss, LPR);
+      inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+    }
+    float s = 0.f;
+    for (int c = lg; c < C; c += LPR) {
+      uint32_t x[16];
+      load16(a.x + (int64_t)t * H + c * 32, x);
+      if (a.use_norm) {
+        uint32_t g[16];
+        load16(a.norm_gain + c * 32, g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float lo = bf16_to_f32(x[i] & 0xffffu) * inv * bf16_to_f32(g[i] & 0xffffu);
+          const float hi = bf16_to_f32(x[i] >> 16) * inv * bf16_to_f32(g[i] >> 16);
+          x[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
+        if (store_xn) {
+          uint4 *o = reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H + c * 32);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = make_uint4(x[i * 4], x[i * 4 + 1], x[i * 4 + 2], x[i * 4 + 3]);
+        }
+      }
+      if (row < E) {
+        uint32_t w[16];
+        load16(a.router_w + (int64_t)row * H + c * 32, w);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = dot2_bf16(w[i], x[i], s);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kMaxBatch; ++tt)
+      if (tt == t) acc[tt] = s;
+  }
+  if (row < E) {
+    const float bias = a.router_b ? a.router_b[row] : 0.f;
+    for (int t = 0; t < B; ++t) {
+      float v = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < kMaxBatch; ++tt)
+        if (tt == t) v = acc[tt];
+      v = group_sum(v, LPR);
+      if (lg == 0) a.ws.logits[t * E + row] = v + bias;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Routing: top-k per token and the sorted list of distinct experts
+// ---------------------------------------------------------------------------
+
+struct Routing {
+  int n;                                // distinct selected experts
+  int expert[kMaxBatch * kMaxTopK];     // ascending expert id
+  uint32_t mask[kMaxBatch * kMaxTopK];  // bit t: token t selected it
+  int sel[kMaxBatch][kMaxTopK];         // per token, descending score
+  float w[kMaxBatch][kMaxTopK];         // renormalised sigmoid weights
+};
+
+// Top-k of every token (one wave per token), its weights, and the sorted
+// list of distinct experts.  Every caller derives the same list from the
+// same logits.
+__device__ inline void build_routing(const DecodeArgs &a, Routing &R, uint32_t *s_mark, int nwaves) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const bool single = a.B == 1;
+  if (!single)
+    for (int e = threadIdx.x; e < a.E; e += nwaves * kWave) s_mark[e] = 0u;
+  __syncthreads();
+  for (int t = wave; t < a.B; t += nwaves) {
+    int sel[kMaxTopK];
+    float selv[kMaxTopK];
+    wave_topk_any(a.ws.logits + t * a.E, a.E, a.k, sel, selv);
+    // lane r < k handles selection r
+    int e = sel[0];
+    float l = selv[0];
+#pragma unroll
+    for (int r = 1; r < kMaxTopK; ++r) {
+      e = (lane == r) ? sel[r] : e;
+      l = (lane == r) ? selv[r] : l;
+    }
+    const float sg = (lane < a.k) ? 1.0f / (1.0f + expf(-l)) : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) sum += __shfl(sg, r, kWave);  // in selection order
+    if (lane < a.k) {
+      R.sel[t][lane] = e;
+      R.w[t][lane] = sg / sum;
+      if (single) {
+        // one token: the distinct list is the selection sorted by index
+        int rank = 0;
+#pragma unroll
+        for (int r = 0; r < kMaxTopK; ++r) rank += (r < a.k && sel[r] < e) ? 1 : 0;
+        R.expert[rank] = e;
+        R.mask[rank] = 1u;
+      } else {
+        atomicOr(&s_mark[e], 1u << t);
+      }
+    }
+    if (single && lane == 0) R.n = a.k;
+  }
+  __syncthreads();
+  if (!single) {
+    if (wave == 0) {
+      int count = 0;
+      for (int base = 0; base < a.E; base += kWave) {
+        const int e = base + lane;
+        const uint32_t m = (e < a.E) ? s_mark[e] : 0u;
+        const unsigned long long ball = __ballot(m != 0u);
+        if (m) {
+          const int slot = count + __popcll(ball & ((1ull << lane) - 1ull));
+          R.expert[slot] = e;
+          R.mask[slot] = m;
+        }
+        count += __popcll(ball);
+      }
+      if (lane == 0) R.n = count;
+    }
+    __syncthreads();
+  }
+}
+
+// Top-k outputs, the entry list and the combine weight of every (entry,
+// token) pair, for the down kernel.
+__device__ inline void publish_routing(const DecodeArgs &a, const Routing &R) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < a.B * a.k; i += blockDim.x) {
+    const int t = i / a.k, r = i % a.k;
+    a.out_idx[i] = R.sel[t][r];
+    a.out_w[i] = R.w[t][r];
+  }
+  for (int i = tid; i < R.n * kMaxBatch; i += blockDim.x) {
+    const int j = i / kMaxBatch, t = i % kMaxBatch;
+    float w = 0.f;
+    if (t < a.B && ((R.mask[j] >> t) & 1u))
+      for (int r = 0; r < a.k; ++r)
+        if (R.sel[t][r] == R.expert[j]) w = R.w[t][r];
+    a.ws.entry_w[i] = w;
+    if (t == 0) {
+      a.ws.entry_expert[j] = R.expert[j];
+      a.ws.entry_mask[j] = R.mask[j];
+    }
+  }
+  if (tid == 0) *a.ws.n_routed = R.n;
+}
+
+// Routing of a batch of several tokens: one block, one wave per token.
+constexpr int kRouteWaves = kMaxBatch;
+
+__global__ __launch_bounds__(kRouteWaves *kWave) void k_route(DecodeArgs a) {
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[kMaxExperts];
+  build_routing(a, R, s_mark, kRouteWaves);
+  publish_routing(a, R);
+}
+
+// ---------------------------------------------------------------------------
+// k_gateup: each lane group computes 4 rows of h for one expert
+// ---------------------------------------------------------------------------
+
+constexpr int kGateupWaves = 4;
+
+// acc[t][r] += W[r0 + r][chunk c] . x_t[chunk c] for the tokens of `mask`.
+template <int WT, int MAXT>
+__device__ __forceinline__ void dot_tokens(const ChunkBF &cb, const uint16_t *xs, int H, int c, uint32_t mask, int B,
+                                  float (&acc)[MAXT][kRows]) {
+  StaticFor<0, MAXT>::run([&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+    if (t < B && ((mask >> t) & 1u)) {
+      uint32_t x[16];
+      load16(xs + (int64_t)t * H + c * 32, x);
+      dot_rows<WT>(cb, x, acc[t]);
+    }
+  });
+}
+
+template <int WT, int MAXT>
+__global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[MAXT == 1 ? kMaxExperts : 1];
+
   const int H = a.H, I = a.I, B = a.B;
   const int LPR = lanes_per_row(H), C = H / 32;
-  const int groups_per_block = kBlock / LPR;
-  const int u = blockIdx.x * groups_per_block + threadIdx.x / LPR;
-  const int lg = threadIdx.x % LPR;
-  const int routed_units = a.max_routed * (I / 8);
+  const int groups = kGateupWaves * (kWave / LPR);
+  const int lane = threadIdx.x & (kWave - 1), lg = lane % LPR;
+  const int u = blockIdx.x * groups + threadIdx.x / LPR;  // 4-row unit of this lane group
+  const int routed_units = a.max_routed * (I / kRows);
 
-  int slot, rg, N;
-  uint32_t mask;
-  const uint8_t *Wg, *Wu;
+  if (a.E > 0 && ((int)blockIdx.x * groups < routed_units || blockIdx.x == 0)) {
+    if (MAXT == 1) {
+      // One token: every block selects the experts itself (cheaper than a
+      // separate launch); block 0 publishes the list for the down kernel.
+      build_routing(a, R, s_mark, kGateupWaves);
+      if (blockIdx.x == 0) publish_routing(a, R);
+    } else {
+      // Several tokens: the routing kernel already wrote the list.
+      if (threadIdx.x == 0) R.n = *a.ws.n_routed;
+      for (int j = threadIdx.x; j < a.max_routed; j += blockDim.x) {
+        R.expert[j] = a.ws.entry_expert[j];
+        R.mask[j] = a.ws.entry_mask[j];
+      }
+      __syncthreads();
+    }
+  }
+
+  int slot = 0, q = 0, N = 0;
+  uint32_t mask = 0;
+  const uint8_t *Wg = nullptr, *Wu = nullptr;
   float Sg = 1.f, Su = 1.f;
   if (u < routed_units) {
-    slot = u / (I / 8);
-    rg = u % (I / 8);
-    if (slot >= *a.ws.n_routed) return;
-    const int e = a.ws.entry_expert[slot];
-    mask = a.ws.entry_mask[slot];
-    N = I;
-    const int64_t mb = (WT == 1) ? nvfp4_matrix_bytes(I, H) : (int64_t)I * H * 2;
-    Wg = a.w_gate + e * mb;
-    Wu = a.w_up + e * mb;
-    if (WT == 1) {
-      Sg = a.w_scale[3 * e + 0];
-      Su = a.w_scale[3 * e + 1];
+    slot = u / (I / kRows);
+    q = u % (I / kRows);
+    if (slot < R.n) {
+      const int e = R.expert[slot];
+      mask = R.mask[slot];
+      N = I;
+      const int64_t mb = (WT == 1) ? nvfp4_matrix_bytes(I, H) : (int64_t)I * H * 2;
+      Wg = a.w_gate + e * mb;
+      Wu = a.w_up + e * mb;
+      if (WT == 1) {
+        Sg = a.w_scale[3 * e + 0];
+        Su = a.w_scale[3 * e + 1];
+      }
     }
-  } else {
-    rg = u - routed_units;
-    if (rg >= a.Is / 8) return;
+  } else if (u - routed_units < a.Is / kRows) {
     slot = a.max_routed;
+    q = u - routed_units;
     mask = (1u << B) - 1u;
     N = a.Is;
     Wg = a.sh_gate;
@@ -334,156 +491,137 @@ __global__ __launch_bounds__(kBlock) void k_gateup(DecodeArgs a) {
       Su = a.sh_scale[1];
     }
   }
-  const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
-  const int Imax = a.I > a.Is ? a.I : a.Is;
 
-  if (WT == 1 && C <= LPR) {
-    // One chunk per lane: load the weights once, reuse them for each token.
-    uint4 ng[8], nu[8], sg, su;
-    load_chunk8_nvfp4(Wg, N, H, rg, lg, ng, sg);
-    load_chunk8_nvfp4(Wu, N, H, rg, lg, nu, su);
-    for (int t = 0; t < B; ++t) {
-      if (!((mask >> t) & 1u)) continue;
-      uint4 xv[4];
-      load_x_chunk(xs + (int64_t)t * H, lg, xv);
-      float ag[8] = {0, 0, 0, 0, 0, 0, 0, 0}, au[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      nvfp4_chunk8(ng, sg, xv, ag);
-      nvfp4_chunk8(nu, su, xv, au);
+  const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
+  float ag[MAXT][kRows], au[MAXT][kRows];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ag[r] = group_sum(ag[r], LPR);
-        au[r] = group_sum(au[r], LPR);
-      }
-      // Every lane holds all 8 sums; lanes of the group split the rows
-      // (a group can have fewer than 8 lanes).
-      for (int r = lg; r < 8; r += LPR) {
-        float g = round_bf16(pick8(ag, r) * Sg);
-        float uu = round_bf16(pick8(au, r) * Su);
-        float h = g / (1.0f + expf(-g)) * uu;
-        a.ws.h[((int64_t)slot * B + t) * Imax + rg * 8 + r] = (uint16_t)f32_to_bf16(h);
-      }
-    }
-  } else {
-    for (int t = 0; t < B; ++t) {
-      if (!((mask >> t) & 1u)) continue;
-      float ag[8] = {0, 0, 0, 0, 0, 0, 0, 0}, au[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int c = lg; c < C; c += LPR) {
-        uint4 xv[4];
-        load_x_chunk(xs + (int64_t)t * H, c, xv);
-        if (WT == 1) {
-          uint4 ng[8], nu[8], sg, su;
-          load_chunk8_nvfp4(Wg, N, H, rg, c, ng, sg);
-          load_chunk8_nvfp4(Wu, N, H, rg, c, nu, su);
-          nvfp4_chunk8(ng, sg, xv, ag);
-          nvfp4_chunk8(nu, su, xv, au);
-        } else {
-          bf16_chunk8(reinterpret_cast<const uint16_t *>(Wg), H, rg, c, xv, ag);
-          bf16_chunk8(reinterpret_cast<const uint16_t *>(Wu), H, rg, c, xv, au);
-        }
-      }
+  for (int t = 0; t < MAXT; ++t)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ag[r] = group_sum(ag[r], LPR);
-        au[r] = group_sum(au[r], LPR);
-      }
-      // Every lane holds all 8 sums; lanes of the group split the rows
-      // (a group can have fewer than 8 lanes).
-      for (int r = lg; r < 8; r += LPR) {
-        float g = round_bf16(pick8(ag, r) * Sg);
-        float uu = round_bf16(pick8(au, r) * Su);
-        float h = g / (1.0f + expf(-g)) * uu;
-        a.ws.h[((int64_t)slot * B + t) * Imax + rg * 8 + r] = (uint16_t)f32_to_bf16(h);
-      }
+    for (int r = 0; r < kRows; ++r) ag[t][r] = au[t][r] = 0.f;
+  if (mask) {
+    for (int c = lg; c < C; c += LPR) {
+      ChunkRaw rg, ru;
+      load_rows<WT>(Wg, N, H, q * kRows, c, rg);
+      load_rows<WT>(Wu, N, H, q * kRows, c, ru);
+      ChunkBF cb;
+      convert_rows<WT>(rg, cb);
+      dot_tokens<WT, MAXT>(cb, xs, H, c, mask, B, ag);
+      convert_rows<WT>(ru, cb);
+      dot_tokens<WT, MAXT>(cb, xs, H, c, mask, B, au);
     }
   }
+  // Per token: fold the 4 gate rows, then the 4 up rows, over the lane
+  // group; lanes 0..3 of the group end up with one row each (the same row
+  // for gate and up), and write h.
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  StaticFor<0, MAXT>::run([&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+    if (t < B) {
+      int row;
+      float g2 = 0.f, u2 = 0.f;
+      const float gs = fold4(ag[t][0], ag[t][1], ag[t][2], ag[t][3], LPR, row, &g2);
+      const float us = fold4(au[t][0], au[t][1], au[t][2], au[t][3], LPR, row, &u2);
+      if (lg < (LPR == 2 ? 2 : kRows) && ((mask >> t) & 1u)) {
+        // with 2-lane groups each lane holds two rows
+        for (int k2 = 0; k2 < (LPR == 2 ? 2 : 1); ++k2) {
+          const float g = round_bf16((k2 ? g2 : gs) * Sg);
+          const float uu = round_bf16((k2 ? u2 : us) * Su);
+          const float h = g / (1.0f + expf(-g)) * uu;
+          a.ws.h[((int64_t)slot * B + t) * Imax + q * kRows + row + k2] = (uint16_t)f32_to_bf16(h);
+        }
+      }
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMV + weighted combine (+ residual)
+// k_down: 4 output rows per block, every expert, weighted combine
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxSlots = 32;  // expert slots reduced per pass of k_down
+constexpr int kMaxDownSlots = 64;  // entries reduced per pass (lane groups beyond idle)
 
-template <int WT>
-__global__ __launch_bounds__(kBlock) void k_down(DecodeArgs a) {
+template <int WT, int MAXT, int DW>
+__global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
   const int H = a.H, B = a.B;
   const int K = (a.E > 0) ? a.I : a.Is;  // Is == I when both exist
   const int LPR = lanes_per_row(K), C = K / 32;
-  const int slots = (kBlock / LPR) < kMaxSlots ? (kBlock / LPR) : kMaxSlots;
-  const int slot_id = threadIdx.x / LPR, lg = threadIdx.x % LPR;
-  const int rg = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), lg = lane % LPR;
+  const int gi = threadIdx.x / LPR;  // lane group = entry slot of a pass
+  const int slots_all = DW * (kWave / LPR);
+  const int slots = slots_all < kMaxDownSlots ? slots_all : kMaxDownSlots;
+  const int r0 = blockIdx.x * kRows;
   const int n_routed = (a.E > 0) ? *a.ws.n_routed : 0;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
   const int Imax = a.I > a.Is ? a.I : a.Is;
 
-  __shared__ float s_part[kMaxSlots][kMaxBatch][8];
-  float total = 0.f;  // owned by thread (t, r) = (tid / 8, tid % 8)
+  __shared__ float s_part[kMaxDownSlots][kRows][MAXT];
+  float total = 0.f;  // thread (row, token) = (tid / MAXT, tid % MAXT), tid < 4*MAXT
 
-  for (int base = 0; base < n_entries; base += slots) {
-    const int j = (slot_id < slots) ? base + slot_id : n_entries;
-    float contrib[kMaxBatch][8];
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) contrib[t][r] = 0.f;
-    if (j < n_entries) {
-      const uint8_t *Wd;
-      float Sd = 1.f;
-      uint32_t mask;
-      int hslot;
-      const float *wt = nullptr;
-      if (j < n_routed) {
-        const int e = a.ws.entry_expert[j];
-        mask = a.ws.entry_mask[j];
-        const int64_t mb = (WT == 1) ? nvfp4_matrix_bytes(H, K) : (int64_t)H * K * 2;
-        Wd = a.w_down + e * mb;
-        if (WT == 1) Sd = a.w_scale[3 * e + 2];
-        hslot = j;
-        wt = a.ws.entry_w + j * kMaxBatch;
-      } else {
-        mask = (1u << B) - 1u;
-        Wd = a.sh_down;
-        if (WT == 1) Sd = a.sh_scale[2];
-        hslot = a.max_routed;
-      }
-      for (int t = 0; t < B; ++t) {
-        if (!((mask >> t) & 1u)) continue;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int c = lg; c < C; c += LPR) {
-          uint4 hv[4];
-          load_x_chunk(a.ws.h + ((int64_t)hslot * B + t) * Imax, c, hv);
-          if (WT == 1) {
-            uint4 nb[8], sc;
-            load_chunk8_nvfp4(Wd, H, K, rg, c, nb, sc);
-            nvfp4_chunk8(nb, sc, hv, acc);
-          } else {
-            bf16_chunk8(reinterpret_cast<const uint16_t *>(Wd), K, rg, c, hv, acc);
-          }
-        }
-        const float w = wt ? wt[t] : 1.0f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) contrib[t][r] = w * round_bf16(group_sum(acc[r], LPR) * Sd);
-      }
-    }
-    if (lg == 0 && slot_id < slots) {
-#pragma unroll
-      for (int t = 0; t < kMaxBatch; ++t)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) s_part[slot_id][t][r] = contrib[t][r];
-    }
+  for (int pass = 0; pass * slots < n_entries; ++pass) {
+    for (int i = threadIdx.x; i < slots * kRows * MAXT; i += blockDim.x) (&s_part[0][0][0])[i] = 0.f;
     __syncthreads();
-    if (threadIdx.x < B * 8) {
-      const int t = threadIdx.x / 8, r = threadIdx.x % 8;
-      for (int s = 0; s < slots; ++s) total += s_part[s][t][r];
+    const int j = (gi < slots) ? pass * slots + gi : n_entries;
+    uint32_t mask = 0;
+    const uint8_t *Wd = nullptr;
+    float Sd = 1.f;
+    int hslot = 0;
+    const float *wt = nullptr;
+    if (j < n_routed) {
+      const int e = a.ws.entry_expert[j];
+      mask = a.ws.entry_mask[j];
+      const int64_t mb = (WT == 1) ? nvfp4_matrix_bytes(H, K) : (int64_t)H * K * 2;
+      Wd = a.w_down + e * mb;
+      if (WT == 1) Sd = a.w_scale[3 * e + 2];
+      hslot = j;
+      wt = a.ws.entry_w + j * kMaxBatch;
+    } else if (j == n_routed && j < n_entries) {
+      mask = (1u << B) - 1u;
+      Wd = a.sh_down;
+      if (WT == 1) Sd = a.sh_scale[2];
+      hslot = a.max_routed;
+    }
+    float acc[MAXT][kRows];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) acc[t][r] = 0.f;
+    if (mask) {
+      for (int c = lg; c < C; c += LPR) {
+        ChunkRaw cr;
+        load_rows<WT>(Wd, H, K, r0, c, cr);
+        ChunkBF cb;
+        convert_rows<WT>(cr, cb);
+        dot_tokens<WT, MAXT>(cb, a.ws.h + (int64_t)hslot * B * Imax, Imax, c, mask, B, acc);
+      }
+    }
+    StaticFor<0, MAXT>::run([&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      if (t < B) {
+        int row;
+        float y2 = 0.f;
+        const float ys = fold4(acc[t][0], acc[t][1], acc[t][2], acc[t][3], LPR, row, &y2);
+        if (lg < (LPR == 2 ? 2 : kRows) && ((mask >> t) & 1u)) {
+          const float w = wt ? wt[t] : 1.0f;
+          s_part[gi][row][t] = w * round_bf16(ys * Sd);
+          if (LPR == 2) s_part[gi][row + 1][t] = w * round_bf16(y2 * Sd);
+        }
+      }
+    });
+    __syncthreads();
+    if (threadIdx.x < kRows * MAXT) {
+      const int r = threadIdx.x / MAXT, t = threadIdx.x % MAXT;
+      for (int s = 0; s < slots; ++s) total += s_part[s][r][t];
     }
     __syncthreads();
   }
-  if (threadIdx.x < B * 8) {
-    const int t = threadIdx.x / 8, r = threadIdx.x % 8;
-    const int64_t o = (int64_t)t * H + rg * 8 + r;
-    float v = round_bf16(total);
-    if (a.residual) v = bf16_to_f32(a.x[o]) + v;
-    a.y[o] = (uint16_t)f32_to_bf16(v);
+  if (threadIdx.x < kRows * MAXT) {
+    const int r = threadIdx.x / MAXT, t = threadIdx.x % MAXT;
+    if (t < B) {
+      const int64_t o = (int64_t)t * H + r0 + r;
+      float v = round_bf16(total);
+      if (a.residual) v = bf16_to_f32(a.x[o]) + v;
+      a.y[o] = (uint16_t)f32_to_bf16(v);
+    }
   }
 }
 
@@ -491,38 +629,57 @@ __global__ __launch_bounds__(kBlock) void k_down(DecodeArgs a) {
 // Host launcher
 // ---------------------------------------------------------------------------
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  if (a.E > 0 || a.use_norm) {
-    const int LPR = lanes_per_row(a.H);
-    const int rows_per_block = kBlock / LPR;
-    const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
-    const size_t lds = (size_t)a.B * a.H * 2;
-    hipLaunchKernelGGL(k_router_topk, dim3(grid), dim3(kBlock), lds, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+template <int WT, int MAXT>
+static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
+  hipError_t e;
+  if (MAXT > 1 && a.E > 0) {
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(kRouteWaves * kWave), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   {
-    const int LPR = lanes_per_row(a.H);
-    const int groups = kBlock / LPR;
-    const int units = a.max_routed * (a.I / 8) + a.Is / 8;
+    const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
+    const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
     const int grid = (units + groups - 1) / groups;
-    if (a.wtype == 1)
-      hipLaunchKernelGGL(k_gateup<1>, dim3(grid), dim3(kBlock), 0, stream, a);
-    else
-      hipLaunchKernelGGL(k_gateup<0>, dim3(grid), dim3(kBlock), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gateup<WT, MAXT>), dim3(grid), dim3(kGateupWaves * kWave), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  {
-    const int grid = a.H / 8;
-    if (a.wtype == 1)
-      hipLaunchKernelGGL(k_down<1>, dim3(grid), dim3(kBlock), 0, stream, a);
-    else
-      hipLaunchKernelGGL(k_down<0>, dim3(grid), dim3(kBlock), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
+  constexpr int DW = MAXT <= 2 ? 2 : MAXT <= 4 ? 4 : 8;
+  hipLaunchKernelGGL((k_down<WT, MAXT, DW>), dim3(a.H / kRows), dim3(DW * kWave), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return ev ? hipEventRecord(ev[5], stream) : hipSuccess;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
+  // ev: NULL, or 6 events recorded before/after the routing (router GEMV
+  // plus, for several tokens, the top-k kernel), gate/up and down stages
+  // (for measurement; recordable under graph capture).
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+  if (a.E > 0 || a.use_norm) {
+    const int rows_per_block = kWave / lanes_per_row(a.H);
+    const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
+    hipLaunchKernelGGL(k_router, dim3(grid), dim3(kWave), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  const int mt = a.B <= 1 ? 1 : a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8;
+  if (a.wtype == 1) {
+    switch (mt) {
+      case 1: return launch_experts<1, 1>(a, stream, ev);
+      case 2: return launch_experts<1, 2>(a, stream, ev);
+      case 4: return launch_experts<1, 4>(a, stream, ev);
+      default: return launch_experts<1, 8>(a, stream, ev);
+    }
+  }
+  switch (mt) {
+    case 1: return launch_experts<0, 1>(a, stream, ev);
+    case 2: return launch_experts<0, 2>(a, stream, ev);
+    case 4: return launch_experts<0, 4>(a, stream, ev);
+    default: return launch_experts<0, 8>(a, stream, ev);
+  }
 }
 
 }  // namespace moe
