@@ -149,6 +149,32 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
                             int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* Workspace bytes moe_decode_step needs for n_layers layers (descs[0..n))
+ * and batches up to max_batch, or 0 if a description is invalid or the
+ * layers' hidden sizes differ. */
+size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch);
+
+/* One decode step of `batch` tokens (1..8) through a stack of pre-norm
+ * residual layers ("vLLM Flint" commentary, section "Only 14 of 49 layers
+ * retain full-history KV": 49 pre-norm layers; "Day-0 Support for Flint on
+ * vLLM", section "Model architecture": layers 0 and 1 use a dense MLP, the
+ * others 256 routed experts plus a shared expert):
+ *   x_0 = x;  x_{i+1} = BF16(x_i + layer_i(xn_i)),  y = x_n,
+ * where xn_i is BF16(RMSNorm(x_i) * gain_i) when weights[i].norm_gain is
+ * set (else x_i) and layer_i is moe_decode_layer's computation (a dense
+ * SwiGLU for n_experts == 0).  The activations between layers live in the
+ * workspace; the call enqueues every layer's kernels back to back on
+ * `stream` (capture it once into a HIP graph to replay a whole step).
+ *  descs, weights: host arrays of n_layers entries (read during the call
+ *  only); device pointers inside as for moe_decode_layer.
+ *  x [batch][H], y [batch][H]: device BF16, must not alias.
+ *  ws: device, ws_bytes >= moe_decode_step_workspace_bytes(descs, n_layers,
+ *  batch), zero-filled before first use, reusable without clearing.
+ * Errors: as moe_decode_layer for each layer (the first failing layer's
+ * status); INVALID_ARG for n_layers < 1 or differing hidden sizes. */
+moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                           const void *x, int32_t batch, void *y, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes moe_prefill_layer needs for up to n_tokens tokens. */
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
 
@@ -165,12 +191,13 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
 const char *moe_status_string(moe_status s);
 
 /* Measurement hook.  With 6 hipEvent_t handles set, every later
- * moe_decode_layer call on this thread records events[0]/[1] before/after
- * its router stage, [2]/[3] around the gate/up stage and [4]/[5] around the
- * down-and-combine stage, on the call's stream (also under graph capture).
- * events == NULL or n_events == 0 turns it off.  The events stay owned by
- * the caller.  Errors: INVALID_ARG for n_events other than 0 or 6 or a
- * null handle. */
+ * moe_decode_layer call on this thread attaches events[0]/[1] as start and
+ * stop of its router GEMV kernel, [2]/[3] of its gate/up kernel and [4]/[5]
+ * of its down-and-combine kernel (the events then time the kernels'
+ * execution, like a kernel trace).  For eager calls only, not under graph
+ * capture.  events == NULL or n_events == 0 turns it off.  The events stay
+ * owned by the caller.  Errors: INVALID_ARG for n_events other than 0 or 6
+ * or a null handle. */
 moe_status moe_set_stage_events(void *const *events, int32_t n_events);
 
 /* The HIP runtime's description of the last HIP failure reported as

@@ -149,3 +149,21 @@ def test_repack_errors(args, want):
     assert lib.moe_repack_nvfp4(*args, None, None) == want
     assert lib.moe_unpack_nvfp4(*args, None) == want
     assert lib.moe_dequant_nvfp4(args[0], args[1], *args[2:], None, None) == want
+
+
+def test_step_validation():
+    lib = m.lib()
+    d = desc()
+    dd = (m.moe_layer_desc * 2)(d, desc(n_experts=0, top_k=0, inter=0, shared_inter=5632))
+    ww = (m.moe_layer_weights * 2)(weights(), weights(router_w=None, w_gate=None, w_up=None, w_down=None))
+    assert m.moe_decode_step_workspace_bytes([d, dd[1]], 1) > m.moe_decode_workspace_bytes(d, 1)
+    assert m.moe_decode_step_workspace_bytes([d, desc(hidden=1024)], 1) == 0
+    assert lib.moe_decode_step(dd, ww, 0, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_decode_step(dd, ww, 2, A(20), 9, A(21), A(22), 1 << 30, None) == m.MOE_ERR_UNSUPPORTED
+    assert lib.moe_decode_step(dd, ww, 2, A(20), 1, A(20), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_decode_step(dd, ww, 2, A(20), 1, A(21), A(22), 64, None) == m.MOE_ERR_WORKSPACE
+    bad = (m.moe_layer_desc * 2)(d, desc(hidden=1024))
+    assert lib.moe_decode_step(bad, ww, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    # a bad weight in the second layer is reported before anything launches
+    ww2 = (m.moe_layer_weights * 2)(weights(), weights(sh_gate=None))
+    assert lib.moe_decode_step(dd, ww2, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG

@@ -71,6 +71,11 @@ _lib.moe_decode_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32
 _lib.moe_decode_layer.restype = _i32
 _lib.moe_decode_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
                                   _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_decode_step_workspace_bytes.restype = _sz
+_lib.moe_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32, _i32]
+_lib.moe_decode_step.restype = _i32
+_lib.moe_decode_step.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _i32, _vp,
+                                 _i32, _vp, _vp, _sz, _vp]
 _lib.moe_prefill_workspace_bytes.restype = _sz
 _lib.moe_prefill_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32]
 _lib.moe_prefill_layer.restype = _i32
@@ -79,7 +84,8 @@ _lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTE
 
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_set_stage_events", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4", "moe_unpack_nvfp4",
            "moe_dequant_nvfp4",
-           "moe_decode_workspace_bytes", "moe_decode_layer", "moe_prefill_workspace_bytes",
+           "moe_decode_workspace_bytes", "moe_decode_layer", "moe_decode_step_workspace_bytes",
+           "moe_decode_step", "moe_prefill_workspace_bytes",
            "moe_prefill_layer")
 
 
@@ -158,6 +164,25 @@ def moe_decode_layer(desc, weights, x, batch, residual, y, topk_idx=None, topk_w
     _check(_lib.moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, int(residual),
                                  _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_decode_layer")
+
+
+def _arrays(descs, weights):
+    n = len(descs)
+    d = (moe_layer_desc * n)(*descs)
+    w = (moe_layer_weights * n)(*weights) if weights is not None else None
+    return n, d, w
+
+
+def moe_decode_step_workspace_bytes(descs, max_batch):
+    n, d, _ = _arrays(descs, None)
+    return _lib.moe_decode_step_workspace_bytes(d, n, max_batch)
+
+
+def moe_decode_step(descs, weights, x, batch, y, ws, ws_bytes, stream=None):
+    """descs / weights: sequences of moe_layer_desc / moe_layer_weights."""
+    n, d, w = _arrays(descs, weights)
+    _check(_lib.moe_decode_step(d, w, n, _ptr(x), batch, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_decode_step")
 
 
 def moe_prefill_workspace_bytes(desc, n_tokens):

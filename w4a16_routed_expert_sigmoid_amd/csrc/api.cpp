@@ -157,14 +157,16 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
   return decode_layout(*desc, max_batch).bytes;
 }
 
-moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
-                            int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
-                            void *ws, size_t ws_bytes, void *stream) {
+// Validates one layer call and fills the kernel arguments; nothing is
+// launched.  ws_bytes must cover decode_layout(desc, batch).
+static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                 int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                                 void *ws, size_t ws_bytes, DecodeArgs &a) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (batch < 1) return MOE_ERR_INVALID_ARG;
   if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
-  // The router stages the batch's activations in 64 KiB of LDS.
+  // The routing kernels stage the batch's activations through 64 KiB.
   if ((size_t)batch * desc->hidden * 2 > 65536) return MOE_ERR_UNSUPPORTED;
   st = check_weights(desc, w);
   if (st != MOE_OK) return st;
@@ -175,7 +177,6 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
   if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
 
   uint8_t *base = (uint8_t *)ws;
-  DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.H = desc->hidden;
   a.I = desc->n_experts > 0 ? desc->inter : 0;
@@ -214,7 +215,68 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
   a.ws.bytes = L.bytes;
   a.out_idx = topk_idx ? topk_idx : a.ws.topk_idx;
   a.out_w = topk_w ? topk_w : a.ws.topk_w;
+  return MOE_OK;
+}
+
+moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                            int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                            void *ws, size_t ws_bytes, void *stream) {
+  DecodeArgs a;
+  const moe_status st = prepare_decode(desc, w, x, batch, residual, y, topk_idx, topk_w, ws, ws_bytes, a);
+  if (st != MOE_OK) return st;
   return hip_status(launch_decode(a, (hipStream_t)stream, g_stage_events_on ? g_stage_events : nullptr));
+}
+
+// Step workspace: two activation buffers, then the largest layer workspace.
+static size_t step_act_bytes(int32_t hidden, int32_t max_batch) { return up((size_t)max_batch * hidden * 2); }
+
+size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch) {
+  if (!descs || n_layers < 1 || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  size_t layer = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return 0;
+    const size_t b = decode_layout(descs[i], max_batch).bytes;
+    layer = b > layer ? b : layer;
+  }
+  return 2 * step_act_bytes(descs[0].hidden, max_batch) + layer;
+}
+
+moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                           const void *x, int32_t batch, void *y, void *ws, size_t ws_bytes, void *stream) {
+  if (!descs || !weights || n_layers < 1) return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const moe_status st = check_desc(&descs[i]);
+    if (st != MOE_OK) return st;
+    if (descs[i].hidden != descs[0].hidden) return MOE_ERR_INVALID_ARG;
+  }
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  if (!x || !y || !ws || x == y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_decode_step_workspace_bytes(descs, n_layers, batch);
+  if (need == 0) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t act = step_act_bytes(descs[0].hidden, batch);
+  uint8_t *a0 = (uint8_t *)ws, *a1 = a0 + act, *lws = a1 + act;
+  const size_t lws_bytes = ws_bytes - 2 * act;
+  // Validate every layer before launching anything.
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const void *in = (i == 0) ? x : ((i & 1) ? (const void *)a0 : (const void *)a1);
+    void *out = (i == n_layers - 1) ? y : ((i & 1) ? (void *)a1 : (void *)a0);
+    DecodeArgs a;
+    const moe_status st = prepare_decode(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, lws,
+                                         lws_bytes, a);
+    if (st != MOE_OK) return st;
+  }
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const void *in = (i == 0) ? x : ((i & 1) ? (const void *)a0 : (const void *)a1);
+    void *out = (i == n_layers - 1) ? y : ((i & 1) ? (void *)a1 : (void *)a0);
+    DecodeArgs a;
+    prepare_decode(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, lws, lws_bytes, a);
+    const moe_status st = hip_status(launch_decode(a, (hipStream_t)stream, nullptr));
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
 }
 
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {

@@ -25,6 +25,8 @@
 // "Model architecture" and "Optimizations"): 256 experts, sigmoid top-6
 // plus a shared expert; only the selected experts' weights are read;
 // weight-only FP4 with BF16 activations; the reference's rounding points.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace moe {
@@ -629,41 +631,49 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 // Host launcher
 // ---------------------------------------------------------------------------
 
+// Launch with optional start/stop events attached to the dispatch itself
+// (they time the kernel's execution, as a kernel trace does).
+template <typename... Args>
+static hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop, Args... args) {
+  if (start && stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  return hipGetLastError();
+}
+
 template <int WT, int MAXT>
 static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
   hipError_t e;
   if (MAXT > 1 && a.E > 0) {
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(kRouteWaves * kWave), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch(k_route, dim3(1), dim3(kRouteWaves * kWave), 0, stream, nullptr, nullptr, a)) != hipSuccess)
+      return e;
   }
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   {
     const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
     const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
     const int grid = (units + groups - 1) / groups;
-    hipLaunchKernelGGL((k_gateup<WT, MAXT>), dim3(grid), dim3(kGateupWaves * kWave), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch(k_gateup<WT, MAXT>, dim3(grid), dim3(kGateupWaves * kWave), 0, stream, ev ? ev[2] : nullptr,
+                    ev ? ev[3] : nullptr, a)) != hipSuccess)
+      return e;
   }
-  if (ev && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
   constexpr int DW = MAXT <= 2 ? 2 : MAXT <= 4 ? 4 : 8;
-  hipLaunchKernelGGL((k_down<WT, MAXT, DW>), dim3(a.H / kRows), dim3(DW * kWave), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return ev ? hipEventRecord(ev[5], stream) : hipSuccess;
+  return launch(k_down<WT, MAXT, DW>, dim3(a.H / kRows), dim3(DW * kWave), 0, stream, ev ? ev[4] : nullptr,
+                ev ? ev[5] : nullptr, a);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
-  // ev: NULL, or 6 events recorded before/after the routing (router GEMV
-  // plus, for several tokens, the top-k kernel), gate/up and down stages
-  // (for measurement; recordable under graph capture).
+  // ev: NULL, or 6 events: start/stop of the router GEMV kernel, of the
+  // gate/up kernel and of the down kernel (attached to the dispatches; for
+  // measurement, eager launches only).
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   if (a.E > 0 || a.use_norm) {
     const int rows_per_block = kWave / lanes_per_row(a.H);
     const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
-    hipLaunchKernelGGL(k_router, dim3(grid), dim3(kWave), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch(k_router, dim3(grid), dim3(kWave), 0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
+                    a)) != hipSuccess)
+      return e;
   }
   const int mt = a.B <= 1 ? 1 : a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8;
   if (a.wtype == 1) {
