@@ -167,3 +167,38 @@ def test_step_validation():
     # a bad weight in the second layer is reported before anything launches
     ww2 = (m.moe_layer_weights * 2)(weights(), weights(sh_gate=None))
     assert lib.moe_decode_step(dd, ww2, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+
+
+def prefill(d=None, w=None, x=A(20), T=100, y=A(21), ws=A(22), ws_bytes=1 << 34):
+    d = d or desc()
+    w = w or weights()
+    return m.lib().moe_prefill_layer(ctypes.byref(d), ctypes.byref(w), x, T, 0, y, None, None, ws, ws_bytes,
+                                     None)
+
+
+def test_prefill_workspace_bytes():
+    # the expert-sorted rows dominate: (k + 1) * T rows of h [I] and y [H]
+    d = desc()
+    n = m.moe_prefill_workspace_bytes(d, 8192)
+    assert n >= 7 * 8192 * (512 + 2048) * 2
+    assert n < 2 * 7 * 8192 * (512 + 2048) * 2
+    assert m.moe_prefill_workspace_bytes(d, 1) < n
+    assert m.moe_prefill_workspace_bytes(d, 0) == 0
+    assert m.moe_prefill_workspace_bytes(d, (1 << 22) + 1) == 0
+    assert m.moe_prefill_workspace_bytes(desc(hidden=100), 10) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(T=0), m.MOE_ERR_INVALID_ARG),
+    (dict(T=(1 << 22) + 1), m.MOE_ERR_UNSUPPORTED),
+    (dict(x=None), m.MOE_ERR_INVALID_ARG),
+    (dict(y=A(20)), m.MOE_ERR_INVALID_ARG),
+    (dict(ws=A(22) + 64), m.MOE_ERR_INVALID_ARG),
+    (dict(x=A(20) + 8), m.MOE_ERR_INVALID_ARG),
+    (dict(ws_bytes=1000), m.MOE_ERR_WORKSPACE),
+    (dict(d=desc(top_k=9)), m.MOE_ERR_INVALID_ARG),
+    (dict(d=desc(n_experts=2048)), m.MOE_ERR_UNSUPPORTED),
+    (dict(w=weights(w_down=None)), m.MOE_ERR_INVALID_ARG),
+])
+def test_prefill_call_errors(kw, want):
+    assert prefill(**kw) == want

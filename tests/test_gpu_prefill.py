@@ -1,0 +1,204 @@
+"""GPU parity of the prefill path (tokens grouped by expert, matrix-core
+GEMMs) against the CPU oracle, through the C ABI.  Each token's result is
+independent of the others, so at the full 8192-token shape the oracle
+checks a spread sample of tokens one by one and properties that hold at
+any size cover the rest."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import compare, from_dev_bits, log, to_dev_bits
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w4a16_routed_expert_sigmoid_amd as moe  # noqa: E402
+
+
+def run(layer, x, dev=None, ws=None, residual=None):
+    dev = dev or moe.DeviceLayer(layer)
+    y, idx, w = dev.prefill(to_dev_bits(x), ws=ws, residual=residual)
+    torch.cuda.synchronize()
+    k = layer["top_k"] if layer["n_experts"] else 0
+    return from_dev_bits(y), idx.cpu().numpy()[:, :k], w.cpu().numpy()[:, :k]
+
+
+def check_routing_properties(layer, idx, w):
+    E, k = layer["n_experts"], layer["top_k"]
+    assert idx.min() >= 0 and idx.max() < E
+    assert all(len(set(r)) == k for r in idx.tolist())
+    assert np.all(w > 0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=2e-6)
+
+
+SMALL = dict(hidden=256, inter=64, shared_inter=64, n_experts=16, top_k=4)
+
+
+@pytest.mark.parametrize("wtype", ["nvfp4", "bf16"])
+@pytest.mark.parametrize("T", [1, 37, 300, 1000])
+def test_prefill_small(wtype, T):
+    # zipf bias: the favoured experts get several 128-row tiles with a
+    # ragged last tile; T = 1000 gives the shared expert 8 tiles, the last
+    # one 104 rows.
+    log(f"test: prefill small {wtype} T={T}")
+    L = synth.make_layer(31, wtype=wtype, bias="zipf", **SMALL)
+    x = synth.tokens(T, 256, stream=500 + T)
+    out, idx, w = run(L, x)
+    check_routing_properties(L, idx, w)
+    _, st = compare(L, x, out, idx, w, what=f"prefill small {wtype} T={T}")
+    counts = np.bincount(idx.reshape(-1), minlength=L["n_experts"])
+    st["max_rows_per_expert"] = int(counts.max())
+    log(f"  {st}")
+
+
+@pytest.mark.parametrize("T", [5, 257])
+def test_prefill_norm_residual(T):
+    L = synth.make_layer(32, bias="zipf", norm=True, residual=True, **SMALL)
+    x = synth.tokens(T, 256, stream=600 + T)
+    out, idx, w = run(L, x)
+    compare(L, x, out, idx, w, what=f"prefill norm+residual T={T}")
+
+
+def test_prefill_ragged_columns_and_depth():
+    # H = 2112 (66 chunks): the down GEMM's last 128-column block holds 64
+    # columns; I = 2080 (65 chunks): the gate/up GEMM's last 64-column block
+    # holds 32 columns and the down GEMM's depth is not a multiple of 64.
+    L = synth.make_layer(33, hidden=2112, inter=2080, shared_inter=2080, n_experts=8, top_k=2, bias="zipf")
+    x = synth.tokens(150, 2112, stream=7)
+    out, idx, w = run(L, x)
+    compare(L, x, out, idx, w, what="ragged columns")
+
+
+def test_prefill_all_experts_selected():
+    L = synth.make_layer(34, hidden=128, inter=64, shared_inter=64, n_experts=8, top_k=8)
+    x = synth.tokens(130, 128, stream=8)
+    out, idx, w = run(L, x)
+    assert all(sorted(r) == list(range(8)) for r in idx.tolist())
+    compare(L, x, out, idx, w, what="k=E")
+
+
+def test_prefill_top1_no_shared():
+    L = synth.make_layer(35, hidden=128, inter=64, shared_inter=0, n_experts=16, top_k=1)
+    x = synth.tokens(77, 128, stream=9)
+    out, idx, w = run(L, x)
+    assert np.all(w == 1.0)
+    compare(L, x, out, idx, w, what="k=1, no shared")
+
+
+def test_prefill_identical_tokens_one_expert_set():
+    # All 600 tokens pick the same k experts: each of them gets 600 rows
+    # (five 128-row tiles), every other expert none.
+    L = synth.make_layer(36, **SMALL)
+    x = np.repeat(synth.tokens(1, 256, stream=10), 600, axis=0)
+    out, idx, w = run(L, x)
+    assert len({tuple(sorted(r)) for r in idx.tolist()}) == 1
+    assert np.all(out == out[0:1])
+    compare(L, x[:3], out[:3], idx[:3], w[:3], what="identical tokens")
+
+
+def test_prefill_zero_input_full_tie():
+    L = synth.make_layer(37, **SMALL)
+    x = np.zeros((50, 256), np.uint16)
+    out, idx, w = run(L, x)
+    assert np.all(idx == np.arange(4)) and np.all(out == 0)
+
+
+@pytest.mark.parametrize("Is,norm", [(2112, True), (256, False)])
+def test_prefill_dense_layer(Is, norm):
+    L = synth.make_layer(38, hidden=256, inter=0, shared_inter=Is, n_experts=0, norm=norm, residual=norm)
+    x = synth.tokens(200, 256, stream=11)
+    out, _, _ = run(L, x)
+    compare(L, x, out, None, None, what="dense prefill")
+
+
+def test_prefill_matches_decode_routing_and_workspace_reuse():
+    # The same tokens through both paths select the same experts (the
+    # oracle checks each path's values), and one prefill workspace serves a
+    # larger and then a smaller call.
+    L = synth.make_layer(39, bias="zipf", norm=True, **SMALL)
+    dev = moe.DeviceLayer(L)
+    ws = torch.zeros(moe.moe_prefill_workspace_bytes(dev.desc, 700), dtype=torch.uint8, device="cuda")
+    for T in (700, 40):
+        x = synth.tokens(T, 256, stream=700 + T)
+        a = run(L, x, dev, ws)
+        b = run(L, x, dev, ws)
+        assert all(np.array_equal(u, v) for u, v in zip(a, b)), T
+        ref, _ = compare(L, x, *a, what=f"reuse T={T}")
+        for t0 in range(0, min(T, 64), 8):
+            yd, idd, _ = dev.decode(to_dev_bits(x[t0:t0 + 8]))
+            torch.cuda.synchronize()
+            for t in range(8):
+                if not ref["flag"][t0 + t]:
+                    assert set(idd.cpu().numpy()[t].tolist()) == set(a[1][t0 + t].tolist())
+
+
+def test_prefill_rejects_and_sizes():
+    L = synth.make_layer(40, **SMALL)
+    dev = moe.DeviceLayer(L)
+    assert moe.moe_prefill_workspace_bytes(dev.desc, 0) == 0
+    n = moe.moe_prefill_workspace_bytes(dev.desc, 100)
+    assert n > 0 and moe.moe_prefill_workspace_bytes(dev.desc, 200) > n
+    ws = torch.zeros(n - 256, dtype=torch.uint8, device="cuda")
+    x = to_dev_bits(synth.tokens(100, 256, stream=12))
+    y = torch.empty_like(x)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_prefill_layer(dev.desc, dev.weights, x, 100, 0, y, None, None, ws, ws.numel())
+    assert e.value.status == moe.MOE_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- full shape
+
+_cache = {}
+
+
+def full_layer(kind):
+    if kind not in _cache:
+        log(f"generating full layer {kind}")
+        if kind == "norm":
+            _cache[kind] = synth.make_layer(2, wtype="nvfp4", bias="zipf", norm=True, residual=True)
+        elif kind == "nvfp4":
+            _cache[kind] = synth.make_layer(0, wtype="nvfp4")
+        elif kind == "dense":
+            _cache[kind] = synth.make_layer(0, inter=0, shared_inter=5632, n_experts=0, norm=True, residual=True)
+    return _cache[kind]
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("kind,T", [("norm", 8192), ("nvfp4", 8192), ("dense", 2048)])
+def test_prefill_full_shape(kind, T):
+    # Residual layers are gated on the layer output with the residual add
+    # off (one BF16 ulp of a residual stream with |x| >= 2 exceeds the
+    # max-abs bar), and the add itself is checked exactly: one BF16 rounding
+    # of x + o.
+    log(f"test: prefill full shape {kind} T={T}")
+    L = full_layer(kind)
+    dev = moe.DeviceLayer(L)
+    x = synth.tokens(T, 2048, stream=900)
+    out, idx, w = run(L, x, dev, residual=0)
+    o = oracle.bf16_to_f64(out)
+    assert np.all(np.isfinite(o))
+    E = L["n_experts"]
+    if E:
+        check_routing_properties(L, idx, w)
+    s = sample_tokens(T, 96, T)
+    _, st = compare(dict(L, residual=0), x[s], out[s], idx[s] if E else None, w[s] if E else None,
+                    what=f"prefill full {kind} T={T}")
+    if L["residual"]:
+        yr, idx_r, _ = run(L, x, dev, residual=1)
+        assert np.array_equal(idx_r, idx)
+        xs, os_ = oracle.bf16_to_f64(x[s]), oracle.bf16_to_f64(out[s])
+        want = np.array([oracle.bf16_round(v) for v in (xs + os_).ravel()], np.uint16).reshape(xs.shape)
+        assert np.array_equal(yr[s], want)
+    if E:
+        counts = np.bincount(idx.reshape(-1), minlength=E)
+        st["rows_per_expert_min_max"] = (int(counts.min()), int(counts.max()))
+    log(f"  {st}")

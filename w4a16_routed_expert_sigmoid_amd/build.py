@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.cpp", "decode.hip", "repack.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "repack.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -279,18 +279,100 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
   return MOE_OK;
 }
 
+// Prefill workspace, carved in this order (each piece 256-byte aligned).
+struct PfLayout {
+  size_t xn, logits, topk_idx, topk_w, counts, offsets, cursors, n_tiles, tiles, sorted_tok, pair_pos, h, y, bytes;
+  int64_t max_tiles;
+};
+
+static constexpr int32_t kMaxPrefillTokens = 1 << 22;
+
+static PfLayout prefill_layout(const moe_layer_desc &d, int64_t T) {
+  PfLayout L;
+  const int64_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = E > 0 ? d.top_k : 0;
+  const int64_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  const int64_t P = T * k, rows = P + (d.shared_inter > 0 ? T : 0);
+  L.max_tiles = prefill_max_tiles(T, k, E, d.shared_inter > 0);
+  size_t o = 0;
+  L.xn = o; o += up(T * H * 2);
+  L.logits = o; o += up(T * E * 4);
+  L.topk_idx = o; o += up(P * 4);
+  L.topk_w = o; o += up(P * 4);
+  L.counts = o; o += up((E + 1) * 4);
+  L.offsets = o; o += up((E + 1) * 4);
+  L.cursors = o; o += up((E + 1) * 4);
+  L.n_tiles = o; o += up(4);
+  L.tiles = o; o += up(L.max_tiles * sizeof(PfTile));
+  L.sorted_tok = o; o += up(P * 4);
+  L.pair_pos = o; o += up(P * 4);
+  L.h = o; o += up(rows * Imax * 2);
+  L.y = o; o += up(rows * H * 2);
+  L.bytes = o;
+  return L;
+}
+
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {
-  (void)desc;
-  (void)n_tokens;
-  return 0;
+  if (check_desc(desc) != MOE_OK || n_tokens < 1 || n_tokens > kMaxPrefillTokens) return 0;
+  return prefill_layout(*desc, n_tokens).bytes;
 }
 
 moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                              int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
                              float *topk_w, void *ws, size_t ws_bytes, void *stream) {
-  (void)desc; (void)w; (void)x; (void)n_tokens; (void)residual; (void)y;
-  (void)topk_idx; (void)topk_w; (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 1) return MOE_ERR_INVALID_ARG;
+  if (n_tokens > kMaxPrefillTokens) return MOE_ERR_UNSUPPORTED;
+  st = check_weights(desc, w);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !ws || x == y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID_ARG;
+  const PfLayout L = prefill_layout(*desc, n_tokens);
+  if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
+
+  uint8_t *base = (uint8_t *)ws;
+  PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.T = n_tokens;
+  a.H = desc->hidden;
+  a.I = desc->n_experts > 0 ? desc->inter : 0;
+  a.Is = desc->shared_inter;
+  a.E = desc->n_experts;
+  a.k = desc->n_experts > 0 ? desc->top_k : 0;
+  a.wtype = desc->wtype;
+  a.residual = residual ? 1 : 0;
+  a.use_norm = w->norm_gain ? 1 : 0;
+  a.P = a.T * a.k;
+  a.max_tiles = (int)L.max_tiles;
+  a.eps = desc->norm_eps;
+  a.x = (const uint16_t *)x;
+  a.y = (uint16_t *)y;
+  a.router_w = (const uint16_t *)w->router_w;
+  a.router_b = w->router_b;
+  a.w_gate = (const uint8_t *)w->w_gate;
+  a.w_up = (const uint8_t *)w->w_up;
+  a.w_down = (const uint8_t *)w->w_down;
+  a.w_scale = w->w_scale;
+  a.sh_gate = (const uint8_t *)w->sh_gate;
+  a.sh_up = (const uint8_t *)w->sh_up;
+  a.sh_down = (const uint8_t *)w->sh_down;
+  a.sh_scale = w->sh_scale;
+  a.norm_gain = (const uint16_t *)w->norm_gain;
+  a.out_idx = topk_idx ? topk_idx : (int32_t *)(base + L.topk_idx);
+  a.out_w = topk_w ? topk_w : (float *)(base + L.topk_w);
+  a.xn = (uint16_t *)(base + L.xn);
+  a.logits = (float *)(base + L.logits);
+  a.counts = (int32_t *)(base + L.counts);
+  a.offsets = (int32_t *)(base + L.offsets);
+  a.cursors = (int32_t *)(base + L.cursors);
+  a.n_tiles = (int32_t *)(base + L.n_tiles);
+  a.tiles = (PfTile *)(base + L.tiles);
+  a.sorted_tok = (int32_t *)(base + L.sorted_tok);
+  a.pair_pos = (int32_t *)(base + L.pair_pos);
+  a.h_rows = (uint16_t *)(base + L.h);
+  a.y_rows = (uint16_t *)(base + L.y);
+  return hip_status(launch_prefill(a, (hipStream_t)stream));
 }
 
 moe_status moe_set_stage_events(void *const *events, int32_t n_events) {

@@ -161,6 +161,53 @@ __device__ inline float group_sum(float v, int width) {
   return v;
 }
 
+// Sum of a double over aligned groups of `width` lanes (each half of the
+// value moves with the 32-bit exchanges above).
+template <int O>
+__device__ inline double xor_lane_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xor_lane<O>((uint32_t)u), hi = xor_lane<O>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+__device__ inline double group_sum_f64(double v, int width) {
+  if (width > 1) v += xor_lane_f64<1>(v);
+  if (width > 2) v += xor_lane_f64<2>(v);
+  if (width > 4) v += xor_lane_f64<4>(v);
+  if (width > 8) v += xor_lane_f64<8>(v);
+  if (width > 16) v += xor_lane_f64<16>(v);
+  if (width > 32) v += xor_lane_f64<32>(v);
+  return v;
+}
+
+// FP64 -> BF16 bits, correctly rounded to nearest even: first to FP32 with
+// round-to-odd (round toward zero, then set the last bit when inexact),
+// then FP32 -> BF16 to nearest even; FP32 keeps 16 more bits than BF16, so
+// the two steps round once.
+__device__ inline uint32_t f64_to_bf16(double d) {
+  if (d != d) return 0x7fc0u;
+  const float f = (float)d;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != d) {
+    if (fabs(back) > fabs(d)) u -= 1u;  // one FP32 step toward zero
+    u |= 1u;
+  }
+  return f32_to_bf16(__uint_as_float(u));
+}
+
+// One element of a pre-norm output: BF16 of x * inv * g, rounded from the
+// product as FP64 gives it (inv = 1/sqrt(mean(x^2) + eps) in FP64).  The
+// FP32 product is within a few FP32 ulps of it, so it rounds the same way
+// unless it lies within 16 ulps of a BF16 rounding midpoint (low 16 bits
+// near 0x8000); those rare elements are redone in FP64.
+__device__ inline uint32_t norm_elem_bf16(float x, float g, float inv_f, double inv) {
+  const float p = x * inv_f * g;
+  const uint32_t low = __float_as_uint(p) & 0xffffu;
+  if (low - 0x7ff0u <= 0x20u) return f64_to_bf16((double)x * inv * (double)g);
+  return f32_to_bf16(p);
+}
+
 // Device pointers of the decode workspace, carved from one caller buffer.
 struct DecodeWs {
   uint32_t *counter;      // completion counter of the router kernel (kept 0)
@@ -193,6 +240,49 @@ struct DecodeArgs {
   float *out_w;
   DecodeWs ws;
 };
+
+// Prefill: one GEMM tile of up to 128 rows of one expert's segment.
+struct PfTile {
+  int p0, cnt, e;  // first row, rows (<= 128), expert (-1: the shared expert)
+};
+
+// Arguments of the prefill kernels (passed by value).  Row space of the
+// grouped GEMMs: rows [0, P) are the P = T*k (token, expert) pairs sorted
+// by expert, rows [P, P + T) the shared expert's, in token order.
+struct PrefillArgs {
+  int T, H, I, Is, E, k, wtype, residual, use_norm, P, max_tiles;
+  float eps;
+  const uint16_t *x;
+  uint16_t *y;
+  const uint16_t *router_w;
+  const float *router_b;
+  const uint8_t *w_gate, *w_up, *w_down;
+  const float *w_scale;
+  const uint8_t *sh_gate, *sh_up, *sh_down;
+  const float *sh_scale;
+  const uint16_t *norm_gain;
+  int32_t *out_idx;  // [T][k]
+  float *out_w;      // [T][k]
+  uint16_t *xn;      // [T][H] (pre-norm layers)
+  float *logits;     // [T][E]
+  int32_t *counts, *offsets, *cursors;  // [E + 1] each
+  int32_t *n_tiles;
+  PfTile *tiles;          // [max_tiles]
+  int32_t *sorted_tok;    // [P] token of each sorted row
+  int32_t *pair_pos;      // [T][k] row of each (token, k) pair
+  uint16_t *h_rows;       // [P + T][max(I, Is)] SiLU(g)*u, BF16
+  uint16_t *y_rows;       // [P + T][H] expert outputs, BF16
+};
+
+// Rows one 128-row tile holds and an upper bound of the tiles of a call.
+constexpr int kPrefillTileRows = 128;
+__host__ __device__ inline int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
+  const int64_t P = T * k;
+  const int64_t routed = E > 0 ? (P + kPrefillTileRows - 1) / kPrefillTileRows + (E < P ? E : P) : 0;
+  return routed + (shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
 hipError_t launch_repack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,

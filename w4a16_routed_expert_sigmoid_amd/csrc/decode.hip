@@ -67,6 +67,7 @@ __device__ __forceinline__ float fold4(float v0, float v1, float v2, float v3, i
 // as -inf; 0 is below every real key and marks "taken / absent".
 __device__ __forceinline__ uint32_t topk_key(float l) {
   if (l != l) l = -INFINITY;
+  l += 0.0f;  // -0 -> +0: equal logits tie by index
   const uint32_t u = __float_as_uint(l);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
@@ -247,21 +248,22 @@ __global__ __launch_bounds__(kWave) void k_router(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
   for (int t = 0; t < B; ++t) {
-    float inv = 1.f;
+    double inv = 1.0;
     if (a.use_norm) {
-      float ss = 0.f;
+      double ss = 0.0;  // squares of BF16 values are exact in FP64
       for (int c = lg; c < C; c += LPR) {
         uint32_t x[16];
         load16(a.x + (int64_t)t * H + c * 32, x);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float lo = bf16_to_f32(x[i] & 0xffffu), hi = bf16_to_f32(x[i] >> 16);
-          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+          const double lo = bf16_to_f32(x[i] & 0xffffu), hi = bf16_to_f32(x[i] >> 16);
+          ss = fma(lo, lo, fma(hi, hi, ss));
         }
       }
-      ss = group_sum(ss, LPR);
-      inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+      ss = group_sum_f64(ss, LPR);
+      inv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
     }
+    const float inv_f = (float)inv;
     float s = 0.f;
     for (int c = lg; c < C; c += LPR) {
       uint32_t x[16];
@@ -271,9 +273,9 @@ __global__ __launch_bounds__(kWave) void k_router(DecodeArgs a) {
         load16(a.norm_gain + c * 32, g);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float lo = bf16_to_f32(x[i] & 0xffffu) * inv * bf16_to_f32(g[i] & 0xffffu);
-          const float hi = bf16_to_f32(x[i] >> 16) * inv * bf16_to_f32(g[i] >> 16);
-          x[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+          const uint32_t lo = norm_elem_bf16(bf16_to_f32(x[i] & 0xffffu), bf16_to_f32(g[i] & 0xffffu), inv_f, inv);
+          const uint32_t hi = norm_elem_bf16(bf16_to_f32(x[i] >> 16), bf16_to_f32(g[i] >> 16), inv_f, inv);
+          x[i] = lo | (hi << 16);
         }
         if (store_xn) {
           uint4 *o = reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H + c * 32);

@@ -1,0 +1,535 @@
+// Prefill of the sigmoid-routed W4A16 MoE layer over T tokens: the same
+// per-token computation as the decode path, organised for the matrix cores.
+// "Day-0 Support for Flint on vLLM", section "Optimizations": the MoE kernel
+// also gives the largest prefill gain (8,192-token prefill measured).
+//
+//   k_pf_norm     (pre-norm layers) xn = BF16(RMSNorm(x) * gain), one wave per token
+//   k_pf_router   logits = xn W_r^T + b: GEMM on v_mfma_f32_32x32x16_bf16
+//   k_pf_topk     sigmoid top-k per token (one wave each), renormalised
+//                 weights, per-expert token counts (LDS histogram per block)
+//   k_pf_scan     expert offsets and the tile list: every expert's rows in
+//                 tiles of 128, then the shared expert's tiles
+//   k_pf_scatter  each (token, k) pair gets a row in its expert's segment
+//   k_pf_gateup   grouped GEMM over the tiles: gathered xn rows x the
+//                 expert's gate and up matrices (NVFP4 dequantised to BF16 in
+//                 LDS once per tile), epilogue h = BF16(SiLU(BF16(g)) BF16(u))
+//   k_pf_down     grouped GEMM: h rows x the expert's down matrix, epilogue
+//                 y = BF16(acc * S_down)
+//   k_pf_combine  out = BF16(sum_j w_j y_row(t,j) + y_shared(t)) (+ residual)
+//
+// Row space of the grouped GEMMs: rows [0, P) are the P = T*k (token,
+// expert) pairs sorted by expert; rows [P, P + T) are the shared expert's
+// (token order).  h and y are stored per row.
+#include "common.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int PBM = kPrefillTileRows;  // tile rows (tokens)
+constexpr int PBN = 128;  // tile columns
+constexpr int PBK = 32;   // K per stage (two 16-element NVFP4 blocks)
+constexpr int PLD = PBK + 8;  // LDS row stride in BF16 elements (padding)
+constexpr int PThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Shared GEMM machinery: 4 waves as 2x2, each wave 64x64 of the 128x128 tile
+// as 2x2 blocks of 32x32 (v_mfma_f32_32x32x16_bf16).  Lane layouts (checked
+// on the GPU): A lane l holds row l%32, k (l/32)*8..+8; B lane l holds column
+// l%32, k (l/32)*8..+8; C lane l, value i is row (i/4)*8 + (l/32)*4 + i%4,
+// column l%32.
+// ---------------------------------------------------------------------------
+
+
+
+// 16 FP4 elements (8 bytes, element 2i in the low nibble of byte i) times
+// the block scale s -> 16 BF16 (exact: E2M1 x E4M3 has <= 6 significant bits).
+__device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, float s, uint32_t (&o)[8]) {
+  const uint32_t w[2] = {w0, w1};
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x2 v;
+      switch (b) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 3); break;
+      }
+      o[d * 4 + b] = f32_to_bf16(v.x * s) | (f32_to_bf16(v.y * s) << 16);
+    }
+  }
+}
+
+// B row of one stage into LDS: 16 K-elements starting at k (k % 16 == 0) of
+// row n of matrix m (rows x K), as BF16.  Rows past the matrix are zero.
+template <int BT>
+__device__ __forceinline__ void stage_b(const uint8_t *m, int rows, int K, int n, int k, uint16_t *dst) {
+  uint4 o0, o1;
+  if (m == nullptr || n >= rows) {
+    o0 = o1 = make_uint4(0, 0, 0, 0);
+  } else if (BT == 1) {
+    const uint2 nib = *reinterpret_cast<const uint2 *>(m + (int64_t)n * (K / 2) + k / 2);
+    const uint8_t sb = m[(int64_t)rows * (K / 2) + ((int64_t)(n >> 3) * (K / 32) + k / 32) * 16 + (n & 7) * 2 +
+                         ((k / 16) & 1)];
+    uint32_t o[8];
+    dequant16(nib.x, nib.y, e4m3_to_f32(sb), o);
+    o0 = make_uint4(o[0], o[1], o[2], o[3]);
+    o1 = make_uint4(o[4], o[5], o[6], o[7]);
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(m) + (int64_t)n * K + k);
+    o0 = p[0];
+    o1 = p[1];
+  }
+  reinterpret_cast<uint4 *>(dst)[0] = o0;
+  reinterpret_cast<uint4 *>(dst)[1] = o1;
+}
+
+__device__ __forceinline__ void stage_a(const uint16_t *row, int k, uint16_t *dst) {
+  uint4 o0, o1;
+  if (row == nullptr) {
+    o0 = o1 = make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(row + k);
+    o0 = p[0];
+    o1 = p[1];
+  }
+  reinterpret_cast<uint4 *>(dst)[0] = o0;
+  reinterpret_cast<uint4 *>(dst)[1] = o1;
+}
+
+// One stage of MFMAs from LDS: acc[mb][nb] += A[wm*64+mb*32..][.] x B[wn*64+nb*32..][.]^T
+__device__ __forceinline__ void mfma_stage(const uint16_t *sA, const uint16_t *sB, f32x16 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int ks = 0; ks < PBK / 16; ++ks) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      a[mb] = *reinterpret_cast<const bf16x8 *>(sA + (wm * 64 + mb * 32 + (lane & 31)) * PLD + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      b[nb] = *reinterpret_cast<const bf16x8 *>(sB + (wn * 64 + nb * 32 + (lane & 31)) * PLD + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// Row / column of value i of acc[mb][nb] within the 128x128 tile.
+__device__ __forceinline__ int acc_row(int mb, int i) {
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+  return wm * 64 + mb * 32 + (i / 4) * 8 + (lane >> 5) * 4 + (i % 4);
+}
+__device__ __forceinline__ int acc_col(int nb) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+  return wn * 64 + nb * 32 + (lane & 31);
+}
+
+
+
+// ---------------------------------------------------------------------------
+// Small kernels
+// ---------------------------------------------------------------------------
+
+__global__ void k_pf_zero(PrefillArgs a) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.E + 1; i += gridDim.x * blockDim.x) a.counts[i] = 0;
+}
+
+__global__ __launch_bounds__(PThreads) void k_pf_norm(PrefillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (PThreads / 64) + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const uint16_t *xr = a.x + (int64_t)t * a.H;
+  double ss = 0.0;  // squares of BF16 values are exact in FP64
+  for (int i = lane * 8; i < a.H; i += 64 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double lo = bf16_to_f32(w[q] & 0xffffu), hi = bf16_to_f32(w[q] >> 16);
+      ss = fma(lo, lo, fma(hi, hi, ss));
+    }
+  }
+  ss = group_sum_f64(ss, 64);
+  const double inv = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+  const float inv_f = (float)inv;
+  for (int i = lane * 8; i < a.H; i += 64 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+    const uint4 g = *reinterpret_cast<const uint4 *>(a.norm_gain + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = norm_elem_bf16(bf16_to_f32(w[q] & 0xffffu), bf16_to_f32(gw[q] & 0xffffu), inv_f, inv);
+      const uint32_t hi = norm_elem_bf16(bf16_to_f32(w[q] >> 16), bf16_to_f32(gw[q] >> 16), inv_f, inv);
+      o[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4 *>(a.xn + (int64_t)t * a.H + i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Orderable 32-bit key of a logit (NaN as -inf; 0 = taken).
+__device__ __forceinline__ uint32_t pf_key(float l) {
+  if (l != l) l = -INFINITY;
+  l += 0.0f;  // -0 -> +0: equal logits tie by index
+  const uint32_t u = __float_as_uint(l);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t pf_wave_max(uint32_t m) {
+  m = max(m, xor_lane<1>(m));
+  m = max(m, xor_lane<2>(m));
+  m = max(m, xor_lane<4>(m));
+  m = max(m, xor_lane<8>(m));
+  m = max(m, xor_lane<16>(m));
+  m = max(m, xor_lane<32>(m));
+  return m;
+}
+
+constexpr int kPfTokensPerWave = 8;
+
+// Top-k of each token (one wave per token at a time), weights, counts.
+__global__ __launch_bounds__(PThreads) void k_pf_topk(PrefillArgs a) {
+  __shared__ uint32_t s_hist[kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < a.E; e += PThreads) s_hist[e] = 0u;
+  __syncthreads();
+  const int t0 = (blockIdx.x * (PThreads / 64) + wave) * kPfTokensPerWave;
+  for (int tt = 0; tt < kPfTokensPerWave; ++tt) {
+    const int t = t0 + tt;
+    if (t >= a.T) break;
+    const float *lt = a.logits + (int64_t)t * a.E;
+    constexpr int J = kMaxExperts / 64;
+    uint32_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + j * 64;
+      key[j] = (e < a.E) ? pf_key(lt[e]) : 0u;
+    }
+    int my_e = 0;
+    float my_l = 0.f;
+    for (int r = 0; r < a.k; ++r) {
+      uint32_t m = key[0];
+#pragma unroll
+      for (int j = 1; j < J; ++j) m = max(m, key[j]);
+      m = pf_wave_max(m);
+      int e = 0x7fffffff;
+#pragma unroll
+      for (int j = J - 1; j >= 0; --j) {
+        const unsigned long long b = __ballot(key[j] == m);
+        if (b) e = j * 64 + (int)__builtin_ctzll(b);
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) key[j] = (lane + j * 64 == e) ? 0u : key[j];
+      if (lane == r) {
+        my_e = e;
+        my_l = lt[e];
+      }
+    }
+    const float s = (lane < a.k) ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
+    float sum = 0.f;
+    for (int r = 0; r < a.k; ++r) sum += __shfl(s, r, 64);
+    if (lane < a.k) {
+      a.out_idx[(int64_t)t * a.k + lane] = my_e;
+      a.out_w[(int64_t)t * a.k + lane] = s / sum;
+      atomicAdd(&s_hist[my_e], 1u);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += PThreads)
+    if (s_hist[e]) atomicAdd(&a.counts[e], (int)s_hist[e]);
+}
+
+// Offsets of every expert's segment and the tile list: one block of 1024
+// threads, thread e owns expert e; two inclusive scans in LDS (rows and
+// tiles per expert).
+constexpr int kScanThreads = 1024;
+static_assert(kScanThreads >= kMaxExperts, "one scan thread per expert");
+
+__global__ __launch_bounds__(kScanThreads) void k_pf_scan(PrefillArgs a) {
+  __shared__ int s_rows[kScanThreads], s_tiles[kScanThreads];
+  const int e = threadIdx.x;
+  const int c = e < a.E ? a.counts[e] : 0;
+  const int nt = (c + PBM - 1) / PBM;
+  s_rows[e] = c;
+  s_tiles[e] = nt;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int vr = e >= o ? s_rows[e - o] : 0, vt = e >= o ? s_tiles[e - o] : 0;
+    __syncthreads();
+    s_rows[e] += vr;
+    s_tiles[e] += vt;
+    __syncthreads();
+  }
+  const int off = s_rows[e] - c, toff = s_tiles[e] - nt;
+  if (e < a.E) {
+    a.offsets[e] = off;
+    a.cursors[e] = off;
+    for (int i = 0; i < nt; ++i) a.tiles[toff + i] = PfTile{off + i * PBM, min(PBM, c - i * PBM), e};
+  }
+  const int routed_tiles = s_tiles[kScanThreads - 1];
+  const int shared_tiles = a.Is > 0 ? (a.T + PBM - 1) / PBM : 0;
+  for (int i = e; i < shared_tiles; i += kScanThreads)
+    a.tiles[routed_tiles + i] = PfTile{a.P + i * PBM, min(PBM, a.T - i * PBM), -1};
+  if (e == 0) {
+    a.offsets[a.E] = s_rows[kScanThreads - 1];
+    *a.n_tiles = routed_tiles + shared_tiles;
+  }
+}
+
+// Rows of the (token, k) pairs in their experts' segments.
+__global__ __launch_bounds__(PThreads) void k_pf_scatter(PrefillArgs a) {
+  __shared__ uint32_t s_cnt[kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  for (int e = threadIdx.x; e < a.E; e += PThreads) s_cnt[e] = 0u;
+  __syncthreads();
+  constexpr int kPairsPerThread = 2;
+  const int64_t q0 = ((int64_t)blockIdx.x * PThreads + threadIdx.x) * kPairsPerThread;
+  const int64_t P = (int64_t)a.T * a.k;
+  int rank[kPairsPerThread], ex[kPairsPerThread];
+#pragma unroll
+  for (int i = 0; i < kPairsPerThread; ++i) {
+    ex[i] = -1;
+    if (q0 + i < P) {
+      ex[i] = a.out_idx[q0 + i];
+      rank[i] = (int)atomicAdd(&s_cnt[ex[i]], 1u);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += PThreads)
+    s_base[e] = s_cnt[e] ? atomicAdd(&a.cursors[e], (int)s_cnt[e]) : 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPairsPerThread; ++i) {
+    if (ex[i] < 0) continue;
+    const int pos = s_base[ex[i]] + rank[i];
+    a.sorted_tok[pos] = (int)((q0 + i) / a.k);
+    a.pair_pos[q0 + i] = pos;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM kernels
+// ---------------------------------------------------------------------------
+
+// Router logits: rows = tokens, columns = experts, B = BF16 router weights.
+__global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[PBM * PLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[PBN * PLD];
+  const int m0 = blockIdx.x * PBM, n0 = blockIdx.y * PBN;
+  const uint16_t *xs = a.use_norm ? a.xn : a.x;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const uint16_t *arow = (m0 + r < a.T) ? xs + (int64_t)(m0 + r) * a.H : nullptr;
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < a.H; k0 += PBK) {
+    stage_a(arow, k0 + half * 16, sA + r * PLD + half * 16);
+    stage_b<0>(reinterpret_cast<const uint8_t *>(a.router_w), a.E, a.H, n0 + r, k0 + half * 16, sB + r * PLD + half * 16);
+    __syncthreads();
+    mfma_stage(sA, sB, acc);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + acc_col(nb);
+      if (n >= a.E) continue;
+      const float b = a.router_b ? a.router_b[n] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + acc_row(mb, i);
+        if (m < a.T) a.logits[(int64_t)m * a.E + n] = acc[mb][nb][i] + b;
+      }
+    }
+}
+
+// Gate/up of one tile: the 128 columns are [gate n0..n0+31, up n0..n0+31,
+// gate n0+32..n0+63, up n0+32..n0+63], so each lane holds g and u of the same
+// (row, column) in acc[mb][0] and acc[mb][1].
+template <int BT>
+__global__ __launch_bounds__(PThreads) void k_pf_gateup(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[PBM * PLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[PBN * PLD];
+  if ((int)blockIdx.x >= *a.n_tiles) return;
+  const PfTile tile = a.tiles[blockIdx.x];
+  const bool shared = tile.e < 0;
+  const int N = shared ? a.Is : a.I;
+  const int n0 = blockIdx.y * 64;
+  if (n0 >= N) return;
+  const uint16_t *xs = a.use_norm ? a.xn : a.x;
+  const int64_t mb_bytes = (BT == 1) ? nvfp4_matrix_bytes(a.I, a.H) : (int64_t)a.I * a.H * 2;
+  const uint8_t *Wg = shared ? a.sh_gate : a.w_gate + tile.e * mb_bytes;
+  const uint8_t *Wu = shared ? a.sh_up : a.w_up + tile.e * mb_bytes;
+  const float Sg = BT == 1 ? (shared ? a.sh_scale[0] : a.w_scale[3 * tile.e]) : 1.f;
+  const float Su = BT == 1 ? (shared ? a.sh_scale[1] : a.w_scale[3 * tile.e + 1]) : 1.f;
+
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const uint16_t *arow = nullptr;
+  if (r < tile.cnt) {
+    const int p = tile.p0 + r;
+    const int tok = shared ? p - a.P : a.sorted_tok[p];
+    arow = xs + (int64_t)tok * a.H;
+  }
+  // B row r of the tile: column c = r -> matrix (gate/up) and row of it
+  const int wn = r >> 6, nb = (r >> 5) & 1, c = r & 31;
+  const uint8_t *Bm = nb ? Wu : Wg;
+  const int brow = n0 + wn * 32 + c;
+
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < a.H; k0 += PBK) {
+    stage_a(arow, k0 + half * 16, sA + r * PLD + half * 16);
+    stage_b<BT>(Bm, N, a.H, brow, k0 + half * 16, sB + r * PLD + half * 16);
+    __syncthreads();
+    mfma_stage(sA, sB, acc);
+    __syncthreads();
+  }
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int n = n0 + (threadIdx.x >> 6 & 1) * 32 + ((threadIdx.x & 63) & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = acc_row(mb, i);
+      if (row < tile.cnt && n < N) {
+        const float g = round_bf16(acc[mb][0][i] * Sg);
+        const float u = round_bf16(acc[mb][1][i] * Su);
+        const float h = g / (1.0f + expf(-g)) * u;
+        a.h_rows[(int64_t)(tile.p0 + row) * Imax + n] = (uint16_t)f32_to_bf16(h);
+      }
+    }
+  }
+}
+
+// Down of one tile: h rows x the expert's down matrix -> y rows.
+template <int BT>
+__global__ __launch_bounds__(PThreads) void k_pf_down(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[PBM * PLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[PBN * PLD];
+  if ((int)blockIdx.x >= *a.n_tiles) return;
+  const PfTile tile = a.tiles[blockIdx.x];
+  const bool shared = tile.e < 0;
+  const int K = shared ? a.Is : a.I;
+  const int n0 = blockIdx.y * PBN;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int64_t mb_bytes = (BT == 1) ? nvfp4_matrix_bytes(a.H, a.I) : (int64_t)a.H * a.I * 2;
+  const uint8_t *Wd = shared ? a.sh_down : a.w_down + tile.e * mb_bytes;
+  const float Sd = BT == 1 ? (shared ? a.sh_scale[2] : a.w_scale[3 * tile.e + 2]) : 1.f;
+
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const uint16_t *arow = (r < tile.cnt) ? a.h_rows + (int64_t)(tile.p0 + r) * Imax : nullptr;
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < K; k0 += PBK) {
+    stage_a(arow, k0 + half * 16, sA + r * PLD + half * 16);
+    stage_b<BT>(Wd, a.H, K, n0 + r, k0 + half * 16, sB + r * PLD + half * 16);
+    __syncthreads();
+    mfma_stage(sA, sB, acc);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + acc_col(nb);
+      if (n >= a.H) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = acc_row(mb, i);
+        if (row < tile.cnt)
+          a.y_rows[(int64_t)(tile.p0 + row) * a.H + n] = (uint16_t)f32_to_bf16(acc[mb][nb][i] * Sd);
+      }
+    }
+}
+
+// out[t] = BF16(sum_j w_j y_row(t, j) + y_shared(t)) (+ residual); 8 columns
+// per thread, one block per token.
+__global__ __launch_bounds__(PThreads) void k_pf_combine(PrefillArgs a) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < a.H; c += PThreads * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < a.k; ++j) {
+      const int p = a.pair_pos[(int64_t)t * a.k + j];
+      const float w = a.out_w[(int64_t)t * a.k + j];
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.y_rows + (int64_t)p * a.H + c);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w, bf16_to_f32(q[i] & 0xffffu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, bf16_to_f32(q[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+    if (a.Is > 0) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(a.y_rows + (int64_t)(a.P + t) * a.H + c);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_to_f32(q[i] & 0xffffu);
+        acc[2 * i + 1] += bf16_to_f32(q[i] >> 16);
+      }
+    }
+    uint32_t o[4];
+    const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)t * a.H + c);
+    const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lo = round_bf16(acc[2 * i]), hi = round_bf16(acc[2 * i + 1]);
+      if (a.residual) {
+        lo += bf16_to_f32(xq[i] & 0xffffu);
+        hi += bf16_to_f32(xq[i] >> 16);
+      }
+      o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    }
+    *reinterpret_cast<uint4 *>(a.y + (int64_t)t * a.H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launcher
+// ---------------------------------------------------------------------------
+
+template <int BT>
+static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
+  hipError_t e;
+#define MOE_CK_LAUNCH() \
+  if ((e = hipGetLastError()) != hipSuccess) return e
+  hipLaunchKernelGGL(k_pf_zero, dim3(1), dim3(256), 0, s, a);
+  MOE_CK_LAUNCH();
+  if (a.use_norm) {
+    hipLaunchKernelGGL(k_pf_norm, dim3((a.T + 3) / 4), dim3(PThreads), 0, s, a);
+    MOE_CK_LAUNCH();
+  }
+  if (a.E > 0) {
+    hipLaunchKernelGGL(k_pf_router, dim3((a.T + PBM - 1) / PBM, (a.E + PBN - 1) / PBN), dim3(PThreads), 0, s, a);
+    MOE_CK_LAUNCH();
+    const int waves = (a.T + kPfTokensPerWave - 1) / kPfTokensPerWave;
+    hipLaunchKernelGGL(k_pf_topk, dim3((waves + 3) / 4), dim3(PThreads), 0, s, a);
+    MOE_CK_LAUNCH();
+  }
+  hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(kScanThreads), 0, s, a);
+  MOE_CK_LAUNCH();
+  if (a.E > 0) {
+    const int64_t pairs = (int64_t)a.T * a.k;
+    hipLaunchKernelGGL(k_pf_scatter, dim3((unsigned)((pairs + 2 * PThreads - 1) / (2 * PThreads))), dim3(PThreads),
+                       0, s, a);
+    MOE_CK_LAUNCH();
+  }
+  const int nmax = a.I > a.Is ? a.I : a.Is;
+  hipLaunchKernelGGL(k_pf_gateup<BT>, dim3(a.max_tiles, (nmax + 63) / 64), dim3(PThreads), 0, s, a);
+  MOE_CK_LAUNCH();
+  hipLaunchKernelGGL(k_pf_down<BT>, dim3(a.max_tiles, (a.H + PBN - 1) / PBN), dim3(PThreads), 0, s, a);
+  MOE_CK_LAUNCH();
+  hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(PThreads), 0, s, a);
+  MOE_CK_LAUNCH();
+#undef MOE_CK_LAUNCH
+  return hipSuccess;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+  return a.wtype == 1 ? launch_prefill_t<1>(a, s) : launch_prefill_t<0>(a, s);
+}
+
+}  // namespace moe
