@@ -72,6 +72,16 @@ def measured_traffic():
     return int(t.group(1))
 
 
+def prefill_flops(T, k=K):
+    """Algorithmic FLOPs of one prefill call: router GEMM, gate/up and down
+    of the T*k routed rows and the T shared rows (2 per multiply-add)."""
+    rows = T * k + T
+    return 2 * T * E * H + 2 * rows * (2 * I) * H + 2 * rows * H * I
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0                       # MI355X dense BF16, published
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -82,6 +92,9 @@ def parse():
     p.add_argument("--distinct-layers", type=int, default=4, help="independently generated layers")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--prefill-tokens", type=int, default=8192)
+    p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill leg")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
@@ -213,6 +226,10 @@ def run(args, dev):
         r8 = run_pool(8, True)
         log(f"batch 8: {r8['ms_step'] * 1e3 / n_layers:.2f} us/layer, stages {r8['stage_us']}")
 
+    pf = None
+    if args.workload == "layer" and not args.no_prefill:
+        pf = run_prefill(args, dev)
+
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -290,9 +307,52 @@ def run(args, dev):
                          "distinct_experts_mean": round(float(np.mean(r8["distinct"])), 2),
                          "tokens_per_s": round(8e6 / us8, 1), "stage_us": [round(v, 3) for v in r8["stage_us"]],
                          "step_equals_layer_calls": r8["step_equals_layers"]}
-    if r1["nonfinite"] or (r8 is not None and r8["nonfinite"]):
+    if pf is not None:
+        out["prefill"] = pf
+    if r1["nonfinite"] or (r8 is not None and r8["nonfinite"]) or (pf is not None and pf["nonfinite"]):
         out["warning"] = "non-finite outputs"
     return out
+
+
+def run_prefill(args, dev):
+    """One NVFP4 MoE layer over T prompt tokens (Zipf-biased router), timed
+    over whole moe_prefill_layer calls with inputs resident on the device."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    T = args.prefill_tokens
+    d = moe.DeviceLayer(synth.make_layer(0, wtype="nvfp4", bias="zipf"), device=dev)
+    x = torch.from_numpy(synth.tokens(T, H, stream=2000).view(np.int16)).to(dev)
+    y = torch.empty_like(x)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ws = torch.zeros(moe.moe_prefill_workspace_bytes(d.desc, T), dtype=torch.uint8, device=dev)
+
+    def call():
+        moe.moe_prefill_layer(d.desc, d.weights, x, T, 0, y, idx, w, ws, ws.numel())
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.prefill_steps
+    flops = prefill_flops(T)
+    tflops = flops / (ms * 1e-3) / 1e12
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=E)
+    log(f"prefill {T} tokens: {ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    return {"tokens": T, "ms_per_layer": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "gflop": round(flops / 1e9, 2), "tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "rows_per_expert_min_mean_max": [int(counts.min()), round(float(counts.mean()), 1), int(counts.max())],
+            "nonfinite": not torch.isfinite(y.view(torch.bfloat16).float()).all().item()}
 
 
 if __name__ == "__main__":

@@ -196,6 +196,16 @@ __device__ inline uint32_t f64_to_bf16(double d) {
   return f32_to_bf16(__uint_as_float(u));
 }
 
+// SiLU(g) * u in FP32 from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, each about 1 ulp).  Callers round the result to
+// BF16, where an FP32 error of a few ulps can only move a value that sits
+// at a BF16 rounding midpoint.  Very negative g gives 2^x = inf and a
+// (correctly) zero SiLU.
+__device__ inline float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // One element of a pre-norm output: BF16 of x * inv * g, rounded from the
 // product as FP64 gives it (inv = 1/sqrt(mean(x^2) + eps) in FP64).  The
 // FP32 product is within a few FP32 ulps of it, so it rounds the same way

@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
         for (int k2 = 0; k2 < (LPR == 2 ? 2 : 1); ++k2) {
           const float g = round_bf16((k2 ? g2 : gs) * Sg);
           const float uu = round_bf16((k2 ? u2 : us) * Su);
-          const float h = g / (1.0f + expf(-g)) * uu;
+          const float h = silu_mul(g, uu);
           a.ws.h[((int64_t)slot * B + t) * Imax + q * kRows + row + k2] = (uint16_t)f32_to_bf16(h);
         }
       }

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(PThreads) void k_pf_gateup(PrefillArgs a) {
       if (row < tile.cnt && n < N) {
         const float g = round_bf16(acc[mb][0][i] * Sg);
         const float u = round_bf16(acc[mb][1][i] * Su);
-        const float h = g / (1.0f + expf(-g)) * u;
+        const float h = silu_mul(g, u);
         a.h_rows[(int64_t)(tile.p0 + row) * Imax + n] = (uint16_t)f32_to_bf16(h);
       }
     }
@@ -443,6 +443,281 @@ __global__ __launch_bounds__(PThreads) void k_pf_down(PrefillArgs a) {
           a.y_rows[(int64_t)(tile.p0 + row) * a.H + n] = (uint16_t)f32_to_bf16(acc[mb][nb][i] * Sd);
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 grouped GEMM (gate/up and down).  A block of 8 waves (two per
+// SIMD, so one wave's dequantisation overlaps the other's MFMAs) computes
+// 128 rows of one tile against 512 weight rows; each wave owns 64 weight
+// rows (two 32-row MFMA column blocks) across all 128 tile rows (four
+// 32-row blocks): 4 x 2 accumulator tiles of 32x32 FP32.
+//   A (activation rows): global -> registers -> LDS, 128 K per stage,
+//     double-buffered, one barrier per stage; the next stage's loads are
+//     in flight during the current stage's MFMAs.
+//   B (weights): global -> registers directly (one stage ahead),
+//     dequantised in registers.  Within a 128-K stage, lane half
+//     h = lane/32 holds K elements [h*64, h*64 + 64) of its weight row
+//     (32 contiguous bytes), and MFMA step s uses elements h*64 + s*8 .. +8;
+//     the A fragments are read from LDS at the same K positions, so every K
+//     element meets its partner.
+//   A 32-row block of the tile that lies wholly past the tile's rows is
+//     skipped (no MFMA issued for it).
+//   The results leave through LDS as whole 16-byte row pieces.
+// ---------------------------------------------------------------------------
+
+constexpr int GWaves = 8;
+constexpr int GThreads = GWaves * kWave;
+constexpr int GBM = kPrefillTileRows;   // 128 tile rows
+constexpr int GBK = 128;                // K per stage
+constexpr int GLDA = GBK + 8;           // LDS row stride, BF16 elements (272 B)
+constexpr int GBN = GWaves * 64;        // weight rows per block
+constexpr int GChunk = 8;               // consecutive work items per XCD chunk
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 FP4 (one dword, element 2i in the low nibble of byte i) times the block
+// scale s -> 8 BF16 (the products are exact in BF16, so taking the upper
+// half of each FP32 product is exact).
+__device__ __forceinline__ bf16x8 dq8(uint32_t w, float s) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(v0.y * s), __float_as_uint(v0.x * s), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(v1.y * s), __float_as_uint(v1.x * s), 0x07060302u);
+  r.z = __builtin_amdgcn_perm(__float_as_uint(v2.y * s), __float_as_uint(v2.x * s), 0x07060302u);
+  r.w = __builtin_amdgcn_perm(__float_as_uint(v3.y * s), __float_as_uint(v3.x * s), 0x07060302u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Raw NVFP4 data of one lane for one stage and one weight row: 64 FP4
+// (8 dwords) and the 4 block scales (two 16-bit scale pairs).
+struct BRaw {
+  uint4 q0, q1;
+  uint32_t s0, s1;
+};
+
+// The lane's two 32-element chunks (c0 + 2h, c0 + 2h + 1) of weight row n
+// of a K-column matrix: nibbles from the row, the scale pair of each chunk
+// from the scale tile (n/8, chunk).  Chunks past K (and rows that do not
+// exist, ok == false) read as zero.
+__device__ __forceinline__ void load_b_stage(const uint8_t *nib_row, const uint8_t *scale_base, int n, int K,
+                                             int k0, int h, bool ok, BRaw &r) {
+  r.q0 = r.q1 = make_uint4(0, 0, 0, 0);
+  r.s0 = r.s1 = 0;
+  if (!ok) return;
+  const int c = (k0 >> 5) + 2 * h;
+  const int C = K >> 5;
+  const int64_t st = ((int64_t)(n >> 3) * C) * 16 + (n & 7) * 2;
+  if (c < C) {
+    r.q0 = *reinterpret_cast<const uint4 *>(nib_row + c * 16);
+    r.s0 = *reinterpret_cast<const uint16_t *>(scale_base + st + (int64_t)c * 16);
+  }
+  if (c + 1 < C) {
+    r.q1 = *reinterpret_cast<const uint4 *>(nib_row + (c + 1) * 16);
+    r.s1 = *reinterpret_cast<const uint16_t *>(scale_base + st + (int64_t)(c + 1) * 16);
+  }
+}
+
+// One wave's MFMAs for one stage: 8 K-steps x AMB 32-row blocks x 2 weight
+// blocks.  AMB is a compile-time count so the step loop is straight-line
+// code; the A fragments of step s + 1 are read from LDS before the MFMAs of
+// step s.
+template <int AMB>
+__device__ __forceinline__ void gemm_stage(const uint16_t *sA, const BRaw (&b)[2], f32x16 (&acc)[4][2]) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  float sc[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    sc[nb][0] = e4m3_to_f32(b[nb].s0 & 0xffu);
+    sc[nb][1] = e4m3_to_f32(b[nb].s0 >> 8);
+    sc[nb][2] = e4m3_to_f32(b[nb].s1 & 0xffu);
+    sc[nb][3] = e4m3_to_f32(b[nb].s1 >> 8);
+  }
+  const uint16_t *arow = sA + l32 * GLDA + h * 64;
+  bf16x8 af[2][AMB];
+#pragma unroll
+  for (int mb = 0; mb < AMB; ++mb) af[0][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 32 * GLDA);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s + 1 < 8) {
+#pragma unroll
+      for (int mb = 0; mb < AMB; ++mb)
+        af[(s + 1) & 1][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 32 * GLDA + (s + 1) * 8);
+    }
+    bf16x8 bf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint4 &q = s < 4 ? b[nb].q0 : b[nb].q1;
+      const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+      bf[nb] = dq8(w, sc[nb][s >> 1]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < AMB; ++mb) {
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[0], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[1], acc[mb][1], 0, 0, 0);
+    }
+  }
+}
+
+// K loop of one block: A stages through LDS (double-buffered), B stages
+// through registers (one stage ahead).
+template <int AMB>
+__device__ __forceinline__ void gemm_mainloop(uint16_t (*sA)[GBM * GLDA], const uint16_t *arow, int ar, int ap,
+                                              const uint8_t *const (&nib)[2], const uint8_t *const (&scl)[2],
+                                              const int (&nrow)[2], const bool (&bok)[2], int K,
+                                              f32x16 (&acc)[4][2]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const int S = (K + GBK - 1) / GBK;
+  uint4 av[4];
+  auto load_a = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = make_uint4(0, 0, 0, 0);
+    if (arow && k0 + ap * 32 < K) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(arow + k0 + ap * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = p[i];
+    }
+  };
+  auto store_a = [&](int buf) {
+    uint4 *d = reinterpret_cast<uint4 *>(&sA[buf][ar * GLDA + ap * 32]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = av[i];
+  };
+  BRaw bcur[2], bnext[2];
+  load_a(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) load_b_stage(nib[j], scl[j], nrow[j], K, 0, h, bok[j], bnext[j]);
+  store_a(0);
+  for (int st = 0; st < S; ++st) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bcur[j] = bnext[j];
+    if (st + 1 < S) {
+      load_a((st + 1) * GBK);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_b_stage(nib[j], scl[j], nrow[j], K, (st + 1) * GBK, h, bok[j], bnext[j]);
+    }
+    __syncthreads();
+    gemm_stage<AMB>(sA[st & 1], bcur, acc);
+    if (st + 1 < S) store_a((st + 1) & 1);
+  }
+}
+
+// The (tile, n-block) item of grid slot `slot`: items are spread over the 8
+// XCDs in chunks of GChunk consecutive items (neighbouring items share A
+// rows or the expert's weights in that XCD's L2).
+__device__ __forceinline__ int gemm_item(int slot) {
+  const int xcd = slot & 7, q = slot >> 3;
+  return ((q / GChunk) * 8 + xcd) * GChunk + (q % GChunk);
+}
+
+// MODE 0: gate/up (K = H) -> h rows; MODE 1: down (K = I or Is) -> y rows.
+template <int MODE>
+__global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nblk) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][GBM * GLDA];
+  const int w = gemm_item(blockIdx.x);
+  if (w >= *a.n_tiles * nblk) return;
+  const PfTile tile = a.tiles[w / nblk];
+  const int nb_i = w % nblk;
+  const bool shared = tile.e < 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int Iw = shared ? a.Is : a.I;
+  const int K = MODE == 0 ? a.H : Iw;
+  const int N = MODE == 0 ? Iw : a.H;
+  const int64_t mat_bytes = nvfp4_matrix_bytes(MODE == 0 ? a.I : a.H, MODE == 0 ? a.H : a.I);
+
+  // A rows: thread (ar, ap) loads 32 K-elements of tile row ar per stage.
+  const int ar = tid >> 2, ap = tid & 3;
+  const uint16_t *arow = nullptr;
+  if (ar < tile.cnt) {
+    const int p = tile.p0 + ar;
+    if (MODE == 0) {
+      const uint16_t *xs = a.use_norm ? a.xn : a.x;
+      arow = xs + (int64_t)(shared ? p - a.P : a.sorted_tok[p]) * a.H;
+    } else {
+      arow = a.h_rows + (int64_t)p * Imax;
+    }
+  }
+  // This lane's two weight rows.  Gate/up: a wave's first 32 weight rows
+  // are gate rows and its next 32 the up rows of the same 32 output columns.
+  const uint8_t *mats[2];
+  int nrow[2];
+  float tscale[2];
+  if (MODE == 0) {
+    const int hc = nb_i * (GBN / 2) + wave * 32 + l32;
+    mats[0] = shared ? a.sh_gate : a.w_gate + tile.e * mat_bytes;
+    mats[1] = shared ? a.sh_up : a.w_up + tile.e * mat_bytes;
+    nrow[0] = nrow[1] = hc;
+    tscale[0] = shared ? a.sh_scale[0] : a.w_scale[3 * tile.e];
+    tscale[1] = shared ? a.sh_scale[1] : a.w_scale[3 * tile.e + 1];
+  } else {
+    mats[0] = mats[1] = shared ? a.sh_down : a.w_down + tile.e * mat_bytes;
+    nrow[0] = nb_i * GBN + wave * 64 + l32;
+    nrow[1] = nrow[0] + 32;
+    tscale[0] = tscale[1] = shared ? a.sh_scale[2] : a.w_scale[3 * tile.e + 2];
+  }
+  const uint8_t *nib[2], *scl[2];
+  bool bok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bok[j] = nrow[j] < N;
+    nib[j] = mats[j] + (int64_t)nrow[j] * (K / 2);
+    scl[j] = mats[j] + (int64_t)N * (K / 2);
+  }
+  const int active_mb = (tile.cnt + 31) >> 5;
+  f32x16 acc[4][2] = {};
+  const uint8_t *const nibc[2] = {nib[0], nib[1]}, *const sclc[2] = {scl[0], scl[1]};
+  switch (active_mb) {
+    case 4: gemm_mainloop<4>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+    case 3: gemm_mainloop<3>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+    case 2: gemm_mainloop<2>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+    default: gemm_mainloop<1>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+  }
+
+  // Epilogue.  Value i of acc[mb][j] is tile row mb*32 + (i/4)*8 + h*4 + i%4
+  // and weight row nrow[j].  The BF16 results of RPP rows at a time go to
+  // LDS (the A buffers, free now) and leave as whole 16-byte row pieces.
+  constexpr int OC = MODE == 0 ? GBN / 2 : GBN;  // output columns of the block
+  constexpr int OS = OC + 8;                     // staging row stride (elements)
+  constexpr int RPP = MODE == 0 ? 128 : 64;      // rows per pass
+  static_assert(RPP * OS * 2 <= (int)sizeof(sA), "a staging pass fits the A buffers");
+  uint16_t *const stg = &sA[0][0];
+  const int col0 = nb_i * OC;
+  uint16_t *out = MODE == 0 ? a.h_rows : a.y_rows;
+  const int64_t ostride = MODE == 0 ? Imax : a.H;
+  constexpr int CPR = OC / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int pass = 0; pass < 128 / RPP; ++pass) {
+    if (pass * RPP >= tile.cnt) break;
+    __syncthreads();  // the A buffers (or the previous pass) are free
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= active_mb || mb * 32 / RPP != pass) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = mb * 32 - pass * RPP + (i >> 2) * 8 + h * 4 + (i & 3);
+        if (MODE == 0) {
+          const float g = round_bf16(acc[mb][0][i] * tscale[0]);
+          const float u = round_bf16(acc[mb][1][i] * tscale[1]);
+          stg[r * OS + wave * 32 + l32] = (uint16_t)f32_to_bf16(silu_mul(g, u));
+        } else {
+          stg[r * OS + wave * 64 + l32] = (uint16_t)f32_to_bf16(acc[mb][0][i] * tscale[0]);
+          stg[r * OS + wave * 64 + 32 + l32] = (uint16_t)f32_to_bf16(acc[mb][1][i] * tscale[1]);
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = min(RPP, tile.cnt - pass * RPP);
+    for (int qi = tid; qi < rows * CPR; qi += GThreads) {
+      const int r = qi / CPR, c8 = qi % CPR;
+      const int col = col0 + c8 * 8;
+      if (col >= N) continue;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + r * OS + c8 * 8);
+      *reinterpret_cast<uint4 *>(out + (int64_t)(tile.p0 + pass * RPP + r) * ostride + col) = v;
+    }
+  }
 }
 
 // out[t] = BF16(sum_j w_j y_row(t, j) + y_shared(t)) (+ residual); 8 columns
@@ -518,10 +793,22 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
     MOE_CK_LAUNCH();
   }
   const int nmax = a.I > a.Is ? a.I : a.Is;
-  hipLaunchKernelGGL(k_pf_gateup<BT>, dim3(a.max_tiles, (nmax + 63) / 64), dim3(PThreads), 0, s, a);
-  MOE_CK_LAUNCH();
-  hipLaunchKernelGGL(k_pf_down<BT>, dim3(a.max_tiles, (a.H + PBN - 1) / PBN), dim3(PThreads), 0, s, a);
-  MOE_CK_LAUNCH();
+  if (BT == 1) {
+    // grid: every (tile, n-block) item, rounded up to whole XCD chunks
+    const int nb_gu = (nmax + GBN / 2 - 1) / (GBN / 2), nb_dn = (a.H + GBN - 1) / GBN;
+    const int64_t round = 8 * GChunk;
+    const int64_t g_gu = ((int64_t)a.max_tiles * nb_gu + round - 1) / round * round;
+    const int64_t g_dn = ((int64_t)a.max_tiles * nb_dn + round - 1) / round * round;
+    hipLaunchKernelGGL(k_pf_gemm_fp4<0>, dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
+    MOE_CK_LAUNCH();
+    hipLaunchKernelGGL(k_pf_gemm_fp4<1>, dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
+    MOE_CK_LAUNCH();
+  } else {
+    hipLaunchKernelGGL(k_pf_gateup<BT>, dim3(a.max_tiles, (nmax + 63) / 64), dim3(PThreads), 0, s, a);
+    MOE_CK_LAUNCH();
+    hipLaunchKernelGGL(k_pf_down<BT>, dim3(a.max_tiles, (a.H + PBN - 1) / PBN), dim3(PThreads), 0, s, a);
+    MOE_CK_LAUNCH();
+  }
   hipLaunchKernelGGL(k_pf_combine, dim3(a.T), dim3(PThreads), 0, s, a);
   MOE_CK_LAUNCH();
 #undef MOE_CK_LAUNCH
