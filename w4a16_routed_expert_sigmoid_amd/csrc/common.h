@@ -22,7 +22,10 @@
 namespace moe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxBatch = 8;   // decode path: up to eight tokens
@@ -88,6 +91,23 @@ __device__ inline float dot8_fp4_bf16(uint32_t w, uint32_t x0, uint32_t x1, uint
   acc = dot2_bf16(MOE_FP4X2_TO_BF16X2(w, 2), x2, acc);
   acc = dot2_bf16(MOE_FP4X2_TO_BF16X2(w, 3), x3, acc);
   return acc;
+}
+
+// 8 FP4 (one dword, element 2i in the low nibble of byte i) times the block
+// scale s -> 8 BF16, an MFMA operand.  E2M1 x E4M3 has at most 6
+// significant bits, so each FP32 product is exact in BF16 and its upper
+// half is the BF16 value.
+__device__ __forceinline__ bf16x8 dq8(uint32_t w, float s) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(v0.y * s), __float_as_uint(v0.x * s), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(v1.y * s), __float_as_uint(v1.x * s), 0x07060302u);
+  r.z = __builtin_amdgcn_perm(__float_as_uint(v2.y * s), __float_as_uint(v2.x * s), 0x07060302u);
+  r.w = __builtin_amdgcn_perm(__float_as_uint(v3.y * s), __float_as_uint(v3.x * s), 0x07060302u);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // value of lane ^ O for a compile-time O: DPP within 16-lane rows (xor 1,

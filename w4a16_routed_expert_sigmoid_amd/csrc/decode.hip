@@ -233,77 +233,133 @@ __device__ __forceinline__ void dot_rows(const ChunkBF &cb, const uint32_t (&x)[
 // k_router: logits (and the pre-norm)
 // ---------------------------------------------------------------------------
 
-// One wave per block, one router row per lane group.  With a pre-norm each
-// lane group computes mean(x^2) over the whole row from its own chunks and
-// normalises the chunks it uses; block 0 also stores xn for the expert
-// kernels (the same code, hence the same bits, in every block).
-__global__ __launch_bounds__(kWave) void k_router(DecodeArgs a) {
+// Four waves per block.  The block first brings the batch's activations
+// into LDS (at most 64 KiB) and, with a pre-norm, normalises them there:
+// the sum of squares of each token in FP64 over the whole block, then every
+// element BF16(x * inv * gain).  Each lane group of LPR lanes then owns one
+// router row, loaded once, and takes its dot product with every token from
+// LDS.  Block 0 also stores xn for the expert kernels (every block computes
+// the same bits).
+constexpr int kRouterWaves = 4;
+constexpr int kRouterThreads = kRouterWaves * kWave;
+
+__global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
+  __shared__ uint4 s_x[kMaxBatch * 4096 / 8];  // [B][H] BF16, B * H <= 32768
+  __shared__ double s_ss[kRouterWaves][kMaxBatch];
   const int H = a.H, E = a.E, B = a.B;
   const int LPR = lanes_per_row(H), C = H / 32;
-  const int lane = threadIdx.x, lg = lane % LPR;
-  const int row = blockIdx.x * (kWave / LPR) + lane / LPR;
-  const bool store_xn = a.use_norm && blockIdx.x == 0 && lane < LPR;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
+  const int row = (blockIdx.x * kRouterWaves + wave) * (kWave / LPR) + lane / LPR;
+  const int n8 = H / 8;  // 16-byte pieces per token row
 
+  // The first chunk of this lane's router row and the first piece of the
+  // norm gain, loaded before anything else.
+  uint32_t w0[16];
+  if (row < E && lg < C) load16(a.router_w + (int64_t)row * H + lg * 32, w0);
+  uint4 g0 = make_uint4(0, 0, 0, 0);
+  if (a.use_norm && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+
+  // 1. activations -> LDS; sums of squares (exact per term in FP64)
+  double ss[kMaxBatch];
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.0;
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t) {
+    if (t >= B) break;
+    for (int i = tid; i < n8; i += kRouterThreads) {
+      const uint4 v = reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H)[i];
+      s_x[t * n8 + i] = v;
+      if (a.use_norm) {
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
+          ss[t] = fma(lo, lo, fma(hi, hi, ss[t]));
+        }
+      }
+    }
+  }
+  if (a.use_norm) {
+#pragma unroll
+    for (int t = 0; t < kMaxBatch; ++t) {
+      if (t >= B) break;
+      const double v = group_sum_f64(ss[t], kWave);
+      if (lane == 0) s_ss[wave][t] = v;
+    }
+  }
+  __syncthreads();
+
+  // 2. pre-norm in LDS: xn = BF16(x * inv * gain)
+  if (a.use_norm) {
+    double inv[kMaxBatch];
+#pragma unroll
+    for (int t = 0; t < kMaxBatch; ++t) {
+      inv[t] = 1.0;
+      if (t < B) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kRouterWaves; ++w) tot += s_ss[w][t];
+        inv[t] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+      }
+    }
+    for (int i = tid; i < n8; i += kRouterThreads) {
+      const uint4 gv = i == tid ? g0 : reinterpret_cast<const uint4 *>(a.norm_gain)[i];
+      const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int t = 0; t < kMaxBatch; ++t) {
+        if (t >= B) break;
+        const float inv_f = (float)inv[t];
+        const uint4 v = s_x[t * n8 + i];
+        uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv[t]);
+          const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv[t]);
+          q[j] = lo | (hi << 16);
+        }
+        const uint4 o = make_uint4(q[0], q[1], q[2], q[3]);
+        s_x[t * n8 + i] = o;
+        if (blockIdx.x == 0) reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = o;
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. router row x every token
+  if (row >= E) return;
   float acc[kMaxBatch];
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
-  for (int t = 0; t < B; ++t) {
-    double inv = 1.0;
-    if (a.use_norm) {
-      double ss = 0.0;  // squares of BF16 values are exact in FP64
-      for (int c = lg; c < C; c += LPR) {
-        uint32_t x[16];
-        load16(a.x + (int64_t)t * H + c * 32, x);
+  for (int c = lg; c < C; c += LPR) {
+    uint32_t w[16];
+    if (c == lg) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const double lo = bf16_to_f32(x[i] & 0xffffu), hi = bf16_to_f32(x[i] >> 16);
-          ss = fma(lo, lo, fma(hi, hi, ss));
-        }
-      }
-      ss = group_sum_f64(ss, LPR);
-      inv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
-    }
-    const float inv_f = (float)inv;
-    float s = 0.f;
-    for (int c = lg; c < C; c += LPR) {
-      uint32_t x[16];
-      load16(a.x + (int64_t)t * H + c * 32, x);
-      if (a.use_norm) {
-        uint32_t g[16];
-        load16(a.norm_gain + c * 32, g);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t lo = norm_elem_bf16(bf16_to_f32(x[i] & 0xffffu), bf16_to_f32(g[i] & 0xffffu), inv_f, inv);
-          const uint32_t hi = norm_elem_bf16(bf16_to_f32(x[i] >> 16), bf16_to_f32(g[i] >> 16), inv_f, inv);
-          x[i] = lo | (hi << 16);
-        }
-        if (store_xn) {
-          uint4 *o = reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H + c * 32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = make_uint4(x[i * 4], x[i * 4 + 1], x[i * 4 + 2], x[i * 4 + 3]);
-        }
-      }
-      if (row < E) {
-        uint32_t w[16];
-        load16(a.router_w + (int64_t)row * H + c * 32, w);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s = dot2_bf16(w[i], x[i], s);
-      }
+      for (int i = 0; i < 16; ++i) w[i] = w0[i];
+    } else {
+      load16(a.router_w + (int64_t)row * H + c * 32, w);
     }
 #pragma unroll
-    for (int tt = 0; tt < kMaxBatch; ++tt)
-      if (tt == t) acc[tt] = s;
+    for (int t = 0; t < kMaxBatch; ++t) {
+      if (t >= B) break;
+      const uint4 *xp = s_x + t * n8 + c * 4;
+      float s = acc[t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = xp[i];
+        s = dot2_bf16(w[i * 4 + 0], v.x, s);
+        s = dot2_bf16(w[i * 4 + 1], v.y, s);
+        s = dot2_bf16(w[i * 4 + 2], v.z, s);
+        s = dot2_bf16(w[i * 4 + 3], v.w, s);
+      }
+      acc[t] = s;
+    }
   }
-  if (row < E) {
-    const float bias = a.router_b ? a.router_b[row] : 0.f;
-    for (int t = 0; t < B; ++t) {
-      float v = 0.f;
+  const float bias = a.router_b ? a.router_b[row] : 0.f;
 #pragma unroll
-      for (int tt = 0; tt < kMaxBatch; ++tt)
-        if (tt == t) v = acc[tt];
-      v = group_sum(v, LPR);
-      if (lg == 0) a.ws.logits[t * E + row] = v + bias;
-    }
+  for (int t = 0; t < kMaxBatch; ++t) {
+    if (t >= B) break;
+    const float v = group_sum(acc[t], LPR);
+    if (lg == 0) a.ws.logits[t * E + row] = v + bias;
   }
 }
 
@@ -539,6 +595,228 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Batches of 2..8 tokens with NVFP4 weights: the expert GEMVs on the matrix
+// cores (v_mfma_f32_16x16x32_bf16, weights as the 16-row A operand, the
+// tokens as the 16 columns of B, padded with zeros).  Each weight element
+// is dequantised once, and the per-token work moves from the vector ALUs
+// to the matrix cores.
+//   Operand layout (checked on the GPU): A lane l holds row l%16, K
+//   elements (l/16)*8 .. +8; B lane l holds column l%16, the same K; C lane
+//   l value i is row (l/16)*4 + i, column l%16.
+//   K order: in a 128-K super-step lane part p = l/16 takes the 32-element
+//   chunk c = 4*ss + p (16 contiguous bytes of FP4 per weight row) and MFMA
+//   step s uses its elements s*8 .. +8, for A and B alike.
+// ---------------------------------------------------------------------------
+
+constexpr int kMmWaves = 8;
+constexpr int kMmRows = 64;  // gate/up weight rows per block (four 16-row groups)
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &q, int s) {
+  return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+}
+
+// Scale pair (blocks 2c, 2c+1) of row n of an N x K NVFP4 matrix.
+__device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int64_t K, int n, int c) {
+  return *reinterpret_cast<const uint16_t *>(m + N * K / 2 + ((int64_t)(n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2);
+}
+
+// Gate/up: block = (entry slot, 64-row group); the 8 waves split K.
+__global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
+  __shared__ float s_red[kMmWaves][32][kWave];
+  const int H = a.H, B = a.B, C = H / 32;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r16 = lane & 15, p = lane >> 4;
+  const int groups = (Imax + kMmRows - 1) / kMmRows;
+  const int slot = blockIdx.x / groups, row0 = (blockIdx.x % groups) * kMmRows;
+  const uint8_t *Wg, *Wu;
+  float Sg, Su;
+  uint32_t mask;
+  int N;
+  if (slot < a.max_routed) {
+    // the count and this slot's entry are read together (the entry arrays
+    // hold max_routed slots)
+    const int n_routed = *a.ws.n_routed;
+    const int e = a.ws.entry_expert[slot];
+    mask = a.ws.entry_mask[slot];
+    if (slot >= n_routed) return;
+    N = a.I;
+    const int64_t mb = nvfp4_matrix_bytes(a.I, H);
+    Wg = a.w_gate + e * mb;
+    Wu = a.w_up + e * mb;
+    Sg = a.w_scale[3 * e + 0];
+    Su = a.w_scale[3 * e + 1];
+  } else {
+    if (row0 >= a.Is) return;  // also: no shared expert
+    mask = (1u << B) - 1u;
+    N = a.Is;
+    Wg = a.sh_gate;
+    Wu = a.sh_up;
+    Sg = a.sh_scale[0];
+    Su = a.sh_scale[1];
+  }
+  if (row0 >= N) return;
+  const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int SS = (C + 3) / 4;
+  // Two super-steps per pass, all their loads issued before any math.
+  for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
+    uint4 qg[2][4], qu[2][4], xv[2][4];
+    uint32_t sg[2][4], su[2][4];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int ss = ss0 + v * kMmWaves;
+      const int c = ss * 4 + p;
+      const bool cok = ss < SS && c < C;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int n = row0 + rg * 16 + r16;
+        const bool ok = cok && n < N;
+        qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
+        su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
+      }
+      const bool tok = cok && r16 < B;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xv[v][s] = tok ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * H + c * 32 + s * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
+          const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
+          acc[rg][0] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
+          acc[rg][1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
+        }
+      }
+  }
+  // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
+      s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
+    const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMmWaves; ++w) {
+      g += s_red[w][rg * 8 + i][l];
+      u += s_red[w][rg * 8 + 4 + i][l];
+    }
+    const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
+    if (t < B && n < N && ((mask >> t) & 1u)) {
+      const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
+      a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
+    }
+  }
+}
+
+// Down and combine: block = 16 output rows; the 8 waves take the entries
+// (selected experts, then the shared expert) in turn, each over the full K.
+__global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
+  __shared__ float s_red[kMmWaves][4][kWave];
+  const int H = a.H, B = a.B;
+  const int K = (a.E > 0) ? a.I : a.Is;  // Is == I when both exist
+  const int C = K / 32, SS = (C + 3) / 4;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r16 = lane & 15, p = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int n_routed = (a.E > 0) ? *a.ws.n_routed : 0;
+  const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
+  float tot[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j = wave; j < n_entries; j += kMmWaves) {
+    const uint8_t *Wd;
+    float Sd;
+    uint32_t mask;
+    int hslot;
+    const float *wt = nullptr;
+    if (j < n_routed) {
+      const int e = a.ws.entry_expert[j];
+      mask = a.ws.entry_mask[j];
+      Wd = a.w_down + e * nvfp4_matrix_bytes(H, K);
+      Sd = a.w_scale[3 * e + 2];
+      hslot = j;
+      wt = a.ws.entry_w + j * kMaxBatch;
+    } else {
+      mask = (1u << B) - 1u;
+      Wd = a.sh_down;
+      Sd = a.sh_scale[2];
+      hslot = a.max_routed;
+    }
+    const bool tok = r16 < B && ((mask >> r16) & 1u);
+    const uint16_t *hrow = a.ws.h + ((int64_t)hslot * B + r16) * Imax;
+    const int n = row0 + r16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // four super-steps (512 K) per pass, all their loads issued first
+    for (int ss0 = 0; ss0 < SS; ss0 += 4) {
+      uint4 q[4], hv[4][4];
+      uint32_t sp[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = (ss0 + v) * 4 + p;
+        const bool cok = c < C;
+        q[v] = cok ? *reinterpret_cast<const uint4 *>(Wd + (int64_t)n * (K / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        sp[v] = cok ? scale_pair(Wd, H, K, n, c) : 0u;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          hv[v][s] = (cok && tok) ? *reinterpret_cast<const uint4 *>(hrow + c * 32 + s * 8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float sc = e4m3_to_f32((sp[v] >> (8 * (s >> 1))) & 0xffu);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              dq8(word_of(q[v], s), sc), __builtin_bit_cast(bf16x8, u32x4{hv[v][s].x, hv[v][s].y, hv[v][s].z, hv[v][s].w}),
+              acc, 0, 0, 0);
+        }
+    }
+    // this lane: rows (l/16)*4 + i, token l%16
+    const int t = lane & 15;
+    const float w = (t < B && ((mask >> t) & 1u)) ? (wt ? wt[t] : 1.0f) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] += w * round_bf16(acc[i] * Sd);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = tot[i];
+  __syncthreads();
+  if (tid < kWave) {
+    const int t = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMmWaves; ++w) v += s_red[w][i][lane];
+      if (t < B) {
+        const int64_t o = (int64_t)t * H + row0 + (lane >> 4) * 4 + i;
+        float r = round_bf16(v);
+        if (a.residual) r = bf16_to_f32(a.x[o]) + r;
+        a.y[o] = (uint16_t)f32_to_bf16(r);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_down: 4 output rows per block, every expert, weighted combine
 // ---------------------------------------------------------------------------
 
@@ -652,6 +930,15 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
     if ((e = launch(k_route, dim3(1), dim3(kRouteWaves * kWave), 0, stream, nullptr, nullptr, a)) != hipSuccess)
       return e;
   }
+  if (WT == 1 && MAXT > 1) {
+    const int Imax = a.I > a.Is ? a.I : a.Is;
+    const int groups = (Imax + kMmRows - 1) / kMmRows;
+    if ((e = launch(k_gateup_mm, dim3((a.max_routed + 1) * groups), dim3(kMmWaves * kWave), 0, stream,
+                    ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a)) != hipSuccess)
+      return e;
+    return launch(k_down_mm, dim3(a.H / 16), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
+                  ev ? ev[5] : nullptr, a);
+  }
   {
     const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
     const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
@@ -671,10 +958,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
   // measurement, eager launches only).
   hipError_t e;
   if (a.E > 0 || a.use_norm) {
-    const int rows_per_block = kWave / lanes_per_row(a.H);
+    const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
     const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
-    if ((e = launch(k_router, dim3(grid), dim3(kWave), 0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr,
-                    a)) != hipSuccess)
+    if ((e = launch(k_router, dim3(grid), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
+                    ev ? ev[1] : nullptr, a)) != hipSuccess)
       return e;
   }
   const int mt = a.B <= 1 ? 1 : a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8;

@@ -24,7 +24,6 @@
 
 namespace moe {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int PBM = kPrefillTileRows;  // tile rows (tokens)
@@ -472,24 +471,6 @@ constexpr int GBK = 128;                // K per stage
 constexpr int GLDA = GBK + 8;           // LDS row stride, BF16 elements (272 B)
 constexpr int GBN = GWaves * 64;        // weight rows per block
 constexpr int GChunk = 8;               // consecutive work items per XCD chunk
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// 8 FP4 (one dword, element 2i in the low nibble of byte i) times the block
-// scale s -> 8 BF16 (the products are exact in BF16, so taking the upper
-// half of each FP32 product is exact).
-__device__ __forceinline__ bf16x8 dq8(uint32_t w, float s) {
-  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  u32x4 r;
-  r.x = __builtin_amdgcn_perm(__float_as_uint(v0.y * s), __float_as_uint(v0.x * s), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(v1.y * s), __float_as_uint(v1.x * s), 0x07060302u);
-  r.z = __builtin_amdgcn_perm(__float_as_uint(v2.y * s), __float_as_uint(v2.x * s), 0x07060302u);
-  r.w = __builtin_amdgcn_perm(__float_as_uint(v3.y * s), __float_as_uint(v3.x * s), 0x07060302u);
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 // Raw NVFP4 data of one lane for one stage and one weight row: 64 FP4
 // (8 dwords) and the 4 block scales (two 16-bit scale pairs).
