@@ -190,15 +190,16 @@ __device__ __forceinline__ uint32_t pf_wave_max(uint32_t m) {
   return m;
 }
 
-constexpr int kPfTokensPerWave = 8;
+constexpr int kPfTokensPerWave = 2;
+constexpr int kPfTopkWaves = 16;
 
 // Top-k of each token (one wave per token at a time), weights, counts.
-__global__ __launch_bounds__(PThreads) void k_pf_topk(PrefillArgs a) {
+__global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a) {
   __shared__ uint32_t s_hist[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < a.E; e += PThreads) s_hist[e] = 0u;
+  for (int e = threadIdx.x; e < a.E; e += kPfTopkWaves * kWave) s_hist[e] = 0u;
   __syncthreads();
-  const int t0 = (blockIdx.x * (PThreads / 64) + wave) * kPfTokensPerWave;
+  const int t0 = (blockIdx.x * kPfTopkWaves + wave) * kPfTokensPerWave;
   for (int tt = 0; tt < kPfTokensPerWave; ++tt) {
     const int t = t0 + tt;
     if (t >= a.T) break;
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(PThreads) void k_pf_topk(PrefillArgs a) {
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += PThreads)
+  for (int e = threadIdx.x; e < a.E; e += kPfTopkWaves * kWave)
     if (s_hist[e]) atomicAdd(&a.counts[e], (int)s_hist[e]);
 }
 
@@ -317,34 +318,63 @@ __global__ __launch_bounds__(PThreads) void k_pf_scatter(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 
 // Router logits: rows = tokens, columns = experts, B = BF16 router weights.
+// 64 x 64 tiles (enough blocks to fill the GPU at E = 256); each of the 4
+// waves owns a 32 x 32 quarter; 64-K stages through LDS, the next stage's
+// loads in flight during the current stage's MFMAs.
+constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8;
+
 __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[PBM * PLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[PBN * PLD];
-  const int m0 = blockIdx.x * PBM, n0 = blockIdx.y * PBN;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][RBM * RLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][RBN * RLD];
+  const int m0 = blockIdx.x * RBM, n0 = blockIdx.y * RBN;
   const uint16_t *xs = a.use_norm ? a.xn : a.x;
-  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*16 .. +16 of the stage
   const uint16_t *arow = (m0 + r < a.T) ? xs + (int64_t)(m0 + r) * a.H : nullptr;
-  f32x16 acc[2][2] = {};
-  for (int k0 = 0; k0 < a.H; k0 += PBK) {
-    stage_a(arow, k0 + half * 16, sA + r * PLD + half * 16);
-    stage_b<0>(reinterpret_cast<const uint8_t *>(a.router_w), a.E, a.H, n0 + r, k0 + half * 16, sB + r * PLD + half * 16);
-    __syncthreads();
-    mfma_stage(sA, sB, acc);
-    __syncthreads();
-  }
+  const uint16_t *brow = (n0 + r < a.E) ? a.router_w + (int64_t)(n0 + r) * a.H : nullptr;
+  uint4 av[2], bv[2];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = n0 + acc_col(nb);
-      if (n >= a.E) continue;
-      const float b = a.router_b ? a.router_b[n] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + acc_row(mb, i);
-        if (m < a.T) a.logits[(int64_t)m * a.E + n] = acc[mb][nb][i] + b;
-      }
+    for (int i = 0; i < 2; ++i) {
+      av[i] = arow ? reinterpret_cast<const uint4 *>(arow + k0 + part * 16)[i] : make_uint4(0, 0, 0, 0);
+      bv[i] = brow ? reinterpret_cast<const uint4 *>(brow + k0 + part * 16)[i] : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      reinterpret_cast<uint4 *>(&sA[buf][r * RLD + part * 16])[i] = av[i];
+      reinterpret_cast<uint4 *>(&sB[buf][r * RLD + part * 16])[i] = bv[i];
+    }
+  };
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc = {};
+  const int S = (a.H + RBK - 1) / RBK;  // H % 32 == 0; a ragged last stage reads zeros past H
+  auto load_k = [&](int k0) {
+    if (k0 + part * 16 < a.H) load(k0);
+    else av[0] = av[1] = bv[0] = bv[1] = make_uint4(0, 0, 0, 0);
+  };
+  load_k(0);
+  store(0);
+  for (int st = 0; st < S; ++st) {
+    if (st + 1 < S) load_k((st + 1) * RBK);
+    __syncthreads();
+    const uint16_t *A = &sA[st & 1][(wm * 32 + (lane & 31)) * RLD + (lane >> 5) * 8];
+    const uint16_t *Bm = &sB[st & 1][(wn * 32 + (lane & 31)) * RLD + (lane >> 5) * 8];
+#pragma unroll
+    for (int ks = 0; ks < RBK / 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(A + ks * 16),
+                                                    *reinterpret_cast<const bf16x8 *>(Bm + ks * 16), acc, 0, 0, 0);
+    if (st + 1 < S) store((st + 1) & 1);
+  }
+  const int n = n0 + wn * 32 + (lane & 31);
+  if (n >= a.E) return;
+  const float bias = a.router_b ? a.router_b[n] : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + wm * 32 + (i / 4) * 8 + (lane >> 5) * 4 + (i % 4);
+    if (m < a.T) a.logits[(int64_t)m * a.E + n] = acc[i] + bias;
+  }
 }
 
 // Gate/up of one tile: the 128 columns are [gate n0..n0+31, up n0..n0+31,
@@ -759,10 +789,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
     MOE_CK_LAUNCH();
   }
   if (a.E > 0) {
-    hipLaunchKernelGGL(k_pf_router, dim3((a.T + PBM - 1) / PBM, (a.E + PBN - 1) / PBN), dim3(PThreads), 0, s, a);
+    hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
     const int waves = (a.T + kPfTokensPerWave - 1) / kPfTokensPerWave;
-    hipLaunchKernelGGL(k_pf_topk, dim3((waves + 3) / 4), dim3(PThreads), 0, s, a);
+    hipLaunchKernelGGL(k_pf_topk, dim3((waves + kPfTopkWaves - 1) / kPfTopkWaves), dim3(kPfTopkWaves * kWave), 0, s,
+                       a);
     MOE_CK_LAUNCH();
   }
   hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(kScanThreads), 0, s, a);
