@@ -1,11 +1,15 @@
 // Small-batch (1..8 tokens) decode path of the sigmoid-routed W4A16 MoE
-// layer: three kernels per layer and no cross-block synchronisation inside a
-// kernel (on this GPU a device-scope atomic on one address serialises across
-// blocks and an agent-scope fence writes back the L2, so the stages are
-// separated by kernel boundaries instead).
+// layer: three to five kernels per layer and no cross-block
+// synchronisation inside a kernel (on this GPU a device-scope atomic on one
+// address serialises across blocks and an agent-scope fence writes back the
+// L2, so the stages are separated by kernel boundaries instead).
 //
-//   k_router   pre-norm (optional, in registers) and router GEMV: logits
-//              l = W_r xn + b in FP32, one row per lane group.
+//   k_norm     (batches of 2..8 tokens with a pre-norm) one block per
+//              token: xn = BF16(x * inv * gain), inv from an FP64 sum of
+//              squares.
+//   k_router   router GEMV l = W_r xn + b in FP32, the batch staged in LDS
+//              (one token: the pre-norm is computed there too), one row
+//              per lane group, each row loaded once for every token.
 //   k_route    (batches of 2..8 tokens) one block: sigmoid top-k of every
 //              token, the sorted list of distinct selected experts with
 //              token masks, the renormalised combine weights.
@@ -13,13 +17,14 @@
 //              1 KB of logits, which is cheaper than another launch, and
 //              block 0 publishes the list) then runs its share of the gate
 //              and up GEMVs of one selected (or the shared) expert: FP4
-//              decoded to BF16 in registers once and reused for every token
-//              routed to the expert, FP32 accumulation, BF16 rounding of g
-//              and u, h = BF16(SiLU(g) u).
+//              decoded to BF16 in registers, FP32 accumulation, BF16
+//              rounding of g and u, h = BF16(SiLU(g) u).
 //   k_down     for every 4-row group of the output: the down GEMV of every
 //              selected expert and of the shared expert, BF16 rounding per
 //              expert, weighted FP32 combine in a fixed order, BF16 output
 //              (plus the residual when asked).
+//   k_gateup_mm, k_down_mm: the same two stages for batches of 2..8 tokens
+//              with NVFP4 weights, on the matrix cores (below).
 //
 // What is computed follows "Day-0 Support for Flint on vLLM" (sections
 // "Model architecture" and "Optimizations"): 256 experts, sigmoid top-6
@@ -233,31 +238,82 @@ __device__ __forceinline__ void dot_rows(const ChunkBF &cb, const uint32_t (&x)[
 // k_router: logits (and the pre-norm)
 // ---------------------------------------------------------------------------
 
-// Four waves per block.  The block first brings the batch's activations
-// into LDS (at most 64 KiB) and, with a pre-norm, normalises them there:
-// the sum of squares of each token in FP64 over the whole block, then every
-// element BF16(x * inv * gain).  Each lane group of LPR lanes then owns one
-// router row, loaded once, and takes its dot product with every token from
-// LDS.  Block 0 also stores xn for the expert kernels (every block computes
-// the same bits).
+// Pre-norm of one token per block (batches of 2..8, where doing it once
+// beats doing it in every router block): xn = BF16(x * inv * gain) with
+// inv = 1/sqrt(mean(x^2) + eps), the sum of squares exact per term in FP64.
+constexpr int kNormThreads = 256;
+
+__global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
+  __shared__ double s_part[kNormThreads / kWave];
+  const int H = a.H, t = blockIdx.x, n8 = H / 8;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H);
+  double ss = 0.0;
+  for (int i = tid; i < n8; i += kNormThreads) {
+    const uint4 v = xr[i];
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
+      ss = fma(lo, lo, fma(hi, hi, ss));
+    }
+  }
+  ss = group_sum_f64(ss, kWave);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / kWave; ++w) tot += s_part[w];
+  const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+  const float inv_f = (float)inv;
+  for (int i = tid; i < n8; i += kNormThreads) {
+    const uint4 v = xr[i], gv = reinterpret_cast<const uint4 *>(a.norm_gain)[i];
+    uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv);
+      const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv);
+      q[j] = lo | (hi << 16);
+    }
+    reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+}
+
+// Router GEMV, four waves per block.  The block first brings the batch's
+// activations into LDS (at most 64 KiB): xn when k_norm already wrote it
+// (xn_ready), else x, normalised there with a pre-norm (the sum of squares
+// of each token in FP64 over the whole block, then every element
+// BF16(x * inv * gain); block 0 also stores xn for the expert kernels, and
+// every block computes the same bits).  Each lane group of LPR lanes then
+// owns one router row, loaded once, and takes its dot product with every
+// token from LDS; lane j of a group takes the 16-byte pieces j, j + LPR,
+// ... of the row, so a wave's LDS and global accesses are contiguous.
 constexpr int kRouterWaves = 4;
 constexpr int kRouterThreads = kRouterWaves * kWave;
 
-__global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
+__global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_ready) {
   __shared__ uint4 s_x[kMaxBatch * 4096 / 8];  // [B][H] BF16, B * H <= 32768
   __shared__ double s_ss[kRouterWaves][kMaxBatch];
   const int H = a.H, E = a.E, B = a.B;
-  const int LPR = lanes_per_row(H), C = H / 32;
+  const int LPR = lanes_per_row(H);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
   const int row = (blockIdx.x * kRouterWaves + wave) * (kWave / LPR) + lane / LPR;
   const int n8 = H / 8;  // 16-byte pieces per token row
+  const bool norm_here = a.use_norm && !xn_ready;
+  const uint16_t *src = xn_ready ? a.ws.xn : a.x;
 
-  // The first chunk of this lane's router row and the first piece of the
-  // norm gain, loaded before anything else.
-  uint32_t w0[16];
-  if (row < E && lg < C) load16(a.router_w + (int64_t)row * H + lg * 32, w0);
+  // The first four pieces of this lane's router row and the first piece of
+  // the norm gain, loaded before anything else.
+  uint4 w0[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = lg + i * LPR;
+    w0[i] = (row < E && j < n8) ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)row * H)[j]
+                                : make_uint4(0, 0, 0, 0);
+  }
   uint4 g0 = make_uint4(0, 0, 0, 0);
-  if (a.use_norm && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+  if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
 
   // 1. activations -> LDS; sums of squares (exact per term in FP64)
   double ss[kMaxBatch];
@@ -267,9 +323,9 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
   for (int t = 0; t < kMaxBatch; ++t) {
     if (t >= B) break;
     for (int i = tid; i < n8; i += kRouterThreads) {
-      const uint4 v = reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H)[i];
+      const uint4 v = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
       s_x[t * n8 + i] = v;
-      if (a.use_norm) {
+      if (norm_here) {
         const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -279,7 +335,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
       }
     }
   }
-  if (a.use_norm) {
+  if (norm_here) {
 #pragma unroll
     for (int t = 0; t < kMaxBatch; ++t) {
       if (t >= B) break;
@@ -290,18 +346,18 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
   __syncthreads();
 
   // 2. pre-norm in LDS: xn = BF16(x * inv * gain)
-  if (a.use_norm) {
+  if (norm_here) {
+    // one thread per token forms 1/sqrt(mean(x^2) + eps) in FP64
+    if (tid < B) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kRouterWaves; ++w) tot += s_ss[w][tid];
+      s_ss[0][tid] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+    }
+    __syncthreads();
     double inv[kMaxBatch];
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
-      inv[t] = 1.0;
-      if (t < B) {
-        double tot = 0.0;
-#pragma unroll
-        for (int w = 0; w < kRouterWaves; ++w) tot += s_ss[w][t];
-        inv[t] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
-      }
-    }
+    for (int t = 0; t < kMaxBatch; ++t) inv[t] = t < B ? s_ss[0][t] : 1.0;
     for (int i = tid; i < n8; i += kRouterThreads) {
       const uint4 gv = i == tid ? g0 : reinterpret_cast<const uint4 *>(a.norm_gain)[i];
       const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -330,26 +386,28 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a) {
   float acc[kMaxBatch];
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
-  for (int c = lg; c < C; c += LPR) {
-    uint32_t w[16];
-    if (c == lg) {
+  for (int j0 = lg; j0 < n8; j0 += 4 * LPR) {
+    uint4 w[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w[i] = w0[i];
-    } else {
-      load16(a.router_w + (int64_t)row * H + c * 32, w);
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i * LPR;
+      if (j0 == lg) w[i] = w0[i];
+      else w[i] = j < n8 ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)row * H)[j] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kMaxBatch; ++t) {
       if (t >= B) break;
-      const uint4 *xp = s_x + t * n8 + c * 4;
       float s = acc[t];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v = xp[i];
-        s = dot2_bf16(w[i * 4 + 0], v.x, s);
-        s = dot2_bf16(w[i * 4 + 1], v.y, s);
-        s = dot2_bf16(w[i * 4 + 2], v.z, s);
-        s = dot2_bf16(w[i * 4 + 3], v.w, s);
+        const int j = j0 + i * LPR;
+        if (j < n8) {
+          const uint4 v = s_x[t * n8 + j];
+          s = dot2_bf16(w[i].x, v.x, s);
+          s = dot2_bf16(w[i].y, v.y, s);
+          s = dot2_bf16(w[i].z, v.z, s);
+          s = dot2_bf16(w[i].w, v.w, s);
+        }
       }
       acc[t] = s;
     }
@@ -957,11 +1015,17 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
   // gate/up kernel and of the down kernel (attached to the dispatches; for
   // measurement, eager launches only).
   hipError_t e;
-  if (a.E > 0 || a.use_norm) {
+  // Batches of several tokens normalise once in k_norm; a single token
+  // normalises inside the router blocks (one launch fewer).
+  const int xn_ready = (a.use_norm && a.B > 1) ? 1 : 0;
+  if (xn_ready) {
+    if ((e = launch(k_norm, dim3(a.B), dim3(kNormThreads), 0, stream, nullptr, nullptr, a)) != hipSuccess) return e;
+  }
+  if (a.E > 0 || (a.use_norm && !xn_ready)) {
     const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
     const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
     if ((e = launch(k_router, dim3(grid), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
-                    ev ? ev[1] : nullptr, a)) != hipSuccess)
+                    ev ? ev[1] : nullptr, a, xn_ready)) != hipSuccess)
       return e;
   }
   const int mt = a.B <= 1 ? 1 : a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8;
