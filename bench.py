@@ -13,6 +13,10 @@ from HBM.  Reported value: achieved HBM GB/s on the selected-weight bytes
 (router + 6 selected experts + shared expert), with microseconds per layer
 beside it; batch-8 figures (Zipf-biased router) are reported alongside.
 
+With the default workload the line also carries "prefill": one NVFP4 MoE
+layer over 8192 prompt tokens (Zipf-biased router), timed over whole
+moe_prefill_layer calls, with its rate against the BF16 matrix-core peak.
+
 --workload step49: the model's decode step instead: 2 dense SwiGLU layers
 (intermediate 5632) and 47 MoE layers, independent seeded weights, RMSNorm
 before each, batch 1, one HIP graph.

@@ -125,7 +125,8 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  * low-latency path the pages describe for up to eight requests: "Day-0
  * Support for Flint on vLLM", section "Optimizations").
  *  x [batch][H] BF16 in; y [batch][H] BF16 out.
- *  Per token: xn = x, or BF16(RMSNorm(x) * gain) when norm_gain is given;
+ *  Per token: xn = x, or, when norm_gain is given, xn = BF16(x /
+ *  sqrt(mean(x^2) + eps) * gain), rounded once from the exact value;
  *  logits l = W_r xn + b (FP32); the top_k experts by logit (ties: lower
  *  index) are kept with weights s_j / sum s, s = sigmoid(l); each selected
  *  expert and the shared expert run as SwiGLU with FP32 accumulation and a
@@ -175,14 +176,27 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
 moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
                            const void *x, int32_t batch, void *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes moe_prefill_layer needs for up to n_tokens tokens. */
+/* Workspace bytes moe_prefill_layer needs for n_tokens tokens (1 ..
+ * 4,194,304), or 0 if the description is invalid or n_tokens is out of
+ * range.  About (k + 1) * n_tokens * (H + max(I, Is)) * 2 bytes: the
+ * expert-sorted intermediate and output rows (342 MB at 8192 tokens for
+ * the full layer). */
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
 
-/* The same layer over n_tokens >= 1 prompt tokens (prefill; the pages
- * measure 8192-token prefill: "Day-0 Support for Flint on vLLM", section
- * "Optimizations").  Same per-token definition and arguments as
- * moe_decode_layer.  Tokens are grouped by expert and each expert runs as
- * a matrix product on the matrix cores. */
+/* The same layer over n_tokens prompt tokens (prefill; the pages measure
+ * 8192-token prefill: "Day-0 Support for Flint on vLLM", section
+ * "Optimizations").  Same per-token definition, arguments and outputs as
+ * moe_decode_layer, for any n_tokens in 1 .. 4,194,304: x, y [n_tokens][H];
+ * topk_idx, topk_w [n_tokens][k] (optional).  The tokens are grouped by
+ * selected expert (plus the shared expert over all tokens) and every
+ * expert's gate/up and down projections run as matrix products on the
+ * matrix cores; each token's result does not depend on the other tokens.
+ *  ws: device workspace of ws_bytes >= moe_prefill_workspace_bytes(desc,
+ *  n_tokens), 256-byte aligned; no zero-fill needed (every call
+ *  initialises what it uses).  Concurrent calls must not share it.
+ * Errors: as moe_decode_layer's shape checks (the same tiled shapes);
+ * INVALID_ARG for n_tokens < 1, null or misaligned pointers, x == y;
+ * UNSUPPORTED for n_tokens > 4,194,304; WORKSPACE; HIP. */
 moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                              int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
                              float *topk_w, void *ws, size_t ws_bytes, void *stream);
