@@ -533,8 +533,9 @@ __device__ __forceinline__ void load_b_stage(const uint8_t *nib_row, const uint8
 
 // One wave's MFMAs for one stage: 8 K-steps x AMB 32-row blocks x 2 weight
 // blocks.  AMB is a compile-time count so the step loop is straight-line
-// code; the A fragments of step s + 1 are read from LDS before the MFMAs of
-// step s.
+// code.  Software-pipelined: the weights of step s + 1 are dequantised and
+// its A fragments read from LDS before the MFMAs of step s are issued, so
+// the vector work of one step overlaps the matrix work of the previous.
 template <int AMB>
 __device__ __forceinline__ void gemm_stage(const uint16_t *sA, const BRaw (&b)[2], f32x16 (&acc)[4][2]) {
   const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
@@ -546,28 +547,30 @@ __device__ __forceinline__ void gemm_stage(const uint16_t *sA, const BRaw (&b)[2
     sc[nb][2] = e4m3_to_f32(b[nb].s1 & 0xffu);
     sc[nb][3] = e4m3_to_f32(b[nb].s1 >> 8);
   }
+  auto dq_step = [&](int s, int nb) {
+    const uint4 &q = s < 4 ? b[nb].q0 : b[nb].q1;
+    const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+    return dq8(w, sc[nb][s >> 1]);
+  };
   const uint16_t *arow = sA + l32 * GLDA + h * 64;
-  bf16x8 af[2][AMB];
+  bf16x8 af[2][AMB], bf[2][2];
 #pragma unroll
   for (int mb = 0; mb < AMB; ++mb) af[0][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 32 * GLDA);
+  bf[0][0] = dq_step(0, 0);
+  bf[0][1] = dq_step(0, 1);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     if (s + 1 < 8) {
 #pragma unroll
       for (int mb = 0; mb < AMB; ++mb)
         af[(s + 1) & 1][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 32 * GLDA + (s + 1) * 8);
-    }
-    bf16x8 bf[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint4 &q = s < 4 ? b[nb].q0 : b[nb].q1;
-      const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-      bf[nb] = dq8(w, sc[nb][s >> 1]);
+      bf[(s + 1) & 1][0] = dq_step(s + 1, 0);
+      bf[(s + 1) & 1][1] = dq_step(s + 1, 1);
     }
 #pragma unroll
     for (int mb = 0; mb < AMB; ++mb) {
-      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[0], acc[mb][0], 0, 0, 0);
-      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[1], acc[mb][1], 0, 0, 0);
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[s & 1][0], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mb], bf[s & 1][1], acc[mb][1], 0, 0, 0);
     }
   }
 }
