@@ -137,9 +137,9 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  *  topk_idx [batch][k] int32, topk_w [batch][k] FP32: optional (NULL)
  *  outputs, in descending score order.
  *  ws: device workspace of ws_bytes >= moe_decode_workspace_bytes(desc,
- *  batch).  It must be zero-filled before its first use; every call leaves
- *  its internal counter at zero again, so it can be reused without
- *  clearing.  Concurrent calls must not share a workspace.
+ *  batch), 256-byte aligned; no zero-fill needed (every call writes what
+ *  it reads before reading it), reusable across calls and batch sizes.
+ *  Concurrent calls must not share a workspace.
  * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
  * for shapes the kernels do not tile (H/32, I/32 and Is/32 must each be at
  * least 2 and either a power of two or at least 64; E at most 1024; Is == I
@@ -170,7 +170,7 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
  *  only); device pointers inside as for moe_decode_layer.
  *  x [batch][H], y [batch][H]: device BF16, must not alias.
  *  ws: device, ws_bytes >= moe_decode_step_workspace_bytes(descs, n_layers,
- *  batch), zero-filled before first use, reusable without clearing.
+ *  batch), 256-byte aligned; no zero-fill needed, reusable across calls.
  * Errors: as moe_decode_layer for each layer (the first failing layer's
  * status); INVALID_ARG for n_layers < 1 or differing hidden sizes. */
 moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,

@@ -31,7 +31,7 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t counter, logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, bytes;
+  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, bytes;
 };
 
 inline int max_routed_of(const moe_layer_desc &d, int B) {
@@ -46,7 +46,6 @@ WsLayout decode_layout(const moe_layer_desc &d, int B) {
   const size_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const size_t R = max_routed_of(d, B);
   size_t o = 0;
-  L.counter = o; o += up(4);
   L.logits = o; o += up(B * E * 4);
   L.xn = o; o += up(B * H * 2);
   L.n_routed = o; o += up(4);
@@ -202,7 +201,6 @@ static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_wei
   a.sh_down = (const uint8_t *)w->sh_down;
   a.sh_scale = w->sh_scale;
   a.norm_gain = (const uint16_t *)w->norm_gain;
-  a.ws.counter = (uint32_t *)(base + L.counter);
   a.ws.logits = (float *)(base + L.logits);
   a.ws.xn = (uint16_t *)(base + L.xn);
   a.ws.n_routed = (int32_t *)(base + L.n_routed);

@@ -240,7 +240,6 @@ __device__ inline uint32_t norm_elem_bf16(float x, float g, float inv_f, double 
 
 // Device pointers of the decode workspace, carved from one caller buffer.
 struct DecodeWs {
-  uint32_t *counter;      // completion counter of the router kernel (kept 0)
   float *logits;          // [B][E]
   uint16_t *xn;           // [B][H] normalised input (pre-norm layers)
   int32_t *n_routed;      // number of distinct selected experts

@@ -1,8 +1,10 @@
 // Small-batch (1..8 tokens) decode path of the sigmoid-routed W4A16 MoE
 // layer: three to five kernels per layer and no cross-block
-// synchronisation inside a kernel (on this GPU a device-scope atomic on one
-// address serialises across blocks and an agent-scope fence writes back the
-// L2, so the stages are separated by kernel boundaries instead).
+// synchronisation inside a kernel.  The stages are separated by kernel
+// boundaries: on this GPU a device-scope atomic on one address serialises
+// across blocks, an agent-scope fence writes back the L2, and data that
+// many blocks read right after another block wrote it must come from
+// memory rather than from each XCD's L2.
 //
 //   k_norm     (batches of 2..8 tokens with a pre-norm) one block per
 //              token: xn = BF16(x * inv * gain), inv from an FP64 sum of
@@ -315,18 +317,23 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   uint4 g0 = make_uint4(0, 0, 0, 0);
   if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
 
-  // 1. activations -> LDS; sums of squares (exact per term in FP64)
+  // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
+  // thread's pieces of every token are loaded before any is stored, so the
+  // loads are in flight together.
   double ss[kMaxBatch];
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.0;
+  for (int i = tid; i < n8; i += kRouterThreads) {
+    uint4 v[kMaxBatch];
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) {
-    if (t >= B) break;
-    for (int i = tid; i < n8; i += kRouterThreads) {
-      const uint4 v = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
-      s_x[t * n8 + i] = v;
+    for (int t = 0; t < kMaxBatch; ++t)
+      if (t < B) v[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
+#pragma unroll
+    for (int t = 0; t < kMaxBatch; ++t) {
+      if (t >= B) break;
+      s_x[t * n8 + i] = v[t];
       if (norm_here) {
-        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t q[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
@@ -552,7 +559,7 @@ __device__ __forceinline__ void dot_tokens(const ChunkBF &cb, const uint16_t *xs
 template <int WT, int MAXT>
 __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
   __shared__ Routing R;
-  __shared__ uint32_t s_mark[MAXT == 1 ? kMaxExperts : 1];
+  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks; several: read from the workspace
 
   const int H = a.H, I = a.I, B = a.B;
   const int LPR = lanes_per_row(H), C = H / 32;
@@ -720,7 +727,8 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int SS = (C + 3) / 4;
-  // Two super-steps per pass, all their loads issued before any math.
+  // Two super-steps per pass, all their loads issued before any math, in
+  // the order the math consumes them (tokens, then row group by row group).
   for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
     uint4 qg[2][4], qu[2][4], xv[2][4];
     uint32_t sg[2][4], su[2][4];
@@ -729,28 +737,28 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
       const int ss = ss0 + v * kMmWaves;
       const int c = ss * 4 + p;
       const bool cok = ss < SS && c < C;
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n = row0 + rg * 16 + r16;
-        const bool ok = cok && n < N;
-        qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
-        su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
-      }
       const bool tok = cok && r16 < B;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         xv[v][s] = tok ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * H + c * 32 + s * 8)
                        : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int n = row0 + rg * 16 + r16;
+        const bool ok = cok && n < N;
+        qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
+        qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
+      }
     }
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
+      for (int rg = 0; rg < 4; ++rg) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
           const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
           const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
           acc[rg][0] =
@@ -787,89 +795,131 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
   }
 }
 
-// Down and combine: block = 16 output rows; the 8 waves take the entries
-// (selected experts, then the shared expert) in turn, each over the full K.
+// One piece (two 128-K super-steps of each K half) of one entry's down
+// weights and h, as one lane loads it.
+struct DnPiece {
+  uint4 q[2], hv[2][4];
+  uint32_t sp[2];
+  float sd, w;  // the entry's FP32 tensor scale and this lane's token weight
+};
+
+// Down and combine: block = 8 output rows; the 8 waves take the entries
+// (selected experts, then the shared expert) in turn, each over the full K,
+// loading the next piece while the current one is multiplied.
+//   The 16x16 MFMA tile is split in two along K: A row m holds weight row
+//   m & 7 over K half m >> 3, B column n holds token n & 7 over K half
+//   n >> 3, so the C entries with m >> 3 == n >> 3 are the two half-K
+//   products of (row, token) and the rest are discarded; lane l and lane
+//   l ^ 40 hold the two halves.  8-row blocks put H/8 blocks on the GPU,
+//   each owning its rows outright (no cross-block combine).
 __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
   __shared__ float s_red[kMmWaves][4][kWave];
   const int H = a.H, B = a.B;
   const int K = (a.E > 0) ? a.I : a.Is;  // Is == I when both exist
-  const int C = K / 32, SS = (C + 3) / 4;
+  const int C = K / 32, C2 = (C + 1) / 2, NP = (C2 + 7) / 8;  // chunks per K half; 8-chunk pieces
   const int Imax = a.I > a.Is ? a.I : a.Is;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int r16 = lane & 15, p = lane >> 4;
-  const int row0 = blockIdx.x * 16;
+  const int m = lane & 15, p = lane >> 4, r8 = m & 7, kh = m >> 3;
+  const int row0 = blockIdx.x * 8;
+  const int n = row0 + r8;
+  const int64_t mbytes = nvfp4_matrix_bytes(H, K);
+  float tot[4] = {0.f, 0.f, 0.f, 0.f};
+  // The entry arrays hold max_routed slots: the first 64 of this wave's
+  // slots are read together with the count.
+  int e_l = -1;
+  uint32_t m_l = 0u;
+  if (wave + lane * kMmWaves < a.max_routed) {
+    e_l = a.ws.entry_expert[wave + lane * kMmWaves];
+    m_l = a.ws.entry_mask[wave + lane * kMmWaves];
+  }
   const int n_routed = (a.E > 0) ? *a.ws.n_routed : 0;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
-  float tot[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = wave; j < n_entries; j += kMmWaves) {
-    const uint8_t *Wd;
-    float Sd;
-    uint32_t mask;
-    int hslot;
-    const float *wt = nullptr;
-    if (j < n_routed) {
-      const int e = a.ws.entry_expert[j];
-      mask = a.ws.entry_mask[j];
-      Wd = a.w_down + e * nvfp4_matrix_bytes(H, K);
-      Sd = a.w_scale[3 * e + 2];
-      hslot = j;
-      wt = a.ws.entry_w + j * kMaxBatch;
-    } else {
-      mask = (1u << B) - 1u;
-      Wd = a.sh_down;
-      Sd = a.sh_scale[2];
-      hslot = a.max_routed;
+  const int mine = wave < n_entries ? (n_entries - wave + kMmWaves - 1) / kMmWaves : 0;
+
+  for (int i0 = 0; i0 < mine; i0 += kWave) {
+    // lane i holds the expert (-1: shared) and token mask of this wave's
+    // entry i0 + i
+    {
+      const int j = wave + (i0 + lane) * kMmWaves;
+      if (i0 > 0 && j < n_routed) {
+        e_l = a.ws.entry_expert[j];
+        m_l = a.ws.entry_mask[j];
+      }
+      if (j >= n_routed) {
+        e_l = -1;
+        m_l = (1u << B) - 1u;
+      }
     }
-    const bool tok = r16 < B && ((mask >> r16) & 1u);
-    const uint16_t *hrow = a.ws.h + ((int64_t)hslot * B + r16) * Imax;
-    const int n = row0 + r16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // four super-steps (512 K) per pass, all their loads issued first
-    for (int ss0 = 0; ss0 < SS; ss0 += 4) {
-      uint4 q[4], hv[4][4];
-      uint32_t sp[4];
+    const int cnt = min(mine - i0, kWave), nu = cnt * NP;
+    auto load = [&](int u, DnPiece &L) __attribute__((always_inline)) {
+      const int ii = u / NP, pc = u - ii * NP;
+      const int e = __builtin_amdgcn_readlane(e_l, ii);
+      const uint32_t msk = (uint32_t)__builtin_amdgcn_readlane((int)m_l, ii);
+      const int j = wave + (i0 + ii) * kMmWaves;
+      const uint8_t *Wd = e >= 0 ? a.w_down + e * mbytes : a.sh_down;
+      const bool tok = r8 < B && ((msk >> r8) & 1u);  // B column m: token m & 7
+      const uint16_t *hrow = a.ws.h + ((int64_t)(e >= 0 ? j : a.max_routed) * B + r8) * Imax;
+      L.sd = e >= 0 ? a.w_scale[3 * e + 2] : a.sh_scale[2];
+      const int t = lane & 15;  // C column of this lane after the MFMAs: token t & 7
+      L.w = ((t & 7) < B && ((msk >> (t & 7)) & 1u)) ? (e >= 0 ? a.ws.entry_w[j * kMaxBatch + (t & 7)] : 1.0f) : 0.f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = (ss0 + v) * 4 + p;
-        const bool cok = c < C;
-        q[v] = cok ? *reinterpret_cast<const uint4 *>(Wd + (int64_t)n * (K / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        sp[v] = cok ? scale_pair(Wd, H, K, n, c) : 0u;
+      for (int v = 0; v < 2; ++v) {
+        const int cc = (pc * 2 + v) * 4 + p;  // chunk within this lane's K half
+        const int c = kh * C2 + cc;
+        const bool cok = cc < C2 && c < C;
+        L.q[v] = cok ? *reinterpret_cast<const uint4 *>(Wd + (int64_t)n * (K / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        L.sp[v] = cok ? scale_pair(Wd, H, K, n, c) : 0u;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          hv[v][s] = (cok && tok) ? *reinterpret_cast<const uint4 *>(hrow + c * 32 + s * 8) : make_uint4(0, 0, 0, 0);
+          L.hv[v][s] = (cok && tok) ? *reinterpret_cast<const uint4 *>(hrow + c * 32 + s * 8) : make_uint4(0, 0, 0, 0);
       }
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int u, const DnPiece &L) __attribute__((always_inline)) {
+      const int ii = u / NP, pc = u - ii * NP;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const float sc = e4m3_to_f32((sp[v] >> (8 * (s >> 1))) & 0xffu);
+          const float sc = e4m3_to_f32((L.sp[v] >> (8 * (s >> 1))) & 0xffu);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              dq8(word_of(q[v], s), sc), __builtin_bit_cast(bf16x8, u32x4{hv[v][s].x, hv[v][s].y, hv[v][s].z, hv[v][s].w}),
-              acc, 0, 0, 0);
+              dq8(word_of(L.q[v], s), sc),
+              __builtin_bit_cast(bf16x8, u32x4{L.hv[v][s].x, L.hv[v][s].y, L.hv[v][s].z, L.hv[v][s].w}), acc, 0, 0, 0);
         }
-    }
-    // this lane: rows (l/16)*4 + i, token l%16
-    const int t = lane & 15;
-    const float w = (t < B && ((mask >> t) & 1u)) ? (wt ? wt[t] : 1.0f) : 0.f;
+      if (pc == NP - 1) {
+        // entry done: lanes l < 32 with l & 8 == 0 add the other K half
+        // (lane l ^ 40) and hold rows (l/16)*4 + i of token l & 7
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tot[i] += w * round_bf16(acc[i] * Sd);
+        for (int i = 0; i < 4; ++i) {
+          const float full = acc[i] + xor_lane<8>(xor_lane<32>(acc[i]));
+          tot[i] += L.w * round_bf16(full * L.sd);
+        }
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    DnPiece P0, P1;
+    if (nu > 0) load(0, P0);
+    for (int u = 0; u < nu; u += 2) {
+      if (u + 1 < nu) load(u + 1, P1);
+      step(u, P0);
+      if (u + 2 < nu) load(u + 2, P0);
+      if (u + 1 < nu) step(u + 1, P1);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = tot[i];
   __syncthreads();
-  if (tid < kWave) {
-    const int t = lane & 15;
+  const int t = lane & 7;
+  if (tid < 32 && (lane & 8) == 0 && t < B) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kMmWaves; ++w) v += s_red[w][i][lane];
-      if (t < B) {
-        const int64_t o = (int64_t)t * H + row0 + (lane >> 4) * 4 + i;
-        float r = round_bf16(v);
-        if (a.residual) r = bf16_to_f32(a.x[o]) + r;
-        a.y[o] = (uint16_t)f32_to_bf16(r);
-      }
+      const int64_t o = (int64_t)t * H + row0 + (lane >> 4) * 4 + i;
+      float r = round_bf16(v);
+      if (a.residual) r = bf16_to_f32(a.x[o]) + r;
+      a.y[o] = (uint16_t)f32_to_bf16(r);
     }
   }
 }
@@ -994,7 +1044,7 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
     if ((e = launch(k_gateup_mm, dim3((a.max_routed + 1) * groups), dim3(kMmWaves * kWave), 0, stream,
                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a)) != hipSuccess)
       return e;
-    return launch(k_down_mm, dim3(a.H / 16), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
+    return launch(k_down_mm, dim3(a.H / 8), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
                   ev ? ev[5] : nullptr, a);
   }
   {
