@@ -171,6 +171,29 @@ def test_workspace_reuse_across_batches_and_determinism():
         compare(L, x, *a, what=f"reuse B={B}")
 
 
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_one_token_handover_garbage_workspace_changing_inputs(fill):
+    # One token: the expert kernel hands h from its gate/up blocks to its
+    # down blocks through the workspace (words, per-XCD tickets, flags and
+    # copies).  A workspace that starts as garbage, and back-to-back calls
+    # with different tokens and layers (so stale data from the previous call
+    # would be wrong), must each give that call's own result.
+    L1 = synth.make_layer(20, bias="zipf", norm=True, **SMALL)
+    L2 = synth.make_layer(21, **SMALL)
+    d1, d2 = moe.DeviceLayer(L1), moe.DeviceLayer(L2)
+    n = max(moe.moe_decode_workspace_bytes(d.desc, 8) for d in (d1, d2))
+    if fill == "ones":
+        ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    else:
+        g = torch.Generator(device="cpu").manual_seed(5)
+        ws = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).cuda()
+    seq = [(L1, d1, 1), (L2, d2, 1), (L1, d1, 8), (L1, d1, 1), (L2, d2, 1), (L2, d2, 3), (L1, d1, 1)]
+    for i, (L, d, B) in enumerate(seq):
+        x = synth.tokens(B, 256, stream=800 + i)
+        out, idx, w = run(L, x, d, ws)
+        compare(L, x, out, idx, w, what=f"hand-over {fill} call {i} B={B}")
+
+
 # ---------------------------------------------------------------- full shapes
 
 _cache = {}

@@ -31,7 +31,8 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, bytes;
+  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, epoch, xcd_ticket, xcd_flag, xcd_h, bytes;
+  size_t stage_elems;
 };
 
 inline int max_routed_of(const moe_layer_desc &d, int B) {
@@ -55,6 +56,14 @@ WsLayout decode_layout(const moe_layer_desc &d, int B) {
   L.topk_idx = o; o += up(B * k * 4);
   L.topk_w = o; o += up(B * k * 4);
   L.h = o; o += up((R + 1) * B * Imax * 2);
+  // one-token path (also reserved at larger batches, so that a workspace
+  // sized for batch b serves every smaller batch)
+  const size_t R1 = max_routed_of(d, 1);
+  L.stage_elems = ((R1 + 1) * Imax + 127) / 128 * 128;
+  L.epoch = o; o += up(4);
+  L.xcd_ticket = o; o += kXcdSlots * 256;
+  L.xcd_flag = o; o += kXcdSlots * 256;
+  L.xcd_h = o; o += up(kXcdSlots * L.stage_elems * 2);
   L.bytes = o;
   return L;
 }
@@ -210,6 +219,11 @@ static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_wei
   a.ws.topk_idx = (int32_t *)(base + L.topk_idx);
   a.ws.topk_w = (float *)(base + L.topk_w);
   a.ws.h = (uint16_t *)(base + L.h);
+  a.ws.epoch = (uint32_t *)(base + L.epoch);
+  a.ws.xcd_ticket = (uint32_t *)(base + L.xcd_ticket);
+  a.ws.xcd_flag = (uint32_t *)(base + L.xcd_flag);
+  a.ws.xcd_h = (uint16_t *)(base + L.xcd_h);
+  a.ws.stage_elems = (int64_t)L.stage_elems;
   a.ws.bytes = L.bytes;
   a.out_idx = topk_idx ? topk_idx : a.ws.topk_idx;
   a.out_w = topk_w ? topk_w : a.ws.topk_w;

@@ -30,6 +30,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxBatch = 8;   // decode path: up to eight tokens
 constexpr int kMaxTopK = 8;
+constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
 constexpr int kMaxExperts = 1024;
 
 __host__ __device__ inline int64_t nvfp4_nibble_bytes(int64_t n, int64_t k) { return n * k / 2; }
@@ -249,6 +250,12 @@ struct DecodeWs {
   int32_t *topk_idx;      // [B][k] (used when the caller passes none)
   float *topk_w;          // [B][k]
   uint16_t *h;            // [(max_routed + 1)][B][Imax] SiLU(g)*u, BF16
+  // one token (gate/up and down in one kernel):
+  uint32_t *epoch;        // call number, advanced by the router kernel
+  uint32_t *xcd_ticket;   // [kXcdSlots][64] word 0: down blocks that arrived on that XCD
+  uint32_t *xcd_flag;     // [kXcdSlots][64] word 0: epoch once the XCD's copy of h is complete
+  uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
+  int64_t stage_elems;    // (one-token max_routed + 1) * Imax, rounded up to 128
   size_t bytes;
 };
 

@@ -1,10 +1,11 @@
 // Small-batch (1..8 tokens) decode path of the sigmoid-routed W4A16 MoE
-// layer: three to five kernels per layer and no cross-block
-// synchronisation inside a kernel.  The stages are separated by kernel
-// boundaries: on this GPU a device-scope atomic on one address serialises
-// across blocks, an agent-scope fence writes back the L2, and data that
-// many blocks read right after another block wrote it must come from
-// memory rather than from each XCD's L2.
+// layer: two to five kernels per layer.  Most stages are separated by
+// kernel boundaries: on this GPU a device-scope atomic on one address
+// serialises across blocks, an agent-scope fence writes back the L2, and
+// data that many blocks read right after another block wrote it must come
+// from memory rather than from each XCD's L2.  The one-token expert kernel
+// hands h over inside the kernel instead, with one reader per XCD going to
+// memory and the rest reading that XCD's L2.
 //
 //   k_norm     (batches of 2..8 tokens with a pre-norm) one block per
 //              token: xn = BF16(x * inv * gain), inv from an FP64 sum of
@@ -25,6 +26,9 @@
 //              selected expert and of the shared expert, BF16 rounding per
 //              expert, weighted FP32 combine in a fixed order, BF16 output
 //              (plus the residual when asked).
+//   k_experts_b1 (one token, routed experts present) k_gateup and k_down
+//              as one kernel: h is handed from the gate/up blocks to the
+//              down blocks inside the kernel, once per XCD (below).
 //   k_gateup_mm, k_down_mm: the same two stages for batches of 2..8 tokens
 //              with NVFP4 weights, on the matrix cores (below).
 //
@@ -316,6 +320,22 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   }
   uint4 g0 = make_uint4(0, 0, 0, 0);
   if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+  if (B == 1 && E > 0) {
+    // One token: the expert kernel hands h over through words, per-XCD
+    // tickets and per-XCD flags that start every call at zero; a flag is
+    // raised to the call number, which is never zero.
+    const int nw = (a.max_routed + 1) * (a.I > a.Is ? a.I : a.Is) / 2;
+    uint32_t *hw = reinterpret_cast<uint32_t *>(a.ws.h);
+    for (int i = blockIdx.x * kRouterThreads + tid; i < nw + 2 * kXcdSlots; i += gridDim.x * kRouterThreads) {
+      uint32_t *w = i < nw ? hw + i
+                           : i < nw + kXcdSlots ? a.ws.xcd_ticket + (i - nw) * 64 : a.ws.xcd_flag + (i - nw - kXcdSlots) * 64;
+      __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      const uint32_t e = *a.ws.epoch + 1u;
+      *a.ws.epoch = e ? e : 1u;
+    }
+  }
 
   // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
   // thread's pieces of every token are loaded before any is stored, so the
@@ -556,24 +576,31 @@ __device__ __forceinline__ void dot_tokens(const ChunkBF &cb, const uint16_t *xs
   });
 }
 
-template <int WT, int MAXT>
-__global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
-  __shared__ Routing R;
-  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks; several: read from the workspace
+// h handed to the down blocks of the same kernel (one token): every 32-bit
+// word (two BF16 values) is written with an agent-scope atomic store as the
+// complement of its bits, so that a reader can tell a written word from the
+// zero the router kernel leaves there; a BF16 0xFFFF (a NaN) is stored as
+// the canonical NaN, so no written word is 0.
+__device__ __forceinline__ uint32_t h_canon(uint32_t b) { return b == 0xffffu ? 0x7fc0u : b; }
 
+// Gate/up GEMVs of block `bid`: 4-row units of the selected experts, then
+// of the shared expert.  PUB: publish h as above (one token only).
+template <int WT, int MAXT, bool PUB>
+__device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routing &R, uint32_t *s_mark) {
+  static_assert(!PUB || MAXT == 1, "published h is the one-token layout");
   const int H = a.H, I = a.I, B = a.B;
   const int LPR = lanes_per_row(H), C = H / 32;
   const int groups = kGateupWaves * (kWave / LPR);
   const int lane = threadIdx.x & (kWave - 1), lg = lane % LPR;
-  const int u = blockIdx.x * groups + threadIdx.x / LPR;  // 4-row unit of this lane group
+  const int u = bid * groups + threadIdx.x / LPR;  // 4-row unit of this lane group
   const int routed_units = a.max_routed * (I / kRows);
 
-  if (a.E > 0 && ((int)blockIdx.x * groups < routed_units || blockIdx.x == 0)) {
+  if (a.E > 0 && (bid * groups < routed_units || bid == 0)) {
     if (MAXT == 1) {
       // One token: every block selects the experts itself (cheaper than a
       // separate launch); block 0 publishes the list for the down kernel.
       build_routing(a, R, s_mark, kGateupWaves);
-      if (blockIdx.x == 0) publish_routing(a, R);
+      if (bid == 0) publish_routing(a, R);
     } else {
       // Several tokens: the routing kernel already wrote the list.
       if (threadIdx.x == 0) R.n = *a.ws.n_routed;
@@ -646,7 +673,19 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
       float g2 = 0.f, u2 = 0.f;
       const float gs = fold4(ag[t][0], ag[t][1], ag[t][2], ag[t][3], LPR, row, &g2);
       const float us = fold4(au[t][0], au[t][1], au[t][2], au[t][3], LPR, row, &u2);
-      if (lg < (LPR == 2 ? 2 : kRows) && ((mask >> t) & 1u)) {
+      if constexpr (PUB) {
+        // rows (row, row + 1) in one word: with 2-lane groups a lane holds
+        // both; otherwise lanes 0 and 1 of the group (rows 0 and 2) take
+        // rows 1 and 3 from lanes 2 and 3
+        const uint32_t h0 = h_canon(f32_to_bf16(silu_mul(round_bf16(gs * Sg), round_bf16(us * Su))));
+        uint32_t h1;
+        if (LPR == 2) h1 = h_canon(f32_to_bf16(silu_mul(round_bf16(g2 * Sg), round_bf16(u2 * Su))));
+        else h1 = xor_lane<2>(h0);
+        if (lg < 2 && mask) {
+          uint32_t *hw = reinterpret_cast<uint32_t *>(a.ws.h + (int64_t)slot * Imax + q * kRows + row);
+          __hip_atomic_store(hw, ~(h0 | (h1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else if (lg < (LPR == 2 ? 2 : kRows) && ((mask >> t) & 1u)) {
         // with 2-lane groups each lane holds two rows
         for (int k2 = 0; k2 < (LPR == 2 ? 2 : 1); ++k2) {
           const float g = round_bf16((k2 ? g2 : gs) * Sg);
@@ -657,6 +696,13 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
       }
     }
   });
+}
+
+template <int WT, int MAXT>
+__global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks; several: read from the workspace
+  gateup_block<WT, MAXT, false>(a, blockIdx.x, R, s_mark);
 }
 
 // ---------------------------------------------------------------------------
@@ -1016,6 +1062,170 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_experts_b1: one token, gate/up and down in one kernel.
+//   Blocks below gu_blocks run the gate/up GEMVs and publish h word by word
+//   (h_canon).  The others each own 8 output rows (two 4-row halves of 2
+//   waves) and derive the routing themselves.  On every XCD the first down
+//   block to arrive (a ticket) copies h once into that XCD's stage through
+//   memory, polling each word until it is written, and raises the XCD's
+//   flag (the call number); the XCD's other down blocks poll the
+//   flag and read the stage from the XCD's L2 (drop_cu_cache), so h
+//   crosses the XCD boundary eight times, not once per block.  Producers
+//   never wait and are dispatched first; every wait is bounded.
+// ---------------------------------------------------------------------------
+
+// Drops this CU's cached lines, so that the next plain loads are served by
+// the XCD's L2 (which holds what other CUs of the XCD stored).  Measured on
+// MI355X: a flag stored by another block of the same XCD is seen about
+// 0.4 us after the store this way, while loads with the sc0 policy alone
+// can keep hitting a stale line in the CU cache.
+__device__ __forceinline__ void drop_cu_cache() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// Poll rounds (each ends in a short sleep) before a wait on another block
+// of the same kernel gives up; reached only if that block never wrote.
+constexpr int kWaitSpin = 1 << 20;
+
+constexpr int kDnHalf = 2 * kWave;  // threads per 4-row half of a down block
+
+template <int WT>
+__device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, Routing &R, uint32_t *s_mark,
+                                              float (&s_part)[2][kMaxDownSlots][kRows], int &s_lead) {
+  const int H = a.H, K = a.I;  // experts present: Is is I or 0
+  const int LPR = lanes_per_row(K), C = K / 32;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), lg = lane % LPR;
+  const int half = tid / kDnHalf, ht = tid % kDnHalf;
+  const int gi = ht / LPR;  // entry slot of a pass
+  const int slots_all = kDnHalf / LPR;
+  const int slots = slots_all < kMaxDownSlots ? slots_all : kMaxDownSlots;
+  const int r0 = dbid * (2 * kRows) + half * kRows;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const uint32_t epoch = *a.ws.epoch;
+  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcdSlots - 1);  // HW_REG_XCC_ID[3:0]
+  if (tid == 0)
+    s_lead = __hip_atomic_fetch_add(a.ws.xcd_ticket + xcc * 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+  build_routing(a, R, s_mark, kGateupWaves);  // ends with a barrier
+  const bool lead = s_lead != 0;
+  const int n_routed = R.n;
+  const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
+  uint16_t *stage = a.ws.xcd_h + (int64_t)xcc * a.ws.stage_elems;
+  float total = 0.f;  // threads ht < 4: row r0 + ht
+
+  for (int pass = 0; pass * slots < n_entries; ++pass) {
+    for (int i = ht; i < slots * kRows; i += kDnHalf) (&s_part[half][0][0])[i] = 0.f;
+    const int j = (gi < slots) ? pass * slots + gi : n_entries;
+    const uint8_t *Wd = nullptr;
+    float Sd = 1.f, w = 0.f;
+    int hslot = 0;
+    if (j < n_routed) {
+      const int e = R.expert[j];
+      const int64_t mb = (WT == 1) ? nvfp4_matrix_bytes(H, K) : (int64_t)H * K * 2;
+      Wd = a.w_down + e * mb;
+      if (WT == 1) Sd = a.w_scale[3 * e + 2];
+      hslot = j;
+      for (int r = 0; r < a.k; ++r)
+        if (R.sel[0][r] == e) w = R.w[0][r];
+    } else if (j == n_routed && j < n_entries) {
+      Wd = a.sh_down;
+      if (WT == 1) Sd = a.sh_scale[2];
+      hslot = a.max_routed;
+      w = 1.f;
+    }
+    // this lane's first weight chunk, loaded before the wait
+    ChunkRaw cr;
+    if (Wd) load_rows<WT>(Wd, H, K, r0, lg, cr);
+    if (pass == 0) {
+      if (lead) {
+        // copy every entry's h words into this XCD's stage (decoded), each
+        // polled until written; a thread re-reads all its unwritten words
+        // in one round
+        const int wps = Imax / 2, nwords = n_entries * wps;
+        const uint32_t *hw = reinterpret_cast<const uint32_t *>(a.ws.h);
+        uint32_t *sw = reinterpret_cast<uint32_t *>(stage);
+        constexpr int kCopy = 8;  // words per thread in flight
+        for (int i0 = 0; i0 < nwords; i0 += kCopy * (int)blockDim.x) {
+          uint32_t v[kCopy];
+          int o[kCopy];
+#pragma unroll
+          for (int k = 0; k < kCopy; ++k) {
+            const int i = i0 + k * (int)blockDim.x + tid, q = i / wps;
+            o[k] = (q < n_routed ? q : a.max_routed) * wps + (i - q * wps);
+            v[k] = i < nwords ? __hip_atomic_load(hw + o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+          }
+          for (int it = 0; it < kWaitSpin; ++it) {
+            bool done = true;
+#pragma unroll
+            for (int k = 0; k < kCopy; ++k) done = done && v[k] != 0u;
+            if (done) break;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int k = 0; k < kCopy; ++k)
+              if (v[k] == 0u) v[k] = __hip_atomic_load(hw + o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int k = 0; k < kCopy; ++k)
+            if (i0 + k * (int)blockDim.x + tid < nwords) sw[o[k]] = ~v[k];
+        }
+        // the copy reaches the L2 before the flag does
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) a.ws.xcd_flag[xcc * 64] = epoch;
+      } else {
+        if (tid == 0) {
+          const volatile uint32_t *flag = a.ws.xcd_flag + xcc * 64;
+          for (int it = 0; it < kWaitSpin; ++it) {
+            drop_cu_cache();
+            if (*flag == epoch) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (pass == 0) drop_cu_cache();  // the stage is read from the L2
+    float acc[kRows] = {0.f, 0.f, 0.f, 0.f};
+    if (Wd) {
+      const int64_t hbase = (int64_t)hslot * Imax;  // the entry's h in the stage
+      for (int c = lg; c < C; c += LPR) {
+        if (c != lg) load_rows<WT>(Wd, H, K, r0, c, cr);
+        uint32_t x[16];
+        load16(stage + hbase + c * 32, x);
+        ChunkBF cb;
+        convert_rows<WT>(cr, cb);
+        dot_rows<WT>(cb, x, acc);
+      }
+    }
+    int row;
+    float y2 = 0.f;
+    const float ys = fold4(acc[0], acc[1], acc[2], acc[3], LPR, row, &y2);
+    if (lg < (LPR == 2 ? 2 : kRows) && Wd) {
+      s_part[half][gi][row] = w * round_bf16(ys * Sd);
+      if (LPR == 2) s_part[half][gi][row + 1] = w * round_bf16(y2 * Sd);
+    }
+    __syncthreads();
+    if (ht < kRows)
+      for (int s2 = 0; s2 < slots; ++s2) total += s_part[half][s2][ht];
+    __syncthreads();
+  }
+  if (ht < kRows) {
+    const int64_t o = r0 + ht;
+    float v = round_bf16(total);
+    if (a.residual) v = bf16_to_f32(a.x[o]) + v;
+    a.y[o] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
+template <int WT>
+__global__ __launch_bounds__(kGateupWaves *kWave) void k_experts_b1(DecodeArgs a, int gu_blocks) {
+  static_assert(kGateupWaves * kWave == 2 * kDnHalf, "a down block is two 4-row halves");
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[1];
+  __shared__ float s_part[2][kMaxDownSlots][kRows];
+  __shared__ int s_lead;
+  if ((int)blockIdx.x < gu_blocks) gateup_block<WT, 1, true>(a, blockIdx.x, R, s_mark);
+  else down_block_b1<WT>(a, (int)blockIdx.x - gu_blocks, R, s_mark, s_part, s_lead);
+}
+
+// ---------------------------------------------------------------------------
 // Host launcher
 // ---------------------------------------------------------------------------
 
@@ -1051,6 +1261,17 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
     const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
     const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
     const int grid = (units + groups - 1) / groups;
+    if (MAXT == 1 && a.E > 0) {
+      // one kernel for both stages; the down stage's events mark its end
+      if ((e = launch(k_experts_b1<WT>, dim3(grid + a.H / (2 * kRows)), dim3(kGateupWaves * kWave), 0, stream,
+                      ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a, grid)) != hipSuccess)
+        return e;
+      if (ev) {
+        if ((e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
+        return hipEventRecord(ev[5], stream);
+      }
+      return hipSuccess;
+    }
     if ((e = launch(k_gateup<WT, MAXT>, dim3(grid), dim3(kGateupWaves * kWave), 0, stream, ev ? ev[2] : nullptr,
                     ev ? ev[3] : nullptr, a)) != hipSuccess)
       return e;
