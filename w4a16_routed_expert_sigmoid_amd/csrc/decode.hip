@@ -309,8 +309,15 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   const bool norm_here = a.use_norm && !xn_ready;
   const uint16_t *src = xn_ready ? a.ws.xn : a.x;
 
-  // The first four pieces of this lane's router row and the first piece of
-  // the norm gain, loaded before anything else.
+  // Loads in the order they are needed (memory operations complete in
+  // issue order): this thread's first piece of every token (the norm and
+  // the staging start as soon as they land), then the first four pieces of
+  // this lane's router row and the first piece of the norm gain, which
+  // arrive while the norm runs.
+  uint4 v0[kMaxBatch];
+#pragma unroll
+  for (int t = 0; t < kMaxBatch; ++t)
+    if (t < B && tid < n8) v0[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[tid];
   uint4 w0[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
     uint4 v[kMaxBatch];
 #pragma unroll
     for (int t = 0; t < kMaxBatch; ++t)
-      if (t < B) v[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
+      if (t < B) v[t] = i == tid ? v0[t] : reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
 #pragma unroll
     for (int t = 0; t < kMaxBatch; ++t) {
       if (t >= B) break;
