@@ -193,7 +193,9 @@ __device__ __forceinline__ uint32_t pf_wave_max(uint32_t m) {
 constexpr int kPfTokensPerWave = 2;
 constexpr int kPfTopkWaves = 16;
 
-// Top-k of each token (one wave per token at a time), weights, counts.
+// Top-k of each token (one wave per token at a time), weights, counts.  J:
+// logits per lane (E <= 64 J).
+template <int J>
 __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a) {
   __shared__ uint32_t s_hist[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -204,7 +206,6 @@ __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a)
     const int t = t0 + tt;
     if (t >= a.T) break;
     const float *lt = a.logits + (int64_t)t * a.E;
-    constexpr int J = kMaxExperts / 64;
     uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -319,9 +320,9 @@ __global__ __launch_bounds__(PThreads) void k_pf_scatter(PrefillArgs a) {
 
 // Router logits: rows = tokens, columns = experts, B = BF16 router weights.
 // 64 x 64 tiles (enough blocks to fill the GPU at E = 256); each of the 4
-// waves owns a 32 x 32 quarter; 64-K stages through LDS, the next stage's
+// waves owns a 32 x 32 quarter; 128-K stages through LDS, the next stage's
 // loads in flight during the current stage's MFMAs.
-constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8;
+constexpr int RBM = 64, RBN = 64, RBK = 128, RLD = RBK + 8;
 
 __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][RBM * RLD];
@@ -329,30 +330,34 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   const int m0 = blockIdx.x * RBM, n0 = blockIdx.y * RBN;
   const uint16_t *xs = a.use_norm ? a.xn : a.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*16 .. +16 of the stage
+  const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*32 .. +32 of the stage
   const uint16_t *arow = (m0 + r < a.T) ? xs + (int64_t)(m0 + r) * a.H : nullptr;
   const uint16_t *brow = (n0 + r < a.E) ? a.router_w + (int64_t)(n0 + r) * a.H : nullptr;
-  uint4 av[2], bv[2];
+  uint4 av[4], bv[4];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      av[i] = arow ? reinterpret_cast<const uint4 *>(arow + k0 + part * 16)[i] : make_uint4(0, 0, 0, 0);
-      bv[i] = brow ? reinterpret_cast<const uint4 *>(brow + k0 + part * 16)[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      av[i] = arow ? reinterpret_cast<const uint4 *>(arow + k0 + part * 32)[i] : make_uint4(0, 0, 0, 0);
+      bv[i] = brow ? reinterpret_cast<const uint4 *>(brow + k0 + part * 32)[i] : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      reinterpret_cast<uint4 *>(&sA[buf][r * RLD + part * 16])[i] = av[i];
-      reinterpret_cast<uint4 *>(&sB[buf][r * RLD + part * 16])[i] = bv[i];
+    for (int i = 0; i < 4; ++i) {
+      reinterpret_cast<uint4 *>(&sA[buf][r * RLD + part * 32])[i] = av[i];
+      reinterpret_cast<uint4 *>(&sB[buf][r * RLD + part * 32])[i] = bv[i];
     }
   };
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc = {};
   const int S = (a.H + RBK - 1) / RBK;  // H % 32 == 0; a ragged last stage reads zeros past H
   auto load_k = [&](int k0) {
-    if (k0 + part * 16 < a.H) load(k0);
-    else av[0] = av[1] = bv[0] = bv[1] = make_uint4(0, 0, 0, 0);
+    if (k0 + part * 32 < a.H) {
+      load(k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = bv[i] = make_uint4(0, 0, 0, 0);
+    }
   };
   load_k(0);
   store(0);
@@ -795,8 +800,9 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
     const int waves = (a.T + kPfTokensPerWave - 1) / kPfTokensPerWave;
-    hipLaunchKernelGGL(k_pf_topk, dim3((waves + kPfTopkWaves - 1) / kPfTopkWaves), dim3(kPfTopkWaves * kWave), 0, s,
-                       a);
+    const dim3 tg((waves + kPfTopkWaves - 1) / kPfTopkWaves), tb(kPfTopkWaves * kWave);
+    if (a.E <= 4 * kWave) hipLaunchKernelGGL(k_pf_topk<4>, tg, tb, 0, s, a);
+    else hipLaunchKernelGGL(k_pf_topk<kMaxExperts / kWave>, tg, tb, 0, s, a);
     MOE_CK_LAUNCH();
   }
   hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(kScanThreads), 0, s, a);
