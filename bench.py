@@ -144,6 +144,13 @@ def run(args, dev):
             w.router_b = bias.data_ptr()
         return w
 
+    # The prefill leg runs first, before the decode layer copies take tens of
+    # GB of device memory.
+    pf = None
+    if args.workload == "layer" and not args.no_prefill:
+        pf = run_prefill(args, dev)
+        torch.cuda.empty_cache()
+
     # ---- layers on the device
     t0 = time.time()
     if args.workload == "layer":
@@ -231,10 +238,6 @@ def run(args, dev):
     if args.workload == "layer":
         r8 = run_pool(8, True)
         log(f"batch 8: {r8['ms_step'] * 1e3 / n_layers:.2f} us/layer, stages {r8['stage_us']}")
-
-    pf = None
-    if args.workload == "layer" and not args.no_prefill:
-        pf = run_prefill(args, dev)
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -5,16 +5,17 @@
 //
 //   k_pf_norm     (pre-norm layers) xn = BF16(RMSNorm(x) * gain), one wave per token
 //   k_pf_router   logits = xn W_r^T + b: GEMM on v_mfma_f32_32x32x16_bf16
+//                 (its first block also clears the expert counts)
 //   k_pf_topk     sigmoid top-k per token (one wave each), renormalised
 //                 weights, per-expert token counts (LDS histogram per block)
 //   k_pf_scan     expert offsets and the tile list: every expert's rows in
 //                 tiles of 128, then the shared expert's tiles
 //   k_pf_scatter  each (token, k) pair gets a row in its expert's segment
-//   k_pf_gateup   grouped GEMM over the tiles: gathered xn rows x the
-//                 expert's gate and up matrices (NVFP4 dequantised to BF16 in
-//                 LDS once per tile), epilogue h = BF16(SiLU(BF16(g)) BF16(u))
-//   k_pf_down     grouped GEMM: h rows x the expert's down matrix, epilogue
-//                 y = BF16(acc * S_down)
+//   k_pf_gemm_fp4<0>, <1>  (NVFP4 weights) grouped GEMMs over the tiles:
+//                 gathered xn rows x the expert's gate and up matrices,
+//                 epilogue h = BF16(SiLU(BF16(g)) BF16(u)); then h rows x the
+//                 down matrix, epilogue y = BF16(acc * S_down) (below)
+//   k_pf_gateup, k_pf_down  the same two GEMMs for BF16 weights
 //   k_pf_combine  out = BF16(sum_j w_j y_row(t,j) + y_shared(t)) (+ residual)
 //
 // Row space of the grouped GEMMs: rows [0, P) are the P = T*k (token,
@@ -135,9 +136,6 @@ __device__ __forceinline__ int acc_col(int nb) {
 // Small kernels
 // ---------------------------------------------------------------------------
 
-__global__ void k_pf_zero(PrefillArgs a) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.E + 1; i += gridDim.x * blockDim.x) a.counts[i] = 0;
-}
 
 __global__ __launch_bounds__(PThreads) void k_pf_norm(PrefillArgs a) {
   const int lane = threadIdx.x & 63;
@@ -323,6 +321,7 @@ __global__ __launch_bounds__(PThreads) void k_pf_scatter(PrefillArgs a) {
 // waves owns a 32 x 32 quarter; 128-K stages through LDS, the next stage's
 // loads in flight during the current stage's MFMAs.
 constexpr int RBM = 64, RBN = 64, RBK = 128, RLD = RBK + 8;
+constexpr int RPART = RBK / 4, RV = RPART / 8;  // K elements and 16-byte loads per thread and stage
 
 __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][RBM * RLD];
@@ -330,33 +329,37 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   const int m0 = blockIdx.x * RBM, n0 = blockIdx.y * RBN;
   const uint16_t *xs = a.use_norm ? a.xn : a.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*32 .. +32 of the stage
+  // the expert counts the top-k kernel accumulates start at zero
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < a.E + 1; i += PThreads) a.counts[i] = 0;
+  const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*RPART .. +RPART of the stage
   const uint16_t *arow = (m0 + r < a.T) ? xs + (int64_t)(m0 + r) * a.H : nullptr;
   const uint16_t *brow = (n0 + r < a.E) ? a.router_w + (int64_t)(n0 + r) * a.H : nullptr;
-  uint4 av[4], bv[4];
+  uint4 av[RV], bv[RV];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = arow ? reinterpret_cast<const uint4 *>(arow + k0 + part * 32)[i] : make_uint4(0, 0, 0, 0);
-      bv[i] = brow ? reinterpret_cast<const uint4 *>(brow + k0 + part * 32)[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < RV; ++i) {
+      av[i] = arow ? reinterpret_cast<const uint4 *>(arow + k0 + part * RPART)[i] : make_uint4(0, 0, 0, 0);
+      bv[i] = brow ? reinterpret_cast<const uint4 *>(brow + k0 + part * RPART)[i] : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      reinterpret_cast<uint4 *>(&sA[buf][r * RLD + part * 32])[i] = av[i];
-      reinterpret_cast<uint4 *>(&sB[buf][r * RLD + part * 32])[i] = bv[i];
+    for (int i = 0; i < RV; ++i) {
+      reinterpret_cast<uint4 *>(&sA[buf][r * RLD + part * RPART])[i] = av[i];
+      reinterpret_cast<uint4 *>(&sB[buf][r * RLD + part * RPART])[i] = bv[i];
     }
   };
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc = {};
   const int S = (a.H + RBK - 1) / RBK;  // H % 32 == 0; a ragged last stage reads zeros past H
   auto load_k = [&](int k0) {
-    if (k0 + part * 32 < a.H) {
+    // H % 32 == 0 and RPART is 16 or 32: a thread's part is wholly in or out
+    if (k0 + part * RPART < a.H) {
       load(k0);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = bv[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < RV; ++i) av[i] = bv[i] = make_uint4(0, 0, 0, 0);
     }
   };
   load_k(0);
@@ -790,8 +793,6 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
   hipError_t e;
 #define MOE_CK_LAUNCH() \
   if ((e = hipGetLastError()) != hipSuccess) return e
-  hipLaunchKernelGGL(k_pf_zero, dim3(1), dim3(256), 0, s, a);
-  MOE_CK_LAUNCH();
   if (a.use_norm) {
     hipLaunchKernelGGL(k_pf_norm, dim3((a.T + 3) / 4), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
