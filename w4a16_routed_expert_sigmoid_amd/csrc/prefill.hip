@@ -737,7 +737,16 @@ __global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nbl
       const int col = col0 + c8 * 8;
       if (col >= N) continue;
       const uint4 v = *reinterpret_cast<const uint4 *>(stg + r * OS + c8 * 8);
-      *reinterpret_cast<uint4 *>(out + (int64_t)(tile.p0 + pass * RPP + r) * ostride + col) = v;
+      uint4 *dst = reinterpret_cast<uint4 *>(out + (int64_t)(tile.p0 + pass * RPP + r) * ostride + col);
+      if (MODE == 1) {
+        // y rows are read once, by the combine kernel: stream them past the L2
+        __builtin_nontemporal_store(v.x, &dst->x);
+        __builtin_nontemporal_store(v.y, &dst->y);
+        __builtin_nontemporal_store(v.z, &dst->z);
+        __builtin_nontemporal_store(v.w, &dst->w);
+      } else {
+        *dst = v;
+      }
     }
   }
 }
