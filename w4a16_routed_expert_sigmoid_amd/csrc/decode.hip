@@ -254,9 +254,17 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
   const int H = a.H, t = blockIdx.x, n8 = H / 8;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H);
+  const uint4 *gr = reinterpret_cast<const uint4 *>(a.norm_gain);
+  // This thread's first piece of x and of the gain, loaded together up
+  // front and kept for the second pass.
+  uint4 x0 = make_uint4(0, 0, 0, 0), g0 = make_uint4(0, 0, 0, 0);
+  if (tid < n8) {
+    x0 = xr[tid];
+    g0 = gr[tid];
+  }
   double ss = 0.0;
   for (int i = tid; i < n8; i += kNormThreads) {
-    const uint4 v = xr[i];
+    const uint4 v = i == tid ? x0 : xr[i];
     const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
   const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
   const float inv_f = (float)inv;
   for (int i = tid; i < n8; i += kNormThreads) {
-    const uint4 v = xr[i], gv = reinterpret_cast<const uint4 *>(a.norm_gain)[i];
+    const uint4 v = i == tid ? x0 : xr[i], gv = i == tid ? g0 : gr[i];
     uint32_t q[4] = {v.x, v.y, v.z, v.w};
     const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
@@ -312,8 +320,8 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   // Loads in the order they are needed (memory operations complete in
   // issue order): this thread's first piece of every token (the norm and
   // the staging start as soon as they land), then the first four pieces of
-  // this lane's router row and the first piece of the norm gain, which
-  // arrive while the norm runs.
+  // this lane's router row, the first piece of the norm gain and the row's
+  // bias, which arrive while the norm runs.
   uint4 v0[kMaxBatch];
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t)
@@ -327,6 +335,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   }
   uint4 g0 = make_uint4(0, 0, 0, 0);
   if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+  const float bias = (a.router_b && row < E) ? a.router_b[row] : 0.f;
   if (B == 1 && E > 0) {
     // One token: the expert kernel hands h over through words, per-XCD
     // tickets and per-XCD flags that start every call at zero; a flag is
@@ -446,7 +455,6 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
       acc[t] = s;
     }
   }
-  const float bias = a.router_b ? a.router_b[row] : 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxBatch; ++t) {
     if (t >= B) break;
