@@ -142,12 +142,16 @@ def test_decode_zero_input_full_tie():
     assert np.all(idx == np.arange(6)) and np.all(out == 0)
 
 
-def test_decode_wide_hidden_multi_chunk_lanes():
-    # H = 4096: 128 chunks per row, two per lane.
-    L = synth.make_layer(17, hidden=4096, inter=128, shared_inter=128, n_experts=16, top_k=4, bias="zipf")
-    x = synth.tokens(8, 4096, stream=9)
+@pytest.mark.parametrize("B,norm", [(8, False), (8, True), (1, True)])
+def test_decode_wide_hidden_multi_chunk_lanes(B, norm):
+    # H = 4096: 128 chunks per row, two per lane; with the pre-norm, each
+    # norm or router thread takes two 16-byte pieces of every token.  The
+    # residual stays off: the bar applies to the layer output alone.
+    L = synth.make_layer(17, hidden=4096, inter=128, shared_inter=128, n_experts=16, top_k=4, bias="zipf",
+                         norm=norm)
+    x = synth.tokens(B, 4096, stream=9)
     out, idx, w = run(L, x)
-    compare(L, x, out, idx, w, what="H=4096")
+    compare(L, x, out, idx, w, what=f"H=4096 B={B} norm={norm}")
 
 
 @pytest.mark.parametrize("Is,norm", [(2112, True), (2112, False), (256, True)])
