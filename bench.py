@@ -109,7 +109,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode layer runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
     import torch
