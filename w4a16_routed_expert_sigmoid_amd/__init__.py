@@ -7,7 +7,7 @@ keep the C names (include/moe.h) and take device pointers as integers (or
 tensors, whose data_ptr() is used); `stream` defaults to torch's current
 stream.  A failing call raises MoeError with the library's status.
 
-The library must have been built (``python -m w4a16_routed_expert_sigmoid_amd.build``
+The library must have been built (``python w4a16_routed_expert_sigmoid_amd/build.py``
 or ``__graft_entry__.build()``); importing fails loudly otherwise.
 """
 import ctypes
@@ -48,7 +48,7 @@ class moe_layer_weights(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
-                      "(python -m w4a16_routed_expert_sigmoid_amd.build)")
+                      "(python w4a16_routed_expert_sigmoid_amd/build.py)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
