@@ -51,12 +51,6 @@ def selected_bytes(distinct):
     return ROUTER_BYTES + (distinct + 1) * (EXPERT_BYTES + 12)
 
 
-def experts_bytes(distinct):
-    """Algorithmic bytes of the expert stage of one layer call: gate, up and
-    down of the distinct selected experts and of the shared expert."""
-    return (distinct + 1) * (EXPERT_BYTES + 12)
-
-
 def kernel_source_sha():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -65,14 +59,14 @@ def kernel_source_sha():
 
 
 def measured_traffic():
-    """HBM bytes per k_experts_b1 launch (batch 1) from the committed counter
+    """HBM bytes per k_layer_b1 launch (batch 1) from the committed counter
     summary, if it was taken on the current kernel sources; else None."""
     try:
         text = open(COUNTERS).read()
     except OSError:
         return None
     m = re.search(r"^source_sha:\s*(\w+)", text, re.M)
-    t = re.search(r"^k_experts_b1_traffic_bytes:\s*(\d+)", text, re.M)
+    t = re.search(r"^k_layer_b1_traffic_bytes:\s*(\d+)", text, re.M)
     if not m or not t or m.group(1) != kernel_source_sha():
         return None
     return int(t.group(1))
@@ -251,12 +245,15 @@ def run(args, dev):
     step_bytes = sum(selected_bytes(d) for d in r1["distinct"]) + n_dense * DENSE_BYTES
     gbs1 = step_bytes / (r1["ms_step"] * 1e-3) / 1e9
 
+    # batch 1: one kernel per layer (router, gate/up and down of the 6
+    # selected experts and the shared expert)
     ex_us = r1["stage_us"][1]
-    ex_gbs = experts_bytes(6) / (ex_us * 1e-6) / 1e9
+    ex_gbs = selected_bytes(6) / (ex_us * 1e-6) / 1e9
     traffic = measured_traffic()
-    roofline = dict(bound="hbm", kernel="k_experts_b1<nvfp4> (gate/up and down of 6 selected + shared expert, 1 token)",
+    roofline = dict(bound="hbm", kernel="k_layer_b1<nvfp4> (router, then gate/up and down of 6 selected + shared "
+                    "expert, 1 token)",
                     achieved=round(ex_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ex_gbs / HBM_PEAK_GBS, 4),
-                    traffic=traffic, algorithmic_bytes_per_launch=experts_bytes(6), avg_launch_us=round(ex_us, 3))
+                    traffic=traffic, algorithmic_bytes_per_launch=selected_bytes(6), avg_launch_us=round(ex_us, 3))
 
     cpu = None
     if not args.no_cpu:
@@ -301,7 +298,7 @@ def run(args, dev):
         "tokens_per_s": round(1e3 / r1["ms_step"], 1) if args.workload == "step49" else round(1e6 / us1, 1),
         "selected_bytes_per_step": int(step_bytes),
         "hbm_frac": round(gbs1 / HBM_PEAK_GBS, 4),
-        "stage_us": {"router": round(r1["stage_us"][0], 3), "experts": round(r1["stage_us"][1], 3)},
+        "stage_us": {"layer_kernel": round(r1["stage_us"][1], 3)},
         "step_equals_layer_calls": r1["step_equals_layers"],
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -138,7 +138,10 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  *  outputs, in descending score order.
  *  ws: device workspace of ws_bytes >= moe_decode_workspace_bytes(desc,
  *  batch), 256-byte aligned; no zero-fill needed (every call writes what
- *  it reads before reading it), reusable across calls and batch sizes.
+ *  it reads before reading it; one token with routed experts runs one
+ *  kernel per layer, whose blocks hand values to each other through sync
+ *  words that the call zeroes first), reusable across calls and batch
+ *  sizes.
  *  Concurrent calls must not share a workspace.
  * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
  * for shapes the kernels do not tile (H/32, I/32 and Is/32 must each be at

@@ -27,6 +27,18 @@ def stack(kind):
         dense = [synth.make_layer(100 + i, hidden=256, inter=0, shared_inter=256, n_experts=0, norm=True,
                                   residual=True) for i in range(2)]
         moes = [synth.make_layer(110 + i, bias="zipf", norm=True, residual=True, **kw) for i in range(3)]
+    elif kind == "mixed":
+        # MoE layers of different shapes in one step (their one-token sync
+        # words share one region of the workspace), a dense layer between
+        dense = [synth.make_layer(120, hidden=256, inter=0, shared_inter=256, n_experts=0, norm=True,
+                                  residual=True)]
+        moes = [synth.make_layer(121, bias="zipf", norm=True, residual=True, hidden=256, inter=64,
+                                 shared_inter=64, n_experts=32, top_k=6),
+                synth.make_layer(122, bias="zipf", norm=True, residual=True, hidden=256, inter=128,
+                                 shared_inter=128, n_experts=64, top_k=8),
+                synth.make_layer(123, norm=True, residual=True, hidden=256, inter=64, shared_inter=0,
+                                 n_experts=16, top_k=2)]
+        return [moes[0], dense[0], moes[1], moes[2], moes[0]]
     else:  # the model's shapes: 2 dense (intermediate 5632) + MoE layers
         dense = [synth.make_layer(i, inter=0, shared_inter=5632, n_experts=0, norm=True, residual=True)
                  for i in range(2)]
@@ -34,7 +46,8 @@ def stack(kind):
     return dense + moes
 
 
-@pytest.mark.parametrize("kind,B", [("small", 1), ("small", 8), ("full", 1), ("full", 8)])
+@pytest.mark.parametrize("kind,B", [("small", 1), ("small", 8), ("mixed", 1), ("mixed", 3), ("full", 1),
+                                    ("full", 8)])
 def test_step_matches_layers_and_oracle(kind, B):
     log(f"test: step {kind} B={B}")
     layers = stack(kind)
@@ -47,6 +60,12 @@ def test_step_matches_layers_and_oracle(kind, B):
     y = torch.empty_like(xt)
     ws = torch.zeros(moe.moe_decode_step_workspace_bytes(descs, B), dtype=torch.uint8, device="cuda")
     moe.moe_decode_step(descs, ws_, xt, B, y, ws, ws.numel())
+    # a second call on the same workspace (which now holds the first call's
+    # sync words) gives the same bits
+    y2 = torch.empty_like(xt)
+    moe.moe_decode_step(descs, ws_, xt, B, y2, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
     # the same layers one call at a time
     cur = xt
     for d in devs:

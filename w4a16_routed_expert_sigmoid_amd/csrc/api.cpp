@@ -31,7 +31,8 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
-  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, epoch, xcd_ticket, xcd_flag, xcd_h, bytes;
+  size_t sync_lines, sync_l, sync_h, sync_bytes;
+  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, xcd_h, bytes;
   size_t stage_elems;
 };
 
@@ -41,12 +42,36 @@ inline int max_routed_of(const moe_layer_desc &d, int B) {
   return m < d.n_experts ? m : d.n_experts;
 }
 
-WsLayout decode_layout(const moe_layer_desc &d, int B) {
+inline size_t imax_of(const moe_layer_desc &d) {
+  return (size_t)(d.inter > d.shared_inter ? d.inter : d.shared_inter);
+}
+
+constexpr size_t kSyncLineBytes = (size_t)kSyncLines * kXcdSlots * 256;
+
+// Bytes of the one-token sync region of a layer: the ticket and flag
+// lines, then the tagged logit and h words.  Zero for a layer without
+// routed experts.
+size_t sync_bytes_of(const moe_layer_desc &d) {
+  if (d.n_experts <= 0) return 0;
+  const size_t words_h = (size_t)(max_routed_of(d, 1) + 1) * imax_of(d) / 2;
+  return kSyncLineBytes + up((size_t)d.n_experts * 8) + up(words_h * 8);
+}
+
+// Layout of one layer's workspace.  The sync region comes first and takes
+// max(sync_cap, this layer's own) bytes, so that the layers of one step,
+// which share the workspace, keep their sync words inside one region that
+// the step zeroes once.
+WsLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0) {
   WsLayout L;
   const size_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = d.n_experts > 0 ? d.top_k : 0;
-  const size_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  const size_t Imax = imax_of(d);
   const size_t R = max_routed_of(d, B);
-  size_t o = 0;
+  const size_t own = sync_bytes_of(d);
+  L.sync_lines = 0;
+  L.sync_l = kSyncLineBytes;
+  L.sync_h = kSyncLineBytes + up(E * 8);
+  L.sync_bytes = own > sync_cap ? own : sync_cap;
+  size_t o = L.sync_bytes;
   L.logits = o; o += up(B * E * 4);
   L.xn = o; o += up(B * H * 2);
   L.n_routed = o; o += up(4);
@@ -56,13 +81,10 @@ WsLayout decode_layout(const moe_layer_desc &d, int B) {
   L.topk_idx = o; o += up(B * k * 4);
   L.topk_w = o; o += up(B * k * 4);
   L.h = o; o += up((R + 1) * B * Imax * 2);
-  // one-token path (also reserved at larger batches, so that a workspace
-  // sized for batch b serves every smaller batch)
+  // one-token stage of h (also reserved at larger batches, so that a
+  // workspace sized for batch b serves every smaller batch)
   const size_t R1 = max_routed_of(d, 1);
   L.stage_elems = ((R1 + 1) * Imax + 127) / 128 * 128;
-  L.epoch = o; o += up(4);
-  L.xcd_ticket = o; o += kXcdSlots * 256;
-  L.xcd_flag = o; o += kXcdSlots * 256;
   L.xcd_h = o; o += up(kXcdSlots * L.stage_elems * 2);
   L.bytes = o;
   return L;
@@ -167,9 +189,12 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
 
 // Validates one layer call and fills the kernel arguments; nothing is
 // launched.  ws_bytes must cover decode_layout(desc, batch).
+// sync_cap: the step's common sync region (0: the layer's own); tag: the
+// layer's position in the enqueuing call, from 1.
 static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                                  int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
-                                 void *ws, size_t ws_bytes, DecodeArgs &a) {
+                                 void *ws, size_t ws_bytes, DecodeArgs &a, size_t sync_cap = 0,
+                                 uint32_t tag = 1) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (batch < 1) return MOE_ERR_INVALID_ARG;
@@ -181,11 +206,12 @@ static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_wei
   if (!x || !y || !ws || x == y) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign)) return MOE_ERR_INVALID_ARG;
   if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID_ARG;
-  const WsLayout L = decode_layout(*desc, batch);
+  const WsLayout L = decode_layout(*desc, batch, sync_cap);
   if (ws_bytes < L.bytes) return MOE_ERR_WORKSPACE;
 
   uint8_t *base = (uint8_t *)ws;
   memset(&a, 0, sizeof(a));
+  a.tag = tag;
   a.H = desc->hidden;
   a.I = desc->n_experts > 0 ? desc->inter : 0;
   a.Is = desc->shared_inter;
@@ -219,9 +245,9 @@ static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_wei
   a.ws.topk_idx = (int32_t *)(base + L.topk_idx);
   a.ws.topk_w = (float *)(base + L.topk_w);
   a.ws.h = (uint16_t *)(base + L.h);
-  a.ws.epoch = (uint32_t *)(base + L.epoch);
-  a.ws.xcd_ticket = (uint32_t *)(base + L.xcd_ticket);
-  a.ws.xcd_flag = (uint32_t *)(base + L.xcd_flag);
+  a.ws.sync_lines = (uint32_t *)(base + L.sync_lines);
+  a.ws.sync_l = (uint64_t *)(base + L.sync_l);
+  a.ws.sync_h = (uint64_t *)(base + L.sync_h);
   a.ws.xcd_h = (uint16_t *)(base + L.xcd_h);
   a.ws.stage_elems = (int64_t)L.stage_elems;
   a.ws.bytes = L.bytes;
@@ -236,18 +262,37 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
   DecodeArgs a;
   const moe_status st = prepare_decode(desc, w, x, batch, residual, y, topk_idx, topk_w, ws, ws_bytes, a);
   if (st != MOE_OK) return st;
+  // One token with routed experts: the layer kernel's hand-overs start
+  // from a zeroed sync region.
+  if (batch == 1 && desc->n_experts > 0) {
+    const moe_status sc = hip_status(
+        launch_sync_clear((uint32_t *)ws, (int64_t)(sync_bytes_of(*desc) / 4), (hipStream_t)stream));
+    if (sc != MOE_OK) return sc;
+  }
   return hip_status(launch_decode(a, (hipStream_t)stream, g_stage_events_on ? g_stage_events : nullptr));
 }
 
 // Step workspace: two activation buffers, then the largest layer workspace.
 static size_t step_act_bytes(int32_t hidden, int32_t max_batch) { return up((size_t)max_batch * hidden * 2); }
 
+// The common sync region of a step's layers.
+static size_t step_sync_cap(const moe_layer_desc *descs, int32_t n_layers) {
+  size_t cap = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const size_t b = sync_bytes_of(descs[i]);
+    cap = b > cap ? b : cap;
+  }
+  return cap;
+}
+
 size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch) {
   if (!descs || n_layers < 1 || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  for (int32_t i = 0; i < n_layers; ++i)
+    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return 0;
+  const size_t cap = step_sync_cap(descs, n_layers);
   size_t layer = 0;
   for (int32_t i = 0; i < n_layers; ++i) {
-    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return 0;
-    const size_t b = decode_layout(descs[i], max_batch).bytes;
+    const size_t b = decode_layout(descs[i], max_batch, cap).bytes;
     layer = b > layer ? b : layer;
   }
   return 2 * step_act_bytes(descs[0].hidden, max_batch) + layer;
@@ -271,20 +316,28 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
   const size_t act = step_act_bytes(descs[0].hidden, batch);
   uint8_t *a0 = (uint8_t *)ws, *a1 = a0 + act, *lws = a1 + act;
   const size_t lws_bytes = ws_bytes - 2 * act;
+  const size_t cap = step_sync_cap(descs, n_layers);
   // Validate every layer before launching anything.
   for (int32_t i = 0; i < n_layers; ++i) {
     const void *in = (i == 0) ? x : ((i & 1) ? (const void *)a0 : (const void *)a1);
     void *out = (i == n_layers - 1) ? y : ((i & 1) ? (void *)a1 : (void *)a0);
     DecodeArgs a;
     const moe_status st = prepare_decode(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, lws,
-                                         lws_bytes, a);
+                                         lws_bytes, a, cap);
     if (st != MOE_OK) return st;
+  }
+  // One token: the layer kernels' sync words start zeroed, once per step;
+  // each layer call then carries its own tag.
+  if (batch == 1 && cap > 0) {
+    const moe_status sc = hip_status(launch_sync_clear((uint32_t *)lws, (int64_t)(cap / 4), (hipStream_t)stream));
+    if (sc != MOE_OK) return sc;
   }
   for (int32_t i = 0; i < n_layers; ++i) {
     const void *in = (i == 0) ? x : ((i & 1) ? (const void *)a0 : (const void *)a1);
     void *out = (i == n_layers - 1) ? y : ((i & 1) ? (void *)a1 : (void *)a0);
     DecodeArgs a;
-    prepare_decode(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, lws, lws_bytes, a);
+    prepare_decode(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, lws, lws_bytes, a, cap,
+                   (uint32_t)i + 1u);
     const moe_status st = hip_status(launch_decode(a, (hipStream_t)stream, nullptr));
     if (st != MOE_OK) return st;
   }

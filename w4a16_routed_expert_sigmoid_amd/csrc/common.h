@@ -255,19 +255,28 @@ struct DecodeWs {
   int32_t *topk_idx;      // [B][k] (used when the caller passes none)
   float *topk_w;          // [B][k]
   uint16_t *h;            // [(max_routed + 1)][B][Imax] SiLU(g)*u, BF16
-  // one token (gate/up and down in one kernel):
-  uint32_t *epoch;        // call number, advanced by the router kernel
-  uint32_t *xcd_ticket;   // [kXcdSlots][64] word 0: down blocks that arrived on that XCD
-  uint32_t *xcd_flag;     // [kXcdSlots][64] word 0: epoch once the XCD's copy of h is complete
+  // One token (router, gate/up and down in one kernel).  Values one block
+  // publishes for others travel in 64-bit words: the value in the low half,
+  // the tag of the layer call that wrote it in the high half.  The sync
+  // region (lines, logit words, h words) is zeroed by the first kernel of
+  // every call; within a call, layer calls carry distinct tags.
+  uint32_t *sync_lines;   // [kSyncLines][kXcdSlots][64]: word 0 of each 256-byte line is used
+  uint64_t *sync_l;       // [E] logit words
+  uint64_t *sync_h;       // [(k + 1) * Imax / 2] h words (two BF16 values each)
   uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
   int64_t stage_elems;    // (one-token max_routed + 1) * Imax, rounded up to 128
   size_t bytes;
 };
 
+// Lines of the sync region: per XCD, the ticket and the flag of the h
+// hand-over.
+enum { kLineHTicket = 0, kLineHFlag = 1, kSyncLines = 2 };
+
 // Arguments of the decode kernels (passed by value).
 struct DecodeArgs {
   int H, I, Is, E, k, B, residual, use_norm, max_routed, wtype;
   float eps;
+  uint32_t tag;  // one token: this layer call's position in the enqueuing call, from 1
   const uint16_t *x;
   uint16_t *y;
   const uint16_t *router_w;
@@ -326,6 +335,7 @@ __host__ __device__ inline int64_t prefill_max_tiles(int64_t T, int64_t k, int64
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+hipError_t launch_sync_clear(uint32_t *region, int64_t words, hipStream_t stream);
 hipError_t launch_repack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
                          int32_t *nan_count, hipStream_t stream);
 hipError_t launch_unpack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,

@@ -1,34 +1,33 @@
 // Small-batch (1..8 tokens) decode path of the sigmoid-routed W4A16 MoE
-// layer: two to five kernels per layer.  Most stages are separated by
-// kernel boundaries: on this GPU a device-scope atomic on one address
-// serialises across blocks, an agent-scope fence writes back the L2, and
-// data that many blocks read right after another block wrote it must come
-// from memory rather than from each XCD's L2.  The one-token expert kernel
-// hands h over inside the kernel instead, with one reader per XCD going to
-// memory and the rest reading that XCD's L2.
+// layer.  One token with routed experts runs the whole layer in one kernel
+// (k_layer_b1), with the logits and h handed between its blocks through
+// tagged words in memory.  Batches of 2..8 tokens and the dense layers run
+// two to five kernels, their stages separated by kernel boundaries: on
+// this GPU a device-scope atomic on one address serialises across blocks,
+// an agent-scope fence writes back the L2, and data that many blocks read
+// right after another block wrote it must come from memory rather than
+// from each XCD's L2.
 //
+//   k_layer_b1 (one token, routed experts present) router rows, gate/up
+//              units and down rows as three kinds of blocks of one kernel
+//              (below); k_sync_clear zeroes its sync words once per call.
 //   k_norm     (batches of 2..8 tokens with a pre-norm) one block per
 //              token: xn = BF16(x * inv * gain), inv from an FP64 sum of
 //              squares.
 //   k_router   router GEMV l = W_r xn + b in FP32, the batch staged in LDS
-//              (one token: the pre-norm is computed there too), one row
+//              (a dense layer of one token: only its pre-norm), one row
 //              per lane group, each row loaded once for every token.
 //   k_route    (batches of 2..8 tokens) one block: sigmoid top-k of every
 //              token, the sorted list of distinct selected experts with
 //              token masks, the renormalised combine weights.
-//   k_gateup   (one token: every block first recomputes the top-k from the
-//              1 KB of logits, which is cheaper than another launch, and
-//              block 0 publishes the list) then runs its share of the gate
-//              and up GEMVs of one selected (or the shared) expert: FP4
-//              decoded to BF16 in registers, FP32 accumulation, BF16
-//              rounding of g and u, h = BF16(SiLU(g) u).
+//   k_gateup   (dense layers, and batches with BF16 weights) its share of
+//              the gate and up GEMVs of one selected (or the shared)
+//              expert: FP4 decoded to BF16 in registers, FP32
+//              accumulation, BF16 rounding of g and u, h = BF16(SiLU(g) u).
 //   k_down     for every 4-row group of the output: the down GEMV of every
 //              selected expert and of the shared expert, BF16 rounding per
 //              expert, weighted FP32 combine in a fixed order, BF16 output
 //              (plus the residual when asked).
-//   k_experts_b1 (one token, routed experts present) k_gateup and k_down
-//              as one kernel: h is handed from the gate/up blocks to the
-//              down blocks inside the kernel, once per XCD (below).
 //   k_gateup_mm, k_down_mm: the same two stages for batches of 2..8 tokens
 //              with NVFP4 weights, on the matrix cores (below).
 //
@@ -336,22 +335,6 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   uint4 g0 = make_uint4(0, 0, 0, 0);
   if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
   const float bias = (a.router_b && row < E) ? a.router_b[row] : 0.f;
-  if (B == 1 && E > 0) {
-    // One token: the expert kernel hands h over through words, per-XCD
-    // tickets and per-XCD flags that start every call at zero; a flag is
-    // raised to the call number, which is never zero.
-    const int nw = (a.max_routed + 1) * (a.I > a.Is ? a.I : a.Is) / 2;
-    uint32_t *hw = reinterpret_cast<uint32_t *>(a.ws.h);
-    for (int i = blockIdx.x * kRouterThreads + tid; i < nw + 2 * kXcdSlots; i += gridDim.x * kRouterThreads) {
-      uint32_t *w = i < nw ? hw + i
-                           : i < nw + kXcdSlots ? a.ws.xcd_ticket + (i - nw) * 64 : a.ws.xcd_flag + (i - nw - kXcdSlots) * 64;
-      __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (blockIdx.x == 0 && tid == 0) {
-      const uint32_t e = *a.ws.epoch + 1u;
-      *a.ws.epoch = e ? e : 1u;
-    }
-  }
 
   // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
   // thread's pieces of every token are loaded before any is stored, so the
@@ -476,9 +459,10 @@ struct Routing {
 };
 
 // Top-k of every token (one wave per token), its weights, and the sorted
-// list of distinct experts.  Every caller derives the same list from the
-// same logits.
-__device__ inline void build_routing(const DecodeArgs &a, Routing &R, uint32_t *s_mark, int nwaves) {
+// list of distinct experts, from logits [B][E].  Every caller derives the
+// same list from the same logits.
+__device__ inline void build_routing(const DecodeArgs &a, const float *logits, Routing &R, uint32_t *s_mark,
+                                     int nwaves) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const bool single = a.B == 1;
   if (!single)
@@ -487,7 +471,7 @@ __device__ inline void build_routing(const DecodeArgs &a, Routing &R, uint32_t *
   for (int t = wave; t < a.B; t += nwaves) {
     int sel[kMaxTopK];
     float selv[kMaxTopK];
-    wave_topk_any(a.ws.logits + t * a.E, a.E, a.k, sel, selv);
+    wave_topk_any(logits + t * a.E, a.E, a.k, sel, selv);
     // lane r < k handles selection r
     int e = sel[0];
     float l = selv[0];
@@ -567,7 +551,7 @@ constexpr int kRouteWaves = kMaxBatch;
 __global__ __launch_bounds__(kRouteWaves *kWave) void k_route(DecodeArgs a) {
   __shared__ Routing R;
   __shared__ uint32_t s_mark[kMaxExperts];
-  build_routing(a, R, s_mark, kRouteWaves);
+  build_routing(a, a.ws.logits, R, s_mark, kRouteWaves);
   publish_routing(a, R);
 }
 
@@ -591,17 +575,24 @@ __device__ __forceinline__ void dot_tokens(const ChunkBF &cb, const uint16_t *xs
   });
 }
 
-// h handed to the down blocks of the same kernel (one token): every 32-bit
-// word (two BF16 values) is written with an agent-scope atomic store as the
-// complement of its bits, so that a reader can tell a written word from the
-// zero the router kernel leaves there; a BF16 0xFFFF (a NaN) is stored as
-// the canonical NaN, so no written word is 0.
-__device__ __forceinline__ uint32_t h_canon(uint32_t b) { return b == 0xffffu ? 0x7fc0u : b; }
+// A value published for other blocks of the same kernel (one token): the
+// value's 32 bits with the layer call's tag above them, in one 64-bit
+// agent-scope store.  A reader polls the word until it carries its own tag.
+__device__ __forceinline__ void publish_tagged(uint64_t *p, uint32_t v, uint32_t tag) {
+  __hip_atomic_store(p, (uint64_t)v | ((uint64_t)tag << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Gate/up GEMVs of block `bid`: 4-row units of the selected experts, then
-// of the shared expert.  PUB: publish h as above (one token only).
+// of the shared expert, on the activations xs ([B][H] BF16, global memory
+// or LDS).  PUB (one token): R already holds the routing, and h is
+// published as tagged words for the down blocks of the same kernel.
+// Otherwise, with routed experts, the routing kernel wrote the list.
 template <int WT, int MAXT, bool PUB>
-__device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routing &R, uint32_t *s_mark) {
+__device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routing &R, const uint16_t *xs) {
   static_assert(!PUB || MAXT == 1, "published h is the one-token layout");
   const int H = a.H, I = a.I, B = a.B;
   const int LPR = lanes_per_row(H), C = H / 32;
@@ -610,21 +601,13 @@ __device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routi
   const int u = bid * groups + threadIdx.x / LPR;  // 4-row unit of this lane group
   const int routed_units = a.max_routed * (I / kRows);
 
-  if (a.E > 0 && (bid * groups < routed_units || bid == 0)) {
-    if (MAXT == 1) {
-      // One token: every block selects the experts itself (cheaper than a
-      // separate launch); block 0 publishes the list for the down kernel.
-      build_routing(a, R, s_mark, kGateupWaves);
-      if (bid == 0) publish_routing(a, R);
-    } else {
-      // Several tokens: the routing kernel already wrote the list.
-      if (threadIdx.x == 0) R.n = *a.ws.n_routed;
-      for (int j = threadIdx.x; j < a.max_routed; j += blockDim.x) {
-        R.expert[j] = a.ws.entry_expert[j];
-        R.mask[j] = a.ws.entry_mask[j];
-      }
-      __syncthreads();
+  if (!PUB && a.E > 0 && bid * groups < routed_units) {
+    if (threadIdx.x == 0) R.n = *a.ws.n_routed;
+    for (int j = threadIdx.x; j < a.max_routed; j += blockDim.x) {
+      R.expert[j] = a.ws.entry_expert[j];
+      R.mask[j] = a.ws.entry_mask[j];
     }
+    __syncthreads();
   }
 
   int slot = 0, q = 0, N = 0;
@@ -659,7 +642,6 @@ __device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routi
     }
   }
 
-  const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
   float ag[MAXT][kRows], au[MAXT][kRows];
 #pragma unroll
   for (int t = 0; t < MAXT; ++t)
@@ -692,14 +674,12 @@ __device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routi
         // rows (row, row + 1) in one word: with 2-lane groups a lane holds
         // both; otherwise lanes 0 and 1 of the group (rows 0 and 2) take
         // rows 1 and 3 from lanes 2 and 3
-        const uint32_t h0 = h_canon(f32_to_bf16(silu_mul(round_bf16(gs * Sg), round_bf16(us * Su))));
+        const uint32_t h0 = f32_to_bf16(silu_mul(round_bf16(gs * Sg), round_bf16(us * Su)));
         uint32_t h1;
-        if (LPR == 2) h1 = h_canon(f32_to_bf16(silu_mul(round_bf16(g2 * Sg), round_bf16(u2 * Su))));
+        if (LPR == 2) h1 = f32_to_bf16(silu_mul(round_bf16(g2 * Sg), round_bf16(u2 * Su)));
         else h1 = xor_lane<2>(h0);
-        if (lg < 2 && mask) {
-          uint32_t *hw = reinterpret_cast<uint32_t *>(a.ws.h + (int64_t)slot * Imax + q * kRows + row);
-          __hip_atomic_store(hw, ~(h0 | (h1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (lg < 2 && mask)
+          publish_tagged(a.ws.sync_h + ((int64_t)slot * Imax + q * kRows + row) / 2, h0 | (h1 << 16), a.tag);
       } else if (lg < (LPR == 2 ? 2 : kRows) && ((mask >> t) & 1u)) {
         // with 2-lane groups each lane holds two rows
         for (int k2 = 0; k2 < (LPR == 2 ? 2 : 1); ++k2) {
@@ -716,8 +696,7 @@ __device__ __forceinline__ void gateup_block(const DecodeArgs &a, int bid, Routi
 template <int WT, int MAXT>
 __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
   __shared__ Routing R;
-  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks; several: read from the workspace
-  gateup_block<WT, MAXT, false>(a, blockIdx.x, R, s_mark);
+  gateup_block<WT, MAXT, false>(a, blockIdx.x, R, a.use_norm ? a.ws.xn : a.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1077,16 +1056,25 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_experts_b1: one token, gate/up and down in one kernel.
-//   Blocks below gu_blocks run the gate/up GEMVs and publish h word by word
-//   (h_canon).  The others each own 8 output rows (two 4-row halves of 2
-//   waves) and derive the routing themselves.  On every XCD the first down
-//   block to arrive (a ticket) copies h once into that XCD's stage through
-//   memory, polling each word until it is written, and raises the XCD's
-//   flag (the call number); the XCD's other down blocks poll the
-//   flag and read the stage from the XCD's L2 (drop_cu_cache), so h
-//   crosses the XCD boundary eight times, not once per block.  Producers
-//   never wait and are dispatched first; every wait is bounded.
+// k_layer_b1: one token with routed experts, the whole layer in one kernel.
+//   Blocks [0, rt_blocks): router rows.  Each block normalises the token in
+//   LDS (every block computes the same bits) and publishes its rows'
+//   logits as tagged words.
+//   Blocks [rt_blocks, rt_blocks + gu_blocks): gate/up units.  Each block
+//   normalises the token into LDS itself; blocks with routed units poll the
+//   E tagged logit words into LDS, derive the routing and publish h as
+//   tagged words.
+//   The rest: down blocks of 8 output rows each (two 4-row halves of 2
+//   waves).  They take the routing like the gate/up blocks, load their
+//   first weight chunk, and take h once per XCD: the first down block on an
+//   XCD (its agent-scope exchange of the layer's tag into the XCD's ticket
+//   returns something else) copies the tagged h words from memory into that
+//   XCD's stage, polling each word until it carries the tag, and raises the
+//   XCD's flag to the tag; the XCD's other down blocks poll the flag and
+//   read the stage from the XCD's L2.  Then the down GEMVs and the weighted
+//   combine in LDS in a fixed expert order.
+// Producers never wait and have lower block indices than their consumers,
+// which the hardware dispatches in order; every wait is bounded.
 // ---------------------------------------------------------------------------
 
 // Drops this CU's cached lines, so that the next plain loads are served by
@@ -1102,9 +1090,194 @@ constexpr int kWaitSpin = 1 << 20;
 
 constexpr int kDnHalf = 2 * kWave;  // threads per 4-row half of a down block
 
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcdSlots - 1);  // HW_REG_XCC_ID[3:0]
+}
+
+__device__ __forceinline__ uint32_t *sync_line(const DecodeArgs &a, int which, int xcc) {
+  return a.ws.sync_lines + ((int64_t)which * kXcdSlots + xcc) * 64;
+}
+
+// True in exactly one block per XCD and layer call: the first to swap the
+// tag into the ticket.
+__device__ __forceinline__ bool take_ticket(const DecodeArgs &a, int which, int xcc) {
+  return __hip_atomic_exchange(sync_line(a, which, xcc), a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+         a.tag;
+}
+
+// Leader: once its stores to the stage have reached the L2, the flag.
+__device__ __forceinline__ void raise_flag(const DecodeArgs &a, int which, int xcc) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) *reinterpret_cast<volatile uint32_t *>(sync_line(a, which, xcc)) = a.tag;
+}
+
+// Others (thread 0): until the XCD's flag carries the tag.
+__device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xcc) {
+  if (threadIdx.x == 0) {
+    const volatile uint32_t *flag = sync_line(a, which, xcc);
+    for (int it = 0; it < kWaitSpin; ++it) {
+      drop_cu_cache();
+      if (*flag == a.tag) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+// The values of n tagged words into dst[0..n) (global memory or LDS), each
+// polled until it carries the tag; a thread keeps kCopy words in flight
+// and re-reads all its missing ones in each round.
+__device__ __forceinline__ void copy_tagged(const uint64_t *src, uint32_t *dst, int n, uint32_t tag) {
+  constexpr int kCopy = 8;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int i0 = 0; i0 < n; i0 += kCopy * nt) {
+    uint64_t v[kCopy];
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+      const int i = i0 + k * nt + tid;
+      v[k] = i < n ? load_tagged(src + i) : (uint64_t)tag << 32;
+    }
+    for (int it = 0; it < kWaitSpin; ++it) {
+      bool done = true;
+#pragma unroll
+      for (int k = 0; k < kCopy; ++k) done = done && (uint32_t)(v[k] >> 32) == tag;
+      if (done) break;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int k = 0; k < kCopy; ++k)
+        if ((uint32_t)(v[k] >> 32) != tag) v[k] = load_tagged(src + i0 + k * nt + tid);
+    }
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+      const int i = i0 + k * nt + tid;
+      if (i < n) dst[i] = (uint32_t)v[k];
+    }
+  }
+}
+
+// The token's routing from the logits the router blocks published: every
+// consumer block polls the E tagged words from memory into its LDS (s_l,
+// E floats).  (A per-XCD copy through one leader, as for h, measured no
+// faster: the 1 KB of logits is small next to the round trip.)  Ends with
+// a barrier.
+__device__ __forceinline__ void take_routing(const DecodeArgs &a, Routing &R, uint32_t *s_mark, float *s_l) {
+  copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_l), a.E, a.tag);
+  __syncthreads();
+  build_routing(a, s_l, R, s_mark, kGateupWaves);
+}
+
+// The token into LDS (s_x: H/8 pieces of 16 bytes) with the pre-norm when
+// the layer has one: xn = BF16(x * inv * gain), inv = 1/sqrt(mean(x^2) +
+// eps) from an FP64 sum of squares (exact per term), reduced in the same
+// order in every block.  x0, g0: this thread's first pieces of x and of
+// the gain, already loaded.  Ends with a barrier.
+__device__ inline void stage_token(const DecodeArgs &a, uint4 *s_x, double *s_red, uint4 x0, uint4 g0) {
+  const int H = a.H, n8 = H / 8;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, nw = blockDim.x / kWave;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(a.x);
+  const uint4 *gr = reinterpret_cast<const uint4 *>(a.norm_gain);
+  double ss = 0.0;
+  for (int i = tid; i < n8; i += blockDim.x) {
+    const uint4 v = i == tid ? x0 : xr[i];
+    s_x[i] = v;
+    if (a.use_norm) {
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
+        ss = fma(lo, lo, fma(hi, hi, ss));
+      }
+    }
+  }
+  if (!a.use_norm) {
+    __syncthreads();
+    return;
+  }
+  ss = group_sum_f64(ss, kWave);
+  if (lane == 0) s_red[wave] = ss;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < nw; ++w) tot += s_red[w];
+  const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+  const float inv_f = (float)inv;
+  for (int i = tid; i < n8; i += blockDim.x) {
+    const uint4 gv = i == tid ? g0 : gr[i];
+    const uint4 v = s_x[i];
+    uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv);
+      const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv);
+      q[j] = lo | (hi << 16);
+    }
+    s_x[i] = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+  __syncthreads();
+}
+
+// This thread's first pieces of x and of the gain.
+__device__ __forceinline__ void first_pieces(const DecodeArgs &a, uint4 &x0, uint4 &g0) {
+  const int tid = threadIdx.x;
+  x0 = g0 = make_uint4(0, 0, 0, 0);
+  if (tid < a.H / 8) {
+    x0 = reinterpret_cast<const uint4 *>(a.x)[tid];
+    if (a.use_norm) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+  }
+}
+
+// Router rows of block rb: one row per lane group of LPR lanes (lane j of
+// a group takes the row's 16-byte pieces j, j + LPR, ...), dotted with the
+// token in LDS; the logit l = W_r xn + b (FP32) is published.
+__device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, double *s_red) {
+  const int H = a.H, E = a.E, n8 = H / 8;
+  const int LPR = lanes_per_row(H);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
+  const int row = (rb * kRouterWaves + wave) * (kWave / LPR) + lane / LPR;
+  const uint4 *wr = reinterpret_cast<const uint4 *>(a.router_w + (int64_t)(row < E ? row : 0) * H);
+  // Loads in the order they are needed (they complete in issue order):
+  // the token, then the row's first four pieces, the gain and the bias.
+  uint4 x0 = make_uint4(0, 0, 0, 0), g0 = make_uint4(0, 0, 0, 0);
+  if (tid < n8) x0 = reinterpret_cast<const uint4 *>(a.x)[tid];
+  uint4 w0[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = lg + i * LPR;
+    w0[i] = (row < E && j < n8) ? wr[j] : make_uint4(0, 0, 0, 0);
+  }
+  if (a.use_norm && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
+  const float bias = (a.router_b && row < E) ? a.router_b[row] : 0.f;
+  stage_token(a, s_x, s_red, x0, g0);
+  if (row >= E) return;
+  float acc = 0.f;
+  for (int j0 = lg; j0 < n8; j0 += 4 * LPR) {
+    uint4 w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i * LPR;
+      if (j0 == lg) w[i] = w0[i];
+      else w[i] = j < n8 ? wr[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i * LPR;
+      if (j < n8) {
+        const uint4 v = s_x[j];
+        acc = dot2_bf16(w[i].x, v.x, acc);
+        acc = dot2_bf16(w[i].y, v.y, acc);
+        acc = dot2_bf16(w[i].z, v.z, acc);
+        acc = dot2_bf16(w[i].w, v.w, acc);
+      }
+    }
+  }
+  const float v = group_sum(acc, LPR);
+  if (lg == 0) publish_tagged(a.ws.sync_l + row, __float_as_uint(v + bias), a.tag);
+}
+
 template <int WT>
-__device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, Routing &R, uint32_t *s_mark,
-                                              float (&s_part)[2][kMaxDownSlots][kRows], int &s_lead) {
+__device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int xcc, Routing &R, uint32_t *s_mark,
+                                              float *s_l, float (&s_part)[2][kMaxDownSlots][kRows],
+                                              int &s_hlead) {
   const int H = a.H, K = a.I;  // experts present: Is is I or 0
   const int LPR = lanes_per_row(K), C = K / 32;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), lg = lane % LPR;
@@ -1114,12 +1287,9 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, Rou
   const int slots = slots_all < kMaxDownSlots ? slots_all : kMaxDownSlots;
   const int r0 = dbid * (2 * kRows) + half * kRows;
   const int Imax = a.I > a.Is ? a.I : a.Is;
-  const uint32_t epoch = *a.ws.epoch;
-  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcdSlots - 1);  // HW_REG_XCC_ID[3:0]
-  if (tid == 0)
-    s_lead = __hip_atomic_fetch_add(a.ws.xcd_ticket + xcc * 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
-  build_routing(a, R, s_mark, kGateupWaves);  // ends with a barrier
-  const bool lead = s_lead != 0;
+  if (tid == 0) s_hlead = take_ticket(a, kLineHTicket, xcc);
+  take_routing(a, R, s_mark, s_l);  // ends with a barrier
+  const bool lead = s_hlead != 0;
   const int n_routed = R.n;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
   uint16_t *stage = a.ws.xcd_h + (int64_t)xcc * a.ws.stage_elems;
@@ -1149,50 +1319,14 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, Rou
     ChunkRaw cr;
     if (Wd) load_rows<WT>(Wd, H, K, r0, lg, cr);
     if (pass == 0) {
+      // One token: the routed entries are slots 0..k-1 and the shared
+      // expert slot k (= max_routed), so the entries' h words are the first
+      // n_entries * Imax / 2 words.
       if (lead) {
-        // copy every entry's h words into this XCD's stage (decoded), each
-        // polled until written; a thread re-reads all its unwritten words
-        // in one round
-        const int wps = Imax / 2, nwords = n_entries * wps;
-        const uint32_t *hw = reinterpret_cast<const uint32_t *>(a.ws.h);
-        uint32_t *sw = reinterpret_cast<uint32_t *>(stage);
-        constexpr int kCopy = 8;  // words per thread in flight
-        for (int i0 = 0; i0 < nwords; i0 += kCopy * (int)blockDim.x) {
-          uint32_t v[kCopy];
-          int o[kCopy];
-#pragma unroll
-          for (int k = 0; k < kCopy; ++k) {
-            const int i = i0 + k * (int)blockDim.x + tid, q = i / wps;
-            o[k] = (q < n_routed ? q : a.max_routed) * wps + (i - q * wps);
-            v[k] = i < nwords ? __hip_atomic_load(hw + o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
-          }
-          for (int it = 0; it < kWaitSpin; ++it) {
-            bool done = true;
-#pragma unroll
-            for (int k = 0; k < kCopy; ++k) done = done && v[k] != 0u;
-            if (done) break;
-            __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int k = 0; k < kCopy; ++k)
-              if (v[k] == 0u) v[k] = __hip_atomic_load(hw + o[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-#pragma unroll
-          for (int k = 0; k < kCopy; ++k)
-            if (i0 + k * (int)blockDim.x + tid < nwords) sw[o[k]] = ~v[k];
-        }
-        // the copy reaches the L2 before the flag does
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) a.ws.xcd_flag[xcc * 64] = epoch;
+        copy_tagged(a.ws.sync_h, reinterpret_cast<uint32_t *>(stage), n_entries * (Imax / 2), a.tag);
+        raise_flag(a, kLineHFlag, xcc);
       } else {
-        if (tid == 0) {
-          const volatile uint32_t *flag = a.ws.xcd_flag + xcc * 64;
-          for (int it = 0; it < kWaitSpin; ++it) {
-            drop_cu_cache();
-            if (*flag == epoch) break;
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
+        wait_flag(a, kLineHFlag, xcc);
       }
     }
     __syncthreads();
@@ -1230,14 +1364,41 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, Rou
 }
 
 template <int WT>
-__global__ __launch_bounds__(kGateupWaves *kWave) void k_experts_b1(DecodeArgs a, int gu_blocks) {
+__global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, int rt_blocks, int gu_blocks) {
   static_assert(kGateupWaves * kWave == 2 * kDnHalf, "a down block is two 4-row halves");
+  static_assert(kRouterThreads == kGateupWaves * kWave, "router blocks have the same size");
+  extern __shared__ uint4 s_x[];  // [H / 8] the token (router and gate/up blocks)
   __shared__ Routing R;
-  __shared__ uint32_t s_mark[1];
+  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks
   __shared__ float s_part[2][kMaxDownSlots][kRows];
-  __shared__ int s_lead;
-  if ((int)blockIdx.x < gu_blocks) gateup_block<WT, 1, true>(a, blockIdx.x, R, s_mark);
-  else down_block_b1<WT>(a, (int)blockIdx.x - gu_blocks, R, s_mark, s_part, s_lead);
+  __shared__ double s_red[kGateupWaves];
+  __shared__ float s_l[kMaxExperts];  // the logits (routed gate/up and down blocks)
+  __shared__ int s_hlead;
+  const int b = blockIdx.x;
+  if (b < rt_blocks) {
+    router_block_b1(a, b, s_x, s_red);
+    return;
+  }
+  const int xcc = xcc_id();
+  if (b < rt_blocks + gu_blocks) {
+    const int bid = b - rt_blocks;
+    const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
+    uint4 x0, g0;
+    first_pieces(a, x0, g0);
+    stage_token(a, s_x, s_red, x0, g0);
+    if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) {
+      take_routing(a, R, s_mark, s_l);
+      if (bid == 0) publish_routing(a, R);
+    }
+    gateup_block<WT, 1, true>(a, bid, R, reinterpret_cast<const uint16_t *>(s_x));
+  } else {
+    down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_l, s_part, s_hlead);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sync_clear(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1276,17 +1437,6 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
     const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
     const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
     const int grid = (units + groups - 1) / groups;
-    if (MAXT == 1 && a.E > 0) {
-      // one kernel for both stages; the down stage's events mark its end
-      if ((e = launch(k_experts_b1<WT>, dim3(grid + a.H / (2 * kRows)), dim3(kGateupWaves * kWave), 0, stream,
-                      ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a, grid)) != hipSuccess)
-        return e;
-      if (ev) {
-        if ((e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
-        return hipEventRecord(ev[5], stream);
-      }
-      return hipSuccess;
-    }
     if ((e = launch(k_gateup<WT, MAXT>, dim3(grid), dim3(kGateupWaves * kWave), 0, stream, ev ? ev[2] : nullptr,
                     ev ? ev[3] : nullptr, a)) != hipSuccess)
       return e;
@@ -1296,11 +1446,45 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
                 ev ? ev[5] : nullptr, a);
 }
 
+// One token with routed experts: the whole layer in one kernel (its events
+// are the gate/up pair; the router and down pairs are recorded empty).
+template <int WT>
+static hipError_t launch_layer_b1(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
+  hipError_t e;
+  const int LPR = lanes_per_row(a.H);
+  const int rows_per_block = kRouterWaves * (kWave / LPR);
+  const int rt = (a.E + rows_per_block - 1) / rows_per_block;
+  const int groups = kGateupWaves * (kWave / LPR);
+  const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
+  const int gu = (units + groups - 1) / groups;
+  const int grid = rt + gu + a.H / (2 * kRows);
+  if (ev) {
+    if ((e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  }
+  if ((e = launch(k_layer_b1<WT>, dim3(grid), dim3(kGateupWaves * kWave), (size_t)a.H * 2, stream,
+                  ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a, rt, gu)) != hipSuccess)
+    return e;
+  if (ev) {
+    if ((e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
+    return hipEventRecord(ev[5], stream);
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sync_clear(uint32_t *region, int64_t words, hipStream_t stream) {
+  const int64_t blocks64 = (words + 255) / 256;
+  const int blocks = (int)(blocks64 < 64 ? (blocks64 > 0 ? blocks64 : 1) : 64);
+  hipLaunchKernelGGL(k_sync_clear, dim3(blocks), dim3(256), 0, stream, region, words);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
   // ev: NULL, or 6 events: start/stop of the router GEMV kernel, of the
   // gate/up kernel and of the down kernel (attached to the dispatches; for
   // measurement, eager launches only).
   hipError_t e;
+  if (a.B == 1 && a.E > 0) return a.wtype == 1 ? launch_layer_b1<1>(a, stream, ev) : launch_layer_b1<0>(a, stream, ev);
   // Batches of several tokens normalise once in k_norm; a single token
   // normalises inside the router blocks (one launch fewer).
   const int xn_ready = (a.use_norm && a.B > 1) ? 1 : 0;
