@@ -263,14 +263,16 @@ struct DecodeWs {
   uint32_t *sync_lines;   // [kSyncLines][kXcdSlots][64]: word 0 of each 256-byte line is used
   uint64_t *sync_l;       // [E] logit words
   uint64_t *sync_h;       // [(k + 1) * Imax / 2] h words (two BF16 values each)
+  float *xcd_l;           // [kXcdSlots][stage_l] per-XCD copy of the logits
   uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
+  int64_t stage_l;        // E rounded up to 64
   int64_t stage_elems;    // (one-token max_routed + 1) * Imax, rounded up to 128
   size_t bytes;
 };
 
-// Lines of the sync region: per XCD, the ticket and the flag of the h
-// hand-over.
-enum { kLineHTicket = 0, kLineHFlag = 1, kSyncLines = 2 };
+// Lines of the sync region: per XCD, the logit ticket and flag, then the h
+// ticket and flag.
+enum { kLineLTicket = 0, kLineLFlag = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
 
 // Arguments of the decode kernels (passed by value).
 struct DecodeArgs {

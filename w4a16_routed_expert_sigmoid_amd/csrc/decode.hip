@@ -1061,20 +1061,19 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 //   LDS (every block computes the same bits) and publishes its rows'
 //   logits as tagged words.
 //   Blocks [rt_blocks, rt_blocks + gu_blocks): gate/up units.  Each block
-//   normalises the token into LDS itself; blocks with routed units poll the
-//   E tagged logit words into LDS, derive the routing and publish h as
-//   tagged words.
+//   normalises the token into LDS itself; blocks with routed units take
+//   the routing (below) and publish h as tagged words.
 //   The rest: down blocks of 8 output rows each (two 4-row halves of 2
-//   waves).  They take the routing like the gate/up blocks, load their
-//   first weight chunk, and take h once per XCD: the first down block on an
-//   XCD (its agent-scope exchange of the layer's tag into the XCD's ticket
-//   returns something else) copies the tagged h words from memory into that
-//   XCD's stage, polling each word until it carries the tag, and raises the
-//   XCD's flag to the tag; the XCD's other down blocks poll the flag and
-//   read the stage from the XCD's L2.  Then the down GEMVs and the weighted
-//   combine in LDS in a fixed expert order.
-// Producers never wait and have lower block indices than their consumers,
-// which the hardware dispatches in order; every wait is bounded.
+//   waves), the weighted combine in LDS in a fixed expert order.
+// Hand-overs (the logits to every routed gate/up block and down block, h
+// to every down block) go through memory once per XCD: the first consumer
+// block on an XCD (its agent-scope exchange of the layer's tag into the
+// XCD's ticket returns something else) copies the tagged words into that
+// XCD's stage, polling each word until it carries the tag, and raises the
+// XCD's flag to the tag; the XCD's other consumers poll the flag and read
+// the stage from the XCD's L2.  Producers never wait and have lower block
+// indices than their consumers, which the hardware dispatches in order;
+// every wait is bounded.
 // ---------------------------------------------------------------------------
 
 // Drops this CU's cached lines, so that the next plain loads are served by
@@ -1124,10 +1123,10 @@ __device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xc
   }
 }
 
-// The values of n tagged words into dst[0..n) (global memory or LDS), each
-// polled until it carries the tag; a thread keeps kCopy words in flight
-// and re-reads all its missing ones in each round.
-__device__ __forceinline__ void copy_tagged(const uint64_t *src, uint32_t *dst, int n, uint32_t tag) {
+// Leader: the values of n tagged words into dst[0..n), each polled until
+// it carries the tag; a thread keeps kCopy words in flight and re-reads
+// all its missing ones in each round.
+__device__ inline void copy_tagged(const uint64_t *src, uint32_t *dst, int n, uint32_t tag) {
   constexpr int kCopy = 8;
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int i0 = 0; i0 < n; i0 += kCopy * nt) {
@@ -1155,15 +1154,23 @@ __device__ __forceinline__ void copy_tagged(const uint64_t *src, uint32_t *dst, 
   }
 }
 
-// The token's routing from the logits the router blocks published: every
-// consumer block polls the E tagged words from memory into its LDS (s_l,
-// E floats).  (A per-XCD copy through one leader, as for h, measured no
-// faster: the 1 KB of logits is small next to the round trip.)  Ends with
-// a barrier.
-__device__ __forceinline__ void take_routing(const DecodeArgs &a, Routing &R, uint32_t *s_mark, float *s_l) {
-  copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_l), a.E, a.tag);
+// The token's routing from the logits the router blocks published, by way
+// of this XCD's copy.  s_lead: a shared word for the ticket.  Ends with a
+// barrier.  (Every consumer block polling the E words itself measured
+// 0.2 us slower per layer: about 450 blocks re-reading the same 2 KB.)
+__device__ inline void take_routing(const DecodeArgs &a, int xcc, Routing &R, uint32_t *s_mark, int &s_lead) {
+  if (threadIdx.x == 0) s_lead = take_ticket(a, kLineLTicket, xcc);
   __syncthreads();
-  build_routing(a, s_l, R, s_mark, kGateupWaves);
+  float *stage = a.ws.xcd_l + (int64_t)xcc * a.ws.stage_l;
+  if (s_lead) {
+    copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(stage), a.E, a.tag);
+    raise_flag(a, kLineLFlag, xcc);
+  } else {
+    wait_flag(a, kLineLFlag, xcc);
+  }
+  __syncthreads();
+  drop_cu_cache();  // the stage is read from the L2
+  build_routing(a, stage, R, s_mark, kGateupWaves);
 }
 
 // The token into LDS (s_x: H/8 pieces of 16 bytes) with the pre-norm when
@@ -1276,7 +1283,7 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
 
 template <int WT>
 __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int xcc, Routing &R, uint32_t *s_mark,
-                                              float *s_l, float (&s_part)[2][kMaxDownSlots][kRows],
+                                              float (&s_part)[2][kMaxDownSlots][kRows], int &s_llead,
                                               int &s_hlead) {
   const int H = a.H, K = a.I;  // experts present: Is is I or 0
   const int LPR = lanes_per_row(K), C = K / 32;
@@ -1288,7 +1295,7 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int
   const int r0 = dbid * (2 * kRows) + half * kRows;
   const int Imax = a.I > a.Is ? a.I : a.Is;
   if (tid == 0) s_hlead = take_ticket(a, kLineHTicket, xcc);
-  take_routing(a, R, s_mark, s_l);  // ends with a barrier
+  take_routing(a, xcc, R, s_mark, s_llead);  // ends with a barrier
   const bool lead = s_hlead != 0;
   const int n_routed = R.n;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
@@ -1372,8 +1379,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
   __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks
   __shared__ float s_part[2][kMaxDownSlots][kRows];
   __shared__ double s_red[kGateupWaves];
-  __shared__ float s_l[kMaxExperts];  // the logits (routed gate/up and down blocks)
-  __shared__ int s_hlead;
+  __shared__ int s_llead, s_hlead;
   const int b = blockIdx.x;
   if (b < rt_blocks) {
     router_block_b1(a, b, s_x, s_red);
@@ -1387,12 +1393,12 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
     first_pieces(a, x0, g0);
     stage_token(a, s_x, s_red, x0, g0);
     if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) {
-      take_routing(a, R, s_mark, s_l);
+      take_routing(a, xcc, R, s_mark, s_llead);
       if (bid == 0) publish_routing(a, R);
     }
     gateup_block<WT, 1, true>(a, bid, R, reinterpret_cast<const uint16_t *>(s_x));
   } else {
-    down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_l, s_part, s_hlead);
+    down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_part, s_llead, s_hlead);
   }
 }
 
