@@ -480,13 +480,17 @@ __device__ inline void build_routing(const DecodeArgs &a, const float *logits, R
       e = (lane == r) ? sel[r] : e;
       l = (lane == r) ? selv[r] : l;
     }
-    const float sg = (lane < a.k) ? 1.0f / (1.0f + expf(-l)) : 0.f;
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) sum += __shfl(sg, r, kWave);  // in selection order
+    // sigmoid from the hardware base-2 exponential and reciprocal (about
+    // 1 ulp each); the sum over lanes 0..7 (0 past k), the same bits in
+    // each of them
+    const float sg = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-l * 1.44269504088896341f))
+                                  : 0.f;
+    float sum = sg + xor_lane<1>(sg);
+    sum += xor_lane<2>(sum);
+    sum += xor_lane<4>(sum);
     if (lane < a.k) {
       R.sel[t][lane] = e;
-      R.w[t][lane] = sg / sum;
+      R.w[t][lane] = sg / sum;  // a correctly rounded division: one expert gets exactly 1
       if (single) {
         // one token: the distinct list is the selection sorted by index
         int rank = 0;
@@ -1076,13 +1080,6 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 // every wait is bounded.
 // ---------------------------------------------------------------------------
 
-// Drops this CU's cached lines, so that the next plain loads are served by
-// the XCD's L2 (which holds what other CUs of the XCD stored).  Measured on
-// MI355X: a flag stored by another block of the same XCD is seen about
-// 0.4 us after the store this way, while loads with the sc0 policy alone
-// can keep hitting a stale line in the CU cache.
-__device__ __forceinline__ void drop_cu_cache() { asm volatile("buffer_inv sc0" ::: "memory"); }
-
 // Poll rounds (each ends in a short sleep) before a wait on another block
 // of the same kernel gives up; reached only if that block never wrote.
 constexpr int kWaitSpin = 1 << 20;
@@ -1111,12 +1108,17 @@ __device__ __forceinline__ void raise_flag(const DecodeArgs &a, int which, int x
   if (threadIdx.x == 0) *reinterpret_cast<volatile uint32_t *>(sync_line(a, which, xcc)) = a.tag;
 }
 
-// Others (thread 0): until the XCD's flag carries the tag.
+// Others (thread 0): until the XCD's flag carries the tag.  The flag is
+// read with volatile loads (issued sc0 sc1), which miss this CU's cache;
+// plain or sc0 reloads can keep returning a stale line from it (measured:
+// no update in 200,000 polls).  Measured on MI355X: a flag raised by
+// another block of the same XCD is seen about 0.4 us after the store.  The
+// stage is then read once, after the flag, so this CU's cache holds no
+// earlier copy of it (the kernel starts with the CU caches invalidated).
 __device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xcc) {
   if (threadIdx.x == 0) {
     const volatile uint32_t *flag = sync_line(a, which, xcc);
     for (int it = 0; it < kWaitSpin; ++it) {
-      drop_cu_cache();
       if (*flag == a.tag) break;
       __builtin_amdgcn_s_sleep(1);
     }
@@ -1169,7 +1171,6 @@ __device__ inline void take_routing(const DecodeArgs &a, int xcc, Routing &R, ui
     wait_flag(a, kLineLFlag, xcc);
   }
   __syncthreads();
-  drop_cu_cache();  // the stage is read from the L2
   build_routing(a, stage, R, s_mark, kGateupWaves);
 }
 
@@ -1337,7 +1338,6 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int
       }
     }
     __syncthreads();
-    if (pass == 0) drop_cu_cache();  // the stage is read from the L2
     float acc[kRows] = {0.f, 0.f, 0.f, 0.f};
     if (Wd) {
       const int64_t hbase = (int64_t)hslot * Imax;  // the entry's h in the stage
