@@ -48,13 +48,13 @@ inline size_t imax_of(const moe_layer_desc &d) {
 
 constexpr size_t kSyncLineBytes = (size_t)kSyncLines * kXcdSlots * 256;
 
-// Bytes of the one-token sync region of a layer: the ticket and flag
-// lines, then the tagged logit and h words.  Zero for a layer without
-// routed experts.
-size_t sync_bytes_of(const moe_layer_desc &d) {
+// Bytes of the sync region of a layer at batch B: the ticket and flag
+// lines, then the tagged logit words ([B][E]) and the one-token h words.
+// Zero for a layer without routed experts.
+size_t sync_bytes_of(const moe_layer_desc &d, int B) {
   if (d.n_experts <= 0) return 0;
   const size_t words_h = (size_t)(max_routed_of(d, 1) + 1) * imax_of(d) / 2;
-  return kSyncLineBytes + up((size_t)d.n_experts * 8) + up(words_h * 8);
+  return kSyncLineBytes + up((size_t)B * d.n_experts * 8) + up(words_h * 8);
 }
 
 // Layout of one layer's workspace.  The sync region comes first and takes
@@ -66,10 +66,10 @@ WsLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0) {
   const size_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = d.n_experts > 0 ? d.top_k : 0;
   const size_t Imax = imax_of(d);
   const size_t R = max_routed_of(d, B);
-  const size_t own = sync_bytes_of(d);
+  const size_t own = sync_bytes_of(d, B);
   L.sync_lines = 0;
   L.sync_l = kSyncLineBytes;
-  L.sync_h = kSyncLineBytes + up(E * 8);
+  L.sync_h = kSyncLineBytes + up(B * E * 8);
   L.sync_bytes = own > sync_cap ? own : sync_cap;
   size_t o = L.sync_bytes;
   L.logits = o; o += up(B * E * 4);
@@ -266,11 +266,11 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
   DecodeArgs a;
   const moe_status st = prepare_decode(desc, w, x, batch, residual, y, topk_idx, topk_w, ws, ws_bytes, a);
   if (st != MOE_OK) return st;
-  // One token with routed experts: the layer kernel's hand-overs start
-  // from a zeroed sync region.
-  if (batch == 1 && desc->n_experts > 0) {
+  // With routed experts the hand-overs inside the kernels (the logits; for
+  // one token also h) start from a zeroed sync region.
+  if (desc->n_experts > 0) {
     const moe_status sc = hip_status(
-        launch_sync_clear((uint32_t *)ws, (int64_t)(sync_bytes_of(*desc) / 4), (hipStream_t)stream));
+        launch_sync_clear((uint32_t *)ws, (int64_t)(sync_bytes_of(*desc, batch) / 4), (hipStream_t)stream));
     if (sc != MOE_OK) return sc;
   }
   return hip_status(launch_decode(a, (hipStream_t)stream, g_stage_events_on ? g_stage_events : nullptr));
@@ -279,11 +279,11 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
 // Step workspace: two activation buffers, then the largest layer workspace.
 static size_t step_act_bytes(int32_t hidden, int32_t max_batch) { return up((size_t)max_batch * hidden * 2); }
 
-// The common sync region of a step's layers.
-static size_t step_sync_cap(const moe_layer_desc *descs, int32_t n_layers) {
+// The common sync region of a step's layers at batch B.
+static size_t step_sync_cap(const moe_layer_desc *descs, int32_t n_layers, int32_t B) {
   size_t cap = 0;
   for (int32_t i = 0; i < n_layers; ++i) {
-    const size_t b = sync_bytes_of(descs[i]);
+    const size_t b = sync_bytes_of(descs[i], B);
     cap = b > cap ? b : cap;
   }
   return cap;
@@ -293,7 +293,7 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
   if (!descs || n_layers < 1 || max_batch < 1 || max_batch > kMaxBatch) return 0;
   for (int32_t i = 0; i < n_layers; ++i)
     if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return 0;
-  const size_t cap = step_sync_cap(descs, n_layers);
+  const size_t cap = step_sync_cap(descs, n_layers, max_batch);
   size_t layer = 0;
   for (int32_t i = 0; i < n_layers; ++i) {
     const size_t b = decode_layout(descs[i], max_batch, cap).bytes;
@@ -320,7 +320,7 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
   const size_t act = step_act_bytes(descs[0].hidden, batch);
   uint8_t *a0 = (uint8_t *)ws, *a1 = a0 + act, *lws = a1 + act;
   const size_t lws_bytes = ws_bytes - 2 * act;
-  const size_t cap = step_sync_cap(descs, n_layers);
+  const size_t cap = step_sync_cap(descs, n_layers, batch);
   // Validate every layer before launching anything.
   for (int32_t i = 0; i < n_layers; ++i) {
     const void *in = (i == 0) ? x : ((i & 1) ? (const void *)a0 : (const void *)a1);
@@ -330,9 +330,9 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
                                          lws_bytes, a, cap);
     if (st != MOE_OK) return st;
   }
-  // One token: the layer kernels' sync words start zeroed, once per step;
-  // each layer call then carries its own tag.
-  if (batch == 1 && cap > 0) {
+  // The layers' sync words start zeroed, once per step; each layer call
+  // then carries its own tag.
+  if (cap > 0) {
     const moe_status sc = hip_status(launch_sync_clear((uint32_t *)lws, (int64_t)(cap / 4), (hipStream_t)stream));
     if (sc != MOE_OK) return sc;
   }

@@ -16,10 +16,11 @@
 //              squares.
 //   k_router   router GEMV l = W_r xn + b in FP32, the batch staged in LDS
 //              (a dense layer of one token: only its pre-norm), one row
-//              per lane group, each row loaded once for every token.
-//   k_route    (batches of 2..8 tokens) one block: sigmoid top-k of every
-//              token, the sorted list of distinct selected experts with
-//              token masks, the renormalised combine weights.
+//              per lane group, each row loaded once for every token; its
+//              last block (one wave per token) waits for the batch's
+//              logits, published as tagged words, and derives the routing:
+//              sigmoid top-k of every token, the sorted list of distinct
+//              selected experts with token masks, the combine weights.
 //   k_gateup   (dense layers, and batches with BF16 weights) its share of
 //              the gate and up GEMVs of one selected (or the shared)
 //              expert: FP4 decoded to BF16 in registers, FP32
@@ -293,7 +294,20 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
   }
 }
 
-// Router GEMV, four waves per block.  The block first brings the batch's
+// A value published for other blocks of the same kernel: the
+// value's 32 bits with the layer call's tag above them, in one 64-bit
+// agent-scope store.  A reader polls the word until it carries its own tag.
+__device__ __forceinline__ void publish_tagged(uint64_t *p, uint32_t v, uint32_t tag) {
+  __hip_atomic_store(p, (uint64_t)v | ((uint64_t)tag << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ void route_block(const DecodeArgs &a, uint4 *lds);
+
+// Router GEMV, W waves per block (4 for one token, 8 for batches).  The block first brings the batch's
 // activations into LDS (at most 64 KiB): xn when k_norm already wrote it
 // (xn_ready), else x, normalised there with a pre-norm (the sum of squares
 // of each token in FP64 over the whole block, then every element
@@ -304,10 +318,17 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
 // ... of the row, so a wave's LDS and global accesses are contiguous.
 constexpr int kRouterWaves = 4;
 constexpr int kRouterThreads = kRouterWaves * kWave;
+constexpr int kRouteWaves = kMaxBatch;  // batches: one wave per token in the routing block
 
-__global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_ready) {
+template <int W>
+__global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready, int route) {
+  constexpr int kRouterWaves = W, kRouterThreads = W * kWave;
   __shared__ uint4 s_x[kMaxBatch * 4096 / 8];  // [B][H] BF16, B * H <= 32768
   __shared__ double s_ss[kRouterWaves][kMaxBatch];
+  if (route && blockIdx.x == gridDim.x - 1) {
+    route_block(a, s_x);
+    return;
+  }
   const int H = a.H, E = a.E, B = a.B;
   const int LPR = lanes_per_row(H);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
@@ -442,7 +463,10 @@ __global__ __launch_bounds__(kRouterThreads) void k_router(DecodeArgs a, int xn_
   for (int t = 0; t < kMaxBatch; ++t) {
     if (t >= B) break;
     const float v = group_sum(acc[t], LPR);
-    if (lg == 0) a.ws.logits[t * E + row] = v + bias;
+    if (lg == 0) {
+      if (route) publish_tagged(a.ws.sync_l + t * E + row, __float_as_uint(v + bias), a.tag);
+      else a.ws.logits[t * E + row] = v + bias;
+    }
   }
 }
 
@@ -549,16 +573,6 @@ __device__ inline void publish_routing(const DecodeArgs &a, const Routing &R) {
   if (tid == 0) *a.ws.n_routed = R.n;
 }
 
-// Routing of a batch of several tokens: one block, one wave per token.
-constexpr int kRouteWaves = kMaxBatch;
-
-__global__ __launch_bounds__(kRouteWaves *kWave) void k_route(DecodeArgs a) {
-  __shared__ Routing R;
-  __shared__ uint32_t s_mark[kMaxExperts];
-  build_routing(a, a.ws.logits, R, s_mark, kRouteWaves);
-  publish_routing(a, R);
-}
-
 // ---------------------------------------------------------------------------
 // k_gateup: each lane group computes 4 rows of h for one expert
 // ---------------------------------------------------------------------------
@@ -577,17 +591,6 @@ __device__ __forceinline__ void dot_tokens(const ChunkBF &cb, const uint16_t *xs
       dot_rows<WT>(cb, x, acc[t]);
     }
   });
-}
-
-// A value published for other blocks of the same kernel (one token): the
-// value's 32 bits with the layer call's tag above them, in one 64-bit
-// agent-scope store.  A reader polls the word until it carries its own tag.
-__device__ __forceinline__ void publish_tagged(uint64_t *p, uint32_t v, uint32_t tag) {
-  __hip_atomic_store(p, (uint64_t)v | ((uint64_t)tag << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Gate/up GEMVs of block `bid`: 4-row units of the selected experts, then
@@ -1156,6 +1159,21 @@ __device__ inline void copy_tagged(const uint64_t *src, uint32_t *dst, int n, ui
   }
 }
 
+// The last block of k_router with `route` (batches of 2..8 tokens, one
+// wave per token): the routing of the batch from the tagged logits the
+// other blocks publish, polled into LDS (B * E floats, at most 32 KiB, in
+// the activation stage this block does not use); the list and the top-k
+// outputs are published for the expert kernels.
+__device__ void route_block(const DecodeArgs &a, uint4 *lds) {
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[kMaxExperts];
+  float *s_l = reinterpret_cast<float *>(lds);
+  copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_l), a.B * a.E, a.tag);
+  __syncthreads();
+  build_routing(a, s_l, R, s_mark, (int)(blockDim.x / kWave));
+  publish_routing(a, R);
+}
+
 // The token's routing from the logits the router blocks published, by way
 // of this XCD's copy.  s_lead: a shared word for the ticket.  Ends with a
 // barrier.  (Every consumer block polling the E words itself measured
@@ -1426,10 +1444,6 @@ static hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, size_t 
 template <int WT, int MAXT>
 static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
   hipError_t e;
-  if (MAXT > 1 && a.E > 0) {
-    if ((e = launch(k_route, dim3(1), dim3(kRouteWaves * kWave), 0, stream, nullptr, nullptr, a)) != hipSuccess)
-      return e;
-  }
   if (WT == 1 && MAXT > 1) {
     const int Imax = a.I > a.Is ? a.I : a.Is;
     const int groups = (Imax + kMmRows - 1) / kMmRows;
@@ -1497,11 +1511,18 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
   if (xn_ready) {
     if ((e = launch(k_norm, dim3(a.B), dim3(kNormThreads), 0, stream, nullptr, nullptr, a)) != hipSuccess) return e;
   }
-  if (a.E > 0 || (a.use_norm && !xn_ready)) {
-    const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
-    const int grid = a.E > 0 ? (a.E + rows_per_block - 1) / rows_per_block : 1;
-    if ((e = launch(k_router, dim3(grid), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
-                    ev ? ev[1] : nullptr, a, xn_ready)) != hipSuccess)
+  if (a.E > 0) {
+    // batches with routed experts: 8-wave blocks, the last of them derives
+    // the routing from the others' logits
+    const int rows_per_block = kRouteWaves * (kWave / lanes_per_row(a.H));
+    const int grid = (a.E + rows_per_block - 1) / rows_per_block + 1;
+    if ((e = launch(k_router<kRouteWaves>, dim3(grid), dim3(kRouteWaves * kWave), 0, stream, ev ? ev[0] : nullptr,
+                    ev ? ev[1] : nullptr, a, xn_ready, 1)) != hipSuccess)
+      return e;
+  } else if (a.use_norm && !xn_ready) {
+    // a dense layer of one token: the pre-norm only
+    if ((e = launch(k_router<kRouterWaves>, dim3(1), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
+                    ev ? ev[1] : nullptr, a, xn_ready, 0)) != hipSuccess)
       return e;
   }
   const int mt = a.B <= 1 ? 1 : a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8;
