@@ -1410,11 +1410,14 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
     uint4 x0, g0;
     first_pieces(a, x0, g0);
     stage_token(a, s_x, s_red, x0, g0);
-    if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) {
-      take_routing(a, xcc, R, s_mark, s_llead);
-      if (bid == 0) publish_routing(a, R);
-    }
+    if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) take_routing(a, xcc, R, s_mark, s_llead);
     gateup_block<WT, 1, true>(a, bid, R, reinterpret_cast<const uint16_t *>(s_x));
+    // the top-k outputs, after this block's share of h (the down blocks
+    // derive the routing themselves and read no entry list)
+    if (bid == 0 && threadIdx.x < (unsigned)a.k) {
+      a.out_idx[threadIdx.x] = R.sel[0][threadIdx.x];
+      a.out_w[threadIdx.x] = R.w[0][threadIdx.x];
+    }
   } else {
     down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_part, s_llead, s_hlead);
   }
