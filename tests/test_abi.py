@@ -169,6 +169,25 @@ def test_step_validation():
     assert lib.moe_decode_step(dd, ww2, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
 
 
+def test_step_workspace_covers_every_layer():
+    # Layers of different shapes share the step's workspace: the layer part
+    # must hold each layer's own workspace (its sync region is laid out for
+    # the largest layer), at every batch, and grow with the batch.
+    ds = [desc(hidden=256, inter=64, shared_inter=64, n_experts=32, top_k=6),
+          desc(hidden=256, n_experts=0, top_k=0, inter=0, shared_inter=256),
+          desc(hidden=256, inter=128, shared_inter=128, n_experts=64, top_k=8),
+          desc(hidden=256, inter=64, shared_inter=0, n_experts=16, top_k=2)]
+    for B in (1, 3, 8):
+        step = m.moe_decode_step_workspace_bytes(ds, B)
+        act = 2 * ((B * 256 * 2 + 255) // 256 * 256)
+        for d in ds:
+            assert step - act >= m.moe_decode_workspace_bytes(d, B) > 0
+    assert m.moe_decode_step_workspace_bytes(ds, 8) >= m.moe_decode_step_workspace_bytes(ds, 3) >= \
+        m.moe_decode_step_workspace_bytes(ds, 1)
+    for d in ds:
+        assert m.moe_decode_workspace_bytes(d, 8) >= m.moe_decode_workspace_bytes(d, 1)
+
+
 def prefill(d=None, w=None, x=A(20), T=100, y=A(21), ws=A(22), ws_bytes=1 << 34):
     d = d or desc()
     w = w or weights()
