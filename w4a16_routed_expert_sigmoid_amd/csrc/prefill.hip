@@ -178,6 +178,11 @@ __device__ __forceinline__ uint32_t pf_key(float l) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The logit of a key (NaN came in as -inf).
+__device__ __forceinline__ float pf_key_logit(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
 __device__ __forceinline__ uint32_t pf_wave_max(uint32_t m) {
   m = max(m, xor_lane<1>(m));
   m = max(m, xor_lane<2>(m));
@@ -227,12 +232,17 @@ __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a)
       for (int j = 0; j < J; ++j) key[j] = (lane + j * 64 == e) ? 0u : key[j];
       if (lane == r) {
         my_e = e;
-        my_l = lt[e];
+        my_l = pf_key_logit(m);
       }
     }
-    const float s = (lane < a.k) ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
-    float sum = 0.f;
-    for (int r = 0; r < a.k; ++r) sum += __shfl(s, r, 64);
+    // the same arithmetic as the decode path: sigmoid from the hardware
+    // base-2 exponential and reciprocal, the sum over lanes 0..7 (0 past k)
+    // in a fixed butterfly order, one correctly rounded division
+    const float s = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-my_l * 1.44269504088896341f))
+                                 : 0.f;
+    float sum = s + xor_lane<1>(s);
+    sum += xor_lane<2>(sum);
+    sum += xor_lane<4>(sum);
     if (lane < a.k) {
       a.out_idx[(int64_t)t * a.k + lane] = my_e;
       a.out_w[(int64_t)t * a.k + lane] = s / sum;
