@@ -788,7 +788,8 @@ __global__ __launch_bounds__(PThreads) void k_pf_combine(PrefillArgs a) {
       }
     }
     uint32_t o[4];
-    const uint4 xv = *reinterpret_cast<const uint4 *>(a.x + (int64_t)t * a.H + c);
+    // the layer input only when it is added back
+    const uint4 xv = a.residual ? *reinterpret_cast<const uint4 *>(a.x + (int64_t)t * a.H + c) : make_uint4(0, 0, 0, 0);
     const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
