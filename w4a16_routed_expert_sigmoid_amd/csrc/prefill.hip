@@ -5,12 +5,13 @@
 //
 //   k_pf_norm     (pre-norm layers) xn = BF16(RMSNorm(x) * gain), one wave per token
 //   k_pf_router   logits = xn W_r^T + b: GEMM on v_mfma_f32_32x32x16_bf16
-//                 (its first block also clears the expert counts)
+//                 (its first block also clears the expert counts and cursors)
 //   k_pf_topk     sigmoid top-k per token (one wave each), renormalised
 //                 weights, per-expert token counts (LDS histogram per block)
-//   k_pf_scan     expert offsets and the tile list: every expert's rows in
-//                 tiles of 128, then the shared expert's tiles
-//   k_pf_scatter  each (token, k) pair gets a row in its expert's segment
+//   k_pf_place    expert offsets (every block scans the counts; block 0
+//                 writes them and the tile list: every expert's rows in tiles
+//                 of 128, then the shared expert's tiles), and each (token, k)
+//                 pair's row in its expert's segment
 //   k_pf_gemm_fp4<0>, <1>  (NVFP4 weights) grouped GEMMs over the tiles:
 //                 gathered xn rows x the expert's gate and up matrices,
 //                 epilogue h = BF16(SiLU(BF16(g)) BF16(u)); then h rows x the
@@ -254,71 +255,93 @@ __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a)
     if (s_hist[e]) atomicAdd(&a.counts[e], (int)s_hist[e]);
 }
 
-// Offsets of every expert's segment and the tile list: one block of 1024
-// threads, thread e owns expert e; two inclusive scans in LDS (rows and
-// tiles per expert).
-constexpr int kScanThreads = 1024;
-static_assert(kScanThreads >= kMaxExperts, "one scan thread per expert");
+// Expert offsets, the tile list and every pair's row.  Each block scans the
+// expert counts in LDS (thread i owns experts 4i .. 4i+3; one scan over the
+// 256 thread sums for rows and one for 128-row tiles); block 0 writes the
+// offsets and the tile list.  Then the block's (token, k) pairs, PThreads * 2
+// at a time: ranks within the block from an LDS histogram, one atomic per
+// expert on a cursor that starts at zero, row = offset + cursor + rank.
+constexpr int kPlaceExp = kMaxExperts / PThreads;  // experts per thread in the scan
+static_assert(kMaxExperts % PThreads == 0, "the scan splits the experts evenly");
+constexpr int kPlaceMaxBlocks = 1024;
 
-__global__ __launch_bounds__(kScanThreads) void k_pf_scan(PrefillArgs a) {
-  __shared__ int s_rows[kScanThreads], s_tiles[kScanThreads];
-  const int e = threadIdx.x;
-  const int c = e < a.E ? a.counts[e] : 0;
-  const int nt = (c + PBM - 1) / PBM;
-  s_rows[e] = c;
-  s_tiles[e] = nt;
-  __syncthreads();
-  for (int o = 1; o < kScanThreads; o <<= 1) {
-    const int vr = e >= o ? s_rows[e - o] : 0, vt = e >= o ? s_tiles[e - o] : 0;
-    __syncthreads();
-    s_rows[e] += vr;
-    s_tiles[e] += vt;
-    __syncthreads();
-  }
-  const int off = s_rows[e] - c, toff = s_tiles[e] - nt;
-  if (e < a.E) {
-    a.offsets[e] = off;
-    a.cursors[e] = off;
-    for (int i = 0; i < nt; ++i) a.tiles[toff + i] = PfTile{off + i * PBM, min(PBM, c - i * PBM), e};
-  }
-  const int routed_tiles = s_tiles[kScanThreads - 1];
-  const int shared_tiles = a.Is > 0 ? (a.T + PBM - 1) / PBM : 0;
-  for (int i = e; i < shared_tiles; i += kScanThreads)
-    a.tiles[routed_tiles + i] = PfTile{a.P + i * PBM, min(PBM, a.T - i * PBM), -1};
-  if (e == 0) {
-    a.offsets[a.E] = s_rows[kScanThreads - 1];
-    *a.n_tiles = routed_tiles + shared_tiles;
-  }
-}
-
-// Rows of the (token, k) pairs in their experts' segments.
-__global__ __launch_bounds__(PThreads) void k_pf_scatter(PrefillArgs a) {
+__global__ __launch_bounds__(PThreads) void k_pf_place(PrefillArgs a) {
+  __shared__ int s_rows[PThreads], s_tl[PThreads];
+  __shared__ int s_off[kMaxExperts];
   __shared__ uint32_t s_cnt[kMaxExperts];
   __shared__ int s_base[kMaxExperts];
-  for (int e = threadIdx.x; e < a.E; e += PThreads) s_cnt[e] = 0u;
-  __syncthreads();
-  constexpr int kPairsPerThread = 2;
-  const int64_t q0 = ((int64_t)blockIdx.x * PThreads + threadIdx.x) * kPairsPerThread;
-  const int64_t P = (int64_t)a.T * a.k;
-  int rank[kPairsPerThread], ex[kPairsPerThread];
+  const int tid = threadIdx.x;
+  int c[kPlaceExp], rows = 0, tl = 0;
 #pragma unroll
-  for (int i = 0; i < kPairsPerThread; ++i) {
-    ex[i] = -1;
-    if (q0 + i < P) {
-      ex[i] = a.out_idx[q0 + i];
-      rank[i] = (int)atomicAdd(&s_cnt[ex[i]], 1u);
+  for (int j = 0; j < kPlaceExp; ++j) {
+    const int e = tid * kPlaceExp + j;
+    c[j] = e < a.E ? a.counts[e] : 0;
+    rows += c[j];
+    tl += (c[j] + PBM - 1) / PBM;
+  }
+  s_rows[tid] = rows;
+  s_tl[tid] = tl;
+  __syncthreads();
+  for (int o = 1; o < PThreads; o <<= 1) {
+    const int vr = tid >= o ? s_rows[tid - o] : 0, vt = tid >= o ? s_tl[tid - o] : 0;
+    __syncthreads();
+    s_rows[tid] += vr;
+    s_tl[tid] += vt;
+    __syncthreads();
+  }
+  int off = s_rows[tid] - rows, toff = s_tl[tid] - tl;
+#pragma unroll
+  for (int j = 0; j < kPlaceExp; ++j) {
+    const int e = tid * kPlaceExp + j;
+    s_off[e] = off;
+    if (blockIdx.x == 0 && e < a.E) {
+      a.offsets[e] = off;
+      const int nt = (c[j] + PBM - 1) / PBM;
+      for (int i = 0; i < nt; ++i) a.tiles[toff + i] = PfTile{off + i * PBM, min(PBM, c[j] - i * PBM), e};
+    }
+    off += c[j];
+    toff += (c[j] + PBM - 1) / PBM;
+  }
+  if (blockIdx.x == 0) {
+    const int routed_tiles = s_tl[PThreads - 1];
+    const int shared_tiles = a.Is > 0 ? (a.T + PBM - 1) / PBM : 0;
+    for (int i = tid; i < shared_tiles; i += PThreads)
+      a.tiles[routed_tiles + i] = PfTile{a.P + i * PBM, min(PBM, a.T - i * PBM), -1};
+    if (tid == 0) {
+      a.offsets[a.E] = s_rows[PThreads - 1];
+      *a.n_tiles = routed_tiles + shared_tiles;
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += PThreads)
-    s_base[e] = s_cnt[e] ? atomicAdd(&a.cursors[e], (int)s_cnt[e]) : 0;
-  __syncthreads();
+
+  constexpr int kPairsPerThread = 2;
+  const int64_t P = (int64_t)a.T * a.k;
+  for (int64_t b0 = (int64_t)blockIdx.x * PThreads * kPairsPerThread; b0 < P;
+       b0 += (int64_t)gridDim.x * PThreads * kPairsPerThread) {
+    for (int e = tid; e < a.E; e += PThreads) s_cnt[e] = 0u;
+    __syncthreads();
+    const int64_t q0 = b0 + (int64_t)tid * kPairsPerThread;
+    int rank[kPairsPerThread], ex[kPairsPerThread];
 #pragma unroll
-  for (int i = 0; i < kPairsPerThread; ++i) {
-    if (ex[i] < 0) continue;
-    const int pos = s_base[ex[i]] + rank[i];
-    a.sorted_tok[pos] = (int)((q0 + i) / a.k);
-    a.pair_pos[q0 + i] = pos;
+    for (int i = 0; i < kPairsPerThread; ++i) {
+      ex[i] = -1;
+      if (q0 + i < P) {
+        ex[i] = a.out_idx[q0 + i];
+        rank[i] = (int)atomicAdd(&s_cnt[ex[i]], 1u);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += PThreads)
+      s_base[e] = s_cnt[e] ? s_off[e] + atomicAdd(&a.cursors[e], (int)s_cnt[e]) : 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPairsPerThread; ++i) {
+      if (ex[i] < 0) continue;
+      const int pos = s_base[ex[i]] + rank[i];
+      a.sorted_tok[pos] = (int)((q0 + i) / a.k);
+      a.pair_pos[q0 + i] = pos;
+    }
+    __syncthreads();
   }
 }
 
@@ -339,9 +362,13 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   const int m0 = blockIdx.x * RBM, n0 = blockIdx.y * RBN;
   const uint16_t *xs = a.use_norm ? a.xn : a.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // the expert counts the top-k kernel accumulates start at zero
+  // the expert counts the top-k kernel accumulates, and the cursors the
+  // placement kernel advances, start at zero
   if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = tid; i < a.E + 1; i += PThreads) a.counts[i] = 0;
+    for (int i = tid; i < a.E + 1; i += PThreads) {
+      a.counts[i] = 0;
+      a.cursors[i] = 0;
+    }
   const int r = tid >> 2, part = tid & 3;  // loads: row r, K elements part*RPART .. +RPART of the stage
   const uint16_t *arow = (m0 + r < a.T) ? xs + (int64_t)(m0 + r) * a.H : nullptr;
   const uint16_t *brow = (n0 + r < a.E) ? a.router_w + (int64_t)(n0 + r) * a.H : nullptr;
@@ -826,12 +853,13 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
     else hipLaunchKernelGGL(k_pf_topk<kMaxExperts / kWave>, tg, tb, 0, s, a);
     MOE_CK_LAUNCH();
   }
-  hipLaunchKernelGGL(k_pf_scan, dim3(1), dim3(kScanThreads), 0, s, a);
-  MOE_CK_LAUNCH();
-  if (a.E > 0) {
+  {
+    // one block at least: it writes the tile list (the shared expert's tiles
+    // even without routed experts)
     const int64_t pairs = (int64_t)a.T * a.k;
-    hipLaunchKernelGGL(k_pf_scatter, dim3((unsigned)((pairs + 2 * PThreads - 1) / (2 * PThreads))), dim3(PThreads),
-                       0, s, a);
+    const int64_t want = (pairs + 2 * PThreads - 1) / (2 * PThreads);
+    const int blocks = (int)(want < 1 ? 1 : want > kPlaceMaxBlocks ? kPlaceMaxBlocks : want);
+    hipLaunchKernelGGL(k_pf_place, dim3(blocks), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
   }
   const int nmax = a.I > a.Is ? a.I : a.Is;
