@@ -136,6 +136,29 @@ def test_prefill_matches_decode_routing_and_workspace_reuse():
                     assert set(idd.cpu().numpy()[t].tolist()) == set(a[1][t0 + t].tolist())
 
 
+def test_prefill_placement_second_pass():
+    # 140,000 tokens x top-4 = 560,000 (token, k) pairs: more than the 1024
+    # placement blocks take in one pass of 512 pairs each, so some blocks
+    # place a second batch.  A token's result depends on that token alone,
+    # so every token must match, bit for bit, the same tokens run in four
+    # chunks that need one pass; a spread sample is checked by the oracle.
+    T, chunks = 140_000, 4
+    log(f"test: prefill placement second pass T={T}")
+    L = synth.make_layer(13, **SMALL)
+    dev = moe.DeviceLayer(L)
+    x = synth.tokens(T, 256, stream=13)
+    out, idx, w = run(L, x, dev)
+    check_routing_properties(L, idx, w)
+    n = T // chunks
+    for c in range(chunks):
+        oc, ic, wc = run(L, x[c * n:(c + 1) * n], dev)
+        assert np.array_equal(ic, idx[c * n:(c + 1) * n]), f"chunk {c} experts"
+        assert np.array_equal(wc, w[c * n:(c + 1) * n]), f"chunk {c} weights"
+        assert np.array_equal(oc, out[c * n:(c + 1) * n]), f"chunk {c} outputs"
+    s = sample_tokens(T, 64, 13)
+    compare(L, x[s], out[s], idx[s], w[s], what=f"prefill second pass T={T}")
+
+
 def test_prefill_rejects_and_sizes():
     L = synth.make_layer(40, **SMALL)
     dev = moe.DeviceLayer(L)
