@@ -110,9 +110,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 
 // Top-k experts of one token's logits by one wave: sel[0..k) in descending
 // logit order, ties to the lower expert index; selv = their logits.  Lane l
-// holds experts l, l+64, ... (J per lane, E <= 64*J).  Each round: a wave
-// max of the 32-bit keys, then ballots find the lowest expert index holding
-// it.  Results are wave-uniform.
+// holds experts l*J .. l*J+J-1 (E <= 64*J), so the lowest expert index with
+// a given key is in the lowest lane holding it.  Each round every lane
+// first notes the first slot holding its own max and what its keys and max
+// are without that slot (work independent of the wave max, which hides it);
+// then the wave max of the lanes' maxima, one ballot for the lowest lane
+// holding it, and that lane drops its slot.  Results are wave-uniform.
 template <int J>
 __device__ __forceinline__ void wave_topk(const float *lt, int E, int k, int (&sel)[kMaxTopK],
                                           float (&selv)[kMaxTopK]) {
@@ -120,27 +123,33 @@ __device__ __forceinline__ void wave_topk(const float *lt, int E, int k, int (&s
   uint32_t key[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int e = lane + j * kWave;
+    const int e = lane * J + j;
     key[j] = (e < E) ? topk_key(lt[e]) : 0u;
   }
+  uint32_t lmax = key[0];
+#pragma unroll
+  for (int j = 1; j < J; ++j) lmax = max(lmax, key[j]);
 #pragma unroll
   for (int r = 0; r < kMaxTopK; ++r) {
     if (r < k) {
-      uint32_t m = key[0];
+      int jm = J - 1;  // some slot holds lmax
 #pragma unroll
-      for (int j = 1; j < J; ++j) m = max(m, key[j]);
-      m = wave_max_u32(m);
-      // lowest expert index with key m: first j with a match, lowest lane
-      int e = 0x7fffffff;
+      for (int j = J - 2; j >= 0; --j) jm = (key[j] == lmax) ? j : jm;
+      uint32_t keyx[J], lx = 0u;
 #pragma unroll
-      for (int j = J - 1; j >= 0; --j) {
-        const unsigned long long b = __ballot(key[j] == m);
-        if (b) e = j * kWave + (int)__builtin_ctzll(b);
+      for (int j = 0; j < J; ++j) {
+        keyx[j] = (j == jm) ? 0u : key[j];
+        lx = max(lx, keyx[j]);
       }
-      sel[r] = e;
+      // k <= E, so an untaken real key (> 0) remains and some lane holds m
+      const uint32_t m = wave_max_u32(lmax);
+      const int L = (int)__builtin_ctzll(__ballot(lmax == m));
+      sel[r] = L * J + __builtin_amdgcn_readlane(jm, L);
       selv[r] = topk_key_logit(m);
+      const bool mine = lane == L;
 #pragma unroll
-      for (int j = 0; j < J; ++j) key[j] = (lane + j * kWave == e) ? 0u : key[j];
+      for (int j = 0; j < J; ++j) key[j] = mine ? keyx[j] : key[j];
+      lmax = mine ? lx : lmax;
     }
   }
 }
