@@ -147,6 +147,27 @@ __device__ inline T xor_lane(T v) {
   }
 }
 
+// Max over the wave, in every lane.  Within 16-lane rows: the quad swaps,
+// then rotations by 4 and 8 (each lane ends with its row's max; 0 is the
+// identity of the unsigned max, so the rotations may fold into the max).
+// Across rows: each lane pair of the row and half swaps holds the two
+// partners' values, whose max is the pair's.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t m) {
+  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = dpp_max_u32<0xB1>(m);   // quad_perm [1,0,3,2]
+  m = dpp_max_u32<0x4E>(m);   // quad_perm [2,3,0,1]
+  m = dpp_max_u32<0x124>(m);  // row_ror:4
+  m = dpp_max_u32<0x128>(m);  // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  m = max((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return max((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+
 // xor_lane with an offset that is a compile-time constant after unrolling.
 template <typename T>
 __device__ inline T xor_lane_n(T v, int o) {

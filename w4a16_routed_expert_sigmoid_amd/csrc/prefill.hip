@@ -184,21 +184,15 @@ __device__ __forceinline__ float pf_key_logit(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-__device__ __forceinline__ uint32_t pf_wave_max(uint32_t m) {
-  m = max(m, xor_lane<1>(m));
-  m = max(m, xor_lane<2>(m));
-  m = max(m, xor_lane<4>(m));
-  m = max(m, xor_lane<8>(m));
-  m = max(m, xor_lane<16>(m));
-  m = max(m, xor_lane<32>(m));
-  return m;
-}
-
 constexpr int kPfTokensPerWave = 2;
 constexpr int kPfTopkWaves = 16;
 
 // Top-k of each token (one wave per token at a time), weights, counts.  J:
-// logits per lane (E <= 64 J).
+// logits per lane (E <= 64 J); lane l holds experts l*J .. l*J+J-1, so the
+// lowest expert index holding a key is in the lowest lane holding it.  Each
+// round every lane notes the first slot of its own max and its keys and max
+// without that slot, beside the wave max; one ballot then names the lowest
+// lane holding the max, which drops its slot (ties to the lower index).
 template <int J>
 __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a) {
   __shared__ uint32_t s_hist[kMaxExperts];
@@ -213,24 +207,32 @@ __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a)
     uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int e = lane + j * 64;
+      const int e = lane * J + j;
       key[j] = (e < a.E) ? pf_key(lt[e]) : 0u;
     }
+    uint32_t lmax = key[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) lmax = max(lmax, key[j]);
     int my_e = 0;
     float my_l = 0.f;
     for (int r = 0; r < a.k; ++r) {
-      uint32_t m = key[0];
+      int jm = J - 1;  // some slot holds lmax
 #pragma unroll
-      for (int j = 1; j < J; ++j) m = max(m, key[j]);
-      m = pf_wave_max(m);
-      int e = 0x7fffffff;
+      for (int j = J - 2; j >= 0; --j) jm = (key[j] == lmax) ? j : jm;
+      uint32_t keyx[J], lx = 0u;
 #pragma unroll
-      for (int j = J - 1; j >= 0; --j) {
-        const unsigned long long b = __ballot(key[j] == m);
-        if (b) e = j * 64 + (int)__builtin_ctzll(b);
+      for (int j = 0; j < J; ++j) {
+        keyx[j] = (j == jm) ? 0u : key[j];
+        lx = max(lx, keyx[j]);
       }
+      // k <= E, so an untaken real key (> 0) remains and some lane holds m
+      const uint32_t m = wave_max_u32(lmax);
+      const int L = (int)__builtin_ctzll(__ballot(lmax == m));
+      const int e = L * J + __builtin_amdgcn_readlane(jm, L);
+      const bool mine = lane == L;
 #pragma unroll
-      for (int j = 0; j < J; ++j) key[j] = (lane + j * 64 == e) ? 0u : key[j];
+      for (int j = 0; j < J; ++j) key[j] = mine ? keyx[j] : key[j];
+      lmax = mine ? lx : lmax;
       if (lane == r) {
         my_e = e;
         my_l = pf_key_logit(m);
