@@ -32,8 +32,8 @@ inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct WsLayout {
   size_t sync_lines, sync_l, sync_h, sync_bytes;
-  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, xcd_h, bytes;
-  size_t stage_elems;
+  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, xcd_l, xcd_h, bytes;
+  size_t stage_l, stage_elems;
 };
 
 inline int max_routed_of(const moe_layer_desc &d, int B) {
@@ -81,10 +81,12 @@ WsLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0) {
   L.topk_idx = o; o += up(B * k * 4);
   L.topk_w = o; o += up(B * k * 4);
   L.h = o; o += up((R + 1) * B * Imax * 2);
-  // one-token h stages (also reserved at larger batches, so that a
-  // workspace sized for batch b serves every smaller batch)
+  // one-token stages (also reserved at larger batches, so that a workspace
+  // sized for batch b serves every smaller batch)
   const size_t R1 = max_routed_of(d, 1);
+  L.stage_l = (E + 63) / 64 * 64;
   L.stage_elems = ((R1 + 1) * Imax + 127) / 128 * 128;
+  L.xcd_l = o; o += up(kXcdSlots * L.stage_l * 4);
   L.xcd_h = o; o += up(kXcdSlots * L.stage_elems * 2);
   L.bytes = o;
   return L;
@@ -248,7 +250,9 @@ static moe_status prepare_decode(const moe_layer_desc *desc, const moe_layer_wei
   a.ws.sync_lines = (uint32_t *)(base + L.sync_lines);
   a.ws.sync_l = (uint64_t *)(base + L.sync_l);
   a.ws.sync_h = (uint64_t *)(base + L.sync_h);
+  a.ws.xcd_l = (float *)(base + L.xcd_l);
   a.ws.xcd_h = (uint16_t *)(base + L.xcd_h);
+  a.ws.stage_l = (int64_t)L.stage_l;
   a.ws.stage_elems = (int64_t)L.stage_elems;
   a.ws.bytes = L.bytes;
   a.out_idx = topk_idx ? topk_idx : a.ws.topk_idx;

@@ -284,15 +284,16 @@ struct DecodeWs {
   uint32_t *sync_lines;   // [kSyncLines][kXcdSlots][64]: word 0 of each 256-byte line is used
   uint64_t *sync_l;       // [E] logit words
   uint64_t *sync_h;       // [(k + 1) * Imax / 2] h words (two BF16 values each)
+  float *xcd_l;           // [kXcdSlots][stage_l] per-XCD copy of the logits
   uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
+  int64_t stage_l;        // E rounded up to 64
   int64_t stage_elems;    // (one-token max_routed + 1) * Imax, rounded up to 128
   size_t bytes;
 };
 
-// Lines of the sync region: per XCD, the logit ticket and the route line
-// (the one-token selection as up to 32 tagged 64-bit words), then the h
+// Lines of the sync region: per XCD, the logit ticket and flag, then the h
 // ticket and flag.
-enum { kLineLTicket = 0, kLineLRoute = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
+enum { kLineLTicket = 0, kLineLFlag = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
 
 // Arguments of the decode kernels (passed by value).
 struct DecodeArgs {

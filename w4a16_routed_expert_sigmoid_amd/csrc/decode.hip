@@ -481,20 +481,6 @@ struct Routing {
   float w[kMaxBatch][kMaxTopK];         // renormalised sigmoid weights
 };
 
-// Renormalised sigmoid weight of the selection lane r < k holds (logit l),
-// by a whole wave: sigmoid from the hardware base-2 exponential and
-// reciprocal (about 1 ulp each); the sum over lanes 0..7 (0 past k), the
-// same bits in each of them; a correctly rounded division, so that a single
-// expert gets exactly 1.  Lanes >= k return garbage.
-__device__ __forceinline__ float routing_weight(float l, int k) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float sg = (lane < k) ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-l * 1.44269504088896341f)) : 0.f;
-  float sum = sg + xor_lane<1>(sg);
-  sum += xor_lane<2>(sum);
-  sum += xor_lane<4>(sum);
-  return sg / sum;
-}
-
 // Top-k of every token (one wave per token), its weights, and the sorted
 // list of distinct experts, from logits [B][E].  Every caller derives the
 // same list from the same logits.
@@ -517,10 +503,17 @@ __device__ inline void build_routing(const DecodeArgs &a, const float *logits, R
       e = (lane == r) ? sel[r] : e;
       l = (lane == r) ? selv[r] : l;
     }
-    const float w = routing_weight(l, a.k);
+    // sigmoid from the hardware base-2 exponential and reciprocal (about
+    // 1 ulp each); the sum over lanes 0..7 (0 past k), the same bits in
+    // each of them
+    const float sg = (lane < a.k) ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-l * 1.44269504088896341f))
+                                  : 0.f;
+    float sum = sg + xor_lane<1>(sg);
+    sum += xor_lane<2>(sum);
+    sum += xor_lane<4>(sum);
     if (lane < a.k) {
       R.sel[t][lane] = e;
-      R.w[t][lane] = w;
+      R.w[t][lane] = sg / sum;  // a correctly rounded division: one expert gets exactly 1
       if (single) {
         // one token: the distinct list is the selection sorted by index
         int rank = 0;
@@ -1180,63 +1173,22 @@ __device__ void route_block(const DecodeArgs &a, uint4 *lds) {
   publish_routing(a, R);
 }
 
-// The token's routing, by way of its XCD's leader: the first block of the
-// XCD to take the ticket polls the router blocks' tagged logits into LDS,
-// runs the top-k, and publishes the k experts and their logits as tagged
-// words in the XCD's route line; the XCD's other blocks poll those 2k words
-// (one round trip, and no top-k of their own).  Every block then derives R
-// from the 2k values.  s_lead: a shared word for the ticket; s_log: LDS for
-// E logits; s_rt: LDS for 2 * kMaxTopK words.  Ends with a barrier.
-// (Every consumer block polling the E logit words itself measured 0.2 us
-// slower per layer: about 450 blocks re-reading the same 2 KB.)
-__device__ inline void take_routing(const DecodeArgs &a, int xcc, Routing &R, float *s_log, uint32_t *s_rt,
-                                    int &s_lead) {
+// The token's routing from the logits the router blocks published, by way
+// of this XCD's copy.  s_lead: a shared word for the ticket.  Ends with a
+// barrier.  (Every consumer block polling the E words itself measured
+// 0.2 us slower per layer: about 450 blocks re-reading the same 2 KB.)
+__device__ inline void take_routing(const DecodeArgs &a, int xcc, Routing &R, uint32_t *s_mark, int &s_lead) {
   if (threadIdx.x == 0) s_lead = take_ticket(a, kLineLTicket, xcc);
   __syncthreads();
-  uint64_t *route = reinterpret_cast<uint64_t *>(sync_line(a, kLineLRoute, xcc));
-  const int k = a.k, lane = threadIdx.x & (kWave - 1);
+  float *stage = a.ws.xcd_l + (int64_t)xcc * a.ws.stage_l;
   if (s_lead) {
-    copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_log), a.E, a.tag);
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      int sel[kMaxTopK];
-      float selv[kMaxTopK];
-      wave_topk_any(s_log, a.E, k, sel, selv);
-      // lane r < k publishes selection r
-      int e = sel[0];
-      float l = selv[0];
-#pragma unroll
-      for (int r = 1; r < kMaxTopK; ++r) {
-        e = (lane == r) ? sel[r] : e;
-        l = (lane == r) ? selv[r] : l;
-      }
-      if (lane < k) {
-        s_rt[lane] = (uint32_t)e;
-        s_rt[k + lane] = __float_as_uint(l);
-        publish_tagged(route + lane, (uint32_t)e, a.tag);
-        publish_tagged(route + k + lane, __float_as_uint(l), a.tag);
-      }
-    }
+    copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(stage), a.E, a.tag);
+    raise_flag(a, kLineLFlag, xcc);
   } else {
-    copy_tagged(route, s_rt, 2 * k, a.tag);
+    wait_flag(a, kLineLFlag, xcc);
   }
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    // lane r < k: selection r, its weight, and its rank by expert index (the
-    // distinct list of one token is the selection sorted)
-    const int e = lane < k ? (int)s_rt[lane] : 0;
-    const float w = routing_weight(lane < k ? __uint_as_float(s_rt[k + lane]) : 0.f, k);
-    if (lane < k) {
-      R.sel[0][lane] = e;
-      R.w[0][lane] = w;
-      int rank = 0;
-      for (int r = 0; r < k; ++r) rank += ((int)s_rt[r] < e) ? 1 : 0;
-      R.expert[rank] = e;
-      R.mask[rank] = 1u;
-    }
-    if (lane == 0) R.n = k;
-  }
-  __syncthreads();
+  build_routing(a, stage, R, s_mark, kGateupWaves);
 }
 
 // The token into LDS (s_x: H/8 pieces of 16 bytes) with the pre-norm when
@@ -1348,8 +1300,7 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
 }
 
 template <int WT>
-__device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int xcc, Routing &R, float *s_log,
-                                              uint32_t *s_rt,
+__device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int xcc, Routing &R, uint32_t *s_mark,
                                               float (&s_part)[2][kMaxDownSlots][kRows], int &s_llead,
                                               int &s_hlead) {
   const int H = a.H, K = a.I;  // experts present: Is is I or 0
@@ -1362,7 +1313,7 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int
   const int r0 = dbid * (2 * kRows) + half * kRows;
   const int Imax = a.I > a.Is ? a.I : a.Is;
   if (tid == 0) s_hlead = take_ticket(a, kLineHTicket, xcc);
-  take_routing(a, xcc, R, s_log, s_rt, s_llead);  // ends with a barrier
+  take_routing(a, xcc, R, s_mark, s_llead);  // ends with a barrier
   const bool lead = s_hlead != 0;
   const int n_routed = R.n;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
@@ -1442,8 +1393,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
   static_assert(kRouterThreads == kGateupWaves * kWave, "router blocks have the same size");
   extern __shared__ uint4 s_x[];  // [H / 8] the token (router and gate/up blocks)
   __shared__ Routing R;
-  __shared__ float s_log[kMaxExperts];      // the XCD leader's copy of the logits
-  __shared__ uint32_t s_rt[2 * kMaxTopK];   // the token's k experts, then their logits
+  __shared__ uint32_t s_mark[1];  // one token: the routing needs no marks
   __shared__ float s_part[2][kMaxDownSlots][kRows];
   __shared__ double s_red[kGateupWaves];
   __shared__ int s_llead, s_hlead;
@@ -1459,7 +1409,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
     uint4 x0, g0;
     first_pieces(a, x0, g0);
     stage_token(a, s_x, s_red, x0, g0);
-    if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) take_routing(a, xcc, R, s_log, s_rt, s_llead);
+    if (bid * groups < a.max_routed * (a.I / kRows) || bid == 0) take_routing(a, xcc, R, s_mark, s_llead);
     gateup_block<WT, 1, true>(a, bid, R, reinterpret_cast<const uint16_t *>(s_x));
     // the top-k outputs, after this block's share of h (the down blocks
     // derive the routing themselves and read no entry list)
@@ -1468,7 +1418,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
       a.out_w[threadIdx.x] = R.w[0][threadIdx.x];
     }
   } else {
-    down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_log, s_rt, s_part, s_llead, s_hlead);
+    down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_part, s_llead, s_hlead);
   }
 }
 
