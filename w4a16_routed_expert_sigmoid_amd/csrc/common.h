@@ -118,13 +118,16 @@ __device__ __forceinline__ bf16x8 dq8(uint32_t w, float s) {
 
 // value of lane ^ O for a compile-time O: DPP within 16-lane rows (xor 1,
 // 2, 4, 8), the gfx950 cross-row swaps for 16 and 32.  No LDS round trip.
+// Every lane reads a valid lane with these patterns, so bound_ctrl and the
+// old value never show; with them set, the compiler can fold the move into
+// the VALU instruction that consumes it.
 template <int CTRL>
 __device__ inline float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ inline uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int O, typename T>
