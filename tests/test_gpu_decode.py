@@ -142,6 +142,28 @@ def test_decode_zero_input_full_tie():
     assert np.all(idx == np.arange(6)) and np.all(out == 0)
 
 
+@pytest.mark.parametrize("E,B", [(32, 1), (1000, 1), (1000, 3)])
+def test_decode_zero_input_full_tie_any_width(E, B):
+    # Every logit equal (zero input, zero bias): the k lowest expert indices
+    # in order, through the one-token kernel (B = 1) and the batch routing,
+    # with 4 and 16 logits per lane in the top-k.
+    L = synth.make_layer(20, hidden=256, inter=64, shared_inter=64, n_experts=E, top_k=6)
+    x = np.zeros((B, 256), np.uint16)
+    out, idx, w = run(L, x)
+    assert np.all(idx == np.arange(6)) and np.all(out == 0)
+
+
+@pytest.mark.parametrize("E,B", [(512, 1), (1000, 1), (1000, 5)])
+def test_decode_many_experts(E, B):
+    # More than 256 experts: the top-k holds 16 logits per lane, and 1000
+    # leaves the last lanes partly empty.
+    log(f"test: decode many experts E={E} B={B}")
+    L = synth.make_layer(19, hidden=256, inter=64, shared_inter=64, n_experts=E, top_k=8, bias="zipf")
+    x = synth.tokens(B, 256, stream=19 + B)
+    out, idx, w = run(L, x)
+    compare(L, x, out, idx, w, what=f"E={E} B={B}")
+
+
 @pytest.mark.parametrize("B,norm", [(8, False), (8, True), (1, True)])
 def test_decode_wide_hidden_multi_chunk_lanes(B, norm):
     # H = 4096: 128 chunks per row, two per lane; with the pre-norm, each

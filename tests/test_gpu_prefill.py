@@ -136,6 +136,17 @@ def test_prefill_matches_decode_routing_and_workspace_reuse():
                     assert set(idd.cpu().numpy()[t].tolist()) == set(a[1][t0 + t].tolist())
 
 
+def test_prefill_many_experts():
+    # 1000 experts: the top-k holds 16 logits per lane (the last lanes partly
+    # empty), and the router's column tiles end ragged.
+    log("test: prefill many experts E=1000")
+    L = synth.make_layer(21, hidden=256, inter=64, shared_inter=64, n_experts=1000, top_k=8, bias="zipf")
+    x = synth.tokens(300, 256, stream=21)
+    out, idx, w = run(L, x)
+    check_routing_properties(L, idx, w)
+    compare(L, x, out, idx, w, what="prefill E=1000")
+
+
 def test_prefill_placement_second_pass():
     # 140,000 tokens x top-4 = 560,000 (token, k) pairs: more than the 1024
     # placement blocks take in one pass of 512 pairs each, so some blocks
