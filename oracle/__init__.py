@@ -24,14 +24,16 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MOE_HOST_LIB_DIR: load the library from another directory (the CPU tests
+# point it at builds with the address and undefined-behaviour sanitizers).
+_LIB = os.path.join(os.environ.get("MOE_HOST_LIB_DIR") or _HERE, "liboracle.so")
 _lib = None
 
 
 def build():
     """Compile oracle.c with gcc into oracle/liboracle.so (always rebuilds)."""
     tmp = _LIB + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-shared", "-fPIC",
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-shared", "-fPIC", "-pthread",
                            "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _LIB)
 
@@ -63,6 +65,8 @@ def lib():
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_round.restype = ctypes.c_uint16
         L.oracle_bf16_round.argtypes = [ctypes.c_double]
+        L.oracle_bf16_round_array.restype = None
+        L.oracle_bf16_round_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.oracle_decode_nvfp4.restype = ctypes.c_int64
         L.oracle_decode_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_double, ctypes.c_void_p]
@@ -70,8 +74,20 @@ def lib():
         L.oracle_moe_tokens.argtypes = [ctypes.POINTER(_Layer), ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_moe_tokens_mt.restype = ctypes.c_int32
+        L.oracle_moe_tokens_mt.argtypes = L.oracle_moe_tokens.argtypes + [ctypes.c_int32]
         _lib = L
     return _lib
+
+
+def host_threads():
+    """Threads the oracle uses by default: the CPUs this process may run on,
+    at most 16 (a one-GPU machine's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def e2m1_value(code):
@@ -89,6 +105,14 @@ def bf16_value(bits):
 def bf16_round(v):
     """FP64 -> BF16 bits, one round-to-nearest-even."""
     return lib().oracle_bf16_round(float(v))
+
+
+def bf16_round_array(v):
+    """Vector form of bf16_round: FP64 array -> BF16 bits (same shape)."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().oracle_bf16_round_array(a.ctypes.data, a.size, out.ctypes.data)
+    return out
 
 
 def bf16_to_f64(bits):
@@ -140,11 +164,13 @@ def _as_layer(layer, keep):
     return s
 
 
-def moe_tokens(layer, x, forced_idx=None):
+def moe_tokens(layer, x, forced_idx=None, threads=1):
     """Run T tokens x [T, H] (bf16 bits) through the layer.
 
     Returns dict(out [T,H] uint16, idx [T,k] int32, w [T,k] f64, flag [T] int32,
     logits [T,E] f64, nan_tokens int).  forced_idx [T,k] replaces the selection.
+    threads > 1 spreads the tokens over host threads (one owner per token, so
+    the results are bit-identical to threads == 1); None = host_threads().
     """
     keep = []
     s = _as_layer(layer, keep)
@@ -161,6 +187,9 @@ def moe_tokens(layer, x, forced_idx=None):
     if forced_idx is not None:
         fp = np.ascontiguousarray(forced_idx, dtype=np.int32).reshape(T, k)
         keep.append(fp)
-    bad = lib().oracle_moe_tokens(ctypes.byref(s), x.ctypes.data, T, _ptr(fp), out.ctypes.data,
-                                  idx.ctypes.data, w.ctypes.data, flag.ctypes.data, logits.ctypes.data)
+    if threads is None:
+        threads = host_threads()
+    bad = lib().oracle_moe_tokens_mt(ctypes.byref(s), x.ctypes.data, T, _ptr(fp), out.ctypes.data,
+                                     idx.ctypes.data, w.ctypes.data, flag.ctypes.data, logits.ctypes.data,
+                                     int(threads))
     return dict(out=out, idx=idx[:, :k], w=w[:, :k], flag=flag, logits=logits[:, :E], nan_tokens=int(bad))

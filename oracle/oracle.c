@@ -31,6 +31,7 @@
  * power-of-two tensor scales).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -101,6 +102,11 @@ uint16_t oracle_bf16_round(double v) {
 }
 
 static inline double bf16r(double v) { return oracle_bf16_value(oracle_bf16_round(v)); }
+
+/* oracle_bf16_round over n values. */
+void oracle_bf16_round_array(const double *v, int64_t n, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_round(v[i]);
+}
 
 /* ------------------------------------------------------------------ */
 /* Weight matrices                                                     */
@@ -343,5 +349,67 @@ int32_t oracle_moe_tokens(const oracle_layer *L, const uint16_t *x, int32_t T, c
                                   logits ? logits + (int64_t)t * L->n_experts : NULL);
     if (rc) ++bad;
   }
+  return bad;
+}
+
+/* The same T tokens over n_threads host threads.  Tokens do not interact,
+ * so each one is computed start to finish by one thread (token t by thread
+ * t % n_threads) exactly as oracle_moe_tokens computes it: the results are
+ * bit-identical for any thread count.  Returns as oracle_moe_tokens. */
+typedef struct {
+  const oracle_layer *L;
+  const uint16_t *x;
+  int32_t T, first, stride;
+  const int32_t *forced;
+  uint16_t *out;
+  int32_t *idx;
+  double *w;
+  int32_t *flags;
+  double *logits;
+  int32_t bad;
+} tok_job;
+
+static void *tok_worker(void *p) {
+  tok_job *j = (tok_job *)p;
+  const int64_t H = j->L->hidden, E = j->L->n_experts;
+  const int32_t k = (E > 0) ? j->L->top_k : 0;
+  for (int32_t t = j->first; t < j->T; t += j->stride) {
+    int32_t rc = oracle_moe_token(j->L, j->x + (int64_t)t * H, j->forced ? j->forced + (int64_t)t * k : NULL,
+                                  j->out + (int64_t)t * H, j->idx ? j->idx + (int64_t)t * k : NULL,
+                                  j->w ? j->w + (int64_t)t * k : NULL, j->flags ? j->flags + t : NULL,
+                                  j->logits ? j->logits + (int64_t)t * E : NULL);
+    if (rc) ++j->bad;
+  }
+  return NULL;
+}
+
+int32_t oracle_moe_tokens_mt(const oracle_layer *L, const uint16_t *x, int32_t T, const int32_t *forced,
+                             uint16_t *out, int32_t *idx, double *w, int32_t *flags, double *logits,
+                             int32_t n_threads) {
+  tables_init(); /* before any thread reads the tables */
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > T) n_threads = T > 0 ? T : 1;
+  tok_job *jobs = (tok_job *)calloc((size_t)n_threads, sizeof(tok_job));
+  pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+  for (int32_t i = 0; i < n_threads; ++i) {
+    tok_job j = {L, x, T, i, n_threads, forced, out, idx, w, flags, logits, 0};
+    jobs[i] = j;
+  }
+  /* thread 0's share runs on the calling thread; a thread that cannot be
+   * started has its share run here too */
+  for (int32_t i = 1; i < n_threads; ++i) {
+    if (pthread_create(&th[i], NULL, tok_worker, &jobs[i]) != 0) {
+      tok_worker(&jobs[i]);
+      jobs[i].stride = 0; /* ran here: nothing to join */
+    }
+  }
+  tok_worker(&jobs[0]);
+  int32_t bad = jobs[0].bad;
+  for (int32_t i = 1; i < n_threads; ++i) {
+    if (jobs[i].stride) pthread_join(th[i], NULL);
+    bad += jobs[i].bad;
+  }
+  free(th);
+  free(jobs);
   return bad;
 }

@@ -74,6 +74,13 @@ def test_bf16_round_matches_torch_on_fp32_inputs():
     assert np.array_equal(got, ref)
 
 
+def test_bf16_round_array_equals_scalar_rounding():
+    v = np.concatenate([np.random.default_rng(4).standard_normal(3000) * 10.0 ** np.arange(-3, 3).repeat(500),
+                        [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, np.inf, -np.inf, 1e39]])
+    got = oracle.bf16_round_array(v)
+    assert np.array_equal(got, np.array([oracle.bf16_round(x) for x in v], np.uint16))
+
+
 def test_bf16_value_exact():
     for bits in (0x0000, 0x8000, 0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x4049):
         ref = bf.bf16_bits_to_f64(np.array([bits], np.uint16))[0]
@@ -363,3 +370,83 @@ def test_full_shape_one_hot_matches_dense_bruteforce():
     r = oracle.moe_tokens(L, x)
     ref, _ = bf.dense_moe(L, x)
     assert np.array_equal(r["out"], ref)
+
+
+# ---------------------------------------------------------------- near-tie flag
+#
+# The flag marks a token whose k-th and (k+1)-th sigmoid scores differ by
+# less than 1e-5 (then more than one expert set is a correct selection).
+# With x = 0 every router dot product is exactly 0, so each logit equals its
+# FP32 bias and the cases below are set by hand.  Near 0 the sigmoid has
+# slope 1/4 and no curvature, so a logit gap d gives a score gap of d/4 to
+# within 1e-13: d = 3.6e-5 -> 9.0e-6 (flagged), d = 4.4e-5 -> 1.1e-5 (not).
+# Each case fails one plausible mistake: always 1, always 0, the gap taken
+# one rank too high or too low, or the gap taken on the logits.
+
+def _flag_of(biases, k):
+    L = tiny_layer(E=len(biases), k=k)
+    L["router_b"] = np.asarray(biases, np.float32)
+    r = oracle.moe_tokens(L, np.zeros((1, 64), np.uint16))
+    return int(r["flag"][0]), r
+
+
+def test_flag_gap_just_below_threshold():
+    # ranks: 5, 5 (experts 1, 4), then 0 (expert 3) = k-th, then -3.6e-5
+    # (expert 5) = (k+1)-th: score gap 9.0e-6 < 1e-5 -> flagged.  A flag
+    # on the logits (gap 3.6e-5) would not fire.
+    f, r = _flag_of([-5, 5, -5, 0, 5, -3.6e-5, -5, -5], 3)
+    assert f == 1
+    assert set(r["idx"][0]) == {1, 3, 4}
+
+
+def test_flag_gap_just_above_threshold():
+    f, r = _flag_of([-5, 5, -5, 0, 5, -4.4e-5, -5, -5], 3)
+    assert f == 0
+    assert set(r["idx"][0]) == {1, 3, 4}
+
+
+def test_flag_near_tie_one_rank_above_boundary_is_not_flagged():
+    # ranks 2 and 3 (0.5 and 0.5 - 2e-6, score gap ~4.7e-7) nearly tie, but
+    # the k-th (k = 3: 0.5 - 2e-6) and (k+1)-th (-2) are far apart.
+    f, r = _flag_of([3, 0.5, -5, 0.5 - 2e-6, -2, -5, -5, -5], 3)
+    assert f == 0
+    assert set(r["idx"][0]) == {0, 1, 3}
+
+
+def test_flag_near_tie_one_rank_below_boundary_is_not_flagged():
+    # ranks 4 and 5 (-1 and -1 - 1e-6) nearly tie; the boundary gap
+    # sigmoid(1) - sigmoid(-1) is 0.46.
+    f, r = _flag_of([3, 2, -5, 1, -1, -1 - 1e-6, -5, -5], 3)
+    assert f == 0
+    assert set(r["idx"][0]) == {0, 1, 3}
+
+
+@pytest.mark.parametrize("base", [28.0, -22.0])
+def test_flag_saturated_scores_tie_while_logits_differ(base):
+    # Logits one apart deep in either tail: sigmoid(28) - sigmoid(27) is
+    # about 1.2e-12 and sigmoid(-22) - sigmoid(-23) about 1.8e-10, both far
+    # below 1e-5, while the logit gap is 1.  Selection still follows the
+    # logits exactly: experts 6, 2, 7 (descending).
+    b = np.full(8, base - 10.0)
+    b[[6, 2, 7, 0]] = [base + 2, base + 1, base, base - 1]
+    f, r = _flag_of(b, 3)
+    assert f == 1
+    assert list(r["idx"][0]) == [6, 2, 7]
+
+
+def test_flag_all_experts_selected_is_never_flagged():
+    # k = E: every expert is selected, so no other set exists.
+    f, r = _flag_of([0.0] * 8, 8)
+    assert f == 0
+    assert list(r["idx"][0]) == list(range(8))
+
+
+def test_threaded_oracle_is_bit_identical():
+    # Tokens are independent and each is owned by one thread.
+    L = tiny_layer(H=128, E=16, k=4, bias="zipf", norm=True, residual=True)
+    x = synth.tokens(37, 128, stream=12)
+    a = oracle.moe_tokens(L, x, threads=1)
+    for n in (2, 5, 64):
+        b = oracle.moe_tokens(L, x, threads=n)
+        for key in ("out", "idx", "w", "flag", "logits"):
+            assert np.array_equal(a[key], b[key]), (n, key)
