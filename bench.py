@@ -1,25 +1,27 @@
 """Benchmark of the small-batch W4A16 sigmoid-routed MoE decode layer on one
 MI355X.
 
-Default workload: one MoE layer (hidden 2048, 256 routed experts of
-intermediate 512 plus one shared expert, sigmoid top-6, NVFP4 weights, BF16
-activations) decoding one token.  A "step" is one token through a stack of L
-copies of the layer (distinct device copies of full 256-expert layers), each
-layer computing x + MoE(RMSNorm(x)) on the previous layer's output (the
-pre-norm residual block of the model), enqueued by one moe_decode_step call
-and replayed as one HIP graph.  The selected-weight footprint of a step
-(L x 13.4 MB) is far above the 256 MB Infinity Cache, so the weights stream
-from HBM.  Reported value: achieved HBM GB/s on the selected-weight bytes
-(router + 6 selected experts + shared expert), with microseconds per layer
-beside it; batch-8 figures (Zipf-biased router) are reported alongside.
+Default workload (the headline value): one NVFP4 MoE layer (hidden 2048,
+256 routed experts of intermediate 512 plus one shared expert, sigmoid
+top-6, BF16 activations) decoding one token.  A "step" is one token through
+a stack of L device copies of full 256-expert layers, each computing
+x + MoE(RMSNorm(x)) on the previous layer's output (the pre-norm residual
+block of the model), enqueued by one moe_decode_step call and replayed as
+one HIP graph.  The selected-weight footprint of a step (L x 13.4 MB) is far
+above the 256 MB Infinity Cache, so the weights stream from HBM.  Value:
+achieved HBM GB/s on the selected-weight bytes (router + 6 selected experts
++ shared expert), with microseconds per layer beside it.
 
-With the default workload the line also carries "prefill": one NVFP4 MoE
-layer over 8192 prompt tokens (Zipf-biased router), timed over whole
-moe_prefill_layer calls, with its rate against the BF16 matrix-core peak.
+The same line carries every configuration the layer is measured on, under
+"configs": BF16 weights at batch 1, NVFP4 at batch 1, NVFP4 at batch 8 with
+a Zipf-biased router, the model's decode step (2 dense SwiGLU layers of
+intermediate 5632 and 47 MoE layers, one HIP graph), and the 8192-token
+prefill of one layer on the matrix cores.  Also: the measured HBM read
+ceiling (a streaming-read kernel), the roofline of the batch-1 layer kernel
+and the CPU oracle's time on the host cores.
 
---workload step49: the model's decode step instead: 2 dense SwiGLU layers
-(intermediate 5632) and 47 MoE layers, independent seeded weights, RMSNorm
-before each, batch 1, one HIP graph.
+--workload step49: the model's decode step alone, with 47 independently
+generated MoE layers instead of device copies of a few.
 
 Prints one JSON line.  Inputs are synthetic and seeded (see synth/).
 """
@@ -37,18 +39,20 @@ sys.path.insert(0, ROOT)
 H, I, E, K = 2048, 512, 256, 6
 NVFP4_MATRIX = I * H * 9 // 16                      # 589,824 B
 EXPERT_BYTES = 3 * NVFP4_MATRIX                      # 1,769,472 B
+EXPERT_BYTES_BF16 = 3 * I * H * 2                    # 6,291,456 B
 ROUTER_BYTES = E * H * 2 + E * 4                     # BF16 weights + FP32 bias
 DENSE_BYTES = 3 * (5632 * H * 9 // 16) + 12          # one dense layer, NVFP4
 HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0                       # MI355X dense BF16, published
 COUNTERS = os.path.join(ROOT, "profiles", "decode_hbm_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_routed_expert_sigmoid_amd", "csrc", f)
-                  for f in ("decode.hip", "common.h")]
+                  for f in ("decode.hip", "common.h", "shapes.h")]
 
 
-def selected_bytes(distinct):
+def selected_bytes(distinct, expert_bytes=EXPERT_BYTES, scales=12):
     """Algorithmic bytes of one MoE layer call: the router, the distinct
     selected experts and the shared expert (with their FP32 tensor scales)."""
-    return ROUTER_BYTES + (distinct + 1) * (EXPERT_BYTES + 12)
+    return ROUTER_BYTES + (distinct + 1) * (expert_bytes + scales)
 
 
 def kernel_source_sha():
@@ -79,24 +83,23 @@ def prefill_flops(T, k=K):
     return 2 * T * E * H + 2 * rows * (2 * I) * H + 2 * rows * H * I
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0                       # MI355X dense BF16, published
-
-
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", choices=["layer", "step49"], default="layer")
-    p.add_argument("--layers", type=int, default=128, help="layer copies per step (cache hygiene)")
-    p.add_argument("--distinct-layers", type=int, default=4, help="independently generated layers")
+    p.add_argument("--layers", type=int, default=128, help="NVFP4 layer copies per step (cache hygiene)")
+    p.add_argument("--bf16-layers", type=int, default=24, help="BF16 layer copies per step (cache hygiene)")
+    p.add_argument("--distinct-layers", type=int, default=4, help="independently generated MoE layers")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="wall time of each oracle leg")
     p.add_argument("--prefill-tokens", type=int, default=8192)
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill leg")
+    p.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight leg")
     p.add_argument("--copy-probe", action="store_true",
-                   help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+                   help="also run a 1 GiB streaming read (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
 
 
@@ -119,6 +122,162 @@ def log(m):
     print(f"[bench] {m}", file=sys.stderr, flush=True)
 
 
+def weights_of(moe, t, bias=None):
+    w = moe.moe_layer_weights()
+    for n, _ in moe.moe_layer_weights._fields_:
+        v = t.get(n)
+        setattr(w, n, None if v is None else v.data_ptr())
+    if bias is not None:
+        w.router_b = bias.data_ptr()
+    return w
+
+
+def time_stack(args, dev, insts, descs, B, bias, label):
+    """One token batch through the stack as one HIP graph (timed over
+    args.steps replays), then the same layers as eager calls with events on
+    their kernel dispatches.  Returns timings, distinct experts per MoE
+    layer and the wait status of both workspaces."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    n_layers = len(insts)
+    wts = [weights_of(moe, t, bias if (bias is not None and descs[i].n_experts) else None)
+           for i, t in enumerate(insts)]
+    x = torch.from_numpy(synth.tokens(B, H, stream=1000).view(np.int16)).to(dev)
+    y = torch.empty_like(x)
+    ws = torch.zeros(moe.moe_decode_step_workspace_bytes(descs, B), dtype=torch.uint8, device=dev)
+    status = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    moe.moe_decode_step(descs, wts, x, B, y, ws, ws.numel())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        moe.moe_decode_step(descs, wts, x, B, y, ws, ws.numel())
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    moe.moe_decode_wait_status(ws, status[0:1])
+    nonfinite = not torch.isfinite(y.view(torch.bfloat16).float()).all().item()
+
+    # Per-layer calls (the same computation), eager, with HIP events
+    # attached to each kernel dispatch (start/stop of its execution), and
+    # the distinct experts per layer from the top-k outputs.
+    acts = [x] + [torch.empty_like(x) for _ in range(n_layers)]
+    ws1 = torch.zeros(max(moe.moe_decode_workspace_bytes(d, B) for d in descs), dtype=torch.uint8, device=dev)
+    idx = torch.zeros((n_layers, B, K), dtype=torch.int32, device=dev)
+    tw = torch.zeros((n_layers, B, K), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_layers)]
+    st_any = torch.zeros(1, dtype=torch.int32, device=dev)
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    st = np.zeros(3)
+    nst = 0
+    for _ in range(3):
+        for i in range(n_layers):
+            has_k = descs[i].n_experts > 0
+            moe.moe_decode_layer_timed(descs[i], wts[i], acts[i], B, 1, acts[i + 1], idx[i] if has_k else None,
+                                       tw[i] if has_k else None, ws1, ws1.numel(), evs[i])
+            moe.moe_decode_wait_status(ws1, status[1:2])
+            st_any.bitwise_or_(status[1:2])
+        torch.cuda.synchronize()
+        for i in range(n_layers):
+            if descs[i].n_experts == 0:
+                continue
+            r = evs[i]
+            st += [r[0].elapsed_time(r[1]), r[2].elapsed_time(r[3]), r[4].elapsed_time(r[5])]
+            nst += 1
+    stage_us = (st / max(nst, 1) * 1e3).tolist()
+    same = torch.equal(acts[-1], y)
+    moe_layers = [i for i in range(n_layers) if descs[i].n_experts > 0]
+    distinct = [len(np.unique(idx[i].cpu().numpy())) for i in moe_layers]
+    wait = int(status[0].item()) | int(st_any.item())
+    log(f"{label}: {ms_step * 1e3 / n_layers:.2f} us/layer in the graph, stage kernels {stage_us} us, "
+        f"wait status {wait}")
+    return dict(ms_step=ms_step, distinct=distinct, stage_us=stage_us, nonfinite=nonfinite,
+                step_equals_layers=bool(same), wait_status=wait)
+
+
+def stream_ceiling(dev):
+    """Best read bandwidth of the streaming-read probe over a 4 GiB buffer
+    (1024 to 8192 blocks of 256 threads)."""
+    import torch
+
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        for _ in range(2):
+            moe.moe_probe_hbm_read(buf, n, blocks, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            moe.moe_probe_hbm_read(buf, n, blocks, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, blocks)
+    del buf
+    log(f"stream read ceiling {best[0]:.0f} GB/s ({best[1]} blocks)")
+    return {"GBps": round(best[0], 1), "bytes": n, "blocks": best[1], "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
+            "kernel": "k_probe_read (moe_probe_hbm_read): 16-byte nontemporal loads, grid-stride, 4 in flight"}
+
+
+def cpu_baseline(seconds):
+    """The oracle (FP64, plain C) on one host thread and on every host thread
+    (one owner per token, so both give the same bits), each for about
+    `seconds` of wall time on whole batch-1 tokens through one full NVFP4
+    MoE layer."""
+    import oracle
+    import synth
+
+    Lh = synth.make_layer(0, wtype="nvfp4", bias="zero")
+
+    def leg(threads):
+        n, t, s = 0, 0.0, 0
+        while t < seconds and n < 200000:
+            m = max(threads, 1) * (1 if threads == 1 else 4)
+            xh = synth.tokens(m, H, stream=5000 + s)
+            c0 = time.perf_counter()
+            oracle.moe_tokens(Lh, xh, threads=threads)
+            t += time.perf_counter() - c0
+            n += m
+            s += 1
+        return n, t
+
+    n1, t1 = leg(1)
+    nt = oracle.host_threads()
+    nn, tn = leg(nt)
+    us1, usn = t1 / n1 * 1e6, tn / nn * 1e6
+    gb = selected_bytes(6)
+    log(f"oracle: {us1:.0f} us/token on 1 thread, {usn:.0f} us/token on {nt} threads")
+    return dict(value=round(gb / (usn * 1e-6) / 1e9, 4), unit="GB/s", cores=nt, kind="oracle",
+                sample=f"{nn} batch-1 tokens through one full NVFP4 MoE layer (FP64) on {nt} host threads, "
+                       f"{tn:.1f} s wall",
+                us_per_token=round(usn, 1),
+                single_thread={"value": round(gb / (us1 * 1e-6) / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "us_per_token": round(us1, 1), "sample": f"{n1} tokens, {t1:.1f} s"})
+
+
+def clone_pool(base, n):
+    return [{k: v.clone() for k, v in base[i % len(base)].t.items()} for i in range(n)]
+
+
 def run(args, dev):
     import numpy as np
     import torch
@@ -126,166 +285,136 @@ def run(args, dev):
     import synth
     import w4a16_routed_expert_sigmoid_amd as moe
 
-    names = ("router_w", "router_b", "w_gate", "w_up", "w_down", "w_scale", "sh_gate", "sh_up", "sh_down",
-             "sh_scale", "norm_gain")
-
-    def weights_of(t, bias=None):
-        w = moe.moe_layer_weights()
-        for n in names:
-            v = t.get(n)
-            setattr(w, n, None if v is None else v.data_ptr())
-        if bias is not None:
-            w.router_b = bias.data_ptr()
-        return w
-
+    configs = {}
     # The prefill leg runs first, before the decode layer copies take tens of
     # GB of device memory.
     pf = None
     if args.workload == "layer" and not args.no_prefill:
         pf = run_prefill(args, dev)
+        configs["prefill_8192_nvfp4"] = pf
         torch.cuda.empty_cache()
 
-    # ---- layers on the device
+    zipf = torch.from_numpy(synth.zipf_offset(E)).to(dev)
     t0 = time.time()
+    dense = [moe.DeviceLayer(synth.make_layer(j, inter=0, shared_inter=5632, n_experts=0, norm=True), device=dev)
+             for j in range(2)]
     if args.workload == "layer":
-        base = [moe.DeviceLayer(synth.make_layer(j, bias="zero", norm=True), device=dev)
+        base = [moe.DeviceLayer(synth.make_layer(2 + j, bias="zero", norm=True), device=dev)
                 for j in range(args.distinct_layers)]
-        insts = [{n: v.clone() for n, v in base[i % len(base)].t.items()} for i in range(args.layers)]
-        descs = [base[0].desc] * args.layers
+        pool = clone_pool(base, args.layers)
+        mdesc = base[0].desc
         del base
     else:
-        insts, descs = [], []
-        for j in range(49):
-            L = (synth.make_layer(j, inter=0, shared_inter=5632, n_experts=0, norm=True) if j < 2
-                 else synth.make_layer(j, bias="zero", norm=True))
-            d = moe.DeviceLayer(L, device=dev)
-            insts.append(d.t)
-            descs.append(d.desc)
-            del L
+        pool, mdesc = [], None
+        for j in range(47):
+            d = moe.DeviceLayer(synth.make_layer(2 + j, bias="zero", norm=True), device=dev)
+            pool.append(d.t)
+            mdesc = d.desc
     torch.cuda.synchronize()
-    nbytes = sum(v.numel() * v.element_size() for t in insts for v in t.values())
-    n_layers = len(insts)
-    log(f"{n_layers} layers, {nbytes / 1e9:.1f} GB on device, built in {time.time() - t0:.1f}s")
-    zipf = torch.from_numpy(synth.zipf_offset(E)).to(dev)
+    nbytes = sum(v.numel() * v.element_size() for t in pool for v in t.values())
+    log(f"{len(pool)} NVFP4 MoE layers, {nbytes / 1e9:.1f} GB on device, built in {time.time() - t0:.1f}s")
 
-    def run_pool(B, zipf_bias):
-        wts = [weights_of(t, zipf if (zipf_bias and descs[i].n_experts) else None) for i, t in enumerate(insts)]
-        x = torch.from_numpy(synth.tokens(B, H, stream=1000).view(np.int16)).to(dev)
-        y = torch.empty_like(x)
-        ws = torch.zeros(moe.moe_decode_step_workspace_bytes(descs, B), dtype=torch.uint8, device=dev)
-        g = torch.cuda.CUDAGraph()
-        moe.moe_decode_step(descs, wts, x, B, y, ws, ws.numel())
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            moe.moe_decode_step(descs, wts, x, B, y, ws, ws.numel())
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_step = e0.elapsed_time(e1) / args.steps
-        nonfinite = not torch.isfinite(y.view(torch.bfloat16).float()).all().item()
+    def gb_per_s(distinct, ms, expert_bytes, scales, extra):
+        b = sum(selected_bytes(d, expert_bytes, scales) for d in distinct) + extra
+        return b, b / (ms * 1e-3) / 1e9
 
-        # Per-layer calls (the same computation), eager, with HIP events
-        # attached to each kernel dispatch (start/stop of its execution), and
-        # the distinct experts per layer from the top-k outputs.
-        acts = [x] + [torch.empty_like(x) for _ in range(n_layers)]
-        ws1 = torch.zeros(max(moe.moe_decode_workspace_bytes(d, B) for d in descs), dtype=torch.uint8, device=dev)
-        idx = torch.zeros((n_layers, B, K), dtype=torch.int32, device=dev)
-        tw = torch.zeros((n_layers, B, K), dtype=torch.float32, device=dev)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_layers)]
-        for row in evs:
-            for e in row:
-                e.record()
-        torch.cuda.synchronize()
-        st = np.zeros(3)
-        nst = 0
-        for _ in range(3):
-            for i in range(n_layers):
-                moe.moe_set_stage_events(evs[i])
-                has_k = descs[i].n_experts > 0
-                moe.moe_decode_layer(descs[i], wts[i], acts[i], B, 1, acts[i + 1], idx[i] if has_k else None,
-                                     tw[i] if has_k else None, ws1, ws1.numel())
-            moe.moe_set_stage_events(None)
-            torch.cuda.synchronize()
-            for i in range(n_layers):
-                if descs[i].n_experts == 0:
-                    continue
-                r = evs[i]
-                st += [r[0].elapsed_time(r[1]), r[2].elapsed_time(r[3]), r[4].elapsed_time(r[5])]
-                nst += 1
-        stage_us = (st / max(nst, 1) * 1e3).tolist()
-        same = torch.equal(acts[-1], y)
-        moe_layers = [i for i in range(n_layers) if descs[i].n_experts > 0]
-        distinct = [len(np.unique(idx[i].cpu().numpy())) for i in moe_layers]
-        return dict(ms_step=ms_step, distinct=distinct, stage_us=stage_us, nonfinite=nonfinite,
-                    step_equals_layers=bool(same))
+    ceiling = stream_ceiling(dev)
+    ceil_gbs = ceiling["GBps"]
 
-    r1 = run_pool(1, False)
-    log(f"batch 1: {r1['ms_step'] * 1e3 / n_layers:.2f} us/layer, stages {r1['stage_us']}")
-    r8 = None
+    def summary(r, n_layers, B, expert_bytes=EXPERT_BYTES, scales=12, extra=0):
+        b, gbs = gb_per_s(r["distinct"], r["ms_step"], expert_bytes, scales, extra)
+        us = r["ms_step"] * 1e3 / n_layers
+        return {"us_per_layer": round(us, 3), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "stream_frac": round(gbs / ceil_gbs, 4), "tokens_per_s": round(B * 1e6 / us, 1),
+                "layers_per_step": n_layers, "ms_per_step": round(r["ms_step"], 4),
+                "selected_bytes_per_step": int(b),
+                "distinct_experts_mean": round(float(np.mean(r["distinct"])), 2) if r["distinct"] else None,
+                "stage_kernel_us": [round(v, 3) for v in r["stage_us"]],
+                "step_equals_layer_calls": r["step_equals_layers"], "wait_status": r["wait_status"]}
+
+    warn = []
+    if pf is not None and pf["nonfinite"]:
+        warn.append("non-finite outputs")
+    r1 = None
     if args.workload == "layer":
-        r8 = run_pool(8, True)
-        log(f"batch 8: {r8['ms_step'] * 1e3 / n_layers:.2f} us/layer, stages {r8['stage_us']}")
+        descs = [mdesc] * len(pool)
+        r1 = time_stack(args, dev, pool, descs, 1, None, "NVFP4 batch 1")
+        configs["nvfp4_b1"] = summary(r1, len(pool), 1)
+        r8 = time_stack(args, dev, pool, descs, 8, zipf, "NVFP4 batch 8 (Zipf)")
+        configs["nvfp4_b8_zipf"] = summary(r8, len(pool), 8)
+        for r in (r1, r8):
+            if r["nonfinite"]:
+                warn.append("non-finite outputs")
+    # the model's decode step: 2 dense layers, then 47 MoE layers
+    step_pool = [d.t for d in dense] + pool[:47]
+    step_descs = [d.desc for d in dense] + [mdesc] * 47
+    r49 = time_stack(args, dev, step_pool, step_descs, 1, None, "49-layer step batch 1")
+    s49 = summary(r49, 49, 1, extra=2 * DENSE_BYTES)
+    s49["tokens_per_s"] = round(1e3 / r49["ms_step"], 1)
+    s49["moe_layers_from"] = ("device copies of %d independently generated layers" % args.distinct_layers
+                              if args.workload == "layer" else "47 independently generated layers")
+    configs["step49_b1"] = s49
+    if r49["nonfinite"]:
+        warn.append("non-finite outputs")
+    r1 = r1 if r1 is not None else r49
+    del pool, step_pool
+    torch.cuda.empty_cache()
+
+    if args.workload == "layer" and not args.no_bf16:
+        t0 = time.time()
+        bbase = [moe.DeviceLayer(synth.make_layer(2 + j, wtype="bf16", bias="zero", norm=True), device=dev)
+                 for j in range(2)]
+        bpool = clone_pool(bbase, args.bf16_layers)
+        bdesc = bbase[0].desc
+        del bbase
+        torch.cuda.synchronize()
+        log(f"{len(bpool)} BF16 MoE layers built in {time.time() - t0:.1f}s")
+        rb = time_stack(args, dev, bpool, [bdesc] * len(bpool), 1, None, "BF16 batch 1")
+        configs["bf16_b1"] = summary(rb, len(bpool), 1, expert_bytes=EXPERT_BYTES_BF16, scales=0)
+        if rb["nonfinite"]:
+            warn.append("non-finite outputs")
+        del bpool
+        torch.cuda.empty_cache()
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        moe.moe_probe_hbm_read(a, a.numel(), 2048, sink)
         torch.cuda.synchronize()
-
-    n_moe = sum(1 for d in descs if d.n_experts > 0)
-    n_dense = n_layers - n_moe
-    us1 = r1["ms_step"] * 1e3 / n_layers
-    step_bytes = sum(selected_bytes(d) for d in r1["distinct"]) + n_dense * DENSE_BYTES
-    gbs1 = step_bytes / (r1["ms_step"] * 1e-3) / 1e9
 
     # batch 1: one kernel per layer (router, gate/up and down of the 6
     # selected experts and the shared expert)
     ex_us = r1["stage_us"][1]
     ex_gbs = selected_bytes(6) / (ex_us * 1e-6) / 1e9
-    traffic = measured_traffic()
     roofline = dict(bound="hbm", kernel="k_layer_b1<nvfp4> (router, then gate/up and down of 6 selected + shared "
                     "expert, 1 token)",
                     achieved=round(ex_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ex_gbs / HBM_PEAK_GBS, 4),
-                    traffic=traffic, algorithmic_bytes_per_launch=selected_bytes(6), avg_launch_us=round(ex_us, 3))
+                    traffic=measured_traffic(), algorithmic_bytes_per_launch=selected_bytes(6),
+                    avg_launch_us=round(ex_us, 3), stream_ceiling_GBps=ceil_gbs,
+                    frac_of_stream_ceiling=round(ex_gbs / ceil_gbs, 4))
 
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        Lh = synth.make_layer(0, wtype="nvfp4", bias="zero")
-        n, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and n < 2000:
-            xh = synth.tokens(1, H, stream=5000 + n)
-            c0 = time.perf_counter()
-            oracle.moe_tokens(Lh, xh)
-            t_cpu += time.perf_counter() - c0
-            n += 1
-        us_cpu = t_cpu / n * 1e6
-        cpu = dict(value=round(selected_bytes(6) / (us_cpu * 1e-6) / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                   sample=f"{n} batch-1 tokens through one full NVFP4 MoE layer, FP64, single thread",
-                   us_per_layer=round(us_cpu, 1))
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
 
+    head = configs["nvfp4_b1"] if args.workload == "layer" else configs["step49_b1"]
     if args.workload == "layer":
         workload = ("one NVFP4 MoE decode layer, batch 1 (hidden 2048, 256 experts top-6 + shared, intermediate "
                     "512); step = one token through a chained stack of %d pre-norm layer copies "
-                    "(x + MoE(RMSNorm(x))) in one HIP graph" % n_layers)
+                    "(x + MoE(RMSNorm(x))) in one HIP graph" % args.layers)
     else:
         workload = ("decode step of the MoE stack, batch 1: 2 dense SwiGLU (intermediate 5632) + 47 NVFP4 MoE "
                     "layers, RMSNorm before each, independent seeded weights, one HIP graph")
+    gbs1 = head["GBps"]
+    wait = max(c.get("wait_status", 0) for c in configs.values() if isinstance(c, dict))
+    if wait:
+        warn.append(f"a bounded wait gave up (status {wait}): outputs invalid")
     out = {
         "metric": "MoE-layer decode us + achieved HBM GB/s (selected weights), batch 1 and 8",
-        "value": round(gbs1, 1),
+        "value": gbs1,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r1["ms_step"], 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -293,29 +422,19 @@ def run(args, dev):
         "data": "synthetic",
         "config": {"workload": workload,
                    "weights": "nvfp4 (E2M1, E4M3 per 16, FP32 per tensor); activations bf16; fp32 accumulation",
-                   "layers_per_step": n_layers, "device_weight_gb": round(nbytes / 1e9, 2)},
-        "us_per_layer": round(us1, 3),
-        "tokens_per_s": round(1e3 / r1["ms_step"], 1) if args.workload == "step49" else round(1e6 / us1, 1),
-        "selected_bytes_per_step": int(step_bytes),
-        "hbm_frac": round(gbs1 / HBM_PEAK_GBS, 4),
-        "stage_us": {"layer_kernel": round(r1["stage_us"][1], 3)},
-        "step_equals_layer_calls": r1["step_equals_layers"],
+                   "layers_per_step": head["layers_per_step"]},
+        "us_per_layer": head["us_per_layer"],
+        "tokens_per_s": head["tokens_per_s"],
+        "hbm_frac": head["hbm_frac"],
+        "stream_frac": head["stream_frac"],
+        "wait_status": wait,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "stream_ceiling": ceiling,
+        "configs": configs,
     }
-    if r8 is not None:
-        us8 = r8["ms_step"] * 1e3 / n_layers
-        bytes8 = float(np.mean([selected_bytes(d) for d in r8["distinct"]]))
-        gbs8 = bytes8 / (us8 * 1e-6) / 1e9
-        out["batch8"] = {"us_per_layer": round(us8, 3), "GBps": round(gbs8, 1),
-                         "hbm_frac": round(gbs8 / HBM_PEAK_GBS, 4),
-                         "distinct_experts_mean": round(float(np.mean(r8["distinct"])), 2),
-                         "tokens_per_s": round(8e6 / us8, 1), "stage_us": [round(v, 3) for v in r8["stage_us"]],
-                         "step_equals_layer_calls": r8["step_equals_layers"]}
-    if pf is not None:
-        out["prefill"] = pf
-    if r1["nonfinite"] or (r8 is not None and r8["nonfinite"]) or (pf is not None and pf["nonfinite"]):
-        out["warning"] = "non-finite outputs"
+    if warn:
+        out["warning"] = "; ".join(sorted(set(warn)))
     return out
 
 

@@ -20,8 +20,9 @@
  *    on an error nothing is launched and the return value says why.  Faults
  *    during kernel execution surface at the caller's next synchronisation.
  *  - Activations are BF16 (raw 16-bit patterns), row-major [tokens][H].
- *    Device pointers must be 16-byte aligned.  Inputs and outputs must not
- *    alias.
+ *    Device pointers must be 16-byte aligned.  No two of the activations x
+ *    and y, the optional top-k outputs and the workspace may share a byte
+ *    (checked: INVALID_ARG).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -140,8 +141,9 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  *  batch), 256-byte aligned; no zero-fill needed (every call writes what
  *  it reads before reading it; one token with routed experts runs one
  *  kernel per layer, whose blocks hand values to each other through sync
- *  words that the call zeroes first), reusable across calls and batch
- *  sizes.
+ *  words that the call zeroes first, in a kernel of its own), reusable
+ *  across calls and batch sizes.  Its first word reports waits that gave
+ *  up (moe_decode_wait_status).
  *  Concurrent calls must not share a workspace.
  * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
  * for shapes the kernels do not tile (H/32, I/32 and Is/32 must each be at
@@ -171,9 +173,12 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
  * `stream` (capture it once into a HIP graph to replay a whole step).
  *  descs, weights: host arrays of n_layers entries (read during the call
  *  only); device pointers inside as for moe_decode_layer.
- *  x [batch][H], y [batch][H]: device BF16, must not alias.
+ *  x [batch][H], y [batch][H]: device BF16, disjoint from each other and
+ *  from ws.
  *  ws: device, ws_bytes >= moe_decode_step_workspace_bytes(descs, n_layers,
- *  batch), 256-byte aligned; no zero-fill needed, reusable across calls.
+ *  batch), 256-byte aligned; no zero-fill needed, reusable across calls;
+ *  its first word reports waits that gave up in any layer of the step
+ *  (moe_decode_wait_status).
  * Errors: as moe_decode_layer for each layer (the first failing layer's
  * status); INVALID_ARG for n_layers < 1 or differing hidden sizes. */
 moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
@@ -198,24 +203,67 @@ size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens)
  *  n_tokens), 256-byte aligned; no zero-fill needed (every call
  *  initialises what it uses).  Concurrent calls must not share it.
  * Errors: as moe_decode_layer's shape checks (the same tiled shapes);
- * INVALID_ARG for n_tokens < 1, null or misaligned pointers, x == y;
+ * INVALID_ARG for n_tokens < 1, null or misaligned pointers, overlapping
+ * buffers;
  * UNSUPPORTED for n_tokens > 4,194,304; WORKSPACE; HIP. */
 moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                              int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
                              float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_decode_layer with its kernels timed: events holds 6 hipEvent_t
+ * handles (caller-owned, created with timing enabled) that are attached to
+ * the kernel dispatches themselves, so they time the kernels' execution as
+ * a kernel trace does: [0]/[1] start and stop of the router kernel, [2]/[3]
+ * of the gate/up kernel, [4]/[5] of the down-and-combine kernel.  A batch of
+ * one token with routed experts runs the whole layer in one kernel, timed
+ * by [2]/[3]; the other pairs are then recorded back to back.  The zeroing
+ * of the sync region is not timed.  For measurement of eager calls (not
+ * under graph capture).  Errors: as moe_decode_layer; INVALID_ARG for a
+ * null events array or handle. */
+moe_status moe_decode_layer_timed(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                  int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                                  void *ws, size_t ws_bytes, void *const *events, void *stream);
+
+/* Health of the last moe_decode_layer or moe_decode_step call on a
+ * workspace.  The blocks of one kernel hand the router logits and the
+ * SwiGLU intermediate to each other through memory, each wait bounded (a
+ * wait that never ends would hang the GPU).  A wait that runs out of polls
+ * ORs a bit into a status word at the start of the workspace, which every
+ * call zeroes first: 1 = the logits, 2 = the intermediate, 4 = the logits of
+ * a batch's routing block.  A non-zero word means that call's outputs must
+ * not be used.  This enqueues a copy of the word into status_out (device
+ * int32) on `stream`, after the calls enqueued before it.
+ * Errors: INVALID_ARG for null or misaligned pointers; HIP. */
+moe_status moe_decode_wait_status(const void *ws, int32_t *status_out, void *stream);
+
+/* Host-side validation alone: what moe_decode_layer, moe_decode_step,
+ * moe_prefill_layer and moe_repack_nvfp4 (and moe_unpack_nvfp4) return for
+ * these arguments before anything would be enqueued (MOE_OK: the call
+ * would launch).  Nothing is launched, no pointer is dereferenced.  The
+ * same checks are built into a host-only library without the HIP runtime. */
+moe_status moe_check_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                  int32_t batch, const void *y, const int32_t *topk_idx, const float *topk_w,
+                                  const void *ws, size_t ws_bytes);
+moe_status moe_check_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                                 const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes);
+moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                   int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
+                                   const void *ws, size_t ws_bytes);
+moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
+
+/* Measurement: reads `bytes` (a multiple of 16) of device memory at src
+ * once, streaming, with `blocks` blocks of 256 threads (grid-stride, four
+ * 16-byte loads in flight per lane); sink: a device int32 that is written
+ * only if the folded data equals a fixed constant (it keeps the loads
+ * live).  The time of this kernel gives the practical HBM read ceiling the
+ * decode kernels are compared with, and its size scales the hardware
+ * traffic counters.  Errors: INVALID_ARG for null, misaligned or
+ * overlapping pointers, a size not a multiple of 16, blocks outside
+ * 1..65536; HIP. */
+moe_status moe_probe_hbm_read(const void *src, size_t bytes, int32_t blocks, int32_t *sink, void *stream);
+
 /* Static description of a status code. */
 const char *moe_status_string(moe_status s);
-
-/* Measurement hook.  With 6 hipEvent_t handles set, every later
- * moe_decode_layer call on this thread attaches events[0]/[1] as start and
- * stop of its router GEMV kernel, [2]/[3] of its gate/up kernel and [4]/[5]
- * of its down-and-combine kernel (the events then time the kernels'
- * execution, like a kernel trace).  For eager calls only, not under graph
- * capture.  events == NULL or n_events == 0 turns it off.  The events stay
- * owned by the caller.  Errors: INVALID_ARG for n_events other than 0 or 6
- * or a null handle. */
-moe_status moe_set_stage_events(void *const *events, int32_t n_events);
 
 /* The HIP runtime's description of the last HIP failure reported as
  * MOE_ERR_HIP on the calling thread ("no HIP error" if none). */

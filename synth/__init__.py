@@ -25,7 +25,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB = os.path.join(_HERE, "libsynth.so")
+# MOE_HOST_LIB_DIR: load the library from another directory (the CPU tests
+# point it at builds with the address and undefined-behaviour sanitizers).
+_LIB = os.path.join(os.environ.get("MOE_HOST_LIB_DIR") or _HERE, "libsynth.so")
 _lib = None
 
 WEIGHT_SEED_BASE = 1000

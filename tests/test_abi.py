@@ -1,5 +1,9 @@
 """The C-ABI library: it loads, exports every declared symbol, and rejects
-bad arguments on the host before touching the GPU (no compute calls here)."""
+bad arguments on the host before touching the GPU (no compute calls here).
+
+Every error case runs twice: through the product entry points of libmoe.so
+and through the same checks built alone into libmoe_host.so, a host-only
+library that needs no HIP runtime."""
 import ctypes
 import os
 import re
@@ -7,12 +11,96 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "w4a16_routed_expert_sigmoid_amd")
+# MOE_HOST_LIB_DIR: the host-only library from another directory (a
+# sanitizer build, see test_sanitizers.py).
+HOST_LIB = os.path.join(os.environ.get("MOE_HOST_LIB_DIR") or PKG, "libmoe_host.so")
 
-m = pytest.importorskip("w4a16_routed_expert_sigmoid_amd")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+W_BF16, W_NVFP4 = 0, 1
 
 # Aligned fake device addresses: validation never dereferences them.
 P = 0x7F0000000000
 A = lambda i: P + 0x100000 * i  # noqa: E731
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("inter", _i32), ("shared_inter", _i32), ("n_experts", _i32),
+                ("top_k", _i32), ("wtype", _i32), ("norm_eps", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("router_w", "router_b", "w_gate", "w_up", "w_down", "w_scale", "sh_gate", "sh_up",
+                                   "sh_down", "sh_scale", "norm_gain")]
+
+
+def _declare(lib):
+    D, W = ctypes.POINTER(Desc), ctypes.POINTER(Weights)
+    lib.moe_check_decode_layer.restype = _i32
+    lib.moe_check_decode_layer.argtypes = [D, W, _vp, _i32, _vp, _vp, _vp, _vp, _sz]
+    lib.moe_check_decode_step.restype = _i32
+    lib.moe_check_decode_step.argtypes = [D, W, _i32, _vp, _i32, _vp, _vp, _sz]
+    lib.moe_check_prefill_layer.restype = _i32
+    lib.moe_check_prefill_layer.argtypes = [D, W, _vp, _i32, _vp, _vp, _vp, _vp, _sz]
+    lib.moe_check_repack_nvfp4.restype = _i32
+    lib.moe_check_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64]
+    lib.moe_decode_workspace_bytes.restype = _sz
+    lib.moe_decode_workspace_bytes.argtypes = [D, _i32]
+    lib.moe_decode_step_workspace_bytes.restype = _sz
+    lib.moe_decode_step_workspace_bytes.argtypes = [D, _i32, _i32]
+    lib.moe_prefill_workspace_bytes.restype = _sz
+    lib.moe_prefill_workspace_bytes.argtypes = [D, _i32]
+    lib.moe_nvfp4_matrix_bytes.restype = _sz
+    lib.moe_nvfp4_matrix_bytes.argtypes = [_i64, _i64]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [_i32]
+    return lib
+
+
+_host = None
+
+
+def host():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_LIB):
+            pytest.skip("libmoe_host.so is not built")
+        _host = _declare(ctypes.CDLL(HOST_LIB))
+    return _host
+
+
+def hip():
+    m = pytest.importorskip("w4a16_routed_expert_sigmoid_amd")
+    return m.lib()
+
+
+LIBS = ["host", "hip"]
+
+
+def desc(**kw):
+    d = dict(hidden=2048, inter=512, shared_inter=512, n_experts=256, top_k=6, wtype=W_NVFP4, norm_eps=1e-6)
+    d.update(kw)
+    return Desc(**d)
+
+
+def weights(**kw):
+    w = Weights(router_w=A(1), router_b=A(2), w_gate=A(3), w_up=A(4), w_down=A(5), w_scale=A(6),
+                sh_gate=A(7), sh_up=A(8), sh_down=A(9), sh_scale=A(10), norm_gain=None)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def decode(which, d=None, w=None, x=A(20), batch=1, y=A(21), idx=None, tw=None, ws=A(22), ws_bytes=1 << 30):
+    d, w = d or desc(), w or weights()
+    if which == "host":
+        return host().moe_check_decode_layer(ctypes.byref(d), ctypes.byref(w), x, batch, y, idx, tw, ws, ws_bytes)
+    lib = hip()
+    ca = (ctypes.byref(Desc.from_buffer_copy(d)), ctypes.byref(Weights.from_buffer_copy(w)))
+    lib.moe_decode_layer.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    return lib.moe_decode_layer(*ca, x, batch, 0, y, idx, tw, ws, ws_bytes, None)
 
 
 def declared_functions():
@@ -22,6 +110,7 @@ def declared_functions():
 
 
 def test_exports_every_declared_symbol():
+    m = pytest.importorskip("w4a16_routed_expert_sigmoid_amd")
     names = declared_functions()
     assert "moe_decode_layer" in names and "moe_repack_nvfp4" in names and "moe_prefill_layer" in names
     lib = ctypes.CDLL(m.LIB_PATH)
@@ -30,143 +119,186 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(m.EXPORTS)
 
 
-def test_status_strings():
+def test_host_library_needs_no_hip_runtime():
+    # It links no HIP library and exports the validation part of the ABI.
+    lib = host()
+    for n in ("moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
+              "moe_check_repack_nvfp4", "moe_decode_workspace_bytes", "moe_decode_step_workspace_bytes",
+              "moe_prefill_workspace_bytes", "moe_nvfp4_matrix_bytes", "moe_status_string"):
+        assert hasattr(lib, n), n
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert HOST_LIB in maps
+    import subprocess
+    out = subprocess.run(["ldd", HOST_LIB], capture_output=True, text=True).stdout
+    assert "amdhip" not in out and "hsa-runtime" not in out, out
+
+
+@pytest.mark.parametrize("which", LIBS)
+def test_status_strings(which):
+    lib = host() if which == "host" else hip()
+    lib.moe_status_string.restype = ctypes.c_char_p
     for st in (0, -1, -2, -3, -4):
-        assert m.status_string(st) and m.status_string(st) != "unknown status"
-    assert m.status_string(7) == "unknown status"
+        s = lib.moe_status_string(st)
+        assert s and s != b"unknown status"
+    assert lib.moe_status_string(7) == b"unknown status"
 
 
 def test_matrix_bytes():
-    assert m.moe_nvfp4_matrix_bytes(512, 2048) == 589824
-    assert m.moe_nvfp4_matrix_bytes(2048, 512) == 589824
-    assert m.moe_nvfp4_matrix_bytes(5632, 2048) == 6488064
-    assert m.moe_nvfp4_matrix_bytes(7, 2048) == 0 and m.moe_nvfp4_matrix_bytes(8, 48) == 0
-
-
-def desc(**kw):
-    d = dict(hidden=2048, inter=512, shared_inter=512, n_experts=256, top_k=6, wtype=m.MOE_W_NVFP4,
-             norm_eps=1e-6)
-    d.update(kw)
-    return m.moe_layer_desc(**d)
-
-
-def weights(**kw):
-    w = m.moe_layer_weights(router_w=A(1), router_b=A(2), w_gate=A(3), w_up=A(4), w_down=A(5), w_scale=A(6),
-                            sh_gate=A(7), sh_up=A(8), sh_down=A(9), sh_scale=A(10), norm_gain=None)
-    for k, v in kw.items():
-        setattr(w, k, v)
-    return w
-
-
-def decode(d=None, w=None, x=A(20), batch=1, y=A(21), ws=A(22), ws_bytes=1 << 30):
-    d = d or desc()
-    w = w or weights()
-    return m.lib().moe_decode_layer(ctypes.byref(d), ctypes.byref(w), x, batch, 0, y, None, None, ws,
-                                    ws_bytes, None)
+    lib = host()
+    assert lib.moe_nvfp4_matrix_bytes(512, 2048) == 589824
+    assert lib.moe_nvfp4_matrix_bytes(2048, 512) == 589824
+    assert lib.moe_nvfp4_matrix_bytes(5632, 2048) == 6488064
+    assert lib.moe_nvfp4_matrix_bytes(7, 2048) == 0 and lib.moe_nvfp4_matrix_bytes(8, 48) == 0
 
 
 def test_workspace_bytes():
-    n1 = m.moe_decode_workspace_bytes(desc(), 1)
-    n8 = m.moe_decode_workspace_bytes(desc(), 8)
+    lib = host()
+    n1 = lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 1)
+    n8 = lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 8)
     assert 0 < n1 < n8
-    assert m.moe_decode_workspace_bytes(desc(), 0) == 0
-    assert m.moe_decode_workspace_bytes(desc(), 9) == 0
-    assert m.moe_decode_workspace_bytes(desc(hidden=100), 1) == 0
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 0) == 0
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 9) == 0
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc(hidden=100)), 1) == 0
 
 
+TK = A(12)  # room for top-k outputs, clear of the weights, x, y and ws
+
+
+def test_a_valid_call_passes_validation():
+    # The fake buffers are disjoint and large enough: validation says the
+    # call would launch (nothing is launched by the check).
+    assert decode("host") == OK
+    assert decode("host", batch=8, idx=TK, tw=TK + 4096) == OK
+    assert prefill("host", idx=TK, tw=TK + 4096) == OK
+
+
+@pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("kw,want", [
-    (dict(batch=0), m.MOE_ERR_INVALID_ARG),
-    (dict(batch=9), m.MOE_ERR_UNSUPPORTED),
-    (dict(x=None), m.MOE_ERR_INVALID_ARG),
-    (dict(y=None), m.MOE_ERR_INVALID_ARG),
-    (dict(ws=None), m.MOE_ERR_INVALID_ARG),
-    (dict(x=A(20) + 2), m.MOE_ERR_INVALID_ARG),
-    (dict(y=A(20)), m.MOE_ERR_INVALID_ARG),
-    (dict(ws=A(22) + 16), m.MOE_ERR_INVALID_ARG),
-    (dict(ws_bytes=100), m.MOE_ERR_WORKSPACE),
+    (dict(batch=0), INVALID),
+    (dict(batch=9), UNSUPPORTED),
+    (dict(x=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(x=A(20) + 2), INVALID),
+    (dict(y=A(20)), INVALID),                          # y == x
+    (dict(y=A(20) + 2048), INVALID),                   # y overlaps x (batch 1: 4 KiB each)
+    (dict(x=A(22) + 4096), INVALID),                   # x inside the workspace
+    (dict(y=A(22) + (1 << 29)), INVALID),              # y inside the workspace
+    (dict(idx=A(21) + 16), INVALID),                   # top-k indices overlap y
+    (dict(idx=TK, tw=TK + 8), INVALID),                # top-k weights overlap the indices
+    (dict(tw=A(22) + 256), INVALID),                   # top-k weights inside the workspace
+    (dict(idx=TK + 2), INVALID),                       # misaligned
+    (dict(ws=A(22) + 16), INVALID),
+    (dict(ws_bytes=100), WORKSPACE),
 ])
-def test_decode_call_errors(kw, want):
-    assert decode(**kw) == want
+def test_decode_call_errors(which, kw, want):
+    assert decode(which, **kw) == want
 
 
+@pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("kw,want", [
-    (dict(top_k=0), m.MOE_ERR_INVALID_ARG),
-    (dict(top_k=9), m.MOE_ERR_INVALID_ARG),
-    (dict(n_experts=4, top_k=6), m.MOE_ERR_INVALID_ARG),
-    (dict(hidden=2047), m.MOE_ERR_INVALID_ARG),
-    (dict(hidden=0), m.MOE_ERR_INVALID_ARG),
-    (dict(inter=500), m.MOE_ERR_INVALID_ARG),
-    (dict(shared_inter=40), m.MOE_ERR_INVALID_ARG),
-    (dict(wtype=7), m.MOE_ERR_INVALID_ARG),
-    (dict(n_experts=0, shared_inter=0), m.MOE_ERR_INVALID_ARG),
-    (dict(norm_eps=float("nan")), m.MOE_ERR_INVALID_ARG),
-    (dict(n_experts=-1), m.MOE_ERR_INVALID_ARG),
-    (dict(hidden=96), m.MOE_ERR_UNSUPPORTED),        # 3 chunks per row: not tiled
-    (dict(inter=32, shared_inter=32), m.MOE_ERR_UNSUPPORTED),  # one chunk per row: not tiled
-    (dict(inter=96, shared_inter=96), m.MOE_ERR_UNSUPPORTED),
-    (dict(n_experts=2048), m.MOE_ERR_UNSUPPORTED),
-    (dict(shared_inter=1024), m.MOE_ERR_UNSUPPORTED),  # shared width != routed width
-    (dict(hidden=8192), m.MOE_ERR_UNSUPPORTED),        # activations exceed the router's LDS stage at B=8
+    (dict(top_k=0), INVALID),
+    (dict(top_k=9), INVALID),
+    (dict(n_experts=4, top_k=6), INVALID),
+    (dict(hidden=2047), INVALID),
+    (dict(hidden=0), INVALID),
+    (dict(inter=500), INVALID),
+    (dict(shared_inter=40), INVALID),
+    (dict(wtype=7), INVALID),
+    (dict(n_experts=0, shared_inter=0), INVALID),
+    (dict(norm_eps=float("nan")), INVALID),
+    (dict(n_experts=-1), INVALID),
+    (dict(hidden=96), UNSUPPORTED),                    # 3 chunks per row: not tiled
+    (dict(inter=32, shared_inter=32), UNSUPPORTED),    # one chunk per row: not tiled
+    (dict(inter=96, shared_inter=96), UNSUPPORTED),
+    (dict(n_experts=2048), UNSUPPORTED),
+    (dict(shared_inter=1024), UNSUPPORTED),            # shared width != routed width
+    (dict(hidden=8192), UNSUPPORTED),                  # activations exceed the router's LDS stage at B=8
 ])
-def test_decode_desc_errors(kw, want):
+def test_decode_desc_errors(which, kw, want):
     batch = 8 if kw.get("hidden") == 8192 else 1
-    assert decode(d=desc(**kw), batch=batch) == want
+    assert decode(which, d=desc(**kw), batch=batch) == want
 
 
+@pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("kw", [
     dict(router_w=None), dict(w_gate=None), dict(w_up=None), dict(w_down=None), dict(w_scale=None),
     dict(sh_gate=None), dict(sh_scale=None), dict(w_gate=A(3) + 8), dict(router_b=A(2) + 1),
 ])
-def test_decode_weight_errors(kw):
-    assert decode(w=weights(**kw)) == m.MOE_ERR_INVALID_ARG
+def test_decode_weight_errors(which, kw):
+    assert decode(which, w=weights(**kw)) == INVALID
 
 
-def test_bf16_layer_needs_no_scales():
+@pytest.mark.parametrize("which", LIBS)
+def test_bf16_layer_needs_no_scales(which):
     # BF16 weights with null scale pointers pass validation up to the
     # workspace check (a tiny workspace keeps it off the GPU).
     w = weights(w_scale=None, sh_scale=None)
-    assert decode(d=desc(wtype=m.MOE_W_BF16), w=w, ws_bytes=1) == m.MOE_ERR_WORKSPACE
+    assert decode(which, d=desc(wtype=W_BF16), w=w, ws_bytes=1) == WORKSPACE
 
 
-def test_dense_layer_needs_no_router():
+@pytest.mark.parametrize("which", LIBS)
+def test_dense_layer_needs_no_router(which):
     w = weights(router_w=None, w_gate=None, w_up=None, w_down=None, w_scale=None)
     d = desc(n_experts=0, top_k=0, inter=0, shared_inter=5632)
-    assert decode(d=d, w=w, ws_bytes=1) == m.MOE_ERR_WORKSPACE
+    assert decode(which, d=d, w=w, ws_bytes=1) == WORKSPACE
 
 
+@pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("args,want", [
-    ((None, A(2), 8, 32, 1), m.MOE_ERR_INVALID_ARG),
-    ((A(1), None, 8, 32, 1), m.MOE_ERR_INVALID_ARG),
-    ((A(1), A(1), 8, 32, 1), m.MOE_ERR_INVALID_ARG),
-    ((A(1), A(1) + 64, 8, 32, 1), m.MOE_ERR_INVALID_ARG),   # overlapping ranges
-    ((A(1), A(2), 7, 32, 1), m.MOE_ERR_INVALID_ARG),
-    ((A(1), A(2), 8, 48, 1), m.MOE_ERR_INVALID_ARG),
-    ((A(1), A(2), 8, 32, 0), m.MOE_ERR_INVALID_ARG),
-    ((A(1) + 4, A(2), 8, 32, 1), m.MOE_ERR_INVALID_ARG),
+    ((None, A(2), 8, 32, 1), INVALID),
+    ((A(1), None, 8, 32, 1), INVALID),
+    ((A(1), A(1), 8, 32, 1), INVALID),
+    ((A(1), A(1) + 64, 8, 32, 1), INVALID),            # overlapping ranges
+    ((A(1), A(2), 7, 32, 1), INVALID),
+    ((A(1), A(2), 8, 48, 1), INVALID),
+    ((A(1), A(2), 8, 32, 0), INVALID),
+    ((A(1) + 4, A(2), 8, 32, 1), INVALID),
 ])
-def test_repack_errors(args, want):
-    lib = m.lib()
+def test_repack_errors(which, args, want):
+    if which == "host":
+        assert host().moe_check_repack_nvfp4(*args) == want
+        return
+    lib = hip()
     assert lib.moe_repack_nvfp4(*args, None, None) == want
     assert lib.moe_unpack_nvfp4(*args, None) == want
     assert lib.moe_dequant_nvfp4(args[0], args[1], *args[2:], None, None) == want
 
 
-def test_step_validation():
-    lib = m.lib()
+def step(which, dd, ww, n, x, B, y, ws, nbytes):
+    if which == "host":
+        return host().moe_check_decode_step(dd, ww, n, x, B, y, ws, nbytes)
+    lib = hip()
+    lib.moe_decode_step.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]
+    return lib.moe_decode_step(ctypes.cast(dd, _vp), ctypes.cast(ww, _vp), n, x, B, y, ws, nbytes, None)
+
+
+def step_bytes(ds, B):
+    arr = (Desc * len(ds))(*ds)
+    return host().moe_decode_step_workspace_bytes(arr, len(ds), B)
+
+
+@pytest.mark.parametrize("which", LIBS)
+def test_step_validation(which):
     d = desc()
-    dd = (m.moe_layer_desc * 2)(d, desc(n_experts=0, top_k=0, inter=0, shared_inter=5632))
-    ww = (m.moe_layer_weights * 2)(weights(), weights(router_w=None, w_gate=None, w_up=None, w_down=None))
-    assert m.moe_decode_step_workspace_bytes([d, dd[1]], 1) > m.moe_decode_workspace_bytes(d, 1)
-    assert m.moe_decode_step_workspace_bytes([d, desc(hidden=1024)], 1) == 0
-    assert lib.moe_decode_step(dd, ww, 0, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
-    assert lib.moe_decode_step(dd, ww, 2, A(20), 9, A(21), A(22), 1 << 30, None) == m.MOE_ERR_UNSUPPORTED
-    assert lib.moe_decode_step(dd, ww, 2, A(20), 1, A(20), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
-    assert lib.moe_decode_step(dd, ww, 2, A(20), 1, A(21), A(22), 64, None) == m.MOE_ERR_WORKSPACE
-    bad = (m.moe_layer_desc * 2)(d, desc(hidden=1024))
-    assert lib.moe_decode_step(bad, ww, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    dd = (Desc * 2)(d, desc(n_experts=0, top_k=0, inter=0, shared_inter=5632))
+    ww = (Weights * 2)(weights(), weights(router_w=None, w_gate=None, w_up=None, w_down=None))
+    assert step_bytes([d, dd[1]], 1) > host().moe_decode_workspace_bytes(ctypes.byref(d), 1)
+    assert step_bytes([d, desc(hidden=1024)], 1) == 0
+    G = 1 << 30
+    assert step(which, dd, ww, 0, A(20), 1, A(21), A(22), G) == INVALID
+    assert step(which, dd, ww, 2, A(20), 9, A(21), A(22), G) == UNSUPPORTED
+    assert step(which, dd, ww, 2, A(20), 1, A(20), A(22), G) == INVALID
+    assert step(which, dd, ww, 2, A(22) + 4096, 1, A(21), A(22), G) == INVALID   # x inside ws
+    assert step(which, dd, ww, 2, A(20), 1, A(21), A(22), 64) == WORKSPACE
+    bad = (Desc * 2)(d, desc(hidden=1024))
+    assert step(which, bad, ww, 2, A(20), 1, A(21), A(22), G) == INVALID
     # a bad weight in the second layer is reported before anything launches
-    ww2 = (m.moe_layer_weights * 2)(weights(), weights(sh_gate=None))
-    assert lib.moe_decode_step(dd, ww2, 2, A(20), 1, A(21), A(22), 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    ww2 = (Weights * 2)(weights(), weights(sh_gate=None))
+    assert step(which, dd, ww2, 2, A(20), 1, A(21), A(22), G) == INVALID
+    if which == "host":
+        assert step(which, dd, ww, 2, A(20), 1, A(21), A(22), G) == OK
 
 
 def test_step_workspace_covers_every_layer():
@@ -177,47 +309,55 @@ def test_step_workspace_covers_every_layer():
           desc(hidden=256, n_experts=0, top_k=0, inter=0, shared_inter=256),
           desc(hidden=256, inter=128, shared_inter=128, n_experts=64, top_k=8),
           desc(hidden=256, inter=64, shared_inter=0, n_experts=16, top_k=2)]
+    lib = host()
     for B in (1, 3, 8):
-        step = m.moe_decode_step_workspace_bytes(ds, B)
+        s = step_bytes(ds, B)
         act = 2 * ((B * 256 * 2 + 255) // 256 * 256)
         for d in ds:
-            assert step - act >= m.moe_decode_workspace_bytes(d, B) > 0
-    assert m.moe_decode_step_workspace_bytes(ds, 8) >= m.moe_decode_step_workspace_bytes(ds, 3) >= \
-        m.moe_decode_step_workspace_bytes(ds, 1)
+            assert s - act >= lib.moe_decode_workspace_bytes(ctypes.byref(d), B) > 0
+    assert step_bytes(ds, 8) >= step_bytes(ds, 3) >= step_bytes(ds, 1)
     for d in ds:
-        assert m.moe_decode_workspace_bytes(d, 8) >= m.moe_decode_workspace_bytes(d, 1)
+        assert lib.moe_decode_workspace_bytes(ctypes.byref(d), 8) >= lib.moe_decode_workspace_bytes(ctypes.byref(d), 1)
 
 
-def prefill(d=None, w=None, x=A(20), T=100, y=A(21), ws=A(22), ws_bytes=1 << 34):
-    d = d or desc()
-    w = w or weights()
-    return m.lib().moe_prefill_layer(ctypes.byref(d), ctypes.byref(w), x, T, 0, y, None, None, ws, ws_bytes,
-                                     None)
+def prefill(which, d=None, w=None, x=A(20), T=100, y=A(21), idx=None, tw=None, ws=A(22), ws_bytes=1 << 34):
+    d, w = d or desc(), w or weights()
+    if which == "host":
+        return host().moe_check_prefill_layer(ctypes.byref(d), ctypes.byref(w), x, T, y, idx, tw, ws, ws_bytes)
+    lib = hip()
+    lib.moe_prefill_layer.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    return lib.moe_prefill_layer(ctypes.byref(Desc.from_buffer_copy(d)), ctypes.byref(Weights.from_buffer_copy(w)),
+                                 x, T, 0, y, idx, tw, ws, ws_bytes, None)
 
 
 def test_prefill_workspace_bytes():
     # the expert-sorted rows dominate: (k + 1) * T rows of h [I] and y [H]
-    d = desc()
-    n = m.moe_prefill_workspace_bytes(d, 8192)
+    lib = host()
+    d = ctypes.byref(desc())
+    n = lib.moe_prefill_workspace_bytes(d, 8192)
     assert n >= 7 * 8192 * (512 + 2048) * 2
     assert n < 2 * 7 * 8192 * (512 + 2048) * 2
-    assert m.moe_prefill_workspace_bytes(d, 1) < n
-    assert m.moe_prefill_workspace_bytes(d, 0) == 0
-    assert m.moe_prefill_workspace_bytes(d, (1 << 22) + 1) == 0
-    assert m.moe_prefill_workspace_bytes(desc(hidden=100), 10) == 0
+    assert lib.moe_prefill_workspace_bytes(d, 1) < n
+    assert lib.moe_prefill_workspace_bytes(d, 0) == 0
+    assert lib.moe_prefill_workspace_bytes(d, (1 << 22) + 1) == 0
+    assert lib.moe_prefill_workspace_bytes(ctypes.byref(desc(hidden=100)), 10) == 0
 
 
+@pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("kw,want", [
-    (dict(T=0), m.MOE_ERR_INVALID_ARG),
-    (dict(T=(1 << 22) + 1), m.MOE_ERR_UNSUPPORTED),
-    (dict(x=None), m.MOE_ERR_INVALID_ARG),
-    (dict(y=A(20)), m.MOE_ERR_INVALID_ARG),
-    (dict(ws=A(22) + 64), m.MOE_ERR_INVALID_ARG),
-    (dict(x=A(20) + 8), m.MOE_ERR_INVALID_ARG),
-    (dict(ws_bytes=1000), m.MOE_ERR_WORKSPACE),
-    (dict(d=desc(top_k=9)), m.MOE_ERR_INVALID_ARG),
-    (dict(d=desc(n_experts=2048)), m.MOE_ERR_UNSUPPORTED),
-    (dict(w=weights(w_down=None)), m.MOE_ERR_INVALID_ARG),
+    (dict(T=0), INVALID),
+    (dict(T=(1 << 22) + 1), UNSUPPORTED),
+    (dict(x=None), INVALID),
+    (dict(y=A(20)), INVALID),
+    (dict(y=A(20) + 4096), INVALID),                   # y overlaps x (100 tokens: 400 KiB)
+    (dict(x=A(22) + (1 << 20)), INVALID),              # x inside the workspace
+    (dict(idx=TK, tw=TK + 1024), INVALID),             # weights overlap the indices (2400 B)
+    (dict(ws=A(22) + 64), INVALID),
+    (dict(x=A(20) + 8), INVALID),
+    (dict(ws_bytes=1000), WORKSPACE),
+    (dict(d=desc(top_k=9)), INVALID),
+    (dict(d=desc(n_experts=2048)), UNSUPPORTED),
+    (dict(w=weights(w_down=None)), INVALID),
 ])
-def test_prefill_call_errors(kw, want):
-    assert prefill(**kw) == want
+def test_prefill_call_errors(which, kw, want):
+    assert prefill(which, **kw) == want

@@ -20,6 +20,7 @@ def run(layer, x, dev=None, ws=None):
     dev = dev or moe.DeviceLayer(layer)
     y, idx, w = dev.decode(to_dev_bits(x), ws=ws)
     torch.cuda.synchronize()
+    assert dev.wait_status() == 0
     k = layer["top_k"] if layer["n_experts"] else 0
     return from_dev_bits(y), idx.cpu().numpy()[:, :k], w.cpu().numpy()[:, :k]
 

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_util import log, to_dev_bits
+from tests.gpu_util import log, to_dev_bits, wait_status
 
 pytestmark = pytest.mark.gpu
 
@@ -56,8 +56,11 @@ def test_graph_replays_match_eager_calls(B):
         x.copy_(xi)
         g.replay()
         torch.cuda.synchronize()
+        assert wait_status(ws) == 0, f"replay {i}"
         ref = eager(xi, ws_eager)
+        assert wait_status(ws_eager) == 0
         assert torch.equal(y, ref), f"replay {i}"
         assert np.all(np.isfinite(y.view(torch.bfloat16).float().cpu().numpy()))
         # eager work on the graph's own workspace between the replays
         assert torch.equal(eager(xi, ws), ref), f"eager on the graph workspace {i}"
+        assert wait_status(ws) == 0

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import bf16_f64, compare, from_dev_bits, log, to_dev_bits
+from tests.gpu_util import bf16_f64, compare, from_dev_bits, log, to_dev_bits, wait_status
 
 pytestmark = pytest.mark.gpu
 
@@ -60,25 +60,29 @@ def test_step_matches_layers_and_oracle(kind, B):
     y = torch.empty_like(xt)
     ws = torch.zeros(moe.moe_decode_step_workspace_bytes(descs, B), dtype=torch.uint8, device="cuda")
     moe.moe_decode_step(descs, ws_, xt, B, y, ws, ws.numel())
+    assert wait_status(ws) == 0
     # a second call on the same workspace (which now holds the first call's
     # sync words) gives the same bits
     y2 = torch.empty_like(xt)
     moe.moe_decode_step(descs, ws_, xt, B, y2, ws, ws.numel())
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+    assert wait_status(ws) == 0
     # the same layers one call at a time
     cur = xt
     for d in devs:
         cur, _, _ = d.decode(cur)
-    torch.cuda.synchronize()
+        assert d.wait_status() == 0
     step_out = from_dev_bits(y)
     assert np.array_equal(step_out, from_dev_bits(cur))
     # per layer against the oracle, each fed the oracle's own input
     xo = x
     for i, (L, d) in enumerate(zip(layers, devs)):
         o, idx, w = d.decode(to_dev_bits(xo), residual=0)
+        assert d.wait_status() == 0
         yr, _, _ = d.decode(to_dev_bits(xo), residual=1)
         torch.cuda.synchronize()
+        assert d.wait_status() == 0
         k = L["top_k"] if L["n_experts"] else 0
         o = from_dev_bits(o)
         compare(dict(L, residual=0), xo, o, idx.cpu().numpy()[:, :k], w.cpu().numpy()[:, :k],

@@ -56,8 +56,6 @@ _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [_i32]
 _lib.moe_last_error_detail.restype = ctypes.c_char_p
 _lib.moe_last_error_detail.argtypes = []
-_lib.moe_set_stage_events.restype = _i32
-_lib.moe_set_stage_events.argtypes = [ctypes.POINTER(_vp), _i32]
 _lib.moe_nvfp4_matrix_bytes.restype = _sz
 _lib.moe_nvfp4_matrix_bytes.argtypes = [_i64, _i64]
 _lib.moe_repack_nvfp4.restype = _i32
@@ -71,6 +69,10 @@ _lib.moe_decode_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32
 _lib.moe_decode_layer.restype = _i32
 _lib.moe_decode_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
                                   _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_decode_layer_timed.restype = _i32
+_lib.moe_decode_layer_timed.argtypes = _lib.moe_decode_layer.argtypes[:-1] + [ctypes.POINTER(_vp), _vp]
+_lib.moe_decode_wait_status.restype = _i32
+_lib.moe_decode_wait_status.argtypes = [_vp, _vp, _vp]
 _lib.moe_decode_step_workspace_bytes.restype = _sz
 _lib.moe_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32, _i32]
 _lib.moe_decode_step.restype = _i32
@@ -82,11 +84,25 @@ _lib.moe_prefill_layer.restype = _i32
 _lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
                                    _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 
-EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_set_stage_events", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4", "moe_unpack_nvfp4",
-           "moe_dequant_nvfp4",
-           "moe_decode_workspace_bytes", "moe_decode_layer", "moe_decode_step_workspace_bytes",
-           "moe_decode_step", "moe_prefill_workspace_bytes",
-           "moe_prefill_layer")
+_lib.moe_probe_hbm_read.restype = _i32
+_lib.moe_probe_hbm_read.argtypes = [_vp, _sz, _i32, _vp, _vp]
+_lib.moe_check_decode_layer.restype = _i32
+_lib.moe_check_decode_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
+                                        _i32, _vp, _vp, _vp, _vp, _sz]
+_lib.moe_check_decode_step.restype = _i32
+_lib.moe_check_decode_step.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _i32,
+                                       _vp, _i32, _vp, _vp, _sz]
+_lib.moe_check_prefill_layer.restype = _i32
+_lib.moe_check_prefill_layer.argtypes = _lib.moe_check_decode_layer.argtypes
+_lib.moe_check_repack_nvfp4.restype = _i32
+_lib.moe_check_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64]
+
+EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4",
+           "moe_unpack_nvfp4", "moe_dequant_nvfp4",
+           "moe_decode_workspace_bytes", "moe_decode_layer", "moe_decode_layer_timed", "moe_decode_wait_status",
+           "moe_decode_step_workspace_bytes", "moe_decode_step", "moe_prefill_workspace_bytes",
+           "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
+           "moe_check_repack_nvfp4", "moe_probe_hbm_read")
 
 
 def lib():
@@ -127,15 +143,6 @@ def moe_last_error_detail():
     return _lib.moe_last_error_detail().decode()
 
 
-def moe_set_stage_events(events):
-    """events: None, or 6 torch.cuda.Event (created with enable_timing=True)."""
-    if not events:
-        _check(_lib.moe_set_stage_events(None, 0), "moe_set_stage_events")
-        return
-    arr = (_vp * len(events))(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
-    _check(_lib.moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
-
-
 def moe_nvfp4_matrix_bytes(rows, cols):
     return _lib.moe_nvfp4_matrix_bytes(rows, cols)
 
@@ -164,6 +171,26 @@ def moe_decode_layer(desc, weights, x, batch, residual, y, topk_idx=None, topk_w
     _check(_lib.moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, int(residual),
                                  _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_decode_layer")
+
+
+def moe_decode_layer_timed(desc, weights, x, batch, residual, y, topk_idx, topk_w, ws, ws_bytes, events,
+                           stream=None):
+    """events: 6 torch.cuda.Event (enable_timing=True) attached to the
+    layer's kernel dispatches: router, gate/up and down (start, stop)."""
+    arr = (_vp * 6)(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in events])
+    _check(_lib.moe_decode_layer_timed(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, int(residual),
+                                       _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, arr,
+                                       _stream(stream)), "moe_decode_layer_timed")
+
+
+def moe_decode_wait_status(ws, status_out, stream=None):
+    """Enqueue a copy of the workspace's wait status word into status_out
+    (a device int32 tensor)."""
+    _check(_lib.moe_decode_wait_status(_ptr(ws), _ptr(status_out), _stream(stream)), "moe_decode_wait_status")
+
+
+def moe_probe_hbm_read(src, nbytes, blocks, sink, stream=None):
+    _check(_lib.moe_probe_hbm_read(_ptr(src), nbytes, blocks, _ptr(sink), _stream(stream)), "moe_probe_hbm_read")
 
 
 def _arrays(descs, weights):

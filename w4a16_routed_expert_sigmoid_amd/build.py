@@ -1,4 +1,6 @@
-"""Compile the HIP library (libmoe.so) for gfx950 with hipcc, in-tree."""
+"""Compile the HIP library (libmoe.so) for gfx950 with hipcc, in-tree, and
+the host-only validation library (libmoe_host.so: the argument checks and
+workspace layouts of the C ABI, no HIP runtime) with g++."""
 import os
 import shutil
 import subprocess
@@ -8,7 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "repack.hip"]
+HOST_LIB = os.path.join(HERE, "libmoe_host.so")
+SOURCES = ["api.cpp", "validate.cpp", "decode.hip", "prefill.hip", "repack.hip", "probe.hip"]
+HOST_SOURCES = ["validate.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -50,5 +54,17 @@ def build(verbose=False):
     return LIB
 
 
+def build_host(out=HOST_LIB, extra_flags=()):
+    """The validation unit alone, with g++ (no HIP headers or runtime).
+    extra_flags: e.g. sanitizer options for a host-only test build."""
+    tmp = out + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-Wall", "-Wextra", *extra_flags,
+           "-I", os.path.join(ROOT, "include")] + [os.path.join(CSRC, s) for s in HOST_SOURCES] + ["-o", tmp]
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_host()

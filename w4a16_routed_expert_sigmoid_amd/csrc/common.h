@@ -19,6 +19,8 @@
 
 #include <type_traits>
 
+#include "shapes.h"
+
 namespace moe {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -26,31 +28,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
-constexpr int kMaxBatch = 8;   // decode path: up to eight tokens
-constexpr int kMaxTopK = 8;
-constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
-constexpr int kMaxExperts = 1024;
-
-__host__ __device__ inline int64_t nvfp4_nibble_bytes(int64_t n, int64_t k) { return n * k / 2; }
-__host__ __device__ inline int64_t nvfp4_matrix_bytes(int64_t n, int64_t k) { return n * k / 2 + n * k / 16; }
-
-// Lanes that share one row: all 64 when a row has >= 64 chunks (each lane
-// then walks chunks lane, lane+64, ...), else the chunk count, which must
-// be a power of two.
-__host__ __device__ inline int lanes_per_row(int k) {
-  int c = k / 32;
-  return c >= kWave ? kWave : c;
-}
-
-// A reduction dimension the GEMV kernels tile: at least two 32-element
-// chunks, and either a power of two of them or at least one per lane.
-__host__ inline bool k_tileable(int64_t k) {
-  if (k < 64 || k % 32) return false;
-  int64_t c = k / 32;
-  return c >= kWave || (c & (c - 1)) == 0;
-}
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -289,14 +266,11 @@ struct DecodeWs {
   uint64_t *sync_h;       // [(k + 1) * Imax / 2] h words (two BF16 values each)
   float *xcd_l;           // [kXcdSlots][stage_l] per-XCD copy of the logits
   uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
+  uint32_t *status;       // OR of kStatus* bits: bounded waits that gave up (zeroed per call)
   int64_t stage_l;        // E rounded up to 64
   int64_t stage_elems;    // (one-token max_routed + 1) * Imax, rounded up to 128
   size_t bytes;
 };
-
-// Lines of the sync region: per XCD, the logit ticket and flag, then the h
-// ticket and flag.
-enum { kLineLTicket = 0, kLineLFlag = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
 
 // Arguments of the decode kernels (passed by value).
 struct DecodeArgs {
@@ -315,11 +289,6 @@ struct DecodeArgs {
   int32_t *out_idx;
   float *out_w;
   DecodeWs ws;
-};
-
-// Prefill: one GEMM tile of up to 128 rows of one expert's segment.
-struct PfTile {
-  int p0, cnt, e;  // first row, rows (<= 128), expert (-1: the shared expert)
 };
 
 // Arguments of the prefill kernels (passed by value).  Row space of the
@@ -350,17 +319,11 @@ struct PrefillArgs {
   uint16_t *y_rows;       // [P + T][H] expert outputs, BF16
 };
 
-// Rows one 128-row tile holds and an upper bound of the tiles of a call.
-constexpr int kPrefillTileRows = 128;
-__host__ __device__ inline int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
-  const int64_t P = T * k;
-  const int64_t routed = E > 0 ? (P + kPrefillTileRows - 1) / kPrefillTileRows + (E < P ? E : P) : 0;
-  return routed + (shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
-}
-
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+// Zeroes words [0, words) of a decode workspace (its status word and sync
+// region) before a call's kernels run.
 hipError_t launch_sync_clear(uint32_t *region, int64_t words, hipStream_t stream);
 hipError_t launch_repack(const void *src, void *dst, int64_t rows, int64_t cols, int64_t n_mats,
                          int32_t *nan_count, hipStream_t stream);
@@ -368,5 +331,6 @@ hipError_t launch_unpack(const void *src, void *dst, int64_t rows, int64_t cols,
                          hipStream_t stream);
 hipError_t launch_dequant(const void *src, float *dst, int64_t rows, int64_t cols, int64_t n_mats,
                           const float *tensor_scale, hipStream_t stream);
+hipError_t launch_probe_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *sink, hipStream_t stream);
 
 }  // namespace moe

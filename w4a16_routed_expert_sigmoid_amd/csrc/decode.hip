@@ -1083,8 +1083,15 @@ __global__ __launch_bounds__(DW *kWave) void k_down(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 // Poll rounds (each ends in a short sleep) before a wait on another block
-// of the same kernel gives up; reached only if that block never wrote.
+// of the same kernel gives up; reached only if that block never wrote.  A
+// wait that gives up sets its bit in the workspace's status word (zeroed
+// by every call), so the caller can tell such a call's outputs from good
+// ones.
 constexpr int kWaitSpin = 1 << 20;
+
+__device__ __forceinline__ void report_giveup(const DecodeArgs &a, uint32_t bit) {
+  __hip_atomic_fetch_or(a.ws.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 constexpr int kDnHalf = 2 * kWave;  // threads per 4-row half of a down block
 
@@ -1117,22 +1124,26 @@ __device__ __forceinline__ void raise_flag(const DecodeArgs &a, int which, int x
 // another block of the same XCD is seen about 0.4 us after the store.  The
 // stage is then read once, after the flag, so this CU's cache holds no
 // earlier copy of it (the kernel starts with the CU caches invalidated).
-__device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xcc) {
+__device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xcc, uint32_t giveup_bit) {
   if (threadIdx.x == 0) {
     const volatile uint32_t *flag = sync_line(a, which, xcc);
-    for (int it = 0; it < kWaitSpin; ++it) {
-      if (*flag == a.tag) break;
-      __builtin_amdgcn_s_sleep(1);
+    bool seen = false;
+    for (int it = 0; it < kWaitSpin && !seen; ++it) {
+      seen = *flag == a.tag;
+      if (!seen) __builtin_amdgcn_s_sleep(1);
     }
+    if (!seen) report_giveup(a, giveup_bit);
   }
 }
 
 // Leader: the values of n tagged words into dst[0..n), each polled until
 // it carries the tag; a thread keeps kCopy words in flight and re-reads
-// all its missing ones in each round.
-__device__ inline void copy_tagged(const uint64_t *src, uint32_t *dst, int n, uint32_t tag) {
+// all its missing ones in each round.  False if some word of this thread
+// never arrived.
+__device__ inline bool copy_tagged(const uint64_t *src, uint32_t *dst, int n, uint32_t tag) {
   constexpr int kCopy = 8;
   const int tid = threadIdx.x, nt = blockDim.x;
+  bool all = true;
   for (int i0 = 0; i0 < n; i0 += kCopy * nt) {
     uint64_t v[kCopy];
 #pragma unroll
@@ -1140,8 +1151,9 @@ __device__ inline void copy_tagged(const uint64_t *src, uint32_t *dst, int n, ui
       const int i = i0 + k * nt + tid;
       v[k] = i < n ? load_tagged(src + i) : (uint64_t)tag << 32;
     }
+    bool done = false;
     for (int it = 0; it < kWaitSpin; ++it) {
-      bool done = true;
+      done = true;
 #pragma unroll
       for (int k = 0; k < kCopy; ++k) done = done && (uint32_t)(v[k] >> 32) == tag;
       if (done) break;
@@ -1150,12 +1162,14 @@ __device__ inline void copy_tagged(const uint64_t *src, uint32_t *dst, int n, ui
       for (int k = 0; k < kCopy; ++k)
         if ((uint32_t)(v[k] >> 32) != tag) v[k] = load_tagged(src + i0 + k * nt + tid);
     }
+    all = all && done;
 #pragma unroll
     for (int k = 0; k < kCopy; ++k) {
       const int i = i0 + k * nt + tid;
       if (i < n) dst[i] = (uint32_t)v[k];
     }
   }
+  return all;
 }
 
 // The last block of k_router with `route` (batches of 2..8 tokens, one
@@ -1167,7 +1181,8 @@ __device__ void route_block(const DecodeArgs &a, uint4 *lds) {
   __shared__ Routing R;
   __shared__ uint32_t s_mark[kMaxExperts];
   float *s_l = reinterpret_cast<float *>(lds);
-  copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_l), a.B * a.E, a.tag);
+  if (!copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(s_l), a.B * a.E, a.tag))
+    report_giveup(a, kStatusRouteWait);
   __syncthreads();
   build_routing(a, s_l, R, s_mark, (int)(blockDim.x / kWave));
   publish_routing(a, R);
@@ -1182,10 +1197,11 @@ __device__ inline void take_routing(const DecodeArgs &a, int xcc, Routing &R, ui
   __syncthreads();
   float *stage = a.ws.xcd_l + (int64_t)xcc * a.ws.stage_l;
   if (s_lead) {
-    copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(stage), a.E, a.tag);
+    if (!copy_tagged(a.ws.sync_l, reinterpret_cast<uint32_t *>(stage), a.E, a.tag))
+      report_giveup(a, kStatusLogitWait);
     raise_flag(a, kLineLFlag, xcc);
   } else {
-    wait_flag(a, kLineLFlag, xcc);
+    wait_flag(a, kLineLFlag, xcc, kStatusLogitWait);
   }
   __syncthreads();
   build_routing(a, stage, R, s_mark, kGateupWaves);
@@ -1348,10 +1364,11 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int
       // expert slot k (= max_routed), so the entries' h words are the first
       // n_entries * Imax / 2 words.
       if (lead) {
-        copy_tagged(a.ws.sync_h, reinterpret_cast<uint32_t *>(stage), n_entries * (Imax / 2), a.tag);
+        if (!copy_tagged(a.ws.sync_h, reinterpret_cast<uint32_t *>(stage), n_entries * (Imax / 2), a.tag))
+          report_giveup(a, kStatusHWait);
         raise_flag(a, kLineHFlag, xcc);
       } else {
-        wait_flag(a, kLineHFlag, xcc);
+        wait_flag(a, kLineHFlag, xcc, kStatusHWait);
       }
     }
     __syncthreads();

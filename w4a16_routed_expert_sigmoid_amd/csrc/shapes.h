@@ -1,0 +1,59 @@
+// Shape arithmetic of the library, in plain C++ with no HIP dependency:
+// sizes of the NVFP4 runtime layout, the tiling limits the kernels
+// accept, and the constants the workspace layouts are built from.  The
+// kernels include it through common.h; the host-only validation unit
+// (validate.cpp) includes it directly, so that unit also builds without
+// the HIP runtime.  Every function is constexpr, which makes it callable
+// from device code as well.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxBatch = 8;   // decode path: up to eight tokens
+constexpr int kMaxTopK = 8;
+constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
+constexpr int kMaxExperts = 1024;
+constexpr int kPrefillTileRows = 128;       // rows of one prefill GEMM tile
+constexpr int32_t kMaxPrefillTokens = 1 << 22;
+constexpr size_t kWsAlign = 256;            // workspace pieces start on 256-byte lines
+
+// Lines of the decode sync region: per XCD, the logit ticket and flag,
+// then the h ticket and flag (256 bytes each, word 0 used).
+enum { kLineLTicket = 0, kLineLFlag = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
+
+// Bits of the decode status word: a bounded wait on another block of the
+// same kernel ran out of polls (the values it waited for never arrived).
+enum { kStatusLogitWait = 1, kStatusHWait = 2, kStatusRouteWait = 4 };
+
+constexpr int64_t nvfp4_nibble_bytes(int64_t n, int64_t k) { return n * k / 2; }
+constexpr int64_t nvfp4_matrix_bytes(int64_t n, int64_t k) { return n * k / 2 + n * k / 16; }
+
+// Lanes that share one row: all 64 when a row has >= 64 chunks (each lane
+// then walks chunks lane, lane+64, ...), else the chunk count, which must
+// be a power of two.
+constexpr int lanes_per_row(int k) { return k / 32 >= kWave ? kWave : k / 32; }
+
+// A reduction dimension the GEMV kernels tile: at least two 32-element
+// chunks, and either a power of two of them or at least one per lane.
+constexpr bool k_tileable(int64_t k) {
+  return k >= 64 && k % 32 == 0 && (k / 32 >= kWave || ((k / 32) & (k / 32 - 1)) == 0);
+}
+
+// Prefill: one GEMM tile of up to 128 rows of one expert's segment.
+struct PfTile {
+  int p0, cnt, e;  // first row, rows (<= 128), expert (-1: the shared expert)
+};
+
+// Upper bound of the 128-row tiles of a prefill call: the routed rows in
+// whole tiles plus one ragged tile per non-empty expert, and the shared
+// expert's rows.
+constexpr int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
+  return (E > 0 ? (T * k + kPrefillTileRows - 1) / kPrefillTileRows + (E < T * k ? E : T * k) : 0) +
+         (shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
+}
+
+}  // namespace moe

@@ -1,0 +1,341 @@
+// Host-side validation and workspace layouts of the C ABI (no HIP).  Every
+// check runs before anything is enqueued, so each error path is exercised
+// on the CPU, with or without the HIP runtime.
+#include "validate.h"
+
+#include <math.h>
+#include <string.h>
+
+namespace moe {
+
+namespace {
+
+inline size_t up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kStatusLine = 256;  // the status word's own line, at byte 0
+constexpr size_t kSyncLineBytes = (size_t)kSyncLines * kXcdSlots * 256;
+
+inline size_t imax_of(const moe_layer_desc &d) {
+  return (size_t)(d.inter > d.shared_inter ? d.inter : d.shared_inter);
+}
+
+// Caller buffers [p, p + n); a null pointer or n == 0 takes no room.
+struct Range {
+  const void *p;
+  size_t n;
+};
+
+inline bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t s = (uintptr_t)a.p, t = (uintptr_t)b.p;
+  return s < t + b.n && t < s + a.n;
+}
+
+// No two of the n ranges overlap.
+bool disjoint(const Range *r, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlap(r[i], r[j])) return false;
+  return true;
+}
+
+}  // namespace
+
+int max_routed_of(const moe_layer_desc &d, int B) {
+  if (d.n_experts <= 0) return 0;
+  const int m = B * d.top_k;
+  return m < d.n_experts ? m : d.n_experts;
+}
+
+// Bytes of the sync region of a layer at batch B: the ticket and flag
+// lines, then the tagged logit words ([B][E]) and the one-token h words.
+// Zero for a layer without routed experts.
+size_t sync_bytes_of(const moe_layer_desc &d, int B) {
+  if (d.n_experts <= 0) return 0;
+  const size_t words_h = (size_t)(max_routed_of(d, 1) + 1) * imax_of(d) / 2;
+  return kSyncLineBytes + up((size_t)B * d.n_experts * 8) + up(words_h * 8);
+}
+
+DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap) {
+  DecodeLayout L;
+  const size_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = d.n_experts > 0 ? d.top_k : 0;
+  const size_t Imax = imax_of(d);
+  const size_t R = max_routed_of(d, B);
+  const size_t own = sync_bytes_of(d, B);
+  const size_t sync = own > sync_cap ? own : sync_cap;
+  L.sync_lines = kStatusLine;
+  L.sync_l = kStatusLine + kSyncLineBytes;
+  L.sync_h = L.sync_l + up(B * E * 8);
+  L.clear_bytes = kStatusLine + sync;
+  size_t o = L.clear_bytes;
+  L.logits = o; o += up(B * E * 4);
+  L.xn = o; o += up(B * H * 2);
+  L.n_routed = o; o += up(4);
+  L.entry_expert = o; o += up(R * 4);
+  L.entry_mask = o; o += up(R * 4);
+  L.entry_w = o; o += up(R * kMaxBatch * 4);
+  L.topk_idx = o; o += up(B * k * 4);
+  L.topk_w = o; o += up(B * k * 4);
+  L.h = o; o += up((R + 1) * B * Imax * 2);
+  // one-token stages (also reserved at larger batches, so that a workspace
+  // sized for batch b serves every smaller batch)
+  const size_t R1 = max_routed_of(d, 1);
+  L.stage_l = (int64_t)((E + 63) / 64 * 64);
+  L.stage_elems = (int64_t)(((R1 + 1) * Imax + 127) / 128 * 128);
+  L.xcd_l = o; o += up(kXcdSlots * (size_t)L.stage_l * 4);
+  L.xcd_h = o; o += up(kXcdSlots * (size_t)L.stage_elems * 2);
+  L.bytes = o;
+  return L;
+}
+
+bool step_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, StepLayout &L) {
+  if (!descs || n_layers < 1 || B < 1 || B > kMaxBatch) return false;
+  for (int32_t i = 0; i < n_layers; ++i)
+    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return false;
+  L.sync_cap = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const size_t b = sync_bytes_of(descs[i], B);
+    L.sync_cap = b > L.sync_cap ? b : L.sync_cap;
+  }
+  L.layer_bytes = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const size_t b = decode_layout(descs[i], B, L.sync_cap).bytes;
+    L.layer_bytes = b > L.layer_bytes ? b : L.layer_bytes;
+  }
+  const size_t act = up((size_t)B * descs[0].hidden * 2);
+  L.act0 = L.layer_bytes;
+  L.act1 = L.act0 + act;
+  L.bytes = L.act1 + act;
+  return true;
+}
+
+PfLayout prefill_layout(const moe_layer_desc &d, int64_t T) {
+  PfLayout L;
+  const int64_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = E > 0 ? d.top_k : 0;
+  const int64_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
+  const int64_t P = T * k, rows = P + (d.shared_inter > 0 ? T : 0);
+  L.max_tiles = prefill_max_tiles(T, k, E, d.shared_inter > 0);
+  size_t o = 0;
+  L.xn = o; o += up(T * H * 2);
+  L.logits = o; o += up(T * E * 4);
+  L.topk_idx = o; o += up(P * 4);
+  L.topk_w = o; o += up(P * 4);
+  L.counts = o; o += up((E + 1) * 4);
+  L.offsets = o; o += up((E + 1) * 4);
+  L.cursors = o; o += up((E + 1) * 4);
+  L.n_tiles = o; o += up(4);
+  L.tiles = o; o += up(L.max_tiles * sizeof(PfTile));
+  L.sorted_tok = o; o += up(P * 4);
+  L.pair_pos = o; o += up(P * 4);
+  L.h = o; o += up(rows * Imax * 2);
+  L.y = o; o += up(rows * H * 2);
+  L.bytes = o;
+  return L;
+}
+
+moe_status check_desc(const moe_layer_desc *d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->hidden % 32) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts < 0 || d->inter < 0 || d->shared_inter < 0) return MOE_ERR_INVALID_ARG;
+  if (d->wtype != MOE_W_BF16 && d->wtype != MOE_W_NVFP4) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts == 0 && d->shared_inter == 0) return MOE_ERR_INVALID_ARG;
+  if (d->n_experts > 0) {
+    if (d->inter <= 0 || d->inter % 32) return MOE_ERR_INVALID_ARG;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->shared_inter % 32) return MOE_ERR_INVALID_ARG;
+  if (!(d->norm_eps >= 0.0f) || isinf(d->norm_eps)) return MOE_ERR_INVALID_ARG;
+  // Shapes the kernels tile.
+  if (d->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!k_tileable(d->hidden)) return MOE_ERR_UNSUPPORTED;
+  if (d->n_experts > 0 && !k_tileable(d->inter)) return MOE_ERR_UNSUPPORTED;
+  if (d->shared_inter > 0 && !k_tileable(d->shared_inter)) return MOE_ERR_UNSUPPORTED;
+  if (d->n_experts > 0 && d->shared_inter > 0 && d->shared_inter != d->inter) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_layer_desc *d, const moe_layer_weights *w) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  const bool fp4 = d->wtype == MOE_W_NVFP4;
+  if (d->n_experts > 0) {
+    if (!w->router_w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+    if (fp4 && !w->w_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->router_w, 16) || !aligned(w->w_gate, 16) || !aligned(w->w_up, 16) ||
+        !aligned(w->w_down, 16))
+      return MOE_ERR_INVALID_ARG;
+    if ((w->router_b && !aligned(w->router_b, 4)) || (w->w_scale && !aligned(w->w_scale, 4)))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (d->shared_inter > 0) {
+    if (!w->sh_gate || !w->sh_up || !w->sh_down) return MOE_ERR_INVALID_ARG;
+    if (fp4 && !w->sh_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->sh_gate, 16) || !aligned(w->sh_up, 16) || !aligned(w->sh_down, 16))
+      return MOE_ERR_INVALID_ARG;
+    if (w->sh_scale && !aligned(w->sh_scale, 4)) return MOE_ERR_INVALID_ARG;
+  }
+  if (w->norm_gain && !aligned(w->norm_gain, 2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status check_decode_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                             int32_t batch, const void *y, const int32_t *topk_idx, const float *topk_w,
+                             const void *ws, size_t ws_bytes, size_t sync_cap, DecodeLayout *L) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  // The routing kernels stage the batch's activations through 64 KiB.
+  if ((size_t)batch * desc->hidden * 2 > 65536) return MOE_ERR_UNSUPPORTED;
+  st = check_weights(desc, w);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID_ARG;
+  // The kernels read x while other blocks write y, the top-k outputs and
+  // the workspace: none of these may share a byte.
+  const size_t act = (size_t)batch * desc->hidden * 2;
+  const size_t tk = desc->n_experts > 0 ? (size_t)batch * desc->top_k * 4 : 0;
+  const Range r[5] = {{x, act}, {y, act}, {topk_idx, tk}, {topk_w, tk}, {ws, ws_bytes}};
+  if (!disjoint(r, 5)) return MOE_ERR_INVALID_ARG;
+  const DecodeLayout lay = decode_layout(*desc, batch, sync_cap);
+  if (ws_bytes < lay.bytes) return MOE_ERR_WORKSPACE;
+  if (L) *L = lay;
+  return MOE_OK;
+}
+
+moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                           const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes,
+                           StepLayout *L) {
+  if (!descs || !weights || n_layers < 1) return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const moe_status st = check_desc(&descs[i]);
+    if (st != MOE_OK) return st;
+    if (descs[i].hidden != descs[0].hidden) return MOE_ERR_INVALID_ARG;
+  }
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  const size_t act = (size_t)batch * descs[0].hidden * 2;
+  const Range r[3] = {{x, act}, {y, act}, {ws, ws_bytes}};
+  if (!disjoint(r, 3)) return MOE_ERR_INVALID_ARG;
+  StepLayout S;
+  if (!step_layout(descs, n_layers, batch, S)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < S.bytes) return MOE_ERR_WORKSPACE;
+  // Every layer as the step runs it: its input and output are the caller's
+  // x / y or an activation buffer past the layer workspace.
+  const uint8_t *base = (const uint8_t *)ws;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const void *in = (i == 0) ? x : base + ((i & 1) ? S.act0 : S.act1);
+    const void *out = (i == n_layers - 1) ? y : base + ((i & 1) ? S.act1 : S.act0);
+    const moe_status st =
+        check_decode_call(&descs[i], &weights[i], in, batch, out, nullptr, nullptr, ws, S.layer_bytes, S.sync_cap,
+                          nullptr);
+    if (st != MOE_OK) return st;
+  }
+  if (L) *L = S;
+  return MOE_OK;
+}
+
+moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                              int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
+                              const void *ws, size_t ws_bytes, PfLayout *L) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 1) return MOE_ERR_INVALID_ARG;
+  if (n_tokens > kMaxPrefillTokens) return MOE_ERR_UNSUPPORTED;
+  st = check_weights(desc, w);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID_ARG;
+  const size_t act = (size_t)n_tokens * desc->hidden * 2;
+  const size_t tk = desc->n_experts > 0 ? (size_t)n_tokens * desc->top_k * 4 : 0;
+  const Range r[5] = {{x, act}, {y, act}, {topk_idx, tk}, {topk_w, tk}, {ws, ws_bytes}};
+  if (!disjoint(r, 5)) return MOE_ERR_INVALID_ARG;
+  const PfLayout lay = prefill_layout(*desc, n_tokens);
+  if (ws_bytes < lay.bytes) return MOE_ERR_WORKSPACE;
+  if (L) *L = lay;
+  return MOE_OK;
+}
+
+moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t n = (size_t)(n_mats * nvfp4_matrix_bytes(rows, cols));
+  const Range r[2] = {{src, n}, {dst, n}};
+  return disjoint(r, 2) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+moe_status check_dequant_call(const void *src, const float *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                              const float *tensor_scale) {
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+  if (tensor_scale && !aligned(tensor_scale, 4)) return MOE_ERR_INVALID_ARG;
+  const Range r[2] = {{src, (size_t)(n_mats * nvfp4_matrix_bytes(rows, cols))},
+                      {dst, (size_t)(n_mats * rows * cols * 4)}};
+  return disjoint(r, 2) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_nvfp4_matrix_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 8 || cols % 32) return 0;
+  return (size_t)nvfp4_matrix_bytes(rows, cols);
+}
+
+size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch) {
+  if (check_desc(desc) != MOE_OK || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  return decode_layout(*desc, max_batch).bytes;
+}
+
+size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch) {
+  StepLayout S;
+  return step_layout(descs, n_layers, max_batch, S) ? S.bytes : 0;
+}
+
+size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {
+  if (check_desc(desc) != MOE_OK || n_tokens < 1 || n_tokens > kMaxPrefillTokens) return 0;
+  return prefill_layout(*desc, n_tokens).bytes;
+}
+
+moe_status moe_check_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                  int32_t batch, const void *y, const int32_t *topk_idx, const float *topk_w,
+                                  const void *ws, size_t ws_bytes) {
+  return check_decode_call(desc, w, x, batch, y, topk_idx, topk_w, ws, ws_bytes, 0, nullptr);
+}
+
+moe_status moe_check_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                                 const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes) {
+  return check_step_call(descs, weights, n_layers, x, batch, y, ws, ws_bytes, nullptr);
+}
+
+moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                   int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
+                                   const void *ws, size_t ws_bytes) {
+  return check_prefill_call(desc, w, x, n_tokens, y, topk_idx, topk_w, ws, ws_bytes, nullptr);
+}
+
+moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
+  return check_repack_call(src, dst, rows, cols, n_mats);
+}
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or batch for this path";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

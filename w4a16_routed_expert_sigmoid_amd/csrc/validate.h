@@ -1,0 +1,58 @@
+// Host-side argument validation and workspace layouts of the C ABI, in
+// plain C++ with no HIP dependency.  libmoe.so compiles this unit next to
+// the kernels; the same source also builds alone into a host-only library
+// (libmoe_host.so) whose checks run without the HIP runtime.
+#pragma once
+
+#include "../../include/moe.h"
+#include "shapes.h"
+
+namespace moe {
+
+// Byte offsets of one layer's decode workspace.  The status word's line
+// comes first, then the sync region (the ticket and flag lines, the tagged
+// logit words [B][E] and the one-token h words); the call zeroes
+// [0, clear_bytes) before its kernels run.
+struct DecodeLayout {
+  size_t sync_lines, sync_l, sync_h, clear_bytes;
+  size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, xcd_l, xcd_h, bytes;
+  int64_t stage_l, stage_elems;
+};
+
+// A step's workspace: the largest layer workspace (all layers share its
+// status word and sync region), then two activation buffers.
+struct StepLayout {
+  size_t sync_cap, layer_bytes, act0, act1, bytes;
+};
+
+// A prefill workspace, carved in this order.
+struct PfLayout {
+  size_t xn, logits, topk_idx, topk_w, counts, offsets, cursors, n_tiles, tiles, sorted_tok, pair_pos, h, y, bytes;
+  int64_t max_tiles;
+};
+
+int max_routed_of(const moe_layer_desc &d, int B);
+size_t sync_bytes_of(const moe_layer_desc &d, int B);
+DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0);
+bool step_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, StepLayout &L);
+PfLayout prefill_layout(const moe_layer_desc &d, int64_t T);
+
+moe_status check_desc(const moe_layer_desc *d);
+moe_status check_weights(const moe_layer_desc *d, const moe_layer_weights *w);
+
+// One layer call of `batch` tokens on workspace [ws, ws + ws_bytes) whose
+// sync region is sized for sync_cap (0: the layer's own); fills *L.
+moe_status check_decode_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                             int32_t batch, const void *y, const int32_t *topk_idx, const float *topk_w,
+                             const void *ws, size_t ws_bytes, size_t sync_cap, DecodeLayout *L);
+moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                           const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes,
+                           StepLayout *L);
+moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                              int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
+                              const void *ws, size_t ws_bytes, PfLayout *L);
+moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
+moe_status check_dequant_call(const void *src, const float *dst, int64_t rows, int64_t cols, int64_t n_mats,
+                              const float *tensor_scale);
+
+}  // namespace moe

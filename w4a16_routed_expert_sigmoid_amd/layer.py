@@ -8,8 +8,8 @@ moe_layer_desc / moe_layer_weights structs the C entry points take.
 import numpy as np
 import torch
 
-from . import (MOE_W_BF16, MOE_W_NVFP4, moe_decode_layer, moe_decode_workspace_bytes, moe_layer_desc,
-               moe_layer_weights, moe_prefill_layer, moe_prefill_workspace_bytes, moe_repack_nvfp4)
+from . import (MOE_W_BF16, MOE_W_NVFP4, moe_decode_layer, moe_decode_wait_status, moe_decode_workspace_bytes,
+               moe_layer_desc, moe_layer_weights, moe_prefill_layer, moe_prefill_workspace_bytes, moe_repack_nvfp4)
 
 
 class DeviceLayer:
@@ -83,7 +83,9 @@ class DeviceLayer:
         return torch.zeros(n, dtype=torch.uint8, device=self.device)
 
     def decode(self, x, ws=None, residual=None, want_topk=True, stream=None):
-        """x: int16 tensor [B, H] of BF16 bits on the device -> (y, idx, w)."""
+        """x: int16 tensor [B, H] of BF16 bits on the device -> (y, idx, w).
+        The call's wait status word is copied into self.status (see
+        wait_status())."""
         B = x.shape[0]
         if ws is None:
             ws = self.workspace(B)
@@ -93,7 +95,14 @@ class DeviceLayer:
         w = torch.empty((B, max(k, 1)), dtype=torch.float32, device=self.device) if want_topk else None
         moe_decode_layer(self.desc, self.weights, x, B, self.residual if residual is None else residual, y,
                          idx if k else None, w if k else None, ws, ws.numel(), stream)
+        if not hasattr(self, "status"):
+            self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        moe_decode_wait_status(ws, self.status, stream)
         return y, idx, w
+
+    def wait_status(self):
+        """The last decode call's wait status (0: no wait gave up); syncs."""
+        return int(self.status.item())
 
     def prefill(self, x, ws=None, residual=None, stream=None):
         T = x.shape[0]
