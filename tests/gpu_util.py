@@ -7,7 +7,14 @@ compare with the CPU oracle to the acceptance bar of the layer:
     are compared with the oracle re-run on the GPU's selection;
   - combine weights within 1e-5 relative of the oracle's (FP32 sigmoid and
     sum against FP64);
-  - outputs: rel-L2 <= 2e-3 over the whole [B][H] block and max-abs <= 1e-2.
+  - outputs: rel-L2 <= 2e-3 over the whole [B][H] block and max-abs <= 1e-2,
+    except that an element may differ from the oracle's by one BF16 ulp
+    where one ulp exceeds 1e-2 (oracle values of magnitude >= 2, e.g. the
+    wide dense layers' outputs): a sum accumulated in FP32 and rounded
+    once can land on the other side of a BF16 rounding midpoint than the
+    FP64 sum, and 1e-2 is finer than the format there.  Such flips are
+    rare (the FP32 sum must lie within its own rounding error of a
+    midpoint), so at most 1 in 10^4 elements may use this allowance.
 """
 import sys
 
@@ -18,6 +25,13 @@ import oracle
 
 REL_L2 = 2e-3
 MAX_ABS = 1e-2
+ULP_FLIP_FRACTION = 1e-4
+
+
+def bf16_ulp(v):
+    """One BF16 ulp at each value (normal range: 2^(exponent - 7))."""
+    m, e = np.frexp(np.abs(np.asarray(v, np.float64)))
+    return np.ldexp(1.0, e - 8)
 
 
 def log(msg):
@@ -99,7 +113,15 @@ def compare(layer, x, gpu_out, gpu_idx, gpu_w, ref=None, what=""):
     r = bf16_f64(out_ref)
     assert np.all(np.isfinite(o)), what
     rel = float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-30))
-    mx = float(np.max(np.abs(o - r)))
+    d = np.abs(o - r)
+    mx = float(np.max(d))
     assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
-    assert mx <= MAX_ABS, f"{what}: max-abs {mx:.3e}"
-    return ref, dict(rel_l2=rel, max_abs=mx, flagged=flagged, bit_exact=float(np.mean(gpu_out == out_ref)))
+    over = d > MAX_ABS
+    n_over = int(np.count_nonzero(over))
+    if n_over:
+        assert np.all(d[over] <= bf16_ulp(r[over])), \
+            f"{what}: max-abs {mx:.3e}, more than one BF16 ulp at {np.argwhere(over & (d > bf16_ulp(r)))[:4]}"
+        assert n_over <= ULP_FLIP_FRACTION * d.size, f"{what}: {n_over} elements one ulp (> 1e-2) apart"
+        log(f"  {what}: {n_over} of {d.size} elements one BF16 ulp (> 1e-2) from the oracle")
+    return ref, dict(rel_l2=rel, max_abs=mx, flagged=flagged, ulp_flips_over_1e2=n_over,
+                     bit_exact=float(np.mean(gpu_out == out_ref)))

@@ -63,3 +63,44 @@ def test_unflagged_token_needs_the_exact_set():
     out, gi, gw = _run(L, x, [4, 1, 5])
     with pytest.raises(AssertionError):
         compare(L, x, out, gi, gw)
+
+
+def _fake_layer_out(L, x):
+    r = oracle.moe_tokens(L, x)
+    return r, r["out"].copy()
+
+
+def test_one_ulp_allowance_only_where_an_ulp_exceeds_the_bar():
+    # A dense layer: oracle outputs; move one element of magnitude >= 2 by
+    # one BF16 ulp (allowed, it is a rounding-midpoint flip), by two ulps
+    # (refused), and one element below 2 by one ulp of 0.0078 (within 1e-2).
+    L = synth.make_layer(0, hidden=256, inter=0, shared_inter=2112, n_experts=0, sigma=0.1)
+    x = synth.tokens(64, 256, stream=3)
+    ref, out = _fake_layer_out(L, x)
+    v = oracle.bf16_to_f64(ref["out"])
+    big = np.argwhere(np.abs(v) >= 2.0)
+    if len(big) == 0:
+        pytest.skip("no output of magnitude >= 2 in this sample")
+    t, j = big[0]
+    one = out.copy()
+    one[t, j] += 1  # next BF16 magnitude: one ulp
+    compare(L, x, one, None, None, ref=ref)
+    two = out.copy()
+    two[t, j] += 2
+    with pytest.raises(AssertionError):
+        compare(L, x, two, None, None, ref=ref)
+
+
+def test_one_ulp_allowance_is_rare():
+    # Flipping many large elements by one ulp is a systematic error.
+    L = synth.make_layer(0, hidden=256, inter=0, shared_inter=2112, n_experts=0, sigma=0.1)
+    x = synth.tokens(64, 256, stream=3)
+    ref, out = _fake_layer_out(L, x)
+    v = oracle.bf16_to_f64(ref["out"])
+    big = np.abs(v) >= 2.0
+    if np.count_nonzero(big) < 3:
+        pytest.skip("too few outputs of magnitude >= 2 in this sample")
+    many = out.copy()
+    many[big] += 1
+    with pytest.raises(AssertionError):
+        compare(L, x, many, None, None, ref=ref)
