@@ -232,9 +232,36 @@ moe_status moe_decode_layer_timed(const moe_layer_desc *desc, const moe_layer_we
  * call zeroes first: 1 = the logits, 2 = the intermediate, 4 = the logits of
  * a batch's routing block.  A non-zero word means that call's outputs must
  * not be used.  This enqueues a copy of the word into status_out (device
- * int32) on `stream`, after the calls enqueued before it.
- * Errors: INVALID_ARG for null or misaligned pointers; HIP. */
+ * int32) on `stream`, after the calls enqueued before it.  ws == NULL: the
+ * workspace of moe_decode_layer_noalloc on the current device.
+ * Errors: INVALID_ARG for a null status_out or misaligned pointers; HIP. */
 moe_status moe_decode_wait_status(const void *ws, int32_t *status_out, void *stream);
+
+/* Bytes of the device array moe_decode_layer_noalloc takes its workspace
+ * from (one per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* moe_decode_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and outputs, with no
+ * workspace argument.  The workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per
+ * GPU, held from the library's load until the process ends; its address is
+ * looked up once per device, on the first call with that device current.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (the call zeroes what must start at zero): calls
+ * that overlap in time on one GPU (other streams or threads) race and give
+ * wrong results; calls ordered on one stream are safe.
+ * moe_decode_wait_status(NULL, ...) reads the array's status word.
+ * Errors: as moe_decode_layer; WORKSPACE when the layer at this batch needs
+ * more than MOE_NOALLOC_SCRATCH_BYTES of workspace
+ * (moe_decode_workspace_bytes(desc, batch); the full 256-expert layer needs
+ * about 0.6 MB at batch 8), before any device call; HIP if the array's
+ * address cannot be looked up. */
+moe_status moe_decode_layer_noalloc(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                    int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                                    void *stream);
 
 /* Host-side validation alone: what moe_decode_layer, moe_decode_step,
  * moe_prefill_layer and moe_repack_nvfp4 (and moe_unpack_nvfp4) return for

@@ -361,3 +361,21 @@ def test_prefill_workspace_bytes():
 ])
 def test_prefill_call_errors(which, kw, want):
     assert prefill(which, **kw) == want
+
+
+def test_noalloc_rejects_layers_beyond_its_array():
+    # The size limit of the no-alloc entry point is checked before any
+    # device call: a layer whose batch-8 workspace exceeds the array is
+    # refused; validation errors come first.
+    m = pytest.importorskip("w4a16_routed_expert_sigmoid_amd")
+    lib = m.lib()
+    big = desc(hidden=256, inter=4096, shared_inter=4096, n_experts=64, top_k=8)
+    assert host().moe_decode_workspace_bytes(ctypes.byref(big), 8) > m.MOE_NOALLOC_SCRATCH_BYTES
+    lib.moe_decode_layer_noalloc.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    call = lambda d, B: lib.moe_decode_layer_noalloc(ctypes.byref(Desc.from_buffer_copy(d)),  # noqa: E731
+                                                     ctypes.byref(Weights.from_buffer_copy(weights())), A(20), B,
+                                                     0, A(21), None, None, None)
+    assert call(big, 8) == WORKSPACE
+    assert call(desc(top_k=9), 1) == INVALID
+    assert call(desc(), 9) == UNSUPPORTED
+    assert call(desc(), 0) == INVALID

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_W_BF16, MOE_W_NVFP4 = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class MoeError(RuntimeError):
@@ -71,6 +72,9 @@ _lib.moe_decode_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER
                                   _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_decode_layer_timed.restype = _i32
 _lib.moe_decode_layer_timed.argtypes = _lib.moe_decode_layer.argtypes[:-1] + [ctypes.POINTER(_vp), _vp]
+_lib.moe_decode_layer_noalloc.restype = _i32
+_lib.moe_decode_layer_noalloc.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
+                                          _i32, _i32, _vp, _vp, _vp, _vp]
 _lib.moe_decode_wait_status.restype = _i32
 _lib.moe_decode_wait_status.argtypes = [_vp, _vp, _vp]
 _lib.moe_decode_step_workspace_bytes.restype = _sz
@@ -100,6 +104,7 @@ _lib.moe_check_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64]
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4",
            "moe_unpack_nvfp4", "moe_dequant_nvfp4",
            "moe_decode_workspace_bytes", "moe_decode_layer", "moe_decode_layer_timed", "moe_decode_wait_status",
+           "moe_decode_layer_noalloc",
            "moe_decode_step_workspace_bytes", "moe_decode_step", "moe_prefill_workspace_bytes",
            "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
            "moe_check_repack_nvfp4", "moe_probe_hbm_read")
@@ -183,9 +188,16 @@ def moe_decode_layer_timed(desc, weights, x, batch, residual, y, topk_idx, topk_
                                        _stream(stream)), "moe_decode_layer_timed")
 
 
+def moe_decode_layer_noalloc(desc, weights, x, batch, residual, y, topk_idx=None, topk_w=None, stream=None):
+    """moe_decode_layer with the library's own per-GPU workspace array."""
+    _check(_lib.moe_decode_layer_noalloc(ctypes.byref(desc), ctypes.byref(weights), _ptr(x), batch, int(residual),
+                                         _ptr(y), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_decode_layer_noalloc")
+
+
 def moe_decode_wait_status(ws, status_out, stream=None):
     """Enqueue a copy of the workspace's wait status word into status_out
-    (a device int32 tensor)."""
+    (a device int32 tensor); ws None: the no-alloc entry point's array."""
     _check(_lib.moe_decode_wait_status(_ptr(ws), _ptr(status_out), _stream(stream)), "moe_decode_wait_status")
 
 

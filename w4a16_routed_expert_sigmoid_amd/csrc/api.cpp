@@ -3,6 +3,9 @@
 // no HIP); nothing here is enqueued before they pass.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.h"
 #include "validate.h"
@@ -89,6 +92,38 @@ moe_status decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, 
   return hip_status(launch_decode(a, stream, events));
 }
 
+// Workspace of moe_decode_layer_noalloc: one fixed array in the library's
+// device memory, so that call allocates nothing.  Host code never passes
+// the array's name to a kernel or a copy (on the host it is only a stand-in
+// for the symbol); it uses the device address hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`.
+hipError_t device_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,8 +192,31 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
   return MOE_OK;
 }
 
+moe_status moe_decode_layer_noalloc(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
+                                    int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
+                                    void *stream) {
+  // The size limit first: it needs no device.
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  if (decode_layout(*desc, batch).bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = hip_status(device_scratch(&ws));
+  if (st != MOE_OK) return st;
+  return decode_layer(desc, w, x, batch, residual, y, topk_idx, topk_w, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr,
+                      (hipStream_t)stream);
+}
+
 moe_status moe_decode_wait_status(const void *ws, int32_t *status_out, void *stream) {
-  if (!ws || !status_out || ((uintptr_t)ws % kWsAlign) || ((uintptr_t)status_out % 4)) return MOE_ERR_INVALID_ARG;
+  if (!ws) {
+    // the array of moe_decode_layer_noalloc on the current device
+    void *p = nullptr;
+    const moe_status st = hip_status(device_scratch(&p));
+    if (st != MOE_OK) return st;
+    ws = p;
+  }
+  if (!status_out || ((uintptr_t)ws % kWsAlign) || ((uintptr_t)status_out % 4)) return MOE_ERR_INVALID_ARG;
   return hip_status(hipMemcpyAsync(status_out, ws, 4, hipMemcpyDeviceToDevice, (hipStream_t)stream));
 }
 
