@@ -70,6 +70,9 @@ def lib():
         L.oracle_decode_nvfp4.restype = ctypes.c_int64
         L.oracle_decode_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_double, ctypes.c_void_p]
+        L.oracle_gemv_nvfp4.restype = ctypes.c_int64
+        L.oracle_gemv_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         L.oracle_moe_tokens.restype = ctypes.c_int32
         L.oracle_moe_tokens.argtypes = [ctypes.POINTER(_Layer), ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -128,6 +131,18 @@ def decode_nvfp4(src, rows, cols, tensor_scale):
     out = np.empty((rows, cols), dtype=np.float64)
     nan = lib().oracle_decode_nvfp4(src.ctypes.data, rows, cols, float(tensor_scale), out.ctypes.data)
     return out, int(nan)
+
+
+def gemv_nvfp4(src, rows, cols, tensor_scale, x):
+    """Dense NVFP4 projection of T tokens: GGUF-like bytes [rows, cols],
+    x [T, cols] BF16 bits -> (y [T, rows] BF16 bits, NaN scale bytes met)."""
+    src = np.ascontiguousarray(src, dtype=np.uint8)
+    assert src.size == rows * (cols // 16) * 9
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1, cols)
+    y = np.empty((x.shape[0], rows), dtype=np.uint16)
+    nan = lib().oracle_gemv_nvfp4(src.ctypes.data, rows, cols, float(tensor_scale), x.ctypes.data, x.shape[0],
+                                  y.ctypes.data)
+    return y, int(nan)
 
 
 def _ptr(a):

@@ -175,6 +175,32 @@ int64_t oracle_decode_nvfp4(const uint8_t *src, int64_t rows, int64_t cols, doub
   return nan_count;
 }
 
+/* A dense projection on the same NVFP4 weights (the small-batch dense
+ * GEMV of "Day-0 Support for Flint on vLLM", section "Optimizations", for
+ * the layers outside the MoE blocks): for each of T tokens,
+ *   y_n = BF16( sum_k W[n][k] x_k ),  W = E2M1 * E4M3 block scale * S,
+ * in FP64 from the BF16 inputs, one rounding at the end (the same rounding
+ * point as the expert GEMVs).  src: GGUF-like NVFP4 bytes [rows][cols];
+ * x [T][cols] and y [T][rows] BF16 bits.  Returns the number of NaN scale
+ * bytes met (0 for a valid matrix). */
+int64_t oracle_gemv_nvfp4(const uint8_t *src, int64_t rows, int64_t cols, double tensor_scale, const uint16_t *x,
+                          int32_t T, uint16_t *y) {
+  tables_init();
+  int64_t nan_count = 0;
+  omat W = {src, rows, cols, OR_W_NVFP4, tensor_scale};
+  double *xv = (double *)malloc(sizeof(double) * (size_t)cols);
+  for (int32_t t = 0; t < T; ++t) {
+    for (int64_t c = 0; c < cols; ++c) xv[c] = oracle_bf16_value(x[(int64_t)t * cols + c]);
+    for (int64_t n = 0; n < rows; ++n) {
+      int64_t nan_row = 0;
+      y[(int64_t)t * rows + n] = oracle_bf16_round(row_dot(&W, n, xv, &nan_row));
+      if (t == 0) nan_count += nan_row;
+    }
+  }
+  free(xv);
+  return nan_count;
+}
+
 /* ------------------------------------------------------------------ */
 /* The layer                                                           */
 /* ------------------------------------------------------------------ */

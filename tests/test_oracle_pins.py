@@ -450,3 +450,48 @@ def test_threaded_oracle_is_bit_identical():
         b = oracle.moe_tokens(L, x, threads=n)
         for key in ("out", "idx", "w", "flag", "logits"):
             assert np.array_equal(a[key], b[key]), (n, key)
+
+
+# ---------------------------------------------------------------- dense NVFP4 GEMV
+
+def test_gemv_constant_code_closed_form():
+    # every element E2M1[c] * E4M3[s] * S: y_n = BF16(E2M1[c] E4M3[s] S sum(x))
+    rows, cols, c, sc, S = 24, 96, 11, 0x3A, 0.75   # code 11 = -1.5, scale 0x3A = 1.25
+    m = _constant_matrix(rows, cols, c, sc)
+    x = synth.tokens(3, cols, stream=31)
+    y, nan = oracle.gemv_nvfp4(m, rows, cols, S, x)
+    assert nan == 0
+    a = bf.E2M1[c] * bf.e4m3_decode(np.array([sc], np.uint8))[0] * S
+    want = bf.bf16_bits(a * bf.bf16_bits_to_f64(x).sum(axis=1))
+    assert np.array_equal(y, np.repeat(want[:, None], rows, axis=1))
+
+
+def test_gemv_one_hot_input_reads_one_column():
+    # x = e_j: y_n = BF16(W[n][j]); with a power-of-two tensor scale every
+    # NVFP4 value is a BF16 number, so y is exactly column j of the decoded
+    # matrix (a transposed operand or a wrong nibble order would not be).
+    rows, cols = 40, 64
+    m, s = synth.nvfp4_stack(9, 0, 1, 1, rows, cols, pow2_tensor_scale=True)
+    W = bf.decode_matrix(m[0], rows, cols, "nvfp4", float(s[0]))
+    for j in (0, 1, 8, 15, 17, 63):
+        x = np.zeros((1, cols), np.uint16)
+        x[0, j] = 0x3F80  # 1.0
+        y, _ = oracle.gemv_nvfp4(m[0], rows, cols, float(s[0]), x)
+        assert np.array_equal(bf.bf16_bits_to_f64(y[0]), W[:, j]), j
+
+
+def test_gemv_matches_bruteforce_decode_and_matmul():
+    rows, cols = 72, 320
+    m, s = synth.nvfp4_stack(10, 0, 1, 1, rows, cols)
+    x = synth.tokens(4, cols, stream=32)
+    y, nan = oracle.gemv_nvfp4(m[0], rows, cols, float(s[0]), x)
+    W = bf.decode_matrix(m[0], rows, cols, "nvfp4", float(s[0]))
+    want = bf.bf16_bits(bf.bf16_bits_to_f64(x) @ W.T)
+    assert nan == 0 and np.array_equal(y, want)
+
+
+def test_gemv_counts_nan_scales():
+    m = _constant_matrix(8, 32, 3, 0x38).copy()
+    m[2, 9] = 0xFF  # scale byte of row 2, block 1
+    _, nan = oracle.gemv_nvfp4(m, 8, 32, 1.0, synth.tokens(2, 32, stream=1))
+    assert nan == 1
