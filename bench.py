@@ -98,6 +98,7 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill leg")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight leg")
+    p.add_argument("--no-gemv", action="store_true", help="skip the dense-projection leg")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB streaming read (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
@@ -294,6 +295,10 @@ def run(args, dev):
         configs["prefill_8192_nvfp4"] = pf
         torch.cuda.empty_cache()
 
+    if args.workload == "layer" and not args.no_gemv:
+        configs["dense_gemv_nvfp4"] = run_gemv(args, dev)
+        torch.cuda.empty_cache()
+
     zipf = torch.from_numpy(synth.zipf_offset(E)).to(dev)
     t0 = time.time()
     dense = [moe.DeviceLayer(synth.make_layer(j, inter=0, shared_inter=5632, n_experts=0, norm=True), device=dev)
@@ -335,6 +340,8 @@ def run(args, dev):
     warn = []
     if pf is not None and pf["nonfinite"]:
         warn.append("non-finite outputs")
+    if any(v.get("nonfinite") for v in configs.get("dense_gemv_nvfp4", {}).values()):
+        warn.append("non-finite outputs")
     r1 = None
     if args.workload == "layer":
         descs = [mdesc] * len(pool)
@@ -349,7 +356,7 @@ def run(args, dev):
     step_pool = [d.t for d in dense] + pool[:47]
     step_descs = [d.desc for d in dense] + [mdesc] * 47
     r49 = time_stack(args, dev, step_pool, step_descs, 1, None, "49-layer step batch 1")
-    s49 = summary(r49, 49, 1, extra=2 * DENSE_BYTES)
+    s49 = summary(r49, 49, 1, extra=2 * DENSE_BYTES + 49 * H * 2)   # + the 49 RMSNorm gains
     s49["tokens_per_s"] = round(1e3 / r49["ms_step"], 1)
     s49["moe_layers_from"] = ("device copies of %d independently generated layers" % args.distinct_layers
                               if args.workload == "layer" else "47 independently generated layers")
@@ -435,6 +442,59 @@ def run(args, dev):
     }
     if warn:
         out["warning"] = "; ".join(sorted(set(warn)))
+    return out
+
+
+def run_gemv(args, dev):
+    """The dense NVFP4 projection at batch 1 and 8 on an LM-head-sized
+    (131072 x 2048) and a fused-QKV-sized (3072 x 2048) matrix: device
+    copies of one repacked matrix, rotated so that one graph replay streams
+    more than 1 GB of weights from HBM; GB/s on the weight bytes."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    out = {}
+    for name, rows in (("lm_head_131072x2048", 131072), ("qkv_3072x2048", 3072)):
+        cols = H
+        m, sc = synth.nvfp4_stack(4242, 0, 1, 1, rows, cols)
+        src = torch.from_numpy(m.reshape(-1)).to(dev)
+        w0 = torch.empty_like(src)
+        moe.moe_repack_nvfp4(src, w0, rows, cols, 1)
+        del src
+        nbytes = w0.numel()
+        copies = max(2, -(-(1 << 30) // nbytes))
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        s = torch.tensor([float(sc[0])], dtype=torch.float32, device=dev)
+        for B in (1, 8):
+            x = torch.from_numpy(synth.tokens(B, cols, stream=77).view(np.int16)).to(dev)
+            y = torch.empty((B, rows), dtype=torch.int16, device=dev)
+            g = torch.cuda.CUDAGraph()
+            moe.moe_gemv_nvfp4(ws[0], s, rows, cols, x, B, y)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for w in ws:
+                    moe.moe_gemv_nvfp4(w, s, rows, cols, x, B, y)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = 5
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(ws))
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"{name}_b{B}"] = {"us": round(us, 3), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "weight_bytes": int(nbytes), "copies_per_replay": len(ws),
+                                   "nonfinite": not torch.isfinite(y.view(torch.bfloat16).float()).all().item()}
+            log(f"gemv {name} B={B}: {us:.2f} us, {gbs:.0f} GB/s")
+        del ws, w0
+        torch.cuda.empty_cache()
     return out
 
 

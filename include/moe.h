@@ -184,6 +184,24 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
 moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
                            const void *x, int32_t batch, void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Dense projection on one NVFP4 matrix for a small batch: the small-batch
+ * dense GEMV the pages run on the same packed NVFP4 weights as the MoE
+ * kernel, for the projections outside the MoE blocks (attention QKV and
+ * output, the LM head; "Day-0 Support for Flint on vLLM", section
+ * "Optimizations").  For t < batch, n < rows:
+ *   y[t][n] = BF16( S * sum_k W[n][k] x[t][k] ),
+ * W[n][k] = E2M1 * E4M3 block scale, FP32 accumulation, one BF16 rounding.
+ *  w: device, one matrix [rows][cols] in the runtime layout written by
+ *     moe_repack_nvfp4; tensor_scale: device FP32 S.
+ *  x [batch][cols] BF16 in; y [batch][rows] BF16 out; batch 1..8.
+ * Errors: INVALID_ARG for null or misaligned pointers, rows % 8 or cols %
+ * 32 != 0, batch < 1, y sharing a byte with w, x or the scale; UNSUPPORTED
+ * for batch > 8 or a column count the kernels do not tile (cols/32 must be
+ * at least 2 and either a power of two or at least 64; one token: cols <=
+ * 32768); HIP. */
+moe_status moe_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                          int32_t batch, void *y, void *stream);
+
 /* Workspace bytes moe_prefill_layer needs for n_tokens tokens (1 ..
  * 4,194,304), or 0 if the description is invalid or n_tokens is out of
  * range.  About (k + 1) * n_tokens * (H + max(I, Is)) * 2 bytes: the
@@ -264,7 +282,8 @@ moe_status moe_decode_layer_noalloc(const moe_layer_desc *desc, const moe_layer_
                                     void *stream);
 
 /* Host-side validation alone: what moe_decode_layer, moe_decode_step,
- * moe_prefill_layer and moe_repack_nvfp4 (and moe_unpack_nvfp4) return for
+ * moe_prefill_layer, moe_repack_nvfp4 (and moe_unpack_nvfp4) and
+ * moe_gemv_nvfp4 return for
  * these arguments before anything would be enqueued (MOE_OK: the call
  * would launch).  Nothing is launched, no pointer is dereferenced.  The
  * same checks are built into a host-only library without the HIP runtime. */
@@ -277,6 +296,8 @@ moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_w
                                    int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
                                    const void *ws, size_t ws_bytes);
 moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
+moe_status moe_check_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                                int32_t batch, const void *y);
 
 /* Measurement: reads `bytes` (a multiple of 16) of device memory at src
  * once, streaming, with `blocks` blocks of 256 threads (grid-stride, four

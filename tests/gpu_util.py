@@ -109,6 +109,13 @@ def compare(layer, x, gpu_out, gpu_idx, gpu_w, ref=None, what=""):
                 check_flagged(ref["logits"][t], forced["idx"][i], forced["w"][i], gpu_idx[t], gpu_w[t], k,
                               f"{what} token {t} (flagged)")
                 out_ref[t] = forced["out"][i]
+    st = check_outputs(gpu_out, out_ref, what)
+    st["flagged"] = flagged
+    return ref, st
+
+
+def check_outputs(gpu_out, out_ref, what=""):
+    """The output bar on BF16 bits (see the module docstring); returns stats."""
     o = bf16_f64(gpu_out)
     r = bf16_f64(out_ref)
     assert np.all(np.isfinite(o)), what
@@ -123,5 +130,4 @@ def compare(layer, x, gpu_out, gpu_idx, gpu_w, ref=None, what=""):
             f"{what}: max-abs {mx:.3e}, more than one BF16 ulp at {np.argwhere(over & (d > bf16_ulp(r)))[:4]}"
         assert n_over <= ULP_FLIP_FRACTION * d.size, f"{what}: {n_over} elements one ulp (> 1e-2) apart"
         log(f"  {what}: {n_over} of {d.size} elements one BF16 ulp (> 1e-2) from the oracle")
-    return ref, dict(rel_l2=rel, max_abs=mx, flagged=flagged, ulp_flips_over_1e2=n_over,
-                     bit_exact=float(np.mean(gpu_out == out_ref)))
+    return dict(rel_l2=rel, max_abs=mx, ulp_flips_over_1e2=n_over, bit_exact=float(np.mean(gpu_out == out_ref)))

@@ -46,6 +46,8 @@ def _declare(lib):
     lib.moe_check_prefill_layer.argtypes = [D, W, _vp, _i32, _vp, _vp, _vp, _vp, _sz]
     lib.moe_check_repack_nvfp4.restype = _i32
     lib.moe_check_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64]
+    lib.moe_check_gemv_nvfp4.restype = _i32
+    lib.moe_check_gemv_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp]
     lib.moe_decode_workspace_bytes.restype = _sz
     lib.moe_decode_workspace_bytes.argtypes = [D, _i32]
     lib.moe_decode_step_workspace_bytes.restype = _sz
@@ -379,3 +381,31 @@ def test_noalloc_rejects_layers_beyond_its_array():
     assert call(desc(top_k=9), 1) == INVALID
     assert call(desc(), 9) == UNSUPPORTED
     assert call(desc(), 0) == INVALID
+
+
+def gemv(which, w=A(1), s=A(2), rows=3072, cols=2048, x=A(20), B=1, y=A(21)):
+    if which == "host":
+        return host().moe_check_gemv_nvfp4(w, s, rows, cols, x, B, y)
+    lib = hip()
+    lib.moe_gemv_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp]
+    return lib.moe_gemv_nvfp4(w, s, rows, cols, x, B, y, None)
+
+
+def test_gemv_valid_call_passes_validation():
+    assert gemv("host") == OK
+    assert gemv("host", w=P + (1 << 36), B=8, rows=131072) == OK   # 151 MB of weights, clear of x and y
+
+
+@pytest.mark.parametrize("which", LIBS)
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=None), INVALID), (dict(s=None), INVALID), (dict(x=None), INVALID), (dict(y=None), INVALID),
+    (dict(rows=0), INVALID), (dict(rows=12), INVALID), (dict(cols=48), INVALID), (dict(cols=0), INVALID),
+    (dict(B=0), INVALID), (dict(B=9), UNSUPPORTED),
+    (dict(cols=96), UNSUPPORTED), (dict(cols=32), UNSUPPORTED), (dict(cols=65536, rows=8), UNSUPPORTED),
+    (dict(w=A(1) + 4), INVALID), (dict(x=A(20) + 8), INVALID), (dict(s=A(2) + 2), INVALID),
+    (dict(y=A(20)), INVALID),                       # y == x
+    (dict(y=A(1) + 4096), INVALID),                 # y inside w (3.5 MB)
+    (dict(y=A(2) - 16, B=1, rows=16), INVALID),     # y (32 B) runs over the scale
+])
+def test_gemv_errors(which, kw, want):
+    assert gemv(which, **kw) == want

@@ -88,6 +88,10 @@ _lib.moe_prefill_layer.restype = _i32
 _lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
                                    _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 
+_lib.moe_gemv_nvfp4.restype = _i32
+_lib.moe_gemv_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp, _vp]
+_lib.moe_check_gemv_nvfp4.restype = _i32
+_lib.moe_check_gemv_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _vp, _i32, _vp]
 _lib.moe_probe_hbm_read.restype = _i32
 _lib.moe_probe_hbm_read.argtypes = [_vp, _sz, _i32, _vp, _vp]
 _lib.moe_check_decode_layer.restype = _i32
@@ -107,7 +111,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes
            "moe_decode_layer_noalloc",
            "moe_decode_step_workspace_bytes", "moe_decode_step", "moe_prefill_workspace_bytes",
            "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
-           "moe_check_repack_nvfp4", "moe_probe_hbm_read")
+           "moe_check_repack_nvfp4", "moe_probe_hbm_read", "moe_gemv_nvfp4", "moe_check_gemv_nvfp4")
 
 
 def lib():
@@ -199,6 +203,12 @@ def moe_decode_wait_status(ws, status_out, stream=None):
     """Enqueue a copy of the workspace's wait status word into status_out
     (a device int32 tensor); ws None: the no-alloc entry point's array."""
     _check(_lib.moe_decode_wait_status(_ptr(ws), _ptr(status_out), _stream(stream)), "moe_decode_wait_status")
+
+
+def moe_gemv_nvfp4(w, tensor_scale, rows, cols, x, batch, y, stream=None):
+    """y[t] = BF16(S * W x[t]) on one repacked NVFP4 matrix, batch 1..8."""
+    _check(_lib.moe_gemv_nvfp4(_ptr(w), _ptr(tensor_scale), rows, cols, _ptr(x), batch, _ptr(y), _stream(stream)),
+           "moe_gemv_nvfp4")
 
 
 def moe_probe_hbm_read(src, nbytes, blocks, sink, stream=None):

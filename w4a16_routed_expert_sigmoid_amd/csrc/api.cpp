@@ -220,6 +220,21 @@ moe_status moe_decode_wait_status(const void *ws, int32_t *status_out, void *str
   return hip_status(hipMemcpyAsync(status_out, ws, 4, hipMemcpyDeviceToDevice, (hipStream_t)stream));
 }
 
+moe_status moe_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                          int32_t batch, void *y, void *stream) {
+  const moe_status st = check_gemv_call(w, tensor_scale, rows, cols, x, batch, y);
+  if (st != MOE_OK) return st;
+  GemvArgs g;
+  g.w = (const uint8_t *)w;
+  g.scale = tensor_scale;
+  g.x = (const uint16_t *)x;
+  g.y = (uint16_t *)y;
+  g.N = (int)rows;
+  g.K = (int)cols;
+  g.B = batch;
+  return hip_status(launch_gemv(g, (hipStream_t)stream));
+}
+
 moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                              int32_t n_tokens, int32_t residual, void *y, int32_t *topk_idx,
                              float *topk_w, void *ws, size_t ws_bytes, void *stream) {

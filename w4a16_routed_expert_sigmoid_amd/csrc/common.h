@@ -319,6 +319,17 @@ struct PrefillArgs {
   uint16_t *y_rows;       // [P + T][H] expert outputs, BF16
 };
 
+// Arguments of the dense NVFP4 projection (passed by value).
+struct GemvArgs {
+  const uint8_t *w;      // one NVFP4 matrix [N][K], runtime layout
+  const float *scale;    // its FP32 tensor scale (device)
+  const uint16_t *x;     // [B][K] BF16
+  uint16_t *y;           // [B][N] BF16
+  int N, K, B;
+};
+constexpr int kGemvThreads = 256;
+
+hipError_t launch_gemv(const GemvArgs &g, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);

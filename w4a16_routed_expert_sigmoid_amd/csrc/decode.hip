@@ -1439,6 +1439,180 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense projection on one NVFP4 matrix for 1..8 tokens: the small-batch
+// dense GEMV the pages pair with the MoE kernel ("Day-0 Support for Flint
+// on vLLM", section "Optimizations": same packed NVFP4 weights, for the
+// projections outside the MoE blocks):
+//   y[t][n] = BF16(S * sum_k W[n][k] x[t][k]),  FP32 accumulation.
+// ---------------------------------------------------------------------------
+
+// One token (k_gemv): the block stages x in LDS once; each lane group of
+// LPR lanes walks 4-row units (grid-stride), the next unit's weights in
+// flight while the current one is multiplied (FP4 converted to BF16 in
+// registers, v_dot2 with FP32 accumulation, block scales in FP32).
+// acc[r] += W[r0 + r][chunk] . x[chunk] for one NVFP4 chunk, converting
+// and multiplying one 8-element dword at a time (a small working set).
+__device__ __forceinline__ void dot_rows_fp4(const ChunkRaw &cr, const uint32_t (&x)[16], float (&acc)[kRows]) {
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const uint4 q = cr.q[r][0];
+    float p0 = dot8_fp4_bf16(q.x, x[0], x[1], x[2], x[3], 0.f);
+    p0 = dot8_fp4_bf16(q.y, x[4], x[5], x[6], x[7], p0);
+    float p1 = dot8_fp4_bf16(q.z, x[8], x[9], x[10], x[11], 0.f);
+    p1 = dot8_fp4_bf16(q.w, x[12], x[13], x[14], x[15], p1);
+    acc[r] = fmaf(e4m3_to_f32(cr.scale[r] & 0xffu), p0, fmaf(e4m3_to_f32(cr.scale[r] >> 8), p1, acc[r]));
+  }
+}
+
+constexpr int kGemvBlocksPerCu = 8;
+constexpr int kGemvCus = 256;  // MI355X compute units: the grid is capped at 8 blocks per CU
+
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs g) {
+  extern __shared__ uint4 s_gx[];  // x [K / 8] pieces of 16 bytes
+  const int K = g.K, LPR = lanes_per_row(K), C = K / 32;
+  const int groups = kGemvThreads / LPR;
+  const int lane = threadIdx.x & (kWave - 1), lg = lane % LPR;
+  for (int i = threadIdx.x; i < K / 8; i += kGemvThreads) s_gx[i] = reinterpret_cast<const uint4 *>(g.x)[i];
+  const int64_t units = g.N / kRows, ustride = (int64_t)gridDim.x * groups;
+  int64_t u = (int64_t)blockIdx.x * groups + threadIdx.x / LPR;
+  const uint16_t *xs = reinterpret_cast<const uint16_t *>(s_gx);
+  const float S = *g.scale;
+  // one chunk per lane and unit when C <= LPR (every tiled K up to 2048),
+  // else the lane walks its chunks inside the unit
+  ChunkRaw nxt;
+  if (u < units) load_rows<1>(g.w, g.N, K, (int)(u * kRows), lg, nxt);
+  __syncthreads();
+  // All lanes of a group take the same units, and the folds exchange
+  // values only inside a group, so groups may leave the loop at different
+  // times.
+  for (; u < units; u += ustride) {
+    float acc[kRows] = {0.f, 0.f, 0.f, 0.f};
+    ChunkRaw cur = nxt;
+    const int64_t un = u + ustride;
+    for (int c = lg; c < C; c += LPR) {
+      if (c != lg) load_rows<1>(g.w, g.N, K, (int)(u * kRows), c, cur);
+      else if (un < units) load_rows<1>(g.w, g.N, K, (int)(un * kRows), lg, nxt);
+      uint32_t x[16];
+      load16(xs + c * 32, x);
+      dot_rows_fp4(cur, x, acc);
+    }
+    int row;
+    float y2 = 0.f;
+    const float ys = fold4(acc[0], acc[1], acc[2], acc[3], LPR, row, &y2);
+    if (lg < (LPR == 2 ? 2 : kRows)) {
+      uint16_t *yr = g.y + u * kRows + row;
+      yr[0] = (uint16_t)f32_to_bf16(ys * S);
+      if (LPR == 2) yr[1] = (uint16_t)f32_to_bf16(y2 * S);
+    }
+  }
+}
+
+// 2..8 tokens (k_gemv_mm): on the matrix cores, as the batch expert kernels
+// do: block = 64 weight rows (four 16-row A tiles), the tokens the 16
+// columns of v_mfma_f32_16x16x32_bf16 (zero past the batch), each weight
+// element dequantised once; the 8 waves split K and their partial sums meet
+// in LDS.  Operand layout as in k_gateup_mm.
+// The batch's x is staged in LDS when it fits the 32 KiB the K-partial
+// sums use afterwards (B * K <= 16384): the token operands are then read
+// from LDS right before their MFMAs and take no registers across the loads.
+constexpr int kGemvMmStage = kMmWaves * 16 * kWave * 4;
+
+template <bool STAGED>
+__global__ __launch_bounds__(kMmWaves *kWave) void k_gemv_mm(GemvArgs g) {
+  __shared__ float s_red[kMmWaves][16][kWave];
+  const int K = g.K, B = g.B, C = K / 32, N = g.N;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r16 = lane & 15, p = lane >> 4;
+  const int row0 = blockIdx.x * kMmRows;
+  const uint16_t *xs = g.x;
+  if (STAGED) {
+    uint4 *st = reinterpret_cast<uint4 *>(&s_red[0][0][0]);
+    for (int i = tid; i < B * K / 8; i += kMmWaves * kWave) st[i] = reinterpret_cast<const uint4 *>(g.x)[i];
+    xs = reinterpret_cast<const uint16_t *>(st);
+    __syncthreads();
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int SS = (C + 3) / 4;
+  // Two 128-K super-steps per pass, all their weight loads issued first.
+  for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
+    uint4 q[2][4], xv[2][4];
+    uint32_t sc[2][4];
+    bool tok[2];
+    int cc[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int ss = ss0 + v * kMmWaves;
+      const int c = ss * 4 + p;
+      const bool cok = ss < SS && c < C;
+      tok[v] = cok && r16 < B;
+      cc[v] = c;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int n = row0 + rg * 16 + r16;
+        const bool ok = cok && n < N;
+        q[v][rg] = ok ? *reinterpret_cast<const uint4 *>(g.w + (int64_t)n * (K / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        sc[v][rg] = ok ? scale_pair(g.w, N, K, n, c) : 0u;
+      }
+      if (!STAGED) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xv[v][s] = tok[v] ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * K + c * 32 + s * 8)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 xq = STAGED ? (tok[v] ? *reinterpret_cast<const uint4 *>(xs + r16 * K + cc[v] * 32 + s * 8)
+                                          : make_uint4(0, 0, 0, 0))
+                                : xv[v][s];
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xq.x, xq.y, xq.z, xq.w});
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float sw = e4m3_to_f32((sc[v][rg] >> (8 * (s >> 1))) & 0xffu);
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(q[v][rg], s), sw), bx, acc[rg], 0, 0, 0);
+        }
+      }
+  }
+  if (STAGED) __syncthreads();  // every wave is done with the staged x
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][rg * 4 + i][lane] = acc[rg][i];
+  __syncthreads();
+  // 1024 (row group, value, lane) sums over the 8 waves, two per thread
+  const float S = *g.scale;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int idx = tid + k2 * kMmWaves * kWave;
+    const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMmWaves; ++w) v += s_red[w][rg * 4 + i][l];
+    const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
+    if (t < B && n < N) g.y[(int64_t)t * N + n] = (uint16_t)f32_to_bf16(v * S);
+  }
+}
+
+hipError_t launch_gemv(const GemvArgs &g, hipStream_t stream) {
+  if (g.B > 1) {
+    const dim3 grid((g.N + kMmRows - 1) / kMmRows), block(kMmWaves * kWave);
+    if ((int64_t)g.B * g.K * 2 <= kGemvMmStage) hipLaunchKernelGGL(k_gemv_mm<true>, grid, block, 0, stream, g);
+    else hipLaunchKernelGGL(k_gemv_mm<false>, grid, block, 0, stream, g);
+    return hipGetLastError();
+  }
+  const int groups = kGemvThreads / lanes_per_row(g.K);
+  const int64_t units = g.N / kRows;
+  const int64_t want = (units + groups - 1) / groups, cap = (int64_t)kGemvCus * kGemvBlocksPerCu;
+  const int grid = (int)(want < cap ? want : cap);
+  hipLaunchKernelGGL(k_gemv, dim3(grid), dim3(kGemvThreads), (size_t)g.K * 2, stream, g);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_sync_clear(uint32_t *p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

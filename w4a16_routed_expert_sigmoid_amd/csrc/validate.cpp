@@ -260,6 +260,23 @@ moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weight
   return MOE_OK;
 }
 
+moe_status check_gemv_call(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                           int32_t batch, const void *y) {
+  if (!w || !tensor_scale || !x || !y) return MOE_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (batch < 1) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(tensor_scale, 4)) return MOE_ERR_INVALID_ARG;
+  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  // one token stages x in 64 KiB of LDS
+  if (!k_tileable(cols) || rows > (int64_t)1 << 30 || (batch == 1 && cols > 32768)) return MOE_ERR_UNSUPPORTED;
+  // the output may share no byte with an input
+  const Range out = {y, (size_t)batch * rows * 2};
+  const Range in[3] = {{w, (size_t)nvfp4_matrix_bytes(rows, cols)}, {x, (size_t)batch * cols * 2}, {tensor_scale, 4}};
+  for (const Range &r : in)
+    if (overlap(out, r)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
   if (!src || !dst) return MOE_ERR_INVALID_ARG;
   if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
@@ -325,6 +342,11 @@ moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_w
 
 moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
   return check_repack_call(src, dst, rows, cols, n_mats);
+}
+
+moe_status moe_check_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                                int32_t batch, const void *y) {
+  return check_gemv_call(w, tensor_scale, rows, cols, x, batch, y);
 }
 
 const char *moe_status_string(moe_status s) {

@@ -51,6 +51,8 @@ moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights 
 moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                               int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
                               const void *ws, size_t ws_bytes, PfLayout *L);
+moe_status check_gemv_call(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
+                           int32_t batch, const void *y);
 moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
 moe_status check_dequant_call(const void *src, const float *dst, int64_t rows, int64_t cols, int64_t n_mats,
                               const float *tensor_scale);
