@@ -233,16 +233,40 @@ __device__ inline float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-// One element of a pre-norm output: BF16 of x * inv * g, rounded from the
-// product as FP64 gives it (inv = 1/sqrt(mean(x^2) + eps) in FP64).  The
-// FP32 product is within a few FP32 ulps of it, so it rounds the same way
-// unless it lies within 16 ulps of a BF16 rounding midpoint (low 16 bits
-// near 0x8000); those rare elements are redone in FP64.
-__device__ inline uint32_t norm_elem_bf16(float x, float g, float inv_f, double inv) {
-  const float p = x * inv_f * g;
-  const uint32_t low = __float_as_uint(p) & 0xffffu;
-  if (low - 0x7ff0u <= 0x20u) return f64_to_bf16((double)x * inv * (double)g);
-  return f32_to_bf16(p);
+// Pre-norm output of the 8 BF16 elements of a 16-byte piece of x and of the
+// gain: BF16 of x * inv * g, rounded from the product as FP64 gives it (inv
+// = 1/sqrt(mean(x^2) + eps) in FP64).  The FP32 product (x * inv_f) * g is
+// within a few FP32 ulps of it, so it rounds the same way unless it lies
+// within 16 ulps of a BF16 rounding midpoint (low 16 bits near 0x8000);
+// those rare elements are redone in FP64.  Eight FP32 products, four packed
+// conversions, and one branch per piece, taken only when some element needs
+// the redo.
+__device__ inline uint4 norm_piece_bf16(uint4 xv, uint4 gv, float inv_f, double inv) {
+  const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w}, gq[4] = {gv.x, gv.y, gv.z, gv.w};
+  float p[8];
+  uint32_t near = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t xb = (e & 1) ? (xq[e >> 1] >> 16) : (xq[e >> 1] & 0xffffu);
+    const uint32_t gb = (e & 1) ? (gq[e >> 1] >> 16) : (gq[e >> 1] & 0xffffu);
+    p[e] = bf16_to_f32(xb) * inv_f * bf16_to_f32(gb);
+    near |= ((__float_as_uint(p[e]) & 0xffffu) - 0x7ff0u <= 0x20u ? 1u : 0u) << e;
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f32x2_to_bf16x2(p[2 * d], p[2 * d + 1]);
+  if (near) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((near >> e) & 1u) {
+        const uint32_t xb = (e & 1) ? (xq[e >> 1] >> 16) : (xq[e >> 1] & 0xffffu);
+        const uint32_t gb = (e & 1) ? (gq[e >> 1] >> 16) : (gq[e >> 1] & 0xffffu);
+        const uint32_t r = f64_to_bf16((double)bf16_to_f32(xb) * inv * (double)bf16_to_f32(gb));
+        o[e >> 1] = (e & 1) ? ((o[e >> 1] & 0xffffu) | (r << 16)) : ((o[e >> 1] & 0xffff0000u) | r);
+      }
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Device pointers of the decode workspace, carved from one caller buffer.

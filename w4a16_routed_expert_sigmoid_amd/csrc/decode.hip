@@ -99,12 +99,18 @@ template <int J>
 __device__ __forceinline__ void wave_topk(const float *lt, int E, int k, int (&sel)[kMaxTopK],
                                           float (&selv)[kMaxTopK]) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint32_t key[J];
+  // Clamped indices keep the J loads unconditional, so they are all in
+  // flight together (a load under a bound test is issued and waited for one
+  // at a time).
+  float lv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane * J + j;
-    key[j] = (e < E) ? topk_key(lt[e]) : 0u;
+    lv[j] = lt[e < E ? e : E - 1];
   }
+  uint32_t key[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) key[j] = (lane * J + j < E) ? topk_key(lv[j]) : 0u;
   uint32_t lmax = key[0];
 #pragma unroll
   for (int j = 1; j < J; ++j) lmax = max(lmax, key[j]);
@@ -281,15 +287,7 @@ __global__ __launch_bounds__(kNormThreads) void k_norm(DecodeArgs a) {
   const float inv_f = (float)inv;
   for (int i = tid; i < n8; i += kNormThreads) {
     const uint4 v = i == tid ? x0 : xr[i], gv = i == tid ? g0 : gr[i];
-    uint32_t q[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv);
-      const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv);
-      q[j] = lo | (hi << 16);
-    }
-    reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = make_uint4(q[0], q[1], q[2], q[3]);
+    reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = norm_piece_bf16(v, gv, inv_f, inv);
   }
 }
 
@@ -336,95 +334,155 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
   const bool norm_here = a.use_norm && !xn_ready;
   const uint16_t *src = xn_ready ? a.ws.xn : a.x;
 
-  // Loads in the order they are needed (memory operations complete in
-  // issue order): this thread's first piece of every token (the norm and
-  // the staging start as soon as they land), then the first four pieces of
-  // this lane's router row, the first piece of the norm gain and the row's
-  // bias, which arrive while the norm runs.
-  uint4 v0[kMaxBatch];
-#pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t)
-    if (t < B && tid < n8) v0[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[tid];
   uint4 w0[4];
+  float bias;
+  if (norm_here && B > 1 && B <= kRouterWaves && n8 <= 8 * kWave) {
+    // Batches (H <= 4096): one wave per token.  Wave t loads token t (lane l
+    // the 16-byte pieces l, l + 64, ..., at most 8) and its gain, sums the
+    // squares in FP64 over its pieces and then across the wave (every lane
+    // ends with the same bits), forms 1/sqrt(mean + eps) itself and normalises its pieces into
+    // LDS: one cross-lane reduction per wave and no cross-wave step before
+    // the normalisation.  The token and the gain are requested before the
+    // router row's first pieces: loads complete in issue order, so the norm
+    // runs while the router weights are still on their way from memory.
+    const int np = (n8 + kWave - 1) / kWave;
+    const bool tok = wave < B;
+    // (indices clamped into the buffers: every load is unconditional, so
+    // the waits before the norm cover the token and the gain only)
+    const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + (int64_t)(tok ? wave : 0) * H);
+    const uint4 *gr = reinterpret_cast<const uint4 *>(a.norm_gain);
+    // a layer without routed experts has no router: its row loads read the
+    // token instead (valid memory) and are discarded
+    const uint4 *wr = E > 0 ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)(row < E ? row : E - 1) * H) : xr;
+    uint4 xv[8], gv[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = lg + i * LPR;
-    w0[i] = (row < E && j < n8) ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)row * H)[j]
-                                : make_uint4(0, 0, 0, 0);
-  }
-  uint4 g0 = make_uint4(0, 0, 0, 0);
-  if (norm_here && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
-  const float bias = (a.router_b && row < E) ? a.router_b[row] : 0.f;
-
-  // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
-  // thread's pieces of every token are loaded before any is stored, so the
-  // loads are in flight together.
-  double ss[kMaxBatch];
+    for (int j = 0; j < 8; ++j) xv[j] = xr[min(lane + j * kWave, n8 - 1)];
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.0;
-  for (int i = tid; i < n8; i += kRouterThreads) {
-    uint4 v[kMaxBatch];
+    for (int j = 0; j < 8; ++j) gv[j] = gr[min(lane + j * kWave, n8 - 1)];
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t)
-      if (t < B) v[t] = i == tid ? v0[t] : reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
+    for (int i = 0; i < 4; ++i) w0[i] = wr[min(lg + i * LPR, n8 - 1)];
+    // pieces past the token (clamped duplicates) take no part in the sums
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
-      if (t >= B) break;
-      s_x[t * n8 + i] = v[t];
-      if (norm_here) {
-        const uint32_t q[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+    for (int j = 0; j < 8; ++j)
+      if (!(j < np && lane + j * kWave < n8)) xv[j] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
-          ss[t] = fma(lo, lo, fma(hi, hi, ss[t]));
+    for (int i = 0; i < 4; ++i)
+      if (!(row < E && lg + i * LPR < n8)) w0[i] = make_uint4(0, 0, 0, 0);
+    bias = (a.router_b && E > 0) ? a.router_b[row < E ? row : E - 1] : 0.f;
+    if (row >= E) bias = 0.f;
+    if (tok) {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t q[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double lo = bf16_to_f32(q[e] & 0xffffu), hi = bf16_to_f32(q[e] >> 16);
+          ss = fma(lo, lo, fma(hi, hi, ss));
+        }
+      }
+      ss = group_sum_f64(ss, kWave);
+      const double inv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
+      const float inv_f = (float)inv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = lane + j * kWave;
+        if (j < np && i < n8) {
+          const uint4 o = norm_piece_bf16(xv[j], gv[j], inv_f, inv);
+          s_x[wave * n8 + i] = o;
+          if (blockIdx.x == 0) reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)wave * H)[i] = o;
         }
       }
     }
-  }
-  if (norm_here) {
-#pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
-      if (t >= B) break;
-      const double v = group_sum_f64(ss[t], kWave);
-      if (lane == 0) s_ss[wave][t] = v;
-    }
-  }
-  __syncthreads();
-
-  // 2. pre-norm in LDS: xn = BF16(x * inv * gain)
-  if (norm_here) {
-    // one thread per token forms 1/sqrt(mean(x^2) + eps) in FP64
-    if (tid < B) {
-      double tot = 0.0;
-#pragma unroll
-      for (int w = 0; w < kRouterWaves; ++w) tot += s_ss[w][tid];
-      s_ss[0][tid] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
-    }
     __syncthreads();
-    double inv[kMaxBatch];
+  } else {
+    // Loads in the order they are needed (memory operations complete in
+    // issue order): this thread's first piece of every token and of the
+    // norm gain (the staging and the norm start as soon as they land), then
+    // the first four pieces of this lane's router row and the row's bias,
+    // which arrive from memory while the norm runs.
+    // (indices clamped into the buffers: every load is unconditional)
+    const int tc = tid < n8 ? tid : n8 - 1;
+    uint4 v0[kMaxBatch];
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) inv[t] = t < B ? s_ss[0][t] : 1.0;
+    for (int t = 0; t < kMaxBatch; ++t)
+      if (t < B) v0[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[tc];
+    uint4 g0 = make_uint4(0, 0, 0, 0);
+    if (norm_here) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tc];
+    // a layer without routed experts (the pre-norm alone) has no router: its
+    // row loads read the token instead (valid memory) and are discarded
+    const uint4 *wr = E > 0 ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)(row < E ? row : E - 1) * H)
+                            : reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w0[i] = wr[min(lg + i * LPR, n8 - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!(row < E && lg + i * LPR < n8)) w0[i] = make_uint4(0, 0, 0, 0);
+    bias = (a.router_b && E > 0) ? a.router_b[row < E ? row : E - 1] : 0.f;
+    if (row >= E) bias = 0.f;
+
+    // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
+    // thread's pieces of every token are loaded before any is stored, so the
+    // loads are in flight together.
+    double ss[kMaxBatch];
+#pragma unroll
+    for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.0;
     for (int i = tid; i < n8; i += kRouterThreads) {
-      const uint4 gv = i == tid ? g0 : reinterpret_cast<const uint4 *>(a.norm_gain)[i];
-      const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint4 v[kMaxBatch];
+#pragma unroll
+      for (int t = 0; t < kMaxBatch; ++t)
+        if (t < B) v[t] = i == tid ? v0[t] : reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
 #pragma unroll
       for (int t = 0; t < kMaxBatch; ++t) {
         if (t >= B) break;
-        const float inv_f = (float)inv[t];
-        const uint4 v = s_x[t * n8 + i];
-        uint32_t q[4] = {v.x, v.y, v.z, v.w};
+        s_x[t * n8 + i] = v[t];
+        if (norm_here) {
+          const uint32_t q[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv[t]);
-          const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv[t]);
-          q[j] = lo | (hi << 16);
+          for (int j = 0; j < 4; ++j) {
+            const double lo = bf16_to_f32(q[j] & 0xffffu), hi = bf16_to_f32(q[j] >> 16);
+            ss[t] = fma(lo, lo, fma(hi, hi, ss[t]));
+          }
         }
-        const uint4 o = make_uint4(q[0], q[1], q[2], q[3]);
-        s_x[t * n8 + i] = o;
-        if (blockIdx.x == 0) reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = o;
+      }
+    }
+    if (norm_here) {
+#pragma unroll
+      for (int t = 0; t < kMaxBatch; ++t) {
+        if (t >= B) break;
+        const double v = group_sum_f64(ss[t], kWave);
+        if (lane == 0) s_ss[wave][t] = v;
       }
     }
     __syncthreads();
+
+    // 2. pre-norm in LDS: xn = BF16(x * inv * gain)
+    if (norm_here) {
+      // one thread per token forms 1/sqrt(mean(x^2) + eps) in FP64
+      if (tid < B) {
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kRouterWaves; ++w) tot += s_ss[w][tid];
+        s_ss[0][tid] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+      }
+      __syncthreads();
+      double inv[kMaxBatch];
+#pragma unroll
+      for (int t = 0; t < kMaxBatch; ++t) inv[t] = t < B ? s_ss[0][t] : 1.0;
+      for (int i = tid; i < n8; i += kRouterThreads) {
+        const uint4 gv = i == tid ? g0 : reinterpret_cast<const uint4 *>(a.norm_gain)[i];
+        const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int t = 0; t < kMaxBatch; ++t) {
+          if (t >= B) break;
+          const float inv_f = (float)inv[t];
+          const uint4 o = norm_piece_bf16(s_x[t * n8 + i], gv, inv_f, inv[t]);
+          s_x[t * n8 + i] = o;
+          if (blockIdx.x == 0) reinterpret_cast<uint4 *>(a.ws.xn + (int64_t)t * H)[i] = o;
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // 3. router row x every token
@@ -731,112 +789,130 @@ __device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int6
   return *reinterpret_cast<const uint16_t *>(m + N * K / 2 + ((int64_t)(n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2);
 }
 
-// Gate/up: block = (entry slot, 64-row group); the 8 waves split K.
+// Gate/up of a batch.  With routed experts every block first derives the
+// routing from the logits (one wave per token: the top-k, then the sorted
+// list of distinct experts), so no separate routing stage runs between the
+// router kernel and this one; block 0 also publishes the list, the combine
+// weights and the top-k outputs for the down kernel.  Work items are
+// (entry, 64-row group) pairs, the shared expert's first (they need no
+// routing), then the distinct selected experts'; blocks take items in
+// turn.  Per item the 8 waves split K and meet in LDS.
 __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
-  __shared__ float s_red[kMmWaves][32][kWave];
+  __shared__ float s_red[kMmWaves][32][kWave];  // before the first item: the logits and marks of the routing
+  __shared__ Routing R;
   const int H = a.H, B = a.B, C = H / 32;
   const int Imax = a.I > a.Is ? a.I : a.Is;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int r16 = lane & 15, p = lane >> 4;
   const int groups = (Imax + kMmRows - 1) / kMmRows;
-  const int slot = blockIdx.x / groups, row0 = (blockIdx.x % groups) * kMmRows;
-  const uint8_t *Wg, *Wu;
-  float Sg, Su;
-  uint32_t mask;
-  int N;
-  if (slot < a.max_routed) {
-    // the count and this slot's entry are read together (the entry arrays
-    // hold max_routed slots)
-    const int n_routed = *a.ws.n_routed;
-    const int e = a.ws.entry_expert[slot];
-    mask = a.ws.entry_mask[slot];
-    if (slot >= n_routed) return;
-    N = a.I;
-    const int64_t mb = nvfp4_matrix_bytes(a.I, H);
-    Wg = a.w_gate + e * mb;
-    Wu = a.w_up + e * mb;
-    Sg = a.w_scale[3 * e + 0];
-    Su = a.w_scale[3 * e + 1];
-  } else {
-    if (row0 >= a.Is) return;  // also: no shared expert
-    mask = (1u << B) - 1u;
-    N = a.Is;
-    Wg = a.sh_gate;
-    Wu = a.sh_up;
-    Sg = a.sh_scale[0];
-    Su = a.sh_scale[1];
+  const int sh_groups = a.Is > 0 ? (a.Is + kMmRows - 1) / kMmRows : 0;
+  int n_items = sh_groups;
+  if (a.E > 0) {
+    float *s_l = &s_red[0][0][0];                                   // [B][E] <= 32 KiB
+    uint32_t *s_mark = reinterpret_cast<uint32_t *>(s_l + B * a.E);  // [E] <= 4 KiB
+    for (int i = tid; i < B * a.E; i += kMmWaves * kWave) s_l[i] = a.ws.logits[i];
+    build_routing(a, s_l, R, s_mark, kMmWaves);  // ends with a barrier
+    if (blockIdx.x == 0) publish_routing(a, R);
+    n_items += R.n * groups;
   }
-  if (row0 >= N) return;
   const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
-
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int SS = (C + 3) / 4;
-  // Two super-steps per pass, all their loads issued before any math, in
-  // the order the math consumes them (tokens, then row group by row group).
-  for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
-    uint4 qg[2][4], qu[2][4], xv[2][4];
-    uint32_t sg[2][4], su[2][4];
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int ss = ss0 + v * kMmWaves;
-      const int c = ss * 4 + p;
-      const bool cok = ss < SS && c < C;
-      const bool tok = cok && r16 < B;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xv[v][s] = tok ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * H + c * 32 + s * 8)
-                       : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n = row0 + rg * 16 + r16;
-        const bool ok = cok && n < N;
-        qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
-        qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
-      }
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const bool shared = item < sh_groups;
+    const int slot = shared ? a.max_routed : (item - sh_groups) / groups;
+    const int row0 = (shared ? item : (item - sh_groups) % groups) * kMmRows;
+    const uint8_t *Wg, *Wu;
+    float Sg, Su;
+    uint32_t mask;
+    int N;
+    if (!shared) {
+      const int e = R.expert[slot];
+      mask = R.mask[slot];
+      N = a.I;
+      const int64_t mb = nvfp4_matrix_bytes(a.I, H);
+      Wg = a.w_gate + e * mb;
+      Wu = a.w_up + e * mb;
+      Sg = a.w_scale[3 * e + 0];
+      Su = a.w_scale[3 * e + 1];
+    } else {
+      mask = (1u << B) - 1u;
+      N = a.Is;
+      Wg = a.sh_gate;
+      Wu = a.sh_up;
+      Sg = a.sh_scale[0];
+      Su = a.sh_scale[1];
     }
+    if (row0 >= N) continue;  // block-uniform
+
+    f32x4 acc[4][2];
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int SS = (C + 3) / 4;
+    // Two super-steps per pass, all their loads issued before any math, in
+    // the order the math consumes them (tokens, then row group by row group).
+    for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
+      uint4 qg[2][4], qu[2][4], xv[2][4];
+      uint32_t sg[2][4], su[2][4];
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
+      for (int v = 0; v < 2; ++v) {
+        const int ss = ss0 + v * kMmWaves;
+        const int c = ss * 4 + p;
+        const bool cok = ss < SS && c < C;
+        const bool tok = cok && r16 < B;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
-          const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
-          const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
-          acc[rg][0] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
-          acc[rg][1] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
+        for (int s = 0; s < 4; ++s)
+          xv[v][s] = tok ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * H + c * 32 + s * 8)
+                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = row0 + rg * 16 + r16;
+          const bool ok = cok && n < N;
+          qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+          sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
+          qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
+          su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
         }
       }
-  }
-  // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
-      s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
+        for (int rg = 0; rg < 4; ++rg) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
+            const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
+            const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
+            acc[rg][0] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
+            acc[rg][1] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
+          }
+        }
     }
-  __syncthreads();
+    // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
+    __syncthreads();  // the routing's logits, or the previous item's sums, are no longer read
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
-    const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-    float g = 0.f, u = 0.f;
+    for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
-    for (int w = 0; w < kMmWaves; ++w) {
-      g += s_red[w][rg * 8 + i][l];
-      u += s_red[w][rg * 8 + 4 + i][l];
-    }
-    const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
-    if (t < B && n < N && ((mask >> t) & 1u)) {
-      const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
-      a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
+      for (int i = 0; i < 4; ++i) {
+        s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
+        s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
+      const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMmWaves; ++w) {
+        g += s_red[w][rg * 8 + i][l];
+        u += s_red[w][rg * 8 + 4 + i][l];
+      }
+      const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
+      if (t < B && n < N && ((mask >> t) & 1u)) {
+        const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
+        a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
+      }
     }
   }
 }
@@ -1243,28 +1319,16 @@ __device__ inline void stage_token(const DecodeArgs &a, uint4 *s_x, double *s_re
   const float inv_f = (float)inv;
   for (int i = tid; i < n8; i += blockDim.x) {
     const uint4 gv = i == tid ? g0 : gr[i];
-    const uint4 v = s_x[i];
-    uint32_t q[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = norm_elem_bf16(bf16_to_f32(q[j] & 0xffffu), bf16_to_f32(g[j] & 0xffffu), inv_f, inv);
-      const uint32_t hi = norm_elem_bf16(bf16_to_f32(q[j] >> 16), bf16_to_f32(g[j] >> 16), inv_f, inv);
-      q[j] = lo | (hi << 16);
-    }
-    s_x[i] = make_uint4(q[0], q[1], q[2], q[3]);
+    s_x[i] = norm_piece_bf16(s_x[i], gv, inv_f, inv);
   }
   __syncthreads();
 }
 
 // This thread's first pieces of x and of the gain.
 __device__ __forceinline__ void first_pieces(const DecodeArgs &a, uint4 &x0, uint4 &g0) {
-  const int tid = threadIdx.x;
-  x0 = g0 = make_uint4(0, 0, 0, 0);
-  if (tid < a.H / 8) {
-    x0 = reinterpret_cast<const uint4 *>(a.x)[tid];
-    if (a.use_norm) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
-  }
+  const int tc = min((int)threadIdx.x, a.H / 8 - 1);  // clamped: unconditional loads
+  x0 = reinterpret_cast<const uint4 *>(a.x)[tc];
+  g0 = a.use_norm ? reinterpret_cast<const uint4 *>(a.norm_gain)[tc] : make_uint4(0, 0, 0, 0);
 }
 
 // Router rows of block rb: one row per lane group of LPR lanes (lane j of
@@ -1276,18 +1340,23 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
   const int row = (rb * kRouterWaves + wave) * (kWave / LPR) + lane / LPR;
   const uint4 *wr = reinterpret_cast<const uint4 *>(a.router_w + (int64_t)(row < E ? row : 0) * H);
-  // Loads in the order they are needed (they complete in issue order):
-  // the token, then the row's first four pieces, the gain and the bias.
-  uint4 x0 = make_uint4(0, 0, 0, 0), g0 = make_uint4(0, 0, 0, 0);
-  if (tid < n8) x0 = reinterpret_cast<const uint4 *>(a.x)[tid];
+  // Loads in the order they are needed (they complete in issue order): the
+  // token and the gain (cache hits: the norm starts as soon as they land),
+  // then the row's first four pieces and the bias, which come from memory
+  // while the norm runs.
+  // (indices clamped into the buffers: every load is unconditional, so the
+  // waits before the norm cover the token and the gain only)
+  const int tc = tid < n8 ? tid : n8 - 1;
+  uint4 x0 = reinterpret_cast<const uint4 *>(a.x)[tc], g0 = make_uint4(0, 0, 0, 0);
+  if (a.use_norm) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tc];
   uint4 w0[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = lg + i * LPR;
-    w0[i] = (row < E && j < n8) ? wr[j] : make_uint4(0, 0, 0, 0);
-  }
-  if (a.use_norm && tid < n8) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tid];
-  const float bias = (a.router_b && row < E) ? a.router_b[row] : 0.f;
+  for (int i = 0; i < 4; ++i) w0[i] = wr[min(lg + i * LPR, n8 - 1)];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (!(row < E && lg + i * LPR < n8)) w0[i] = make_uint4(0, 0, 0, 0);
+  float bias = a.router_b ? a.router_b[row < E ? row : E - 1] : 0.f;
+  if (row >= E) bias = 0.f;
   stage_token(a, s_x, s_red, x0, g0);
   if (row >= E) return;
   float acc = 0.f;
@@ -1634,13 +1703,19 @@ static hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, size_t 
   return hipGetLastError();
 }
 
+// Blocks of k_gateup_mm: at most one per compute unit (8 waves of over 200
+// registers each fill one), each taking work items in turn.
+constexpr int kMmGateupBlocks = 256;
+
 template <int WT, int MAXT>
 static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {
   hipError_t e;
   if (WT == 1 && MAXT > 1) {
     const int Imax = a.I > a.Is ? a.I : a.Is;
     const int groups = (Imax + kMmRows - 1) / kMmRows;
-    if ((e = launch(k_gateup_mm, dim3((a.max_routed + 1) * groups), dim3(kMmWaves * kWave), 0, stream,
+    const int items = a.max_routed * groups + (a.Is + kMmRows - 1) / kMmRows;
+    const int grid = items < kMmGateupBlocks ? items : kMmGateupBlocks;
+    if ((e = launch(k_gateup_mm, dim3(grid), dim3(kMmWaves * kWave), 0, stream,
                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a)) != hipSuccess)
       return e;
     return launch(k_down_mm, dim3(a.H / 8), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
@@ -1698,8 +1773,23 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
   // measurement, eager launches only).
   hipError_t e;
   if (a.B == 1 && a.E > 0) return a.wtype == 1 ? launch_layer_b1<1>(a, stream, ev) : launch_layer_b1<0>(a, stream, ev);
-  // Batches of several tokens normalise once in k_norm; a single token
-  // normalises inside the router blocks (one launch fewer).
+  // NVFP4 batches with routed experts: three kernels.  The router blocks
+  // normalise the batch themselves (block 0 also stores xn) and store plain
+  // logits; the gate/up blocks derive the routing from them.
+  if (a.wtype == 1 && a.B > 1 && a.E > 0) {
+    const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
+    if ((e = launch(k_router<kRouterWaves>, dim3((a.E + rows_per_block - 1) / rows_per_block),
+                    dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, a, 0, 0)) !=
+        hipSuccess)
+      return e;
+    switch (a.B <= 2 ? 2 : a.B <= 4 ? 4 : 8) {
+      case 2: return launch_experts<1, 2>(a, stream, ev);
+      case 4: return launch_experts<1, 4>(a, stream, ev);
+      default: return launch_experts<1, 8>(a, stream, ev);
+    }
+  }
+  // Other batches of several tokens normalise once in k_norm; a single
+  // token normalises inside the router blocks (one launch fewer).
   const int xn_ready = (a.use_norm && a.B > 1) ? 1 : 0;
   if (xn_ready) {
     if ((e = launch(k_norm, dim3(a.B), dim3(kNormThreads), 0, stream, nullptr, nullptr, a)) != hipSuccess) return e;

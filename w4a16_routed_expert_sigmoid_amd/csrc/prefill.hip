@@ -159,15 +159,7 @@ __global__ __launch_bounds__(PThreads) void k_pf_norm(PrefillArgs a) {
   for (int i = lane * 8; i < a.H; i += 64 * 8) {
     const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
     const uint4 g = *reinterpret_cast<const uint4 *>(a.norm_gain + i);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = norm_elem_bf16(bf16_to_f32(w[q] & 0xffffu), bf16_to_f32(gw[q] & 0xffffu), inv_f, inv);
-      const uint32_t hi = norm_elem_bf16(bf16_to_f32(w[q] >> 16), bf16_to_f32(gw[q] >> 16), inv_f, inv);
-      o[q] = lo | (hi << 16);
-    }
-    *reinterpret_cast<uint4 *>(a.xn + (int64_t)t * a.H + i) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(a.xn + (int64_t)t * a.H + i) = norm_piece_bf16(v, g, inv_f, inv);
   }
 }
 
