@@ -99,8 +99,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill leg")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight leg")
     p.add_argument("--no-gemv", action="store_true", help="skip the dense-projection leg")
+    p.add_argument("--no-mid", action="store_true", help="skip the 16..256-token leg")
     p.add_argument("--copy-probe", action="store_true",
-                   help="also run a 1 GiB streaming read (counter calibration under rocprofv3 --pmc)")
+                   help="also run a 1 GiB streaming read and a 1 GiB copy (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
 
 
@@ -340,8 +341,6 @@ def run(args, dev):
     warn = []
     if pf is not None and pf["nonfinite"]:
         warn.append("non-finite outputs")
-    if any(v.get("nonfinite") for v in configs.get("dense_gemv_nvfp4", {}).values()):
-        warn.append("non-finite outputs")
     r1 = None
     if args.workload == "layer":
         descs = [mdesc] * len(pool)
@@ -352,8 +351,10 @@ def run(args, dev):
         for r in (r1, r8):
             if r["nonfinite"]:
                 warn.append("non-finite outputs")
+    if args.workload == "layer" and not args.no_mid:
+        configs["mid_batch_nvfp4_zipf"] = run_mid_batch(args, dev, pool, mdesc, zipf, ceil_gbs)
     # the model's decode step: 2 dense layers, then 47 MoE layers
-    step_pool = [d.t for d in dense] + pool[:47]
+    step_pool = [d.t for d in dense] + [pool[i % len(pool)] for i in range(47)]
     step_descs = [d.desc for d in dense] + [mdesc] * 47
     r49 = time_stack(args, dev, step_pool, step_descs, 1, None, "49-layer step batch 1")
     s49 = summary(r49, 49, 1, extra=2 * DENSE_BYTES + 49 * H * 2)   # + the 49 RMSNorm gains
@@ -384,10 +385,15 @@ def run(args, dev):
         torch.cuda.empty_cache()
 
     if args.copy_probe:
+        # known sizes for scaling the traffic counters: a 1 GiB streaming
+        # read, then a 1 GiB device copy (1 GiB read + 1 GiB written)
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         moe.moe_probe_hbm_read(a, a.numel(), 2048, sink)
+        b = torch.empty_like(a)
+        b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     # batch 1: one kernel per layer (router, gate/up and down of the 6
     # selected experts and the shared expert)
@@ -410,6 +416,9 @@ def run(args, dev):
     else:
         workload = ("decode step of the MoE stack, batch 1: 2 dense SwiGLU (intermediate 5632) + 47 NVFP4 MoE "
                     "layers, RMSNorm before each, independent seeded weights, one HIP graph")
+    if any(v.get("nonfinite") for k in ("dense_gemv_nvfp4", "mid_batch_nvfp4_zipf")
+           for v in configs.get(k, {}).values()):
+        warn.append("non-finite outputs")
     gbs1 = head["GBps"]
     wait = max(c.get("wait_status", 0) for c in configs.values() if isinstance(c, dict))
     if wait:
@@ -445,9 +454,60 @@ def run(args, dev):
     return out
 
 
+def run_mid_batch(args, dev, pool, desc, zipf, ceil_gbs):
+    """Batches between the decode path and the long prefill: T tokens
+    through moe_prefill_layer on the full NVFP4 layer with the Zipf-biased
+    router, one call per layer copy, replayed as one HIP graph over enough
+    copies that the selected weights stream from HBM."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    out = {}
+    for T in (16, 32, 64, 128, 256):
+        x = torch.from_numpy(synth.tokens(T, H, stream=3000 + T).view(np.int16)).to(dev)
+        y = torch.empty_like(x)
+        idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        ws = torch.zeros(moe.moe_prefill_workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
+        wts = [weights_of(moe, t, zipf) for t in pool]
+        moe.moe_prefill_layer(desc, wts[0], x, T, 0, y, idx, w, ws, ws.numel())
+        torch.cuda.synchronize()
+        distinct = len(np.unique(idx.cpu().numpy()))
+        per_call = selected_bytes(distinct)
+        n = int(min(len(wts), max(8, -(-(2 << 30) // per_call))))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                moe.moe_prefill_layer(desc, wts[i], x, T, 0, y, idx, w, ws, ws.numel())
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        gbs = per_call / (us * 1e-6) / 1e9
+        out[f"T{T}"] = {"us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+                        "distinct_experts": distinct, "selected_bytes": int(per_call), "GBps": round(gbs, 1),
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "stream_frac": round(gbs / ceil_gbs, 4),
+                        "tflops": round(prefill_flops(T) / (us * 1e-6) / 1e12, 1), "layer_calls_per_replay": n,
+                        "nonfinite": not torch.isfinite(y.view(torch.bfloat16).float()).all().item()}
+        log(f"mid batch T={T}: {us:.1f} us/layer, {distinct} distinct experts, {gbs:.0f} GB/s")
+        del ws, g
+    return out
+
+
 def run_gemv(args, dev):
     """The dense NVFP4 projection at batch 1 and 8 on an LM-head-sized
-    (131072 x 2048) and a fused-QKV-sized (3072 x 2048) matrix: device
+    (131072 x 2048) and a fused-QKV-sized (5120 x 2048: 32 query and 4 + 4
+    KV heads of 128) matrix: device
     copies of one repacked matrix, rotated so that one graph replay streams
     more than 1 GB of weights from HBM; GB/s on the weight bytes."""
     import numpy as np
@@ -457,7 +517,7 @@ def run_gemv(args, dev):
     import w4a16_routed_expert_sigmoid_amd as moe
 
     out = {}
-    for name, rows in (("lm_head_131072x2048", 131072), ("qkv_3072x2048", 3072)):
+    for name, rows in (("lm_head_131072x2048", 131072), ("qkv_5120x2048", 5120)):
         cols = H
         m, sc = synth.nvfp4_stack(4242, 0, 1, 1, rows, cols)
         src = torch.from_numpy(m.reshape(-1)).to(dev)

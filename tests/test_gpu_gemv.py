@@ -1,7 +1,8 @@
 """GPU parity of the dense NVFP4 projection (moe_gemv_nvfp4) against the
 CPU oracle, through the C ABI: shapes of the projections outside the MoE
-blocks (attention QKV and output, an LM-head slice; the widths are readings,
-the pages fix only the hidden size 2048) and ragged ones, batches 1..8."""
+blocks (attention QKV and output from 32 query and 4 KV heads of 128, an
+LM-head slice whose vocabulary the pages do not give) and ragged ones,
+batches 1..8."""
 import numpy as np
 import pytest
 import torch
@@ -28,8 +29,8 @@ def _matrix(rows, cols, seed):
 
 @pytest.mark.parametrize("rows,cols,B", [
     (8, 64, 1), (24, 128, 3), (264, 2112, 2),          # ragged: last block partly filled; 66 chunks per row
-    (3072, 2048, 1), (3072, 2048, 8),                  # fused QKV (16 query + 2x4 KV heads of 128)
-    (2048, 2048, 5),                                   # attention output
+    (5120, 2048, 1), (5120, 2048, 8),                  # fused QKV: (32 query + 4 + 4 KV heads) x 128
+    (2048, 4096, 5), (2048, 4096, 1),                  # attention output: 32 heads x 128 in
     (2048, 5632, 1), (5632, 2048, 4),                  # dense MLP shapes
     (16384, 2048, 1), (16384, 2048, 8),                # an LM-head slice
     (256, 4096, 8), (512, 5632, 3),                    # batch x cols above the LDS stage: x from memory

@@ -197,6 +197,8 @@ def full_layer(kind):
             _cache[kind] = synth.make_layer(0, wtype="nvfp4")
         elif kind == "dense":
             _cache[kind] = synth.make_layer(0, inter=0, shared_inter=5632, n_experts=0, norm=True, residual=True)
+        elif kind == "zipf":
+            _cache[kind] = synth.make_layer(0, wtype="nvfp4", bias="zipf")
     return _cache[kind]
 
 
@@ -233,4 +235,21 @@ def test_prefill_full_shape(kind, T):
     if E:
         counts = np.bincount(idx.reshape(-1), minlength=E)
         st["rows_per_expert_min_max"] = (int(counts.min()), int(counts.max()))
+    log(f"  {st}")
+
+
+@pytest.mark.parametrize("T", [9, 16, 32, 64, 128, 256])
+def test_mid_batch_full_shape(T):
+    # Between the decode path (up to 8 tokens) and the 8192-token prefill:
+    # the full NVFP4 layer with the Zipf-biased router (the skew of the
+    # batch-8 decode workload) through moe_prefill_layer, every token
+    # against the oracle.
+    log(f"test: mid batch full shape T={T}")
+    L = full_layer("zipf")
+    dev = moe.DeviceLayer(L)
+    x = synth.tokens(T, 2048, stream=950 + T)
+    out, idx, w = run(L, x, dev)
+    check_routing_properties(L, idx, w)
+    _, st = compare(L, x, out, idx, w, what=f"mid batch T={T}")
+    st["distinct"] = len(np.unique(idx))
     log(f"  {st}")
