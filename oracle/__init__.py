@@ -1,4 +1,5 @@
-"""CPU oracle of the W4A16 sigmoid-routed MoE layer (FP64, plain C).
+"""CPU oracle of the W4A16 sigmoid-routed MoE layer and of the decode
+attention beside it (FP64, plain C).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
 the CPU-baseline leg of the benchmark, never by the product package.  This
@@ -51,6 +52,12 @@ class _Layer(ctypes.Structure):
     ]
 
 
+class _Attn(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("rope", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+                ("norm_eps", ctypes.c_double)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -73,6 +80,12 @@ def lib():
         L.oracle_gemv_nvfp4.restype = ctypes.c_int64
         L.oracle_gemv_nvfp4.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.oracle_attn_prep.restype = None
+        L.oracle_attn_prep.argtypes = [ctypes.POINTER(_Attn), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_attn_decode.restype = None
+        L.oracle_attn_decode.argtypes = [ctypes.POINTER(_Attn), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_moe_tokens.restype = ctypes.c_int32
         L.oracle_moe_tokens.argtypes = [ctypes.POINTER(_Layer), ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -143,6 +156,50 @@ def gemv_nvfp4(src, rows, cols, tensor_scale, x):
     nan = lib().oracle_gemv_nvfp4(src.ctypes.data, rows, cols, float(tensor_scale), x.ctypes.data, x.shape[0],
                                   y.ctypes.data)
     return y, int(nan)
+
+
+def _attn(a):
+    return _Attn(n_q=a["n_q"], n_kv=a["n_kv"], head_dim=a["head_dim"], window=a.get("window", 0),
+                 rope=int(a.get("rope", 0)), rope_theta=float(a.get("rope_theta", 10000.0)),
+                 norm_eps=float(a.get("eps", np.float32(1e-6))))
+
+
+def attn_prep(a, qkv, pos, q_gain, k_gain):
+    """Q/K norm + RoPE of T tokens: qkv [T, (n_q + 2 n_kv) * D] BF16 bits,
+    pos [T] -> (q [T, n_q, D], k [T, n_kv, D], v [T, n_kv, D]) BF16 bits.
+    a: dict(n_q, n_kv, head_dim, window, rope, rope_theta, eps)."""
+    D, nq, nkv = a["head_dim"], a["n_q"], a["n_kv"]
+    qkv = np.ascontiguousarray(qkv, dtype=np.uint16).reshape(-1, (nq + 2 * nkv) * D)
+    T = qkv.shape[0]
+    qg = np.ascontiguousarray(q_gain, dtype=np.uint16)
+    kg = np.ascontiguousarray(k_gain, dtype=np.uint16)
+    q = np.empty((T, nq, D), np.uint16)
+    k = np.empty((T, nkv, D), np.uint16)
+    v = np.empty((T, nkv, D), np.uint16)
+    s = _attn(a)
+    for t in range(T):
+        lib().oracle_attn_prep(ctypes.byref(s), qkv[t].ctypes.data, int(pos[t]), qg.ctypes.data, kg.ctypes.data,
+                               q[t].ctypes.data, k[t].ctypes.data, v[t].ctypes.data)
+    return q, k, v
+
+
+def attn_decode(a, q, k_cache, v_cache, pos, sinks=None):
+    """Decode attention of T tokens: q [T, n_q, D] BF16 bits; k_cache,
+    v_cache [T, slots, n_kv, D] BF16 bits (one cache per token's sequence);
+    pos [T]; sinks [n_q] FP32 or None -> out [T, n_q, D] BF16 bits."""
+    D, nq = a["head_dim"], a["n_q"]
+    q = np.ascontiguousarray(q, dtype=np.uint16).reshape(-1, nq * D)
+    T = q.shape[0]
+    kc = np.ascontiguousarray(k_cache, dtype=np.uint16)
+    vc = np.ascontiguousarray(v_cache, dtype=np.uint16)
+    slots = kc.shape[1]
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float32)
+    out = np.empty((T, nq, D), np.uint16)
+    s = _attn(a)
+    for t in range(T):
+        lib().oracle_attn_decode(ctypes.byref(s), q[t].ctypes.data, kc[t].ctypes.data, vc[t].ctypes.data, slots,
+                                 int(pos[t]), None if sk is None else sk.ctypes.data, out[t].ctypes.data)
+    return out
 
 
 def _ptr(a):

@@ -19,6 +19,12 @@
  *     reference rounding.
  *   - "vLLM Flint" (English commentary), section "Only 14 of 49 layers
  *     retain full-history KV": 49 pre-norm layers, hidden size 2048.
+ *   - the same two pages on attention: 35 layers attend over a 513-token
+ *     sliding window with RoPE, 14 over the full context without positional
+ *     encoding; GQA with 32 query and 4 KV heads; per-head Q/K RMSNorm;
+ *     learned attention sinks; BF16 KV cache of 28 KiB per token over the
+ *     14 full layers (head_dim 128); the Q/K norm, RoPE and KV write are one
+ *     fused step, decode attention handles sinks and the window.
  * Readings where the pages are silent (rounding points, tie-break, router
  * bias, renormalisation, shared-expert weight, SwiGLU orientation, NVFP4
  * value, GGUF block byte order, RMSNorm form) are listed in the design notes
@@ -28,7 +34,10 @@
  * outside this file (format definitions and a library decoder, hand-worked
  * rounding ties, closed forms, top-k invariants, permutation equivariance,
  * a brute-force dense MoE with a one-hot gate, and NVFP4 == BF16 at
- * power-of-two tensor scales).
+ * power-of-two tensor scales); the attention functions against closed
+ * forms, rotations written as complex products, and torch's float64
+ * scaled-dot-product attention with GQA heads repeated, the window as a mask
+ * and the sink as an extra key.
  */
 #include <math.h>
 #include <pthread.h>
@@ -438,4 +447,114 @@ int32_t oracle_moe_tokens_mt(const oracle_layer *L, const uint16_t *x, int32_t T
   free(th);
   free(jobs);
   return bad;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* Attention of a decode token ("Day-0 Support for Flint on vLLM",     */
+/* sections "Model architecture" and "Optimizations")                  */
+/* ------------------------------------------------------------------ */
+
+/* Shape of one attention layer: GQA with n_q query heads and n_kv K/V
+ * heads of head_dim (query head h reads K/V head h / (n_q / n_kv)).
+ * window: 0 = the whole context; W = the last W positions, the current one
+ * included (the pages' 513-token sliding window).  rope: 1 = RoPE on q and
+ * k (the sliding-window layers), 0 = none (the full-context layers). */
+typedef struct {
+  int32_t n_q, n_kv, head_dim, window, rope;
+  double rope_theta, norm_eps;
+} oracle_attn;
+
+/* Per-head RMSNorm with a gain shared by the heads, rounded once:
+ * out_d = BF16(x_d / sqrt(mean(x^2) + eps) * g_d). */
+static void head_rmsnorm(const double *x, const uint16_t *g, int32_t D, double eps, double *out) {
+  double ss = 0.0;
+  for (int32_t d = 0; d < D; ++d) ss += x[d] * x[d];
+  double inv = 1.0 / sqrt(ss / (double)D + eps);
+  for (int32_t d = 0; d < D; ++d) out[d] = bf16r(x[d] * inv * oracle_bf16_value(g[d]));
+}
+
+/* RoPE, rotate-half form (a reading: the pages say only "RoPE"): element d
+ * < D/2 pairs with d + D/2, rotated by the angle pos * theta^(-2d/D):
+ *   (a, b) -> BF16(a cos - b sin), BF16(b cos + a sin). */
+static void head_rope(double *x, int32_t D, int64_t pos, double theta) {
+  for (int32_t d = 0; d < D / 2; ++d) {
+    double ang = (double)pos * pow(theta, -2.0 * (double)d / (double)D);
+    double c = cos(ang), sn = sin(ang);
+    double a = x[d], b = x[d + D / 2];
+    x[d] = bf16r(a * c - b * sn);
+    x[d + D / 2] = bf16r(b * c + a * sn);
+  }
+}
+
+/* Q/K norm, RoPE and the K/V to be cached, for one token.
+ *  qkv [(n_q + 2 n_kv) * D] BF16: q heads, then k heads, then v heads.
+ *  q_out [n_q * D], k_out [n_kv * D], v_out [n_kv * D] BF16.
+ * q and k: per-head RMSNorm with q_gain / k_gain [D], then RoPE at pos
+ * when the layer has it; v is stored as given. */
+void oracle_attn_prep(const oracle_attn *A, const uint16_t *qkv, int64_t pos, const uint16_t *q_gain,
+                      const uint16_t *k_gain, uint16_t *q_out, uint16_t *k_out, uint16_t *v_out) {
+  const int32_t D = A->head_dim;
+  double *x = (double *)malloc(sizeof(double) * (size_t)D);
+  double *y = (double *)malloc(sizeof(double) * (size_t)D);
+  for (int32_t h = 0; h < A->n_q + A->n_kv; ++h) {
+    const int q = h < A->n_q;
+    const uint16_t *src = qkv + (int64_t)h * D;
+    for (int32_t d = 0; d < D; ++d) x[d] = oracle_bf16_value(src[d]);
+    head_rmsnorm(x, q ? q_gain : k_gain, D, A->norm_eps, y);
+    if (A->rope) head_rope(y, D, pos, A->rope_theta);
+    uint16_t *dst = q ? q_out + (int64_t)h * D : k_out + (int64_t)(h - A->n_q) * D;
+    for (int32_t d = 0; d < D; ++d) dst[d] = oracle_bf16_round(y[d]);
+  }
+  for (int64_t i = 0; i < (int64_t)A->n_kv * D; ++i) v_out[i] = qkv[(int64_t)(A->n_q + A->n_kv) * D + i];
+  free(y);
+  free(x);
+}
+
+/* Decode attention of one token at position pos over its cache.
+ *  q [n_q * D] BF16 (normed, roped);
+ *  k_cache, v_cache [slots][n_kv][D] BF16; position p lives in slot
+ *  p % slots (slots >= the positions attended: the whole context for a
+ *  full layer, at least the window for a sliding one);
+ *  sinks [n_q] FP32 learned logits, or NULL (none);
+ *  out [n_q * D] BF16.
+ * Per query head h (K/V head g = h / (n_q / n_kv)), over the positions
+ * lo..pos, lo = 0 or pos - window + 1 (not below 0):
+ *   s_i = (q_h . k_i) / sqrt(D),  m = max(max_i s_i, sink_h),
+ *   out = BF16( sum_i e^(s_i - m) v_i / (sum_i e^(s_i - m) + e^(sink_h - m)) ),
+ * the sink taking part in the normalisation only (a reading of "learned
+ * attention sinks"). */
+void oracle_attn_decode(const oracle_attn *A, const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                        int64_t slots, int64_t pos, const float *sinks, uint16_t *out) {
+  const int32_t D = A->head_dim, G = A->n_q / A->n_kv;
+  int64_t lo = 0;
+  if (A->window > 0 && pos - A->window + 1 > 0) lo = pos - A->window + 1;
+  const int64_t n = pos - lo + 1;
+  double *s = (double *)malloc(sizeof(double) * (size_t)n);
+  double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+  const double scale = 1.0 / sqrt((double)D);
+  for (int32_t h = 0; h < A->n_q; ++h) {
+    const int32_t g = h / G;
+    double m = sinks ? (double)sinks[h] : -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t slot = (lo + i) % slots;
+      const uint16_t *k = k_cache + (slot * A->n_kv + g) * D;
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += oracle_bf16_value(q[(int64_t)h * D + d]) * oracle_bf16_value(k[d]);
+      s[i] = dot * scale;
+      if (s[i] > m) m = s[i];
+    }
+    double den = sinks ? exp((double)sinks[h] - m) : 0.0;
+    for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t slot = (lo + i) % slots;
+      const uint16_t *v = v_cache + (slot * A->n_kv + g) * D;
+      const double p = exp(s[i] - m);
+      den += p;
+      for (int32_t d = 0; d < D; ++d) acc[d] += p * oracle_bf16_value(v[d]);
+    }
+    for (int32_t d = 0; d < D; ++d) out[(int64_t)h * D + d] = oracle_bf16_round(acc[d] / den);
+  }
+  free(acc);
+  free(s);
 }
