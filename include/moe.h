@@ -242,14 +242,15 @@ moe_status moe_decode_layer_timed(const moe_layer_desc *desc, const moe_layer_we
                                   int32_t batch, int32_t residual, void *y, int32_t *topk_idx, float *topk_w,
                                   void *ws, size_t ws_bytes, void *const *events, void *stream);
 
-/* Health of the last moe_decode_layer or moe_decode_step call on a
- * workspace.  The blocks of one kernel hand the router logits and the
- * SwiGLU intermediate to each other through memory, each wait bounded (a
- * wait that never ends would hang the GPU).  A wait that runs out of polls
- * ORs a bit into a status word at the start of the workspace, which every
- * call zeroes first: 1 = the logits, 2 = the intermediate, 4 = the logits of
- * a batch's routing block.  A non-zero word means that call's outputs must
- * not be used.  This enqueues a copy of the word into status_out (device
+/* Health of the last moe_decode_layer, moe_decode_step or moe_attn_decode
+ * call on a workspace.  The blocks of one MoE kernel hand the router logits
+ * and the SwiGLU intermediate to each other through memory, each wait
+ * bounded (a wait that never ends would hang the GPU).  A wait that runs
+ * out of polls ORs a bit into a status word at the start of the workspace,
+ * which every call zeroes first: 1 = the logits, 2 = the intermediate, 4 =
+ * the logits of a batch's routing block.  moe_attn_decode writes bit 8 there
+ * (a position out of range).  A non-zero word means that call's outputs
+ * must not be used.  This enqueues a copy of the word into status_out (device
  * int32) on `stream`, after the calls enqueued before it.  ws == NULL: the
  * workspace of moe_decode_layer_noalloc on the current device.
  * Errors: INVALID_ARG for a null status_out or misaligned pointers; HIP. */
@@ -298,6 +299,102 @@ moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_w
 moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
 moe_status moe_check_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
                                 int32_t batch, const void *y);
+
+/* ------------------------------------------------------------------
+ * Decode attention beside the MoE blocks ("Day-0 Support for Flint on
+ * vLLM", sections "Model architecture" and "Optimizations"; "vLLM Flint"
+ * commentary, section "Only 14 of 49 layers retain full-history KV"):
+ * GQA with n_q query heads and n_kv K/V heads of 128 (32 and 4 in the
+ * model), per-head Q/K RMSNorm, learned attention sinks, BF16 KV cache;
+ * sliding-window layers (513 positions, RoPE) and full-context layers (no
+ * positional encoding).  The Q/K norm, RoPE and KV write are one kernel
+ * (moe_attn_prep); decode attention is moe_attn_decode.
+ *
+ * Caches (caller-owned device memory, one per layer, `slots` positions per
+ * token row; position p lives in slot p % slots, so a window layer keeps a
+ * ring and a full-context layer needs slots > every position):
+ *   k_cache [batch][n_kv][slots][128] BF16  (a key row per slot)
+ *   v_cache [batch][n_kv][128][slots] BF16  (values stored transposed: row
+ *                                            d holds element d of every slot)
+ * Positions `pos` are device int64 [batch] (graph replays may change them),
+ * 0 .. 2^40 - 1.
+ * ------------------------------------------------------------------ */
+typedef struct moe_attn_desc {
+  int32_t n_q;        /* query heads; n_q % n_kv == 0 and n_q / n_kv <= 16 */
+  int32_t n_kv;       /* K/V heads, >= 1 */
+  int32_t head_dim;   /* 128 (the only supported value) */
+  int32_t window;     /* 0: full context; W > 0: the last W positions, the
+                         current one included; W <= slots */
+  int32_t rope;       /* 1: RoPE on q and k at the token's position, 0: none */
+  int32_t slots;      /* cache positions per token row, a multiple of 32 */
+  double rope_theta;  /* RoPE base (> 1) when rope == 1 */
+  float norm_eps;     /* per-head RMSNorm epsilon, >= 0 */
+} moe_attn_desc;
+
+/* Q/K norm, RoPE and KV-cache write for `batch` decode tokens (1..256).
+ * For token t at position p = pos[t], with D = 128 and the head vectors of
+ * qkv[t] = [q heads (n_q x D) | k heads (n_kv x D) | v heads (n_kv x D)]:
+ *   q', k' = per head BF16(x / sqrt(mean(x^2) + eps) * gain)   (q_gain for
+ *            q heads, k_gain for k heads; one gain of D shared by the heads)
+ *   with rope: element d < D/2 pairs with d + D/2, rotated by the angle
+ *            p * theta^(-2d/D): (a, b) -> (BF16(a cos - b sin), BF16(b cos + a sin))
+ *   q_out[t] = q' ([n_q][D]); k' and v go to slot p % slots of token row t
+ *   of k_cache and v_cache (layouts above).
+ *  qkv [batch][(n_q + 2 n_kv) * 128] BF16; q_gain, k_gain [128] BF16;
+ *  q_out [batch][n_q][128] BF16; all device, 16-byte aligned.
+ * A token whose position is negative, at least 2^40, or not below `slots`
+ * in a full-context layer writes nothing to the caches and zeros to q_out.
+ * Errors: INVALID_ARG for null or misaligned pointers, batch outside
+ * 1..256, a bad description, q_out sharing a byte with an input or a
+ * cache; UNSUPPORTED for head_dim != 128 or n_q / n_kv > 16; HIP. */
+moe_status moe_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                         const void *q_gain, const void *k_gain, void *q_out, void *k_cache, void *v_cache,
+                         void *stream);
+
+/* Workspace bytes moe_attn_decode needs for `batch` tokens attending at
+ * most max_ctx positions each (0: the layer's bound, window or slots), or 0
+ * for invalid arguments.  256 bytes (the status word's line) plus, when the
+ * context is long enough to be split over several blocks per head, FP32
+ * partial results: batch * n_kv * chunks * (G * 128 + 2 G rounded up to 4)
+ * * 4 bytes, G = n_q / n_kv (about 1 MB at one token and 100K positions). */
+size_t moe_attn_workspace_bytes(const moe_attn_desc *desc, int32_t batch, int64_t max_ctx);
+
+/* Decode attention of `batch` tokens (1..256) over their caches.  For token
+ * t at p = pos[t] and query head h (K/V head g = h / (n_q / n_kv)), over
+ * the positions i = lo..p (lo = 0, or p - W + 1 floored at 0 with a window)
+ * read from slot i % slots:
+ *   s_i = q[t][h] . k_i / sqrt(128),  m = max(s_i, sink_h),
+ *   out[t][h] = BF16( sum_i e^(s_i - m) v_i / (sum_i e^(s_i - m) + e^(sink_h - m)) )
+ * with sink_h = sinks[h] (a logit that joins the normalisation and
+ * contributes no value), or no sink term when sinks == NULL.  FP32
+ * arithmetic on the matrix cores (scores and probabilities times values),
+ * one BF16 rounding.
+ *  q [batch][n_q][128] BF16 (from moe_attn_prep); caches as above;
+ *  sinks [n_q] FP32 or NULL; out [batch][n_q][128] BF16; all device.
+ *  max_ctx: the most positions any token attends (p + 1, or W with a
+ *  window), 0 = the layer's bound; it sizes the grid; a smaller bound
+ *  shortens calls at short contexts.
+ *  ws: device workspace of ws_bytes >= moe_attn_workspace_bytes(desc,
+ *  batch, max_ctx), 256-byte aligned, no zero-fill needed.  Its first word
+ *  is the call's status: bit 8 = a token's position was out of range (as for
+ *  moe_attn_prep) or attends more than max_ctx positions
+ *  (its output rows are zero); moe_decode_wait_status reads it.
+ * Errors: INVALID_ARG for null or misaligned pointers, a bad description,
+ * batch outside 1..256, max_ctx < 0 or above the layer's bound, out sharing
+ * a byte with an input, a cache or ws; UNSUPPORTED as moe_attn_prep;
+ * WORKSPACE; HIP. */
+moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                           const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Host-side validation alone of moe_attn_prep and moe_attn_decode, as for
+ * the calls above. */
+moe_status moe_check_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                               const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
+                               const void *v_cache);
+moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,
+                                 const void *v_cache, const int64_t *pos, int32_t batch, int64_t max_ctx,
+                                 const float *sinks, const void *out, const void *ws, size_t ws_bytes);
 
 /* Measurement: reads `bytes` (a multiple of 16) of device memory at src
  * once, streaming, with `blocks` blocks of 256 threads (grid-stride, four

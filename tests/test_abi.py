@@ -31,6 +31,11 @@ class Desc(ctypes.Structure):
                 ("top_k", _i32), ("wtype", _i32), ("norm_eps", ctypes.c_float)]
 
 
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("n_q", _i32), ("n_kv", _i32), ("head_dim", _i32), ("window", _i32), ("rope", _i32),
+                ("slots", _i32), ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_float)]
+
+
 class Weights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("router_w", "router_b", "w_gate", "w_up", "w_down", "w_scale", "sh_gate", "sh_up",
                                    "sh_down", "sh_scale", "norm_gain")]
@@ -58,6 +63,13 @@ def _declare(lib):
     lib.moe_nvfp4_matrix_bytes.argtypes = [_i64, _i64]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [_i32]
+    AD = ctypes.POINTER(AttnDesc)
+    lib.moe_check_attn_prep.restype = _i32
+    lib.moe_check_attn_prep.argtypes = [AD, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.moe_check_attn_decode.restype = _i32
+    lib.moe_check_attn_decode.argtypes = [AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz]
+    lib.moe_attn_workspace_bytes.restype = _sz
+    lib.moe_attn_workspace_bytes.argtypes = [AD, _i32, _i64]
     return lib
 
 
@@ -126,7 +138,8 @@ def test_host_library_needs_no_hip_runtime():
     lib = host()
     for n in ("moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
               "moe_check_repack_nvfp4", "moe_decode_workspace_bytes", "moe_decode_step_workspace_bytes",
-              "moe_prefill_workspace_bytes", "moe_nvfp4_matrix_bytes", "moe_status_string"):
+              "moe_prefill_workspace_bytes", "moe_nvfp4_matrix_bytes", "moe_status_string",
+              "moe_check_attn_prep", "moe_check_attn_decode", "moe_attn_workspace_bytes"):
         assert hasattr(lib, n), n
     with open("/proc/self/maps") as f:
         maps = f.read()
@@ -409,3 +422,102 @@ def test_gemv_valid_call_passes_validation():
 ])
 def test_gemv_errors(which, kw, want):
     assert gemv(which, **kw) == want
+
+
+# ---------------------------------------------------------------- attention
+
+# Caches far apart from everything else (the full-context case is ~1 GB).
+KC, VC = P + (1 << 36), P + (2 << 36)
+
+
+def adesc(**kw):
+    d = dict(n_q=32, n_kv=4, head_dim=128, window=513, rope=1, slots=544, rope_theta=10000.0, norm_eps=1e-6)
+    d.update(kw)
+    return AttnDesc(**d)
+
+
+def aprep(which, d=None, qkv=A(1), pos=A(2), B=1, qg=A(3), kg=A(4), q=A(5), kc=KC, vc=VC):
+    d = d or adesc()
+    if which == "host":
+        return host().moe_check_attn_prep(ctypes.byref(d), qkv, pos, B, qg, kg, q, kc, vc)
+    lib = hip()
+    lib.moe_attn_prep.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+    return lib.moe_attn_prep(ctypes.byref(AttnDesc.from_buffer_copy(d)), qkv, pos, B, qg, kg, q, kc, vc, None)
+
+
+def adecode(which, d=None, q=A(5), kc=KC, vc=VC, pos=A(2), B=1, max_ctx=0, sinks=A(6), out=A(7), ws=A(8),
+            ws_bytes=1 << 20):
+    d = d or adesc()
+    if which == "host":
+        return host().moe_check_attn_decode(ctypes.byref(d), q, kc, vc, pos, B, max_ctx, sinks, out, ws, ws_bytes)
+    lib = hip()
+    lib.moe_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]
+    return lib.moe_attn_decode(ctypes.byref(AttnDesc.from_buffer_copy(d)), q, kc, vc, pos, B, max_ctx, sinks, out,
+                               ws, ws_bytes, None)
+
+
+def attn_ws(d, B, max_ctx=0):
+    return host().moe_attn_workspace_bytes(ctypes.byref(d), B, max_ctx)
+
+
+def test_attn_valid_calls_pass_validation():
+    assert aprep("host") == OK and adecode("host") == OK
+    full = adesc(window=0, rope=0, slots=100032)
+    assert aprep("host", d=full, B=8) == OK
+    assert adecode("host", d=full, B=8, max_ctx=100001, sinks=None, ws_bytes=attn_ws(full, 8, 100001)) == OK
+
+
+def test_attn_workspace_bytes():
+    # one chunk (the 513 window fits in 17 tiles): the status line only
+    assert attn_ws(adesc(), 1) == 256 and attn_ws(adesc(), 8) == 256
+    # 100,001 positions over 4 KV heads at one token: 64 chunks of 49 tiles;
+    # partials of 8 heads x (m, l, 128 values) in FP32
+    full = adesc(window=0, rope=0, slots=100032)
+    assert attn_ws(full, 1, 100001) == 256 + 64 * 4 * 8 * 130 * 4
+    # at 8 tokens: 8 chunks per (token, KV head)
+    assert attn_ws(full, 8, 100001) == 256 + 8 * 8 * 4 * 8 * 130 * 4
+    # a short context stays in one chunk
+    assert attn_ws(full, 1, 700) == 256
+    assert attn_ws(full, 1, 100033) == 0 and attn_ws(full, 0, 5) == 0 and attn_ws(adesc(head_dim=64), 1) == 0
+
+
+@pytest.mark.parametrize("which", LIBS)
+@pytest.mark.parametrize("kw,want", [
+    (dict(qkv=None), INVALID), (dict(pos=None), INVALID), (dict(qg=None), INVALID), (dict(kg=None), INVALID),
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vc=None), INVALID),
+    (dict(B=0), INVALID), (dict(B=257), INVALID),
+    (dict(qkv=A(1) + 8), INVALID), (dict(pos=A(2) + 4), INVALID), (dict(q=A(5) + 2), INVALID),
+    (dict(d=adesc(head_dim=64)), UNSUPPORTED), (dict(d=adesc(n_q=64, n_kv=2)), UNSUPPORTED),
+    (dict(d=adesc(n_q=30)), INVALID), (dict(d=adesc(n_kv=0)), INVALID), (dict(d=adesc(slots=500)), INVALID),
+    (dict(d=adesc(window=545)), INVALID), (dict(d=adesc(window=-1)), INVALID), (dict(d=adesc(rope=2)), INVALID),
+    (dict(d=adesc(rope_theta=1.0)), INVALID), (dict(d=adesc(norm_eps=-1.0)), INVALID),
+    (dict(d=adesc(norm_eps=float("nan"))), INVALID),
+    (dict(q=A(1)), INVALID),                 # q_out == qkv
+    (dict(q=KC + 4096), INVALID),            # q_out inside the key cache
+    (dict(vc=KC + 65536), INVALID),          # the caches overlap
+    (dict(kc=A(3)), INVALID),                # the key cache over a gain
+])
+def test_attn_prep_errors(which, kw, want):
+    assert aprep(which, **kw) == want
+
+
+@pytest.mark.parametrize("which", LIBS)
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vc=None), INVALID), (dict(pos=None), INVALID),
+    (dict(out=None), INVALID), (dict(ws=None), INVALID), (dict(B=0), INVALID), (dict(B=257), INVALID),
+    (dict(max_ctx=-1), INVALID), (dict(max_ctx=514), INVALID),
+    (dict(d=adesc(window=0), max_ctx=545), INVALID),
+    (dict(ws=A(8) + 128), INVALID), (dict(sinks=A(6) + 2), INVALID), (dict(out=A(7) + 8), INVALID),
+    (dict(d=adesc(head_dim=256)), UNSUPPORTED),
+    (dict(out=A(5)), INVALID),               # out == q
+    (dict(out=A(6) - 64), INVALID),          # out runs over the sinks
+    (dict(ws=KC + 256), INVALID),            # workspace inside the key cache
+    (dict(ws_bytes=255), WORKSPACE),
+    (dict(d=adesc(window=0, rope=0, slots=100032), max_ctx=100001, ws_bytes=300000), WORKSPACE),
+])
+def test_attn_decode_errors(which, kw, want):
+    assert adecode(which, **kw) == want
+
+
+def test_attn_sinks_are_optional():
+    assert adecode("host", sinks=None) == OK

@@ -47,6 +47,12 @@ class moe_layer_weights(ctypes.Structure):
         "sh_gate", "sh_up", "sh_down", "sh_scale", "norm_gain")]
 
 
+class moe_attn_desc(ctypes.Structure):
+    _fields_ = [("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("rope", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_float)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
                       "(python w4a16_routed_expert_sigmoid_amd/build.py)")
@@ -105,13 +111,27 @@ _lib.moe_check_prefill_layer.argtypes = _lib.moe_check_decode_layer.argtypes
 _lib.moe_check_repack_nvfp4.restype = _i32
 _lib.moe_check_repack_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64]
 
+_AD = ctypes.POINTER(moe_attn_desc)
+_lib.moe_attn_prep.restype = _i32
+_lib.moe_attn_prep.argtypes = [_AD, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_attn_workspace_bytes.restype = _sz
+_lib.moe_attn_workspace_bytes.argtypes = [_AD, _i32, _i64]
+_lib.moe_attn_decode.restype = _i32
+_lib.moe_attn_decode.argtypes = [_AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_check_attn_prep.restype = _i32
+_lib.moe_check_attn_prep.argtypes = [_AD, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_check_attn_decode.restype = _i32
+_lib.moe_check_attn_decode.argtypes = [_AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz]
+
 EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes", "moe_repack_nvfp4",
            "moe_unpack_nvfp4", "moe_dequant_nvfp4",
            "moe_decode_workspace_bytes", "moe_decode_layer", "moe_decode_layer_timed", "moe_decode_wait_status",
            "moe_decode_layer_noalloc",
            "moe_decode_step_workspace_bytes", "moe_decode_step", "moe_prefill_workspace_bytes",
            "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
-           "moe_check_repack_nvfp4", "moe_probe_hbm_read", "moe_gemv_nvfp4", "moe_check_gemv_nvfp4")
+           "moe_check_repack_nvfp4", "moe_probe_hbm_read", "moe_gemv_nvfp4", "moe_check_gemv_nvfp4",
+           "moe_attn_prep", "moe_attn_workspace_bytes", "moe_attn_decode", "moe_check_attn_prep",
+           "moe_check_attn_decode")
 
 
 def lib():
@@ -209,6 +229,24 @@ def moe_gemv_nvfp4(w, tensor_scale, rows, cols, x, batch, y, stream=None):
     """y[t] = BF16(S * W x[t]) on one repacked NVFP4 matrix, batch 1..8."""
     _check(_lib.moe_gemv_nvfp4(_ptr(w), _ptr(tensor_scale), rows, cols, _ptr(x), batch, _ptr(y), _stream(stream)),
            "moe_gemv_nvfp4")
+
+
+def moe_attn_prep(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache, stream=None):
+    """Q/K norm + RoPE of `batch` tokens; q to q_out, k and v into the caches."""
+    _check(_lib.moe_attn_prep(ctypes.byref(desc), _ptr(qkv), _ptr(pos), batch, _ptr(q_gain), _ptr(k_gain),
+                              _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "moe_attn_prep")
+
+
+def moe_attn_workspace_bytes(desc, batch, max_ctx=0):
+    return _lib.moe_attn_workspace_bytes(ctypes.byref(desc), batch, max_ctx)
+
+
+def moe_attn_decode(desc, q, k_cache, v_cache, pos, batch, out, ws, ws_bytes, max_ctx=0, sinks=None,
+                    stream=None):
+    """Decode attention with sinks and the layer's window over the caches."""
+    _check(_lib.moe_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos), batch,
+                                max_ctx, _ptr(sinks), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_attn_decode")
 
 
 def moe_probe_hbm_read(src, nbytes, blocks, sink, stream=None):

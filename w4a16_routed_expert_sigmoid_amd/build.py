@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 HOST_LIB = os.path.join(HERE, "libmoe_host.so")
-SOURCES = ["api.cpp", "validate.cpp", "decode.hip", "prefill.hip", "repack.hip", "probe.hip"]
+SOURCES = ["api.cpp", "validate.cpp", "decode.hip", "prefill.hip", "repack.hip", "probe.hip", "attn.hip"]
 HOST_SOURCES = ["validate.cpp"]
 
 HIPCC_FLAGS = [

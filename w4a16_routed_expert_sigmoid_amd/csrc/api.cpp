@@ -1,6 +1,7 @@
 // C ABI of the library: dispatch of the validated calls to the kernels.
 // Argument checks and workspace layouts live in validate.cpp (host-only,
 // no HIP); nothing here is enqueued before they pass.
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -283,6 +284,57 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
   a.h_rows = (uint16_t *)(base + L.h);
   a.y_rows = (uint16_t *)(base + L.y);
   return hip_status(launch_prefill(a, (hipStream_t)stream));
+}
+
+moe_status moe_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                         const void *q_gain, const void *k_gain, void *q_out, void *k_cache, void *v_cache,
+                         void *stream) {
+  const moe_status st = check_attn_prep_call(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache);
+  if (st != MOE_OK) return st;
+  AttnPrepArgs a;
+  a.qkv = (const uint16_t *)qkv;
+  a.q_gain = (const uint16_t *)q_gain;
+  a.k_gain = (const uint16_t *)k_gain;
+  a.pos = pos;
+  a.q_out = (uint16_t *)q_out;
+  a.k_cache = (uint16_t *)k_cache;
+  a.v_cache = (uint16_t *)v_cache;
+  a.n_q = desc->n_q;
+  a.n_kv = desc->n_kv;
+  a.slots = desc->slots;
+  a.window = desc->window;
+  a.rope = desc->rope;
+  a.log2_theta = desc->rope ? log2(desc->rope_theta) : 0.0;
+  a.eps = (double)desc->norm_eps;
+  return hip_status(launch_attn_prep(a, batch, (hipStream_t)stream));
+}
+
+moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                           const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
+                           void *ws, size_t ws_bytes, void *stream) {
+  const moe_status st =
+      check_attn_decode_call(desc, q, k_cache, v_cache, pos, batch, max_ctx, sinks, out, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const AttnPlan plan = attn_plan_of(*desc, batch, max_ctx);
+  AttnDecodeArgs a;
+  a.q = (const uint16_t *)q;
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.pos = pos;
+  a.sinks = sinks;
+  a.out = (uint16_t *)out;
+  a.status = (uint32_t *)ws;
+  a.part = plan.chunks > 1 ? (float *)((uint8_t *)ws + attn_partial_offset()) : nullptr;
+  a.n_q = desc->n_q;
+  a.n_kv = desc->n_kv;
+  a.G = desc->n_q / desc->n_kv;
+  a.slots = desc->slots;
+  a.window = desc->window;
+  a.B = batch;
+  a.span = plan.span;
+  a.tpc = plan.tpc;
+  a.chunks = plan.chunks;
+  return hip_status(launch_attn_decode(a, (hipStream_t)stream));
 }
 
 moe_status moe_probe_hbm_read(const void *src, size_t bytes, int32_t blocks, int32_t *sink, void *stream) {

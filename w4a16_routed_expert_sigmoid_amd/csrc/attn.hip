@@ -1,0 +1,396 @@
+// Decode attention beside the MoE blocks ("Day-0 Support for Flint on
+// vLLM", sections "Model architecture" and "Optimizations"; "vLLM Flint"
+// commentary, section "Only 14 of 49 layers retain full-history KV"): GQA
+// 32/4 with head_dim 128, per-head Q/K RMSNorm, learned sinks, sliding-window
+// layers with RoPE and full-context layers without it, BF16 KV cache.
+//
+//   k_attn_prep     one wave per head of a token: per-head RMSNorm (FP64
+//                   sum of squares and scale, one BF16 rounding), RoPE of the
+//                   pairs (d, d + 64) with FP64 angles (one BF16 rounding),
+//                   q out, k and v written into the caches.  The norm, the
+//                   rotation and the cache write the pages fuse into one
+//                   kernel.
+//   k_attn_decode   flash-decoding: a block of 8 waves takes a chunk of
+//                   32-position tiles of one (token, KV head); per tile a wave
+//                   computes the scores of the group's query heads on the
+//                   matrix cores (v_mfma_f32_16x16x32_bf16: 16 positions x
+//                   16 head columns x 32 dims), an online base-2 softmax in
+//                   FP32, and P V on the matrix cores with P split into two
+//                   BF16 terms (hi + lo, about 16 significant bits).  The
+//                   block merges its waves through LDS, then writes the
+//                   final BF16 output (one chunk) or an FP32 partial.
+//   k_attn_combine  merges a token's partials and applies the sink.
+//
+// Cache layouts (per token row and KV head): keys [slots][128], values
+// transposed [128][slots].  With values transposed, the 8 positions a lane
+// feeds into P V are 16 contiguous bytes of one value row, and the
+// probabilities leave the score MFMA already in the lane order that P V
+// takes (see k_attn_decode).
+#include "common.h"
+
+namespace moe {
+
+// Positions lo..pos a token attends; false for a position the layer cannot
+// hold or that attends more than `span` positions.
+__device__ __forceinline__ bool attn_range(int64_t pos, int window, int slots, int64_t span, int64_t &lo) {
+  if (pos < 0 || pos >= kAttnMaxPos) return false;
+  if (window > 0) {
+    lo = pos - window + 1 > 0 ? pos - window + 1 : 0;
+  } else {
+    if (pos >= slots) return false;
+    lo = 0;
+  }
+  return pos - lo + 1 <= span;
+}
+
+// ---------------------------------------------------------------------------
+// Q/K norm + RoPE + KV write.  Grid (ceil(units / 4), B), 4 waves; unit u of
+// a token: q heads 0..n_q-1, k heads, then v heads.  Lane l holds elements
+// l and l + 64, the RoPE pair.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int units = a.n_q + 2 * a.n_kv;
+  if (u >= units) return;
+  const int64_t pos = a.pos[b];
+  int64_t lo;
+  const bool ok = attn_range(pos, a.window, a.slots, (int64_t)1 << 62, lo);
+  const int64_t slot = ok ? pos % a.slots : 0;
+  const uint16_t *src = a.qkv + ((int64_t)b * units + u) * kAttnD;
+  const uint32_t x0b = src[lane], x1b = src[lane + 64];
+
+  if (u >= a.n_q + a.n_kv) {  // v head: element d goes to row d of the transposed cache
+    if (!ok) return;
+    const int g = u - a.n_q - a.n_kv;
+    uint16_t *vt = a.v_cache + ((int64_t)b * a.n_kv + g) * kAttnD * a.slots + slot;
+    vt[(int64_t)lane * a.slots] = (uint16_t)x0b;
+    vt[(int64_t)(lane + 64) * a.slots] = (uint16_t)x1b;
+    return;
+  }
+  const bool is_q = u < a.n_q;
+  uint16_t *dst = is_q ? a.q_out + ((int64_t)b * a.n_q + u) * kAttnD
+                       : a.k_cache + (((int64_t)b * a.n_kv + (u - a.n_q)) * a.slots + slot) * kAttnD;
+  if (!ok) {
+    if (is_q) dst[lane] = dst[lane + 64] = 0;
+    return;
+  }
+  // RMSNorm of the head: squares of BF16 values are exact in FP64.
+  const double x0 = (double)bf16_to_f32(x0b), x1 = (double)bf16_to_f32(x1b);
+  double ss = x0 * x0 + x1 * x1;
+  ss = group_sum_f64(ss, kWave);
+  const double inv = 1.0 / sqrt(ss / (double)kAttnD + a.eps);
+  const uint16_t *gain = is_q ? a.q_gain : a.k_gain;
+  const double g0 = (double)bf16_to_f32(gain[lane]), g1 = (double)bf16_to_f32(gain[lane + 64]);
+  uint32_t y0 = f64_to_bf16(x0 * inv * g0), y1 = f64_to_bf16(x1 * inv * g1);
+  if (a.rope) {
+    // angle = pos * theta^(-2 lane / 128), in FP64
+    const double f = exp2(-(double)lane / 64.0 * a.log2_theta);
+    double sn, cs;
+    sincos((double)pos * f, &sn, &cs);
+    const double ya = (double)bf16_to_f32(y0), yb = (double)bf16_to_f32(y1);
+    y0 = f64_to_bf16(ya * cs - yb * sn);
+    y1 = f64_to_bf16(yb * cs + ya * sn);
+  }
+  dst[lane] = (uint16_t)y0;
+  dst[lane + 64] = (uint16_t)y1;
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention.  Grid (chunks, n_kv, B), 8 waves.
+//
+// Lane l = 16 g + r (r = l % 16, g = l / 16).  MFMA 16x16x32 lane layouts:
+// A lane l holds row r, k-group g (8 elements); B lane l holds column r,
+// k-group g; C lane l value i is row 4g + i, column r.  A dot product only
+// needs A and B to pair the same k elements, so any fixed assignment of
+// dims (or positions) to a k-group's 8 elements works.
+//
+// Scores, per 32-position tile and per half tt (0, 1): A = keys of 16
+// positions, row r <-> position offset 8 (r / 4) + 4 tt + r % 4; k-step s
+// (dims 32 s .. 32 s + 31) gives group g the dims 8 (4 s + g) .. + 8, i.e.
+// the 4 groups read 64 contiguous bytes of each key row.  B = q of the
+// group's heads, column r = head r (zero beyond G).  So C value i of lane l
+// is the score of head r at position offset 8 g + 4 tt + i: each lane holds
+// one head's scores at 8 consecutive positions 8 g .. 8 g + 7.
+//
+// P V, per 16-dim tile dt: out^T[dims][heads] += V^T[dims][32 positions] *
+// P[32 positions][heads].  A lane l = value row dt*16 + r, positions
+// 8 g .. 8 g + 7 (16 contiguous bytes of the transposed cache); B lane l =
+// head r, the same 8 positions: exactly the 8 probabilities the lane holds.
+// C lane l value i = dim dt*16 + 4 g + i of head r.
+// ---------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+struct AttnTileRegs {
+  u32x4 k[2][4];  // keys: half tt, k-step s
+  u32x4 v[8];     // transposed values: dim tile dt
+};
+
+__device__ __forceinline__ void attn_load_tile(AttnTileRegs &t, const uint16_t *kb, const uint16_t *vb, int slots,
+                                               int64_t tile, int r, int g) {
+  const int s0 = (int)((tile * kAttnTile) % slots);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint16_t *row = kb + (int64_t)(s0 + (r >> 2) * 8 + tt * 4 + (r & 3)) * kAttnD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t.k[tt][s] = ld16(row + (s * 4 + g) * 8);
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) t.v[dt] = ld16(vb + (int64_t)(dt * 16 + r) * slots + s0 + g * 8);
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Sum / max over the 4 lanes of one head column (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float col_sum(float v) {
+  v += xor_lane<16>(v);
+  return v + xor_lane<32>(v);
+}
+__device__ __forceinline__ float col_max(float v) {
+  v = fmaxf(v, xor_lane<16>(v));
+  return fmaxf(v, xor_lane<32>(v));
+}
+
+constexpr int kAccStride = kAttnD + 4;  // LDS row of one head's accumulator (floats)
+
+__global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeArgs a) {
+  __shared__ float s_acc[kAttnWaves][kAttnMaxGroup][kAccStride];
+  __shared__ float s_m[kAttnWaves][kAttnMaxGroup], s_l[kAttnWaves][kAttnMaxGroup];
+
+  const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int G = a.G;
+
+  // One chunk per token: this kernel writes the status word (block 0).
+  if (a.chunks == 1 && c == 0 && kv == 0 && b == 0 && threadIdx.x < kWave) {
+    uint32_t bad = 0;
+    for (int t = threadIdx.x; t < a.B; t += kWave) {
+      int64_t lo;
+      bad |= attn_range(a.pos[t], a.window, a.slots, a.span, lo) ? 0u : (uint32_t)kStatusBadPos;
+    }
+    bad = wave_max_u32(bad);
+    if (threadIdx.x == 0) *a.status = bad;
+  }
+
+  const int64_t pos = a.pos[b];
+  int64_t lo = 0;
+  const bool ok = attn_range(pos, a.window, a.slots, a.span, lo);
+  uint16_t *outb = a.out + ((int64_t)b * a.n_q + (int64_t)kv * G) * kAttnD;
+  if (!ok) {  // zero output rows (the combine kernel does it for split plans)
+    if (a.chunks == 1)
+      for (int i = threadIdx.x; i < G * kAttnD / 8; i += blockDim.x)
+        reinterpret_cast<u32x4 *>(outb)[i] = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const int64_t ft = lo / kAttnTile, lt = pos / kAttnTile;
+  const int64_t t0 = ft + (int64_t)c * a.tpc;
+  if (t0 > lt) return;  // this token needs fewer chunks
+  const int64_t t1 = t0 + a.tpc - 1 < lt ? t0 + a.tpc - 1 : lt;
+
+  // q of head r of the group, dims 8 (4 s + g) .. + 8 for k-step s
+  u32x4 qv[4];
+  {
+    const int hq = r < G ? r : 0;
+    const uint16_t *qh = a.q + ((int64_t)b * a.n_q + (int64_t)kv * G + hq) * kAttnD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 v = ld16(qh + (s * 4 + g) * 8);
+      qv[s] = r < G ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+  const uint16_t *kb = a.k_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
+  const uint16_t *vb = a.v_cache + ((int64_t)b * a.n_kv + kv) * kAttnD * a.slots;
+  const float qscale = kLog2e / sqrtf((float)kAttnD);
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int64_t t = t0 + wave;
+  if (t <= t1) {
+    AttnTileRegs cur, nxt;
+    attn_load_tile(cur, kb, vb, a.slots, t, r, g);
+    for (; t <= t1; t += kAttnWaves) {
+      // next tile (unconditional: past the end it reloads this tile, a cache hit)
+      const int64_t tn = t + kAttnWaves <= t1 ? t + kAttnWaves : t;
+      attn_load_tile(nxt, kb, vb, a.slots, tn, r, g);
+
+      f32x4 sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sc[tt] = mfma16(cur.k[tt][s], qv[s], sc[tt]);
+      }
+      // positions 32 t + 8 g + j, j = 4 tt + i
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][j & 3] * qscale;
+      const int64_t p0 = t * kAttnTile + g * 8;
+      const bool edge = t * kAttnTile < lo || t * kAttnTile + kAttnTile - 1 > pos;
+      uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
+      if (edge) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool in = p0 + j >= lo && p0 + j <= pos;
+          if (!in) {
+            x[j] = -INFINITY;
+            vmask[j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          }
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+      mx = col_max(mx);
+      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid position
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
+        ps += p[j];
+      }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      // P as two BF16 terms
+      u32x4 ph, pl;
+      {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          h[w] = f32x2_to_bf16x2(p[2 * w], p[2 * w + 1]);
+          const float r0 = p[2 * w] - bf16_to_f32(h[w] & 0xFFFFu);
+          const float r1 = p[2 * w + 1] - bf16_to_f32(h[w] >> 16);
+          l[w] = f32x2_to_bf16x2(r0, r1);
+        }
+        ph = u32x4{h[0], h[1], h[2], h[3]};
+        pl = u32x4{l[0], l[1], l[2], l[3]};
+      }
+      const u32x4 vm = u32x4{vmask[0], vmask[1], vmask[2], vmask[3]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt] *= alpha;
+        const u32x4 vv = cur.v[dt] & vm;
+        acc[dt] = mfma16(vv, ph, acc[dt]);
+        acc[dt] = mfma16(vv, pl, acc[dt]);
+      }
+      cur = nxt;
+    }
+  }
+  l_run = col_sum(l_run);
+
+  // merge the waves
+  if (g == 0) {
+    s_m[wave][r] = m_run;
+    s_l[wave][r] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<f32x4 *>(&s_acc[wave][r][dt * 16 + g * 4]) = acc[dt];
+  __syncthreads();
+
+  // thread -> (head n, dims 4 d4 .. + 4)
+  for (int idx = threadIdx.x; idx < G * (kAttnD / 4); idx += blockDim.x) {
+    const int n = idx / (kAttnD / 4), d = (idx % (kAttnD / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][n]);
+    float L = 0.f;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_m[w][n] - M);  // 0 for a wave with no tile
+      L += f * s_l[w][n];
+      A += f * *reinterpret_cast<const f32x4 *>(&s_acc[w][n][d]);
+    }
+    if (a.chunks == 1) {
+      const float sk = a.sinks ? a.sinks[kv * G + n] * kLog2e : -INFINITY;
+      const float M2 = fmaxf(M, sk);
+      const float f = __builtin_amdgcn_exp2f(M - M2);
+      const float inv = 1.0f / (L * f + __builtin_amdgcn_exp2f(sk - M2));
+      const f32x4 o = A * (f * inv);
+      *reinterpret_cast<uint2 *>(outb + n * kAttnD + d) = uint2{f32x2_to_bf16x2(o[0], o[1]), f32x2_to_bf16x2(o[2], o[3])};
+    } else {
+      float *pp = a.part + (((int64_t)b * a.n_kv + kv) * a.chunks + c) * attn_part_floats(G);
+      *reinterpret_cast<f32x4 *>(pp + n * kAttnD + d) = A;
+      if (d == 0) {
+        pp[G * kAttnD + n] = M;
+        pp[G * kAttnD + G + n] = L;
+      }
+    }
+  }
+}
+
+// Grid (n_kv, B), 512 threads: merge a token's chunk partials, apply the sink.
+__global__ __launch_bounds__(512) void k_attn_combine(AttnDecodeArgs a) {
+  const int kv = blockIdx.x, b = blockIdx.y;
+  const int G = a.G;
+  if (kv == 0 && b == 0 && threadIdx.x < kWave) {
+    uint32_t bad = 0;
+    for (int t = threadIdx.x; t < a.B; t += kWave) {
+      int64_t lo;
+      bad |= attn_range(a.pos[t], a.window, a.slots, a.span, lo) ? 0u : (uint32_t)kStatusBadPos;
+    }
+    bad = wave_max_u32(bad);
+    if (threadIdx.x == 0) *a.status = bad;
+  }
+  const int64_t pos = a.pos[b];
+  int64_t lo = 0;
+  const bool ok = attn_range(pos, a.window, a.slots, a.span, lo);
+  uint16_t *outb = a.out + ((int64_t)b * a.n_q + (int64_t)kv * G) * kAttnD;
+  int nch = 0;
+  if (ok) {
+    const int64_t tiles = pos / kAttnTile - lo / kAttnTile + 1;
+    nch = (int)((tiles + a.tpc - 1) / a.tpc);
+  }
+  const int64_t pf = attn_part_floats(G);
+  const float *pb = a.part + ((int64_t)b * a.n_kv + kv) * a.chunks * pf;
+  for (int idx = threadIdx.x; idx < G * (kAttnD / 4); idx += blockDim.x) {
+    const int n = idx / (kAttnD / 4), d = (idx % (kAttnD / 4)) * 4;
+    if (!ok) {
+      *reinterpret_cast<uint2 *>(outb + n * kAttnD + d) = uint2{0u, 0u};
+      continue;
+    }
+    float M = -INFINITY;
+    for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, pb[ch * pf + G * kAttnD + n]);
+    const float sk = a.sinks ? a.sinks[kv * G + n] * kLog2e : -INFINITY;
+    const float M2 = fmaxf(M, sk);
+    float L = __builtin_amdgcn_exp2f(sk - M2);
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < nch; ++ch) {
+      const float *pp = pb + ch * pf;
+      const float f = __builtin_amdgcn_exp2f(pp[G * kAttnD + n] - M2);
+      L += f * pp[G * kAttnD + G + n];
+      A += f * *reinterpret_cast<const f32x4 *>(pp + n * kAttnD + d);
+    }
+    const f32x4 o = A * (1.0f / L);
+    *reinterpret_cast<uint2 *>(outb + n * kAttnD + d) = uint2{f32x2_to_bf16x2(o[0], o[1]), f32x2_to_bf16x2(o[2], o[3])};
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_attn_prep(const AttnPrepArgs &a, int B, hipStream_t stream) {
+  const int units = a.n_q + 2 * a.n_kv;
+  hipLaunchKernelGGL(k_attn_prep, dim3((units + 3) / 4, B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_attn_decode, dim3(a.chunks, a.n_kv, a.B), dim3(kAttnWaves * kWave), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.chunks == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_kv, a.B), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

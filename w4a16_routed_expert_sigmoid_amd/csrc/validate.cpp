@@ -277,6 +277,93 @@ moe_status check_gemv_call(const void *w, const float *tensor_scale, int64_t row
   return MOE_OK;
 }
 
+moe_status check_attn_desc(const moe_attn_desc *d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->n_q < 1 || d->n_kv < 1 || d->n_q > 4096 || d->n_q % d->n_kv) return MOE_ERR_INVALID_ARG;
+  if (d->head_dim < 1 || d->slots < kAttnTile || d->slots % kAttnTile) return MOE_ERR_INVALID_ARG;
+  if (d->window < 0 || d->window > d->slots) return MOE_ERR_INVALID_ARG;
+  if (d->rope != 0 && d->rope != 1) return MOE_ERR_INVALID_ARG;
+  if (d->rope && !(d->rope_theta > 1.0 && isfinite(d->rope_theta))) return MOE_ERR_INVALID_ARG;
+  if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps)) return MOE_ERR_INVALID_ARG;
+  if (d->head_dim != kAttnD || d->n_q / d->n_kv > kAttnMaxGroup) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t attn_span(const moe_attn_desc &d, int64_t max_ctx) {
+  const int64_t bound = d.window > 0 ? d.window : d.slots;
+  if (max_ctx < 0 || max_ctx > bound) return -1;
+  return max_ctx > 0 ? max_ctx : bound;
+}
+
+AttnPlan attn_plan_of(const moe_attn_desc &d, int32_t batch, int64_t max_ctx) {
+  return attn_plan(attn_span(d, max_ctx), d.window > 0, batch, d.n_kv);
+}
+
+size_t attn_partial_offset() { return kStatusLine; }
+
+size_t attn_workspace_bytes(const moe_attn_desc &d, int32_t batch, int64_t max_ctx) {
+  const AttnPlan p = attn_plan_of(d, batch, max_ctx);
+  size_t b = kStatusLine;
+  if (p.chunks > 1)
+    b += up((size_t)batch * d.n_kv * p.chunks * (size_t)attn_part_floats(d.n_q / d.n_kv) * sizeof(float));
+  return b;
+}
+
+namespace {
+inline size_t cache_bytes(const moe_attn_desc &d, int32_t batch) {
+  return (size_t)batch * d.n_kv * (size_t)d.slots * kAttnD * 2;
+}
+
+// Each output range shares no byte with any other range.
+bool outputs_disjoint(const Range *r, int n, int n_out) {
+  for (int i = 0; i < n_out; ++i)
+    for (int j = 0; j < n; ++j)
+      if (j != i && overlap(r[i], r[j])) return false;
+  return true;
+}
+}  // namespace
+
+moe_status check_attn_prep_call(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
+                                const void *v_cache) {
+  const moe_status st = check_attn_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!qkv || !pos || !q_gain || !k_gain || !q_out || !k_cache || !v_cache) return MOE_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kAttnMaxBatch) return MOE_ERR_INVALID_ARG;
+  if (!aligned(qkv, 16) || !aligned(pos, 8) || !aligned(q_gain, 16) || !aligned(k_gain, 16) ||
+      !aligned(q_out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return MOE_ERR_INVALID_ARG;
+  const size_t cb = cache_bytes(*desc, batch);
+  const Range r[7] = {{q_out, (size_t)batch * desc->n_q * kAttnD * 2},
+                      {k_cache, cb},
+                      {v_cache, cb},
+                      {qkv, (size_t)batch * (desc->n_q + 2 * desc->n_kv) * kAttnD * 2},
+                      {pos, (size_t)batch * 8},
+                      {q_gain, kAttnD * 2},
+                      {k_gain, kAttnD * 2}};
+  return outputs_disjoint(r, 7, 3) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+moe_status check_attn_decode_call(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                                  const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks,
+                                  const void *out, const void *ws, size_t ws_bytes) {
+  const moe_status st = check_attn_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!q || !k_cache || !v_cache || !pos || !out || !ws) return MOE_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kAttnMaxBatch) return MOE_ERR_INVALID_ARG;
+  if (attn_span(*desc, max_ctx) < 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pos, 8) ||
+      !aligned(out, 16) || !aligned(ws, kWsAlign) || (sinks && !aligned(sinks, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t cb = cache_bytes(*desc, batch);
+  const size_t act = (size_t)batch * desc->n_q * kAttnD * 2;
+  const Range r[7] = {{out, act}, {ws, ws_bytes}, {q, act}, {k_cache, cb}, {v_cache, cb},
+                      {pos, (size_t)batch * 8}, {sinks, sinks ? (size_t)desc->n_q * 4 : 0}};
+  if (!outputs_disjoint(r, 7, 2)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < attn_workspace_bytes(*desc, batch, max_ctx)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
 moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
   if (!src || !dst) return MOE_ERR_INVALID_ARG;
   if (rows <= 0 || cols <= 0 || n_mats <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
@@ -342,6 +429,24 @@ moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_w
 
 moe_status moe_check_repack_nvfp4(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats) {
   return check_repack_call(src, dst, rows, cols, n_mats);
+}
+
+size_t moe_attn_workspace_bytes(const moe_attn_desc *desc, int32_t batch, int64_t max_ctx) {
+  if (check_attn_desc(desc) != MOE_OK || batch < 1 || batch > kAttnMaxBatch) return 0;
+  if (attn_span(*desc, max_ctx) < 0) return 0;
+  return attn_workspace_bytes(*desc, batch, max_ctx);
+}
+
+moe_status moe_check_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                               const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
+                               const void *v_cache) {
+  return check_attn_prep_call(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache);
+}
+
+moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,
+                                 const void *v_cache, const int64_t *pos, int32_t batch, int64_t max_ctx,
+                                 const float *sinks, const void *out, const void *ws, size_t ws_bytes) {
+  return check_attn_decode_call(desc, q, k_cache, v_cache, pos, batch, max_ctx, sinks, out, ws, ws_bytes);
 }
 
 moe_status moe_check_gemv_nvfp4(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,

@@ -53,6 +53,20 @@ moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weight
                               const void *ws, size_t ws_bytes, PfLayout *L);
 moe_status check_gemv_call(const void *w, const float *tensor_scale, int64_t rows, int64_t cols, const void *x,
                            int32_t batch, const void *y);
+// Attention: the description's checks, the positions a token may attend
+// (max_ctx, or the layer's bound when 0; -1 when out of range), the chunk
+// plan and the workspace size (status line, then the partials when split).
+moe_status check_attn_desc(const moe_attn_desc *d);
+int64_t attn_span(const moe_attn_desc &d, int64_t max_ctx);
+AttnPlan attn_plan_of(const moe_attn_desc &d, int32_t batch, int64_t max_ctx);
+size_t attn_partial_offset();
+size_t attn_workspace_bytes(const moe_attn_desc &d, int32_t batch, int64_t max_ctx);
+moe_status check_attn_prep_call(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
+                                const void *v_cache);
+moe_status check_attn_decode_call(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
+                                  const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks,
+                                  const void *out, const void *ws, size_t ws_bytes);
 moe_status check_repack_call(const void *src, const void *dst, int64_t rows, int64_t cols, int64_t n_mats);
 moe_status check_dequant_call(const void *src, const float *dst, int64_t rows, int64_t cols, int64_t n_mats,
                               const float *tensor_scale);
