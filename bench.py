@@ -20,8 +20,14 @@ prefill of one layer on the matrix cores.  Also: the measured HBM read
 ceiling (a streaming-read kernel), the roofline of the batch-1 layer kernel
 and the CPU oracle's time on the host cores.
 
+Beside the MoE layer: the dense NVFP4 projection (LM-head and fused-QKV
+shapes) and the decode attention of one 49-layer step at 100K context (14
+full-context layers, 35 sliding-window layers; Q/K norm, RoPE and KV write,
+then attention with sinks), at batch 1 and 8.
+
 --workload step49: the model's decode step alone, with 47 independently
 generated MoE layers instead of device copies of a few.
+--attn-only: the attention leg alone (for profiling).
 
 Prints one JSON line.  Inputs are synthetic and seeded (see synth/).
 """
@@ -100,6 +106,12 @@ def parse():
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-weight leg")
     p.add_argument("--no-gemv", action="store_true", help="skip the dense-projection leg")
     p.add_argument("--no-mid", action="store_true", help="skip the 16..256-token leg")
+    p.add_argument("--no-attn", action="store_true", help="skip the decode-attention leg")
+    p.add_argument("--attn-ctx", type=int, default=100000,
+                   help="decode position of the attention leg (the pages' 100K context)")
+    p.add_argument("--attn-batches", default="1,8", help="batches of the attention leg")
+    p.add_argument("--attn-only", action="store_true",
+                   help="run only the decode-attention leg and print its results (profiling)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB streaming read and a 1 GiB copy (counter calibration under rocprofv3 --pmc)")
     return p.parse_args()
@@ -116,7 +128,12 @@ def main():
     torch.cuda.set_device(dev)
     side = torch.cuda.Stream()  # a non-default stream: graph capture needs one
     with torch.cuda.stream(side):
-        out = run(args, dev)
+        if args.attn_only:
+            out = {"attn_step_100k": run_attention(args, dev)}
+            if args.copy_probe:
+                copy_probe(dev)
+        else:
+            out = run(args, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -240,6 +257,21 @@ def stream_ceiling(dev):
             "kernel": "k_probe_read (moe_probe_hbm_read): 16-byte nontemporal loads, grid-stride, 4 in flight"}
 
 
+def copy_probe(dev):
+    """Known sizes for scaling the traffic counters: a 1 GiB streaming read,
+    then a 1 GiB device copy (1 GiB read + 1 GiB written)."""
+    import torch
+
+    import w4a16_routed_expert_sigmoid_amd as moe
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    moe.moe_probe_hbm_read(a, a.numel(), 2048, sink)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def cpu_baseline(seconds):
     """The oracle (FP64, plain C) on one host thread and on every host thread
     (one owner per token, so both give the same bits), each for about
@@ -300,6 +332,10 @@ def run(args, dev):
         configs["dense_gemv_nvfp4"] = run_gemv(args, dev)
         torch.cuda.empty_cache()
 
+    if args.workload == "layer" and not args.no_attn:
+        configs["attn_step_100k"] = run_attention(args, dev)
+        torch.cuda.empty_cache()
+
     zipf = torch.from_numpy(synth.zipf_offset(E)).to(dev)
     t0 = time.time()
     dense = [moe.DeviceLayer(synth.make_layer(j, inter=0, shared_inter=5632, n_experts=0, norm=True), device=dev)
@@ -326,6 +362,8 @@ def run(args, dev):
 
     ceiling = stream_ceiling(dev)
     ceil_gbs = ceiling["GBps"]
+    for v in configs.get("attn_step_100k", {}).values():
+        v["full_decode_stream_frac"] = round(v["full_decode_GBps"] / ceil_gbs, 4)
 
     def summary(r, n_layers, B, expert_bytes=EXPERT_BYTES, scales=12, extra=0):
         b, gbs = gb_per_s(r["distinct"], r["ms_step"], expert_bytes, scales, extra)
@@ -385,15 +423,7 @@ def run(args, dev):
         torch.cuda.empty_cache()
 
     if args.copy_probe:
-        # known sizes for scaling the traffic counters: a 1 GiB streaming
-        # read, then a 1 GiB device copy (1 GiB read + 1 GiB written)
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        moe.moe_probe_hbm_read(a, a.numel(), 2048, sink)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        copy_probe(dev)
 
     # batch 1: one kernel per layer (router, gate/up and down of the 6
     # selected experts and the shared expert)
@@ -416,7 +446,9 @@ def run(args, dev):
     else:
         workload = ("decode step of the MoE stack, batch 1: 2 dense SwiGLU (intermediate 5632) + 47 NVFP4 MoE "
                     "layers, RMSNorm before each, independent seeded weights, one HIP graph")
-    if any(v.get("nonfinite") for k in ("dense_gemv_nvfp4", "mid_batch_nvfp4_zipf")
+    if any(v.get("status") for v in configs.get("attn_step_100k", {}).values()):
+        warn.append("attention status non-zero: outputs invalid")
+    if any(v.get("nonfinite") for k in ("dense_gemv_nvfp4", "mid_batch_nvfp4_zipf", "attn_step_100k")
            for v in configs.get(k, {}).values()):
         warn.append("non-finite outputs")
     gbs1 = head["GBps"]
@@ -556,6 +588,122 @@ def run_gemv(args, dev):
         del ws, w0
         torch.cuda.empty_cache()
     return out
+
+
+ATTN_NQ, ATTN_NKV, ATTN_D, ATTN_WINDOW, ATTN_RING = 32, 4, 128, 513, 544
+
+
+def run_attention(args, dev):
+    """Decode attention of one 49-layer step at the pages' decode setting
+    (context 100K): 14 full-context layers (no RoPE) attending every
+    position and 35 sliding-window layers (513 positions, RoPE, a 544-slot
+    ring), GQA 32/4 of 128, sinks, each layer = moe_attn_prep (Q/K norm,
+    RoPE, KV write) then moe_attn_decode, all 49 in one HIP graph.  Caches
+    hold seeded random BF16 (the full layers' 14 x 205 MB per token stream
+    from HBM every step).  Also the full-context decode alone, timed per
+    call with events: GB/s on the K and V bytes it must read."""
+    import torch
+
+    import w4a16_routed_expert_sigmoid_amd as moe
+
+    ctx = args.attn_ctx                       # position of the decoded token
+    span = ctx + 1
+    full_slots = -(-span // 32) * 32
+    full = moe.moe_attn_desc(ATTN_NQ, ATTN_NKV, ATTN_D, 0, 0, full_slots, 0.0, 1e-6)
+    swa = moe.moe_attn_desc(ATTN_NQ, ATTN_NKV, ATTN_D, ATTN_WINDOW, 1, ATTN_RING, 10000.0, 1e-6)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4711)
+    out = {}
+    for B in [int(b) for b in args.attn_batches.split(",") if b]:
+        t0 = time.time()
+        layers = []
+        for i in range(49):
+            is_full = i % 7 >= 5                   # 14 of 49
+            d = full if is_full else swa
+            slots = full_slots if is_full else ATTN_RING
+            n = B * ATTN_NKV * slots * ATTN_D
+            L = dict(desc=d, full=is_full, max_ctx=span if is_full else 0,
+                     kc=torch.randn(n, device=dev, dtype=torch.bfloat16, generator=gen).view(torch.int16),
+                     vc=torch.randn(n, device=dev, dtype=torch.bfloat16, generator=gen).view(torch.int16),
+                     qkv=torch.randn(B * (ATTN_NQ + 2 * ATTN_NKV) * ATTN_D, device=dev, dtype=torch.bfloat16,
+                                     generator=gen).view(torch.int16),
+                     qg=(1 + 0.02 * torch.randn(ATTN_D, device=dev, generator=gen)).bfloat16().view(torch.int16),
+                     kg=(1 + 0.02 * torch.randn(ATTN_D, device=dev, generator=gen)).bfloat16().view(torch.int16),
+                     sinks=torch.randn(ATTN_NQ, device=dev, generator=gen),
+                     q=torch.empty(B * ATTN_NQ * ATTN_D, dtype=torch.int16, device=dev),
+                     o=torch.empty(B * ATTN_NQ * ATTN_D, dtype=torch.int16, device=dev))
+            L["ws_bytes"] = moe.moe_attn_workspace_bytes(d, B, L["max_ctx"])
+            L["ws"] = torch.empty(L["ws_bytes"], dtype=torch.uint8, device=dev)
+            layers.append(L)
+        pos = torch.full((B,), ctx, dtype=torch.int64, device=dev)
+        torch.cuda.synchronize()
+        cache_bytes = sum(2 * L["kc"].numel() * 2 for L in layers)
+        log(f"attention B={B}: 49 layers, caches {cache_bytes / 1e9:.2f} GB, built in {time.time() - t0:.1f}s")
+
+        def layer_call(L):
+            moe.moe_attn_prep(L["desc"], L["qkv"], pos, B, L["qg"], L["kg"], L["q"], L["kc"], L["vc"])
+            moe.moe_attn_decode(L["desc"], L["q"], L["kc"], L["vc"], pos, B, L["o"], L["ws"], L["ws_bytes"],
+                                max_ctx=L["max_ctx"], sinks=L["sinks"])
+
+        for L in layers:
+            layer_call(L)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for L in layers:
+                layer_call(L)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        step_us = e0.elapsed_time(e1) * 1e3 / reps
+        # the full-context decode alone (split + combine kernels), per call
+        fulls = [L for L in layers if L["full"]]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3 * 14)]
+        k = 0
+        for _ in range(3):
+            for L in fulls:
+                ev[k][0].record()
+                moe.moe_attn_decode(L["desc"], L["q"], L["kc"], L["vc"], pos, B, L["o"], L["ws"], L["ws_bytes"],
+                                    max_ctx=L["max_ctx"], sinks=L["sinks"])
+                ev[k][1].record()
+                k += 1
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) * 1e3 for a, b in ev[14:])   # skip the first pass
+        full_us = times[len(times) // 2]
+        kv_bytes = B * ATTN_NKV * span * ATTN_D * 2 * 2
+        swa_bytes = B * ATTN_NKV * ATTN_WINDOW * ATTN_D * 2 * 2
+        step_bytes = 14 * kv_bytes + 35 * swa_bytes
+        status = 0
+        for L in layers:
+            status |= _ws_status(moe, L["ws"])
+        nonfinite = any(not torch.isfinite(L["o"].view(torch.bfloat16).float()).all().item() for L in layers)
+        full_gbs = kv_bytes / (full_us * 1e-6) / 1e9
+        out[f"b{B}"] = {
+            "us_per_step": round(step_us, 2), "tokens_per_s": round(B * 1e6 / step_us, 1),
+            "step_GBps": round(step_bytes / (step_us * 1e-6) / 1e9, 1), "step_kv_bytes": int(step_bytes),
+            "full_decode_us": round(full_us, 2), "full_decode_GBps": round(full_gbs, 1),
+            "full_decode_hbm_frac": round(full_gbs / HBM_PEAK_GBS, 4), "full_decode_kv_bytes": int(kv_bytes),
+            "context_positions": span, "status": status, "nonfinite": nonfinite,
+            "layers": "14 full-context (no RoPE) + 35 window-513 (RoPE), prep + decode each"}
+        log(f"attention B={B}: {step_us:.1f} us per 49-layer step, full-context decode {full_us:.1f} us "
+            f"({full_gbs:.0f} GB/s), status {status}")
+        del layers, g
+        torch.cuda.empty_cache()
+    return out
+
+
+def _ws_status(moe, ws):
+    import torch
+    s = torch.full((1,), -1, dtype=torch.int32, device=ws.device)
+    moe.moe_decode_wait_status(ws, s)
+    return int(s.item())
 
 
 def run_prefill(args, dev):

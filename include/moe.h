@@ -313,9 +313,14 @@ moe_status moe_check_gemv_nvfp4(const void *w, const float *tensor_scale, int64_
  * Caches (caller-owned device memory, one per layer, `slots` positions per
  * token row; position p lives in slot p % slots, so a window layer keeps a
  * ring and a full-context layer needs slots > every position):
- *   k_cache [batch][n_kv][slots][128] BF16  (a key row per slot)
- *   v_cache [batch][n_kv][128][slots] BF16  (values stored transposed: row
- *                                            d holds element d of every slot)
+ *   k_cache, v_cache: [batch][n_kv][slots / 32] tiles of 32 slots x 128
+ *   BF16 (8 KiB), each tile in the lane order of the matrix-core operands
+ *   that read it.  Element d of the slot at offset o (0..31) of its tile is
+ *   tile element
+ *     keys:   ((((o/4) % 2) * 4 + d/32) * 64 + ((d/8) % 4) * 16 + (o/8) * 4 + o % 4) * 8 + d % 8
+ *     values: ((d/16) * 64 + (o/8) * 16 + d % 16) * 8 + o % 8
+ *   (integer division).  moe_attn_prep writes the decoded token's slot;
+ *   moe_attn_kv_write writes any positions from natural [n_kv][128] rows.
  * Positions `pos` are device int64 [batch] (graph replays may change them),
  * 0 .. 2^40 - 1.
  * ------------------------------------------------------------------ */
@@ -326,7 +331,8 @@ typedef struct moe_attn_desc {
   int32_t window;     /* 0: full context; W > 0: the last W positions, the
                          current one included; W <= slots */
   int32_t rope;       /* 1: RoPE on q and k at the token's position, 0: none */
-  int32_t slots;      /* cache positions per token row, a multiple of 32 */
+  int32_t slots;      /* cache positions per token row, a multiple of 32,
+                         at most 2^24 */
   double rope_theta;  /* RoPE base (> 1) when rope == 1 */
   float norm_eps;     /* per-head RMSNorm epsilon, >= 0 */
 } moe_attn_desc;
@@ -346,10 +352,25 @@ typedef struct moe_attn_desc {
  * in a full-context layer writes nothing to the caches and zeros to q_out.
  * Errors: INVALID_ARG for null or misaligned pointers, batch outside
  * 1..256, a bad description, q_out sharing a byte with an input or a
- * cache; UNSUPPORTED for head_dim != 128 or n_q / n_kv > 16; HIP. */
+ * cache; UNSUPPORTED for head_dim != 128, n_q / n_kv > 16 or slots above
+ * 2^24; HIP. */
 moe_status moe_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
                          const void *q_gain, const void *k_gain, void *q_out, void *k_cache, void *v_cache,
                          void *stream);
+
+/* K and V rows into the caches (a prompt's keys and values, a cache
+ * restore): for token row b < batch and i < n, the n_kv x 128 key and value
+ * rows k_rows[b][i], v_rows[b][i] (BF16, keys already normed and rotated)
+ * go to the slot of position pos[b * n + i] (device int64).  Positions out
+ * of range (as for moe_attn_prep) are skipped; positions of one token row
+ * that share a slot leave one of their rows there, unspecified which.
+ *  k_rows, v_rows [batch][n][n_kv][128] BF16; all device, 16-byte aligned
+ *  (pos 8-byte).
+ * Errors: INVALID_ARG for null or misaligned pointers, n < 1 or above
+ * 2^24, batch outside 1..256, a bad description, a cache sharing a byte
+ * with an input or the other cache; UNSUPPORTED as moe_attn_prep; HIP. */
+moe_status moe_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, const void *v_rows, const int64_t *pos,
+                             int32_t n, int32_t batch, void *k_cache, void *v_cache, void *stream);
 
 /* Workspace bytes moe_attn_decode needs for `batch` tokens attending at
  * most max_ctx positions each (0: the layer's bound, window or slots), or 0
@@ -387,11 +408,14 @@ moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void 
                            const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Host-side validation alone of moe_attn_prep and moe_attn_decode, as for
- * the calls above. */
+/* Host-side validation alone of moe_attn_prep, moe_attn_kv_write and
+ * moe_attn_decode, as for the calls above. */
 moe_status moe_check_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
                                const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
                                const void *v_cache);
+moe_status moe_check_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, const void *v_rows,
+                                   const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
+                                   const void *v_cache);
 moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,
                                  const void *v_cache, const int64_t *pos, int32_t batch, int64_t max_ctx,
                                  const float *sinks, const void *out, const void *ws, size_t ws_bytes);

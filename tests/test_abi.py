@@ -68,6 +68,8 @@ def _declare(lib):
     lib.moe_check_attn_prep.argtypes = [AD, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
     lib.moe_check_attn_decode.restype = _i32
     lib.moe_check_attn_decode.argtypes = [AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz]
+    lib.moe_check_attn_kv_write.restype = _i32
+    lib.moe_check_attn_kv_write.argtypes = [AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]
     lib.moe_attn_workspace_bytes.restype = _sz
     lib.moe_attn_workspace_bytes.argtypes = [AD, _i32, _i64]
     return lib
@@ -139,7 +141,8 @@ def test_host_library_needs_no_hip_runtime():
     for n in ("moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
               "moe_check_repack_nvfp4", "moe_decode_workspace_bytes", "moe_decode_step_workspace_bytes",
               "moe_prefill_workspace_bytes", "moe_nvfp4_matrix_bytes", "moe_status_string",
-              "moe_check_attn_prep", "moe_check_attn_decode", "moe_attn_workspace_bytes"):
+              "moe_check_attn_prep", "moe_check_attn_decode", "moe_attn_workspace_bytes",
+              "moe_check_attn_kv_write"):
         assert hasattr(lib, n), n
     with open("/proc/self/maps") as f:
         maps = f.read()
@@ -488,6 +491,7 @@ def test_attn_workspace_bytes():
     (dict(B=0), INVALID), (dict(B=257), INVALID),
     (dict(qkv=A(1) + 8), INVALID), (dict(pos=A(2) + 4), INVALID), (dict(q=A(5) + 2), INVALID),
     (dict(d=adesc(head_dim=64)), UNSUPPORTED), (dict(d=adesc(n_q=64, n_kv=2)), UNSUPPORTED),
+    (dict(d=adesc(window=0, slots=(1 << 24) + 32)), UNSUPPORTED),
     (dict(d=adesc(n_q=30)), INVALID), (dict(d=adesc(n_kv=0)), INVALID), (dict(d=adesc(slots=500)), INVALID),
     (dict(d=adesc(window=545)), INVALID), (dict(d=adesc(window=-1)), INVALID), (dict(d=adesc(rope=2)), INVALID),
     (dict(d=adesc(rope_theta=1.0)), INVALID), (dict(d=adesc(norm_eps=-1.0)), INVALID),
@@ -521,3 +525,29 @@ def test_attn_decode_errors(which, kw, want):
 
 def test_attn_sinks_are_optional():
     assert adecode("host", sinks=None) == OK
+
+
+def akv(which, d=None, k=A(1), v=A(3), pos=A(2), n=100, B=1, kc=KC, vc=VC):
+    d = d or adesc()
+    if which == "host":
+        return host().moe_check_attn_kv_write(ctypes.byref(d), k, v, pos, n, B, kc, vc)
+    lib = hip()
+    lib.moe_attn_kv_write.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+    return lib.moe_attn_kv_write(ctypes.byref(AttnDesc.from_buffer_copy(d)), k, v, pos, n, B, kc, vc, None)
+
+
+def test_attn_kv_write_valid_call_passes_validation():
+    assert akv("host") == OK and akv("host", B=256, n=1) == OK
+
+
+@pytest.mark.parametrize("which", LIBS)
+@pytest.mark.parametrize("kw,want", [
+    (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(pos=None), INVALID), (dict(kc=None), INVALID),
+    (dict(vc=None), INVALID), (dict(n=0), INVALID), (dict(n=(1 << 24) + 1), INVALID), (dict(B=0), INVALID),
+    (dict(B=257), INVALID), (dict(k=A(1) + 8), INVALID), (dict(pos=A(2) + 4), INVALID),
+    (dict(kc=KC + 2), INVALID), (dict(d=adesc(head_dim=64)), UNSUPPORTED), (dict(d=adesc(slots=40)), INVALID),
+    (dict(vc=KC + 4096), INVALID),           # the caches overlap
+    (dict(kc=A(3) - 4096), INVALID),         # the key cache runs over the value rows
+])
+def test_attn_kv_write_errors(which, kw, want):
+    assert akv(which, **kw) == want

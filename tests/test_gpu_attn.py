@@ -43,6 +43,28 @@ def bf16_ulp_diff(a, b):
     return np.abs(fa - fb) / ulp
 
 
+# The cache's tile layout (the C header's formulas): element d of the slot
+# at offset o of a 32-slot tile.
+_O, _D = np.meshgrid(np.arange(32), np.arange(D), indexing="ij")
+K_INDEX = (((_O // 4) % 2 * 4 + _D // 32) * 64 + (_D // 8) % 4 * 16 + (_O // 8) * 4 + _O % 4) * 8 + _D % 8
+V_INDEX = ((_D // 16) * 64 + (_O // 8) * 16 + _D % 16) * 8 + _O % 8
+
+
+def pack_cache(logical, index):
+    """[B][slots][n_kv][D] -> [B][n_kv][slots/32][4096] in the tile layout."""
+    B, slots, nkv, _ = logical.shape
+    t = logical.reshape(B, slots // 32, 32, nkv, D).transpose(0, 3, 1, 2, 4)   # B, nkv, tiles, o, d
+    out = np.empty((B, nkv, slots // 32, 32 * D), logical.dtype)
+    out[..., index.ravel()] = t.reshape(B, nkv, slots // 32, 32 * D)
+    return out
+
+
+def unpack_cache(packed, index, slots):
+    B, nkv = packed.shape[:2]
+    t = packed.reshape(B, nkv, slots // 32, 32 * D)[..., index.ravel()].reshape(B, nkv, slots // 32, 32, D)
+    return t.transpose(0, 2, 3, 1, 4).reshape(B, slots, nkv, D)
+
+
 def check_rounded(gpu, ref, what):
     d = bf16_ulp_diff(gpu, ref)
     n = int(np.count_nonzero(d > 0))
@@ -100,8 +122,8 @@ class Case:
         self.d_pos = torch.from_numpy(self.pos).cuda()
         self.d_qg, self.d_kg = to_dev_bits(self.qg), to_dev_bits(self.kg)
         self.d_q = torch.empty((self.B, self.n_q, D), dtype=torch.int16, device="cuda")
-        self.d_k = to_dev_bits(self.kc.transpose(0, 2, 1, 3))   # [B][n_kv][slots][D]
-        self.d_v = to_dev_bits(self.vc.transpose(0, 2, 3, 1))   # [B][n_kv][D][slots]
+        self.d_k = to_dev_bits(pack_cache(self.kc, K_INDEX))
+        self.d_v = to_dev_bits(pack_cache(self.vc, V_INDEX))
         self.d_sinks = None if self.sinks is None else torch.from_numpy(self.sinks).cuda()
         self.d_out = torch.empty((self.B, self.n_q, D), dtype=torch.int16, device="cuda")
         self.ws_bytes = moe.moe_attn_workspace_bytes(self.desc, self.B, self.max_ctx)
@@ -129,8 +151,8 @@ class Case:
             check_rounded(self.g_q[ok], self.ref_q[ok], f"{what} q")
         assert np.all(self.g_q[bad] == 0), f"{what}: q of a bad position"
         if caches:
-            gk = from_dev_bits(self.d_k).reshape(self.B, self.n_kv, self.slots, D).transpose(0, 2, 1, 3)
-            gv = from_dev_bits(self.d_v).reshape(self.B, self.n_kv, D, self.slots).transpose(0, 3, 1, 2)
+            gk = unpack_cache(from_dev_bits(self.d_k), K_INDEX, self.slots)
+            gv = unpack_cache(from_dev_bits(self.d_v), V_INDEX, self.slots)
             assert np.array_equal(gv, self.ref_vc), f"{what}: value cache"
             check_rounded(gk, self.ref_kc, f"{what} key cache")
         good = [t for t in range(self.B) if self.span_ok(self.pos[t])]
@@ -188,7 +210,7 @@ def test_attn_window_batch8():
 def test_attn_bad_positions_give_zeros_and_status():
     c = run("attn bad positions", window=0, rope=0, slots=64, pos=(-1, 5, 64, 63), seed=8)
     # the caches of the bad tokens are untouched
-    gk = from_dev_bits(c.d_k).reshape(c.B, c.n_kv, c.slots, D).transpose(0, 2, 1, 3)
+    gk = unpack_cache(from_dev_bits(c.d_k), K_INDEX, c.slots)
     assert np.array_equal(gk[[0, 2]], c.kc[[0, 2]])
 
 
@@ -236,3 +258,39 @@ def test_attn_graph_replays_follow_device_positions():
         c.d_v.copy_(v0)
         c.launch()
         assert np.array_equal(c.fetch().g_out, replay), pos
+
+
+def test_pack_helpers_round_trip():
+    x = np.arange(2 * 64 * 4 * D, dtype=np.uint16).reshape(2, 64, 4, D)
+    for idx in (K_INDEX, V_INDEX):
+        assert np.array_equal(unpack_cache(pack_cache(x, idx), idx, 64), x)
+
+
+@pytest.mark.parametrize("window,slots,first,n", [(0, 256, 0, 256), (513, 544, 1000, 600), (0, 64, 50, 20)])
+def test_kv_write_places_rows_in_the_layout(window, slots, first, n):
+    # rows of positions first .. first + n - 1 (later positions of a ring
+    # overwrite earlier ones in the same slot: written here one call each,
+    # in position order); positions beyond a full layer's slots are skipped
+    log(f"test: kv_write window={window} slots={slots} first={first} n={n}")
+    B, nkv = 2, 4
+    desc = moe.moe_attn_desc(32, nkv, D, window, 0, slots, 0.0, 1e-6)
+    k = synth.normal_bf16(77, 1, 0, 1.0, B * n * nkv * D).reshape(B, n, nkv, D)
+    v = synth.normal_bf16(77, 2, 0, 1.0, B * n * nkv * D).reshape(B, n, nkv, D)
+    kc0 = synth.normal_bf16(77, 3, 0, 1.0, B * slots * nkv * D).reshape(B, slots, nkv, D)
+    d_k, d_v = to_dev_bits(pack_cache(kc0, K_INDEX)), to_dev_bits(pack_cache(kc0, V_INDEX))
+    ref_k, ref_v = kc0.copy(), kc0.copy()
+    for i in range(n):
+        p = first + i
+        if window == 0 and p >= slots:
+            continue
+        ref_k[:, p % slots] = k[:, i]
+        ref_v[:, p % slots] = v[:, i]
+    # one position per call keeps the ring's overwrite order
+    step = n if window == 0 or n <= slots else 1
+    for i0 in range(0, n, step):
+        m = min(step, n - i0)
+        pos = torch.from_numpy(np.array([[first + i0 + i for i in range(m)]] * B, np.int64)).cuda()
+        moe.moe_attn_kv_write(desc, to_dev_bits(k[:, i0:i0 + m]), to_dev_bits(v[:, i0:i0 + m]), pos, m, B, d_k, d_v)
+    torch.cuda.synchronize()
+    assert np.array_equal(unpack_cache(from_dev_bits(d_k), K_INDEX, slots), ref_k)
+    assert np.array_equal(unpack_cache(from_dev_bits(d_v), V_INDEX, slots), ref_v)

@@ -42,7 +42,7 @@ def test_cpu_code_clean_under_asan_and_ubsan(tmp_path):
     env = dict(os.environ, MOE_HOST_LIB_DIR=d, LD_PRELOAD=asan,
                ASAN_OPTIONS="detect_leaks=0:alloc_dealloc_mismatch=0:abort_on_error=0:exitcode=97",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1:exitcode=98")
-    files = ["tests/test_oracle_pins.py", "tests/test_synth.py", "tests/test_compare_helper.py",
+    files = ["tests/test_oracle_pins.py", "tests/test_oracle_attn.py", "tests/test_synth.py", "tests/test_compare_helper.py",
              "tests/test_abi.py"]
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu",
                         "-k", "not hip and not exports", *files],

@@ -120,6 +120,10 @@ _lib.moe_attn_decode.restype = _i32
 _lib.moe_attn_decode.argtypes = [_AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_check_attn_prep.restype = _i32
 _lib.moe_check_attn_prep.argtypes = [_AD, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_attn_kv_write.restype = _i32
+_lib.moe_attn_kv_write.argtypes = [_AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+_lib.moe_check_attn_kv_write.restype = _i32
+_lib.moe_check_attn_kv_write.argtypes = [_AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]
 _lib.moe_check_attn_decode.restype = _i32
 _lib.moe_check_attn_decode.argtypes = [_AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz]
 
@@ -131,7 +135,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes
            "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
            "moe_check_repack_nvfp4", "moe_probe_hbm_read", "moe_gemv_nvfp4", "moe_check_gemv_nvfp4",
            "moe_attn_prep", "moe_attn_workspace_bytes", "moe_attn_decode", "moe_check_attn_prep",
-           "moe_check_attn_decode")
+           "moe_check_attn_decode", "moe_attn_kv_write", "moe_check_attn_kv_write")
 
 
 def lib():
@@ -235,6 +239,12 @@ def moe_attn_prep(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache
     """Q/K norm + RoPE of `batch` tokens; q to q_out, k and v into the caches."""
     _check(_lib.moe_attn_prep(ctypes.byref(desc), _ptr(qkv), _ptr(pos), batch, _ptr(q_gain), _ptr(k_gain),
                               _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "moe_attn_prep")
+
+
+def moe_attn_kv_write(desc, k_rows, v_rows, pos, n, batch, k_cache, v_cache, stream=None):
+    """K/V rows [batch][n][n_kv][128] into the cache slots of positions pos [batch][n]."""
+    _check(_lib.moe_attn_kv_write(ctypes.byref(desc), _ptr(k_rows), _ptr(v_rows), _ptr(pos), n, batch,
+                                  _ptr(k_cache), _ptr(v_cache), _stream(stream)), "moe_attn_kv_write")
 
 
 def moe_attn_workspace_bytes(desc, batch, max_ctx=0):

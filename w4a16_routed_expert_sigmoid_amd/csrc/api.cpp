@@ -309,6 +309,23 @@ moe_status moe_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64
   return hip_status(launch_attn_prep(a, batch, (hipStream_t)stream));
 }
 
+moe_status moe_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, const void *v_rows, const int64_t *pos,
+                             int32_t n, int32_t batch, void *k_cache, void *v_cache, void *stream) {
+  const moe_status st = check_attn_kv_write_call(desc, k_rows, v_rows, pos, n, batch, k_cache, v_cache);
+  if (st != MOE_OK) return st;
+  AttnKvWriteArgs a;
+  a.k_rows = (const uint16_t *)k_rows;
+  a.v_rows = (const uint16_t *)v_rows;
+  a.pos = pos;
+  a.k_cache = (uint16_t *)k_cache;
+  a.v_cache = (uint16_t *)v_cache;
+  a.n = n;
+  a.n_kv = desc->n_kv;
+  a.slots = desc->slots;
+  a.window = desc->window;
+  return hip_status(launch_attn_kv_write(a, batch, (hipStream_t)stream));
+}
+
 moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                            const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
                            void *ws, size_t ws_bytes, void *stream) {

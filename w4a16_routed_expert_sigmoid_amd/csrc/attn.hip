@@ -20,12 +20,16 @@
 //                   block merges its waves through LDS, then writes the
 //                   final BF16 output (one chunk) or an FP32 partial.
 //   k_attn_combine  merges a token's partials and applies the sink.
+//   k_attn_kv_write K/V rows (natural layout) into cache slots.
 //
-// Cache layouts (per token row and KV head): keys [slots][128], values
-// transposed [128][slots].  With values transposed, the 8 positions a lane
-// feeds into P V are 16 contiguous bytes of one value row, and the
-// probabilities leave the score MFMA already in the lane order that P V
-// takes (see k_attn_decode).
+// Cache layout (per token row and KV head): tiles of 32 positions, each
+// stored in the lane order of the MFMA operands that read it (attn_k_index,
+// attn_v_index), so every operand is one contiguous 1 KiB wave load.  Read
+// in the operands' natural layout instead, a 16-lane group would touch 16
+// rows per load and the address units, not HBM, would set the pace.  The
+// values are stored by dimension within a tile, so the 8 positions a lane
+// feeds into P V are 16 contiguous bytes, and the probabilities leave the
+// score MFMA already in the lane order that P V takes (see k_attn_decode).
 #include "common.h"
 
 namespace moe {
@@ -62,19 +66,23 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
   const uint16_t *src = a.qkv + ((int64_t)b * units + u) * kAttnD;
   const uint32_t x0b = src[lane], x1b = src[lane + 64];
 
-  if (u >= a.n_q + a.n_kv) {  // v head: element d goes to row d of the transposed cache
+  // the cache tile of the slot, and the position's offset in it
+  const int o = (int)(slot % kAttnTile);
+  const int64_t tile = (slot / kAttnTile) * kAttnTileElems;
+  if (u >= a.n_q + a.n_kv) {  // v head
     if (!ok) return;
     const int g = u - a.n_q - a.n_kv;
-    uint16_t *vt = a.v_cache + ((int64_t)b * a.n_kv + g) * kAttnD * a.slots + slot;
-    vt[(int64_t)lane * a.slots] = (uint16_t)x0b;
-    vt[(int64_t)(lane + 64) * a.slots] = (uint16_t)x1b;
+    uint16_t *vt = a.v_cache + ((int64_t)b * a.n_kv + g) * a.slots * kAttnD + tile;
+    vt[attn_v_index(o, lane)] = (uint16_t)x0b;
+    vt[attn_v_index(o, lane + 64)] = (uint16_t)x1b;
     return;
   }
   const bool is_q = u < a.n_q;
-  uint16_t *dst = is_q ? a.q_out + ((int64_t)b * a.n_q + u) * kAttnD
-                       : a.k_cache + (((int64_t)b * a.n_kv + (u - a.n_q)) * a.slots + slot) * kAttnD;
   if (!ok) {
-    if (is_q) dst[lane] = dst[lane + 64] = 0;
+    if (is_q) {
+      uint16_t *dq = a.q_out + ((int64_t)b * a.n_q + u) * kAttnD;
+      dq[lane] = dq[lane + 64] = 0;
+    }
     return;
   }
   // RMSNorm of the head: squares of BF16 values are exact in FP64.
@@ -94,8 +102,38 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
     y0 = f64_to_bf16(ya * cs - yb * sn);
     y1 = f64_to_bf16(yb * cs + ya * sn);
   }
-  dst[lane] = (uint16_t)y0;
-  dst[lane + 64] = (uint16_t)y1;
+  if (is_q) {
+    uint16_t *dq = a.q_out + ((int64_t)b * a.n_q + u) * kAttnD;
+    dq[lane] = (uint16_t)y0;
+    dq[lane + 64] = (uint16_t)y1;
+  } else {
+    uint16_t *kt = a.k_cache + ((int64_t)b * a.n_kv + (u - a.n_q)) * a.slots * kAttnD + tile;
+    kt[attn_k_index(o, lane)] = (uint16_t)y0;
+    kt[attn_k_index(o, lane + 64)] = (uint16_t)y1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K/V rows into the cache layout.  Grid (n, B), 4 waves; wave w writes KV
+// heads w, w + 4, ... of row i of token row b, lane l elements l and l + 64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attn_kv_write(AttnKvWriteArgs a) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t pos = a.pos[(int64_t)b * a.n + i];
+  int64_t lo;
+  if (!attn_range(pos, a.window, a.slots, (int64_t)1 << 62, lo)) return;
+  const int64_t slot = pos % a.slots;
+  const int o = (int)(slot % kAttnTile);
+  const int64_t tile = (slot / kAttnTile) * kAttnTileElems;
+  for (int g = threadIdx.x >> 6; g < a.n_kv; g += 4) {
+    const int64_t row = (((int64_t)b * a.n + i) * a.n_kv + g) * kAttnD;
+    const int64_t base = ((int64_t)b * a.n_kv + g) * a.slots * kAttnD + tile;
+    a.k_cache[base + attn_k_index(o, lane)] = a.k_rows[row + lane];
+    a.k_cache[base + attn_k_index(o, lane + 64)] = a.k_rows[row + lane + 64];
+    a.v_cache[base + attn_v_index(o, lane)] = a.v_rows[row + lane];
+    a.v_cache[base + attn_v_index(o, lane + 64)] = a.v_rows[row + lane + 64];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,15 +147,15 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
 //
 // Scores, per 32-position tile and per half tt (0, 1): A = keys of 16
 // positions, row r <-> position offset 8 (r / 4) + 4 tt + r % 4; k-step s
-// (dims 32 s .. 32 s + 31) gives group g the dims 8 (4 s + g) .. + 8, i.e.
-// the 4 groups read 64 contiguous bytes of each key row.  B = q of the
+// (dims 32 s .. 32 s + 31) gives group g the dims 8 (4 s + g) .. + 8 (the
+// cache tile holds exactly this operand as 1 KiB in lane order).  B = q of the
 // group's heads, column r = head r (zero beyond G).  So C value i of lane l
 // is the score of head r at position offset 8 g + 4 tt + i: each lane holds
 // one head's scores at 8 consecutive positions 8 g .. 8 g + 7.
 //
 // P V, per 16-dim tile dt: out^T[dims][heads] += V^T[dims][32 positions] *
-// P[32 positions][heads].  A lane l = value row dt*16 + r, positions
-// 8 g .. 8 g + 7 (16 contiguous bytes of the transposed cache); B lane l =
+// P[32 positions][heads].  A lane l = value dim dt*16 + r, positions
+// 8 g .. 8 g + 7 (16 contiguous bytes of the cache tile); B lane l =
 // head r, the same 8 positions: exactly the 8 probabilities the lane holds.
 // C lane l value i = dim dt*16 + 4 g + i of head r.
 // ---------------------------------------------------------------------------
@@ -130,17 +168,18 @@ struct AttnTileRegs {
   u32x4 v[8];     // transposed values: dim tile dt
 };
 
-__device__ __forceinline__ void attn_load_tile(AttnTileRegs &t, const uint16_t *kb, const uint16_t *vb, int slots,
-                                               int64_t tile, int r, int g) {
-  const int s0 = (int)((tile * kAttnTile) % slots);
+// Cache tile st of a token row's KV head; each operand is one contiguous
+// 1 KiB wave load (lane order of the tile layout).
+__device__ __forceinline__ void attn_load_tile(AttnTileRegs &t, const uint16_t *kb, const uint16_t *vb, int st,
+                                               int lane) {
+  const int64_t off = (int64_t)st * kAttnTileElems + lane * 8;
+  const uint16_t *kt = kb + off, *vt = vb + off;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const uint16_t *row = kb + (int64_t)(s0 + (r >> 2) * 8 + tt * 4 + (r & 3)) * kAttnD;
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) t.k[tt][s] = ld16(row + (s * 4 + g) * 8);
-  }
+    for (int s = 0; s < 4; ++s) t.k[tt][s] = ld16(kt + (tt * 4 + s) * 512);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) t.v[dt] = ld16(vb + (int64_t)(dt * 16 + r) * slots + s0 + g * 8);
+  for (int dt = 0; dt < 8; ++dt) t.v[dt] = ld16(vt + dt * 512);
 }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -165,7 +204,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
   __shared__ float s_m[kAttnWaves][kAttnMaxGroup], s_l[kAttnWaves][kAttnMaxGroup];
 
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: tile indices and the edge test stay in
+  // scalar registers and branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int G = a.G;
 
@@ -207,7 +248,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
     }
   }
   const uint16_t *kb = a.k_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
-  const uint16_t *vb = a.v_cache + ((int64_t)b * a.n_kv + kv) * kAttnD * a.slots;
+  const uint16_t *vb = a.v_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
   const float qscale = kLog2e / sqrtf((float)kAttnD);
 
   f32x4 acc[8];
@@ -215,76 +256,111 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
   for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  int64_t t = t0 + wave;
-  if (t <= t1) {
-    AttnTileRegs cur, nxt;
-    attn_load_tile(cur, kb, vb, a.slots, t, r, g);
-    for (; t <= t1; t += kAttnWaves) {
-      // next tile (unconditional: past the end it reloads this tile, a cache hit)
-      const int64_t tn = t + kAttnWaves <= t1 ? t + kAttnWaves : t;
-      attn_load_tile(nxt, kb, vb, a.slots, tn, r, g);
-
-      f32x4 sc[2];
+  // Tiles t0 + wave, t0 + wave + 8, ... of the chunk, two register sets
+  // used in turn: the loads of the next tile are in flight while this one
+  // is computed (a copy between the sets would wait for them).  Loads are
+  // unconditional: past the end they reload the last tile, a cache hit.
+  auto tile_step = [&](const AttnTileRegs &cur, int64_t t) {
+    f32x4 sc[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sc[tt] = mfma16(cur.k[tt][s], qv[s], sc[tt]);
-      }
-      // positions 32 t + 8 g + j, j = 4 tt + i
-      float x[8];
+      for (int s = 0; s < 4; ++s) sc[tt] = mfma16(cur.k[tt][s], qv[s], sc[tt]);
+    }
+    // positions 32 t + 8 g + j, j = 4 tt + i
+    float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][j & 3] * qscale;
-      const int64_t p0 = t * kAttnTile + g * 8;
-      const bool edge = t * kAttnTile < lo || t * kAttnTile + kAttnTile - 1 > pos;
-      uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
-      if (edge) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool in = p0 + j >= lo && p0 + j <= pos;
-          if (!in) {
-            x[j] = -INFINITY;
-            vmask[j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          }
-        }
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-      mx = col_max(mx);
-      const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid position
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float p[8], ps = 0.f;
+    for (int j = 0; j < 8; ++j) x[j] = sc[j >> 2][j & 3] * qscale;
+    // A tile that straddles lo or pos (uniform): positions outside lo..pos
+    // get no weight, and their values (possibly never written) are zeroed
+    // so that 0 * garbage cannot make a NaN.
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    const int64_t tp = t * kAttnTile;
+    const bool edge = tp < lo || tp + kAttnTile - 1 > pos;
+    if (edge) {
+      const int first = (int)(lo - tp > 0 ? lo - tp : 0);                         // 0..31
+      const int last = (int)(pos - tp < kAttnTile - 1 ? pos - tp : kAttnTile - 1);  // 0..31
+      uint32_t vm[4] = {~0u, ~0u, ~0u, ~0u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
-        ps += p[j];
+        const int o = g * 8 + j;
+        const bool in = o >= first && o <= last;
+        x[j] = in ? x[j] : -INFINITY;
+        vm[j >> 1] &= in ? ~0u : ((j & 1) ? 0x0000FFFFu : 0xFFFF0000u);
       }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      // P as two BF16 terms
-      u32x4 ph, pl;
-      {
-        uint32_t h[4], l[4];
+      vmask = u32x4{vm[0], vm[1], vm[2], vm[3]};
+    }
+    float mx = x[0];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          h[w] = f32x2_to_bf16x2(p[2 * w], p[2 * w + 1]);
-          const float r0 = p[2 * w] - bf16_to_f32(h[w] & 0xFFFFu);
-          const float r1 = p[2 * w + 1] - bf16_to_f32(h[w] >> 16);
-          l[w] = f32x2_to_bf16x2(r0, r1);
-        }
-        ph = u32x4{h[0], h[1], h[2], h[3]};
-        pl = u32x4{l[0], l[1], l[2], l[3]};
-      }
-      const u32x4 vm = u32x4{vmask[0], vmask[1], vmask[2], vmask[3]};
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    mx = col_max(mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid position
+    const bool rescale = __any(m_new != m_run);  // rare once the maxima settle
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
+      ps += p[j];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // P as two BF16 terms
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      h[w] = f32x2_to_bf16x2(p[2 * w], p[2 * w + 1]);
+      const float r0 = p[2 * w] - bf16_to_f32(h[w] & 0xFFFFu);
+      const float r1 = p[2 * w + 1] - bf16_to_f32(h[w] >> 16);
+      l[w] = f32x2_to_bf16x2(r0, r1);
+    }
+    const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]}, pl = u32x4{l[0], l[1], l[2], l[3]};
+    if (rescale) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    }
+    if (edge) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        acc[dt] *= alpha;
-        const u32x4 vv = cur.v[dt] & vm;
+        const u32x4 vv = cur.v[dt] & vmask;
         acc[dt] = mfma16(vv, ph, acc[dt]);
         acc[dt] = mfma16(vv, pl, acc[dt]);
       }
-      cur = nxt;
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt] = mfma16(cur.v[dt], ph, acc[dt]);
+        acc[dt] = mfma16(cur.v[dt], pl, acc[dt]);
+      }
+    }
+  };
+  // Cache tiles follow the tiles: st = t mod (slots / 32), advanced by
+  // addition (no division per tile).
+  int64_t t = t0 + wave;
+  if (t <= t1) {
+    const int nst = a.slots / kAttnTile;
+    auto advance = [nst](int st) {
+      st += kAttnWaves;
+      while (st >= nst) st -= nst;
+      return st;
+    };
+    int sa = (int)(t % nst);
+    AttnTileRegs ra, rb;
+    attn_load_tile(ra, kb, vb, sa, lane);
+    for (;;) {
+      const int64_t tb = t + kAttnWaves;
+      const int sb = advance(sa);
+      attn_load_tile(rb, kb, vb, tb <= t1 ? sb : sa, lane);
+      tile_step(ra, t);
+      if (tb > t1) break;
+      const int64_t ta = tb + kAttnWaves;
+      const int sa2 = advance(sb);
+      attn_load_tile(ra, kb, vb, ta <= t1 ? sa2 : sb, lane);
+      tile_step(rb, tb);
+      if (ta > t1) break;
+      t = ta;
+      sa = sa2;
     }
   }
   l_run = col_sum(l_run);
@@ -331,50 +407,79 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
   }
 }
 
-// Grid (n_kv, B), 512 threads: merge a token's chunk partials, apply the sink.
-__global__ __launch_bounds__(512) void k_attn_combine(AttnDecodeArgs a) {
-  const int kv = blockIdx.x, b = blockIdx.y;
-  const int G = a.G;
-  if (kv == 0 && b == 0 && threadIdx.x < kWave) {
+// Grid (n_q, B), 256 threads: merge one query head's chunk partials and
+// apply its sink.  Thread (cg, col): column col of 32 four-dim columns,
+// chunks cg, cg + 8, ...; the 8 chunk groups are summed through LDS.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(AttnDecodeArgs a) {
+  constexpr int kGroups = kCombineThreads / 32;
+  __shared__ float s_m[kCombineThreads / kWave], s_l[kGroups];
+  __shared__ f32x4 s_acc[kGroups][32];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int G = a.G, kv = h / G, n = h % G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (h == 0 && b == 0 && tid < kWave) {
     uint32_t bad = 0;
-    for (int t = threadIdx.x; t < a.B; t += kWave) {
+    for (int t = tid; t < a.B; t += kWave) {
       int64_t lo;
       bad |= attn_range(a.pos[t], a.window, a.slots, a.span, lo) ? 0u : (uint32_t)kStatusBadPos;
     }
     bad = wave_max_u32(bad);
-    if (threadIdx.x == 0) *a.status = bad;
+    if (tid == 0) *a.status = bad;
   }
   const int64_t pos = a.pos[b];
   int64_t lo = 0;
   const bool ok = attn_range(pos, a.window, a.slots, a.span, lo);
-  uint16_t *outb = a.out + ((int64_t)b * a.n_q + (int64_t)kv * G) * kAttnD;
-  int nch = 0;
-  if (ok) {
-    const int64_t tiles = pos / kAttnTile - lo / kAttnTile + 1;
-    nch = (int)((tiles + a.tpc - 1) / a.tpc);
+  uint16_t *outh = a.out + ((int64_t)b * a.n_q + h) * kAttnD;
+  const int cg = tid / 32, col = tid % 32;
+  if (!ok) {
+    if (tid < 32) *reinterpret_cast<uint2 *>(outh + col * 4) = uint2{0u, 0u};
+    return;
   }
+  const int64_t tiles = pos / kAttnTile - lo / kAttnTile + 1;
+  const int nch = (int)((tiles + a.tpc - 1) / a.tpc);
   const int64_t pf = attn_part_floats(G);
   const float *pb = a.part + ((int64_t)b * a.n_kv + kv) * a.chunks * pf;
-  for (int idx = threadIdx.x; idx < G * (kAttnD / 4); idx += blockDim.x) {
-    const int n = idx / (kAttnD / 4), d = (idx % (kAttnD / 4)) * 4;
-    if (!ok) {
-      *reinterpret_cast<uint2 *>(outb + n * kAttnD + d) = uint2{0u, 0u};
-      continue;
+  const float sk = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+
+  // the largest chunk maximum, and the sink
+  float m = -INFINITY;
+  for (int ch = tid; ch < nch; ch += kCombineThreads) m = fmaxf(m, pb[ch * pf + G * kAttnD + n]);
+  m = fmaxf(m, xor_lane<1>(m));
+  m = fmaxf(m, xor_lane<2>(m));
+  m = fmaxf(m, xor_lane<4>(m));
+  m = fmaxf(m, xor_lane<8>(m));
+  m = fmaxf(m, xor_lane<16>(m));
+  m = fmaxf(m, xor_lane<32>(m));
+  if (lane == 0) s_m[wave] = m;
+  __syncthreads();
+  float M = sk;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / kWave; ++w) M = fmaxf(M, s_m[w]);
+
+  // chunk group cg sums chunks cg, cg + 8, ... (independent loads)
+  float L = 0.f;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = cg; ch < nch; ch += kGroups) {
+    const float *pp = pb + ch * pf;
+    const float f = __builtin_amdgcn_exp2f(pp[G * kAttnD + n] - M);
+    L += f * pp[G * kAttnD + G + n];
+    A += f * *reinterpret_cast<const f32x4 *>(pp + n * kAttnD + col * 4);
+  }
+  s_acc[cg][col] = A;
+  if (col == 0) s_l[cg] = L;
+  __syncthreads();
+  if (tid < 32) {
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    float Lt = __builtin_amdgcn_exp2f(sk - M);
+#pragma unroll
+    for (int c = 0; c < kGroups; ++c) {
+      S += s_acc[c][tid];
+      Lt += s_l[c];
     }
-    float M = -INFINITY;
-    for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, pb[ch * pf + G * kAttnD + n]);
-    const float sk = a.sinks ? a.sinks[kv * G + n] * kLog2e : -INFINITY;
-    const float M2 = fmaxf(M, sk);
-    float L = __builtin_amdgcn_exp2f(sk - M2);
-    f32x4 A = {0.f, 0.f, 0.f, 0.f};
-    for (int ch = 0; ch < nch; ++ch) {
-      const float *pp = pb + ch * pf;
-      const float f = __builtin_amdgcn_exp2f(pp[G * kAttnD + n] - M2);
-      L += f * pp[G * kAttnD + G + n];
-      A += f * *reinterpret_cast<const f32x4 *>(pp + n * kAttnD + d);
-    }
-    const f32x4 o = A * (1.0f / L);
-    *reinterpret_cast<uint2 *>(outb + n * kAttnD + d) = uint2{f32x2_to_bf16x2(o[0], o[1]), f32x2_to_bf16x2(o[2], o[3])};
+    const f32x4 o = S * (1.0f / Lt);
+    *reinterpret_cast<uint2 *>(outh + tid * 4) = uint2{f32x2_to_bf16x2(o[0], o[1]), f32x2_to_bf16x2(o[2], o[3])};
   }
 }
 
@@ -385,11 +490,16 @@ hipError_t launch_attn_prep(const AttnPrepArgs &a, int B, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_attn_kv_write(const AttnKvWriteArgs &a, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(k_attn_kv_write, dim3(a.n, B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(k_attn_decode, dim3(a.chunks, a.n_kv, a.B), dim3(kAttnWaves * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.chunks == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_kv, a.B), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_q, a.B), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

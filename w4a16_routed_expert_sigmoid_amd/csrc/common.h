@@ -387,7 +387,15 @@ struct AttnDecodeArgs {
   int tpc, chunks;
 };
 
+struct AttnKvWriteArgs {
+  const uint16_t *k_rows, *v_rows;  // [B][n][n_kv][128]
+  const int64_t *pos;               // [B][n]
+  uint16_t *k_cache, *v_cache;
+  int n, n_kv, slots, window;
+};
+
 hipError_t launch_attn_prep(const AttnPrepArgs &a, int B, hipStream_t stream);
+hipError_t launch_attn_kv_write(const AttnKvWriteArgs &a, int B, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *sink, hipStream_t stream);
 

@@ -39,6 +39,22 @@ constexpr int kAttnWaves = 8;
 constexpr int kAttnMaxBatch = 256;
 constexpr int kAttnTargetBlocks = 256;  // one block per CU of the chip
 constexpr int64_t kAttnMaxPos = (int64_t)1 << 40;  // positions 0 .. 2^40 - 1
+constexpr int32_t kAttnMaxSlots = 1 << 24;         // cache positions per token row
+
+// KV-cache tiles: 32 positions of one (token row, KV head), 4096 BF16 keys
+// then, in the value cache, 4096 BF16 values, each stored in the lane order
+// of the matrix-core operands that read them, so that every 16-byte lane
+// load of the decode kernel is part of one contiguous 1 KiB wave load.
+// Position offset o (0..31) in its tile, dimension d (0..127):
+//   keys:   operand (half tt, k-step s) of the score product; lane 16 g + r
+//           holds position 8 (r / 4) + 4 tt + r % 4, dims 8 (4 s + g) .. + 8
+//   values: operand dt of the value product; lane 16 g + r holds dim
+//           16 dt + r, positions 8 g .. 8 g + 7
+constexpr int kAttnTileElems = kAttnTile * kAttnD;
+constexpr int attn_k_index(int o, int d) {
+  return ((((o >> 2) & 1) * 4 + (d >> 5)) * 64 + ((d >> 3) & 3) * 16 + (((o >> 3) << 2) | (o & 3))) * 8 + (d & 7);
+}
+constexpr int attn_v_index(int o, int d) { return ((d >> 4) * 64 + (o >> 3) * 16 + (d & 15)) * 8 + (o & 7); }
 
 // FP32 partial of one (token, KV head, chunk): the G heads' 128 weighted
 // value sums, then their running maxima and sums, padded to 16 bytes.

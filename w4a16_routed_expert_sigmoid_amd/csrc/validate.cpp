@@ -285,7 +285,8 @@ moe_status check_attn_desc(const moe_attn_desc *d) {
   if (d->rope != 0 && d->rope != 1) return MOE_ERR_INVALID_ARG;
   if (d->rope && !(d->rope_theta > 1.0 && isfinite(d->rope_theta))) return MOE_ERR_INVALID_ARG;
   if (!(d->norm_eps >= 0.0f) || !isfinite(d->norm_eps)) return MOE_ERR_INVALID_ARG;
-  if (d->head_dim != kAttnD || d->n_q / d->n_kv > kAttnMaxGroup) return MOE_ERR_UNSUPPORTED;
+  if (d->head_dim != kAttnD || d->n_q / d->n_kv > kAttnMaxGroup || d->slots > kAttnMaxSlots)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -342,6 +343,22 @@ moe_status check_attn_prep_call(const moe_attn_desc *desc, const void *qkv, cons
                       {q_gain, kAttnD * 2},
                       {k_gain, kAttnD * 2}};
   return outputs_disjoint(r, 7, 3) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+moe_status check_attn_kv_write_call(const moe_attn_desc *desc, const void *k_rows, const void *v_rows,
+                                   const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
+                                   const void *v_cache) {
+  const moe_status st = check_attn_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!k_rows || !v_rows || !pos || !k_cache || !v_cache) return MOE_ERR_INVALID_ARG;
+  if (n < 1 || n > (1 << 24) || batch < 1 || batch > kAttnMaxBatch) return MOE_ERR_INVALID_ARG;
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(pos, 8) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return MOE_ERR_INVALID_ARG;
+  const size_t cb = cache_bytes(*desc, batch);
+  const size_t rows = (size_t)batch * n * desc->n_kv * kAttnD * 2;
+  const Range r[5] = {{k_cache, cb}, {v_cache, cb}, {k_rows, rows}, {v_rows, rows}, {pos, (size_t)batch * n * 8}};
+  return outputs_disjoint(r, 5, 2) ? MOE_OK : MOE_ERR_INVALID_ARG;
 }
 
 moe_status check_attn_decode_call(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
@@ -441,6 +458,12 @@ moe_status moe_check_attn_prep(const moe_attn_desc *desc, const void *qkv, const
                                const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
                                const void *v_cache) {
   return check_attn_prep_call(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache);
+}
+
+moe_status moe_check_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, const void *v_rows,
+                                   const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
+                                   const void *v_cache) {
+  return check_attn_kv_write_call(desc, k_rows, v_rows, pos, n, batch, k_cache, v_cache);
 }
 
 moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,
