@@ -188,6 +188,33 @@ def time_stack(args, dev, insts, descs, B, bias, label):
     moe.moe_decode_wait_status(ws, status[0:1])
     nonfinite = not torch.isfinite(y.view(torch.bfloat16).float()).all().item()
 
+    # One token: the same stack through the persistent step (runs of MoE
+    # layers in one kernel each), its own graph, timed the same way.
+    ms_persist, persist_same, persist_wait = None, None, 0
+    if B == 1:
+        wsp = torch.zeros(moe.moe_decode_step_persistent_workspace_bytes(descs, B), dtype=torch.uint8, device=dev)
+        yp = torch.empty_like(x)
+        moe.moe_decode_step_persistent(descs, wts, x, B, yp, wsp, wsp.numel())
+        torch.cuda.synchronize()
+        gp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp):
+            moe.moe_decode_step_persistent(descs, wts, x, B, yp, wsp, wsp.numel())
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            gp.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            gp.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_persist = e0.elapsed_time(e1) / args.steps
+        persist_same = bool(torch.equal(yp, y))
+        st_p = torch.full((1,), -1, dtype=torch.int32, device=dev)
+        moe.moe_decode_wait_status(wsp, st_p)
+        persist_wait = int(st_p.item())
+        del wsp, gp
+
     # Per-layer calls (the same computation), eager, with HIP events
     # attached to each kernel dispatch (start/stop of its execution), and
     # the distinct experts per layer from the top-k outputs.
@@ -221,11 +248,12 @@ def time_stack(args, dev, insts, descs, B, bias, label):
     same = torch.equal(acts[-1], y)
     moe_layers = [i for i in range(n_layers) if descs[i].n_experts > 0]
     distinct = [len(np.unique(idx[i].cpu().numpy())) for i in moe_layers]
-    wait = int(status[0].item()) | int(st_any.item())
+    wait = int(status[0].item()) | int(st_any.item()) | persist_wait
     log(f"{label}: {ms_step * 1e3 / n_layers:.2f} us/layer in the graph, stage kernels {stage_us} us, "
-        f"wait status {wait}")
+        f"wait status {wait}" + (f"; persistent step {ms_persist * 1e3 / n_layers:.2f} us/layer, "
+                                 f"equal {persist_same}" if ms_persist else ""))
     return dict(ms_step=ms_step, distinct=distinct, stage_us=stage_us, nonfinite=nonfinite,
-                step_equals_layers=bool(same), wait_status=wait)
+                step_equals_layers=bool(same), wait_status=wait, ms_persist=ms_persist, persist_same=persist_same)
 
 
 def stream_ceiling(dev):
@@ -374,7 +402,10 @@ def run(args, dev):
                 "selected_bytes_per_step": int(b),
                 "distinct_experts_mean": round(float(np.mean(r["distinct"])), 2) if r["distinct"] else None,
                 "stage_kernel_us": [round(v, 3) for v in r["stage_us"]],
-                "step_equals_layer_calls": r["step_equals_layers"], "wait_status": r["wait_status"]}
+                "step_equals_layer_calls": r["step_equals_layers"], "wait_status": r["wait_status"],
+                "persistent_step_us_per_layer": (round(r["ms_persist"] * 1e3 / n_layers, 3)
+                                                 if r["ms_persist"] else None),
+                "persistent_step_equals_step": r["persist_same"]}
 
     warn = []
     if pf is not None and pf["nonfinite"]:
@@ -402,6 +433,8 @@ def run(args, dev):
     configs["step49_b1"] = s49
     if r49["nonfinite"]:
         warn.append("non-finite outputs")
+    if any(r is not None and r["persist_same"] is False for r in (r1, r49)):
+        warn.append("the persistent step's output differs from the step's")
     r1 = r1 if r1 is not None else r49
     del pool, step_pool
     torch.cuda.empty_cache()

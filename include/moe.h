@@ -184,6 +184,32 @@ size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_la
 moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
                            const void *x, int32_t batch, void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Workspace bytes moe_decode_step_persistent needs: the step's, plus the
+ * per-layer hand-over stages of one persistent launch (about 4.7 MB for
+ * the full 256-expert layer at hidden 2048), or 0 as for the step. */
+size_t moe_decode_step_persistent_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers,
+                                                  int32_t max_batch);
+
+/* moe_decode_step with cross-layer overlap: the same computation, inputs
+ * and outputs, bit for bit.  At batch 1, runs of consecutive layers with
+ * routed experts and one shape (up to 24 per launch) run in one persistent
+ * kernel: a layer's output is handed to the next layer's blocks inside the
+ * kernel instead of across a launch, and each block requests its next
+ * layer's routing-independent weights (router rows) before that hand-over
+ * ("Day-0 Support for Flint on vLLM", section "Optimizations": the
+ * low-latency path starts each kernel's weight loads while the previous one
+ * runs).  Other layers, and runs whose blocks cannot all be resident on the
+ * device at once (checked per call), run as in moe_decode_step.  The
+ * persistent kernel's blocks wait on each other, so nothing else should run
+ * on the GPU at the same time: a wait that is starved gives up after a
+ * bounded time and reports status bit 16 (moe_decode_wait_status).
+ *  ws: ws_bytes >= moe_decode_step_persistent_workspace_bytes(descs,
+ *  n_layers, batch); otherwise as moe_decode_step.
+ * Errors: as moe_decode_step; WORKSPACE; HIP. */
+moe_status moe_decode_step_persistent(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                      int32_t n_layers, const void *x, int32_t batch, void *y, void *ws,
+                                      size_t ws_bytes, void *stream);
+
 /* Dense projection on one NVFP4 matrix for a small batch: the small-batch
  * dense GEMV the pages run on the same packed NVFP4 weights as the MoE
  * kernel, for the projections outside the MoE blocks (attention QKV and
@@ -248,7 +274,8 @@ moe_status moe_decode_layer_timed(const moe_layer_desc *desc, const moe_layer_we
  * bounded (a wait that never ends would hang the GPU).  A wait that runs
  * out of polls ORs a bit into a status word at the start of the workspace,
  * which every call zeroes first: 1 = the logits, 2 = the intermediate, 4 =
- * the logits of a batch's routing block.  moe_attn_decode writes bit 8 there
+ * the logits of a batch's routing block, 16 = a layer's input in the
+ * persistent step.  moe_attn_decode writes bit 8 there
  * (a position out of range).  A non-zero word means that call's outputs
  * must not be used.  This enqueues a copy of the word into status_out (device
  * int32) on `stream`, after the calls enqueued before it.  ws == NULL: the
@@ -293,6 +320,9 @@ moe_status moe_check_decode_layer(const moe_layer_desc *desc, const moe_layer_we
                                   const void *ws, size_t ws_bytes);
 moe_status moe_check_decode_step(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
                                  const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes);
+moe_status moe_check_decode_step_persistent(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                            int32_t n_layers, const void *x, int32_t batch, const void *y,
+                                            const void *ws, size_t ws_bytes);
 moe_status moe_check_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                                    int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
                                    const void *ws, size_t ws_bytes);

@@ -57,6 +57,10 @@ def _declare(lib):
     lib.moe_decode_workspace_bytes.argtypes = [D, _i32]
     lib.moe_decode_step_workspace_bytes.restype = _sz
     lib.moe_decode_step_workspace_bytes.argtypes = [D, _i32, _i32]
+    lib.moe_decode_step_persistent_workspace_bytes.restype = _sz
+    lib.moe_decode_step_persistent_workspace_bytes.argtypes = [D, _i32, _i32]
+    lib.moe_check_decode_step_persistent.restype = _i32
+    lib.moe_check_decode_step_persistent.argtypes = [D, W, _i32, _vp, _i32, _vp, _vp, _sz]
     lib.moe_prefill_workspace_bytes.restype = _sz
     lib.moe_prefill_workspace_bytes.argtypes = [D, _i32]
     lib.moe_nvfp4_matrix_bytes.restype = _sz
@@ -551,3 +555,20 @@ def test_attn_kv_write_valid_call_passes_validation():
 ])
 def test_attn_kv_write_errors(which, kw, want):
     assert akv(which, **kw) == want
+
+
+def test_persistent_step_workspace_and_checks():
+    d = desc()
+    ds = (Desc * 3)(d, d, d)
+    ww = (Weights * 3)(weights(), weights(), weights())
+    step = host().moe_decode_step_workspace_bytes(ds, 3, 1)
+    pers = host().moe_decode_step_persistent_workspace_bytes(ds, 3, 1)
+    # the step's bytes plus 24 per-layer stage sets: logits (16 x 256 FP32),
+    # h (16 x 7 x 512 BF16) and the layer input (16 x 2048 BF16)
+    assert pers == step + 24 * (16 * 256 * 4 + 16 * 3584 * 2 + 16 * 2048 * 2)
+    chk = host().moe_check_decode_step_persistent
+    assert chk(ds, ww, 3, A(20), 1, A(21), A(22), pers) == OK
+    assert chk(ds, ww, 3, A(20), 1, A(21), A(22), pers - 1) == WORKSPACE
+    assert chk(ds, ww, 3, A(20), 9, A(21), A(22), pers) == UNSUPPORTED
+    assert chk(ds, ww, 0, A(20), 1, A(21), A(22), pers) == INVALID
+    assert chk(ds, ww, 3, A(20), 1, A(20), A(22), pers) == INVALID   # y == x

@@ -89,6 +89,14 @@ _lib.moe_decode_step.restype = _i32
 _lib.moe_decode_step.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _i32, _vp,
                                  _i32, _vp, _vp, _sz, _vp]
 _lib.moe_prefill_workspace_bytes.restype = _sz
+_lib.moe_decode_step_persistent_workspace_bytes.restype = _sz
+_lib.moe_decode_step_persistent_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32, _i32]
+_lib.moe_decode_step_persistent.restype = _i32
+_lib.moe_decode_step_persistent.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _i32,
+                                            _vp, _i32, _vp, _vp, _sz, _vp]
+_lib.moe_check_decode_step_persistent.restype = _i32
+_lib.moe_check_decode_step_persistent.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights),
+                                                  _i32, _vp, _i32, _vp, _vp, _sz]
 _lib.moe_prefill_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer_desc), _i32]
 _lib.moe_prefill_layer.restype = _i32
 _lib.moe_prefill_layer.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights), _vp,
@@ -135,7 +143,9 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes
            "moe_prefill_layer", "moe_check_decode_layer", "moe_check_decode_step", "moe_check_prefill_layer",
            "moe_check_repack_nvfp4", "moe_probe_hbm_read", "moe_gemv_nvfp4", "moe_check_gemv_nvfp4",
            "moe_attn_prep", "moe_attn_workspace_bytes", "moe_attn_decode", "moe_check_attn_prep",
-           "moe_check_attn_decode", "moe_attn_kv_write", "moe_check_attn_kv_write")
+           "moe_check_attn_decode", "moe_attn_kv_write", "moe_check_attn_kv_write",
+           "moe_decode_step_persistent", "moe_decode_step_persistent_workspace_bytes",
+           "moe_check_decode_step_persistent")
 
 
 def lib():
@@ -280,6 +290,18 @@ def moe_decode_step(descs, weights, x, batch, y, ws, ws_bytes, stream=None):
     n, d, w = _arrays(descs, weights)
     _check(_lib.moe_decode_step(d, w, n, _ptr(x), batch, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_decode_step")
+
+
+def moe_decode_step_persistent_workspace_bytes(descs, max_batch):
+    n, d, _ = _arrays(descs, None)
+    return _lib.moe_decode_step_persistent_workspace_bytes(d, n, max_batch)
+
+
+def moe_decode_step_persistent(descs, weights, x, batch, y, ws, ws_bytes, stream=None):
+    """moe_decode_step with runs of batch-1 MoE layers in one persistent kernel."""
+    n, d, w = _arrays(descs, weights)
+    _check(_lib.moe_decode_step_persistent(d, w, n, _ptr(x), batch, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_decode_step_persistent")
 
 
 def moe_prefill_workspace_bytes(desc, n_tokens):

@@ -69,6 +69,7 @@ void fill_decode_args(const moe_layer_desc *desc, const moe_layer_weights *w, co
   a.ws.sync_lines = (uint32_t *)(base + L.sync_lines);
   a.ws.sync_l = (uint64_t *)(base + L.sync_l);
   a.ws.sync_h = (uint64_t *)(base + L.sync_h);
+  a.ws.sync_y = (uint64_t *)(base + L.sync_y);
   a.ws.xcd_l = (float *)(base + L.xcd_l);
   a.ws.xcd_h = (uint16_t *)(base + L.xcd_h);
   a.ws.stage_l = L.stage_l;
@@ -189,6 +190,70 @@ moe_status moe_decode_step(const moe_layer_desc *descs, const moe_layer_weights 
     fill_decode_args(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, ws, L, (uint32_t)i + 1u, a);
     sc = hip_status(launch_decode(a, (hipStream_t)stream, nullptr));
     if (sc != MOE_OK) return sc;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_decode_step_persistent(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                      int32_t n_layers, const void *x, int32_t batch, void *y, void *ws,
+                                      size_t ws_bytes, void *stream) {
+  PersistLayout P;
+  const moe_status st = check_step_persistent_call(descs, weights, n_layers, x, batch, y, ws, ws_bytes, &P);
+  if (st != MOE_OK) return st;
+  const StepLayout &S = P.step;
+  uint8_t *base = (uint8_t *)ws;
+  const size_t clear = decode_layout(descs[0], batch, S.sync_cap).clear_bytes;
+  moe_status sc = hip_status(launch_sync_clear((uint32_t *)ws, (int64_t)(clear / 4), (hipStream_t)stream));
+  if (sc != MOE_OK) return sc;
+  // Runs of layers that one persistent launch takes, the others one by
+  // one; activations alternate between the two step buffers.
+  const void *in = x;
+  int32_t n_out = 0;  // outputs written so far
+  for (int32_t i = 0; i < n_layers;) {
+    int32_t end = persist_run_end(descs, weights, n_layers, batch, i);
+    const DecodeLayout L = decode_layout(descs[i], batch, S.sync_cap);
+    DecodeArgs a;
+    if (end > i + 1) {
+      fill_decode_args(&descs[i], &weights[i], in, batch, 1, nullptr, nullptr, nullptr, ws, L, (uint32_t)i + 1u, a);
+      bool fits = false;
+      sc = hip_status(persist_fits(a, &fits));
+      if (sc != MOE_OK) return sc;
+      if (!fits) end = i + 1;
+    }
+    void *out = (end == n_layers) ? y : base + ((n_out & 1) ? S.act1 : S.act0);
+    if (end > i + 1) {
+      PersistArgs p;
+      memset(&p, 0, sizeof(p));
+      fill_decode_args(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, ws, L, (uint32_t)i + 1u, p.a);
+      p.stages = base + P.stages;
+      p.slot_bytes = (int64_t)P.slot_bytes;
+      p.off_h = (int64_t)P.off_h;
+      p.off_y = (int64_t)P.off_y;
+      p.n_layers = end - i;
+      for (int32_t j = i; j < end; ++j) {
+        const moe_layer_weights &w = weights[j];
+        PersistLayer &q = p.L[j - i];
+        q.router_w = (const uint16_t *)w.router_w;
+        q.router_b = w.router_b;
+        q.w_gate = (const uint8_t *)w.w_gate;
+        q.w_up = (const uint8_t *)w.w_up;
+        q.w_down = (const uint8_t *)w.w_down;
+        q.w_scale = w.w_scale;
+        q.sh_gate = (const uint8_t *)w.sh_gate;
+        q.sh_up = (const uint8_t *)w.sh_up;
+        q.sh_down = (const uint8_t *)w.sh_down;
+        q.sh_scale = w.sh_scale;
+        q.norm_gain = (const uint16_t *)w.norm_gain;
+      }
+      sc = hip_status(launch_step_b1(p, (hipStream_t)stream));
+    } else {
+      fill_decode_args(&descs[i], &weights[i], in, batch, 1, out, nullptr, nullptr, ws, L, (uint32_t)i + 1u, a);
+      sc = hip_status(launch_decode(a, (hipStream_t)stream, nullptr));
+    }
+    if (sc != MOE_OK) return sc;
+    in = out;
+    ++n_out;
+    i = end;
   }
   return MOE_OK;
 }

@@ -288,6 +288,7 @@ struct DecodeWs {
   uint32_t *sync_lines;   // [kSyncLines][kXcdSlots][64]: word 0 of each 256-byte line is used
   uint64_t *sync_l;       // [E] logit words
   uint64_t *sync_h;       // [(k + 1) * Imax / 2] h words (two BF16 values each)
+  uint64_t *sync_y;       // [H / 2] layer-output words of the persistent step (two BF16 each)
   float *xcd_l;           // [kXcdSlots][stage_l] per-XCD copy of the logits
   uint16_t *xcd_h;        // [kXcdSlots][stage_elems] per-XCD copy of h
   uint32_t *status;       // OR of kStatus* bits: bounded waits that gave up (zeroed per call)
@@ -357,6 +358,32 @@ hipError_t launch_gemv(const GemvArgs &g, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+
+// The persistent one-token step: n_layers consecutive MoE layers of one
+// shape in one launch.  a: the shapes and workspace of the first layer, x
+// its input, y the last layer's output, tag the first layer's tag; L: each
+// layer's weights; stage_*: the per-layer stage sets (slot l at base + l *
+// slot_bytes).
+struct PersistLayer {
+  const uint16_t *router_w;
+  const float *router_b;
+  const uint8_t *w_gate, *w_up, *w_down;
+  const float *w_scale;
+  const uint8_t *sh_gate, *sh_up, *sh_down;
+  const float *sh_scale;
+  const uint16_t *norm_gain;
+};
+struct PersistArgs {
+  DecodeArgs a;
+  uint8_t *stages;
+  int64_t slot_bytes, off_h, off_y;
+  int n_layers;
+  PersistLayer L[kPersistMaxLayers];
+};
+// Whether the persistent kernel's blocks for these shapes can all be
+// resident at once on the current device (its hand-overs need that).
+hipError_t persist_fits(const DecodeArgs &a, bool *fits);
+hipError_t launch_step_b1(const PersistArgs &p, hipStream_t stream);
 // Zeroes words [0, words) of a decode workspace (its status word and sync
 // region) before a call's kernels run.
 hipError_t launch_sync_clear(uint32_t *region, int64_t words, hipStream_t stream);

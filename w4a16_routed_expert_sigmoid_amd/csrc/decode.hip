@@ -1179,21 +1179,24 @@ __device__ __forceinline__ uint32_t *sync_line(const DecodeArgs &a, int which, i
   return a.ws.sync_lines + ((int64_t)which * kXcdSlots + xcc) * 64;
 }
 
-// True in exactly one block per XCD and layer call: the first to swap the
-// tag into the ticket.
+// True in exactly one block per XCD and layer call: the first to raise the
+// ticket to the tag (tags grow within a call: a block that arrives after a
+// later layer's leader is not a leader).
 __device__ __forceinline__ bool take_ticket(const DecodeArgs &a, int which, int xcc) {
-  return __hip_atomic_exchange(sync_line(a, which, xcc), a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+  return __hip_atomic_fetch_max(sync_line(a, which, xcc), a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
          a.tag;
 }
 
-// Leader: once its stores to the stage have reached the L2, the flag.
+// Leader: once its stores to the stage have reached the L2, the flag,
+// raised to the tag and never lowered (a later layer may have raised it).
 __device__ __forceinline__ void raise_flag(const DecodeArgs &a, int which, int xcc) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) *reinterpret_cast<volatile uint32_t *>(sync_line(a, which, xcc)) = a.tag;
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_max(sync_line(a, which, xcc), a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Others (thread 0): until the XCD's flag carries the tag.  The flag is
+// Others (thread 0): until the XCD's flag reaches the tag.  The flag is
 // read with volatile loads (issued sc0 sc1), which miss this CU's cache;
 // plain or sc0 reloads can keep returning a stale line from it (measured:
 // no update in 200,000 polls).  Measured on MI355X: a flag raised by
@@ -1205,7 +1208,7 @@ __device__ __forceinline__ void wait_flag(const DecodeArgs &a, int which, int xc
     const volatile uint32_t *flag = sync_line(a, which, xcc);
     bool seen = false;
     for (int it = 0; it < kWaitSpin && !seen; ++it) {
-      seen = *flag == a.tag;
+      seen = *flag >= a.tag;
       if (!seen) __builtin_amdgcn_s_sleep(1);
     }
     if (!seen) report_giveup(a, giveup_bit);
@@ -1333,8 +1336,13 @@ __device__ __forceinline__ void first_pieces(const DecodeArgs &a, uint4 &x0, uin
 
 // Router rows of block rb: one row per lane group of LPR lanes (lane j of
 // a group takes the row's 16-byte pieces j, j + LPR, ...), dotted with the
-// token in LDS; the logit l = W_r xn + b (FP32) is published.
-__device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, double *s_red) {
+// token in LDS; the logit l = W_r xn + b (FP32) is published.  WAIT (the
+// persistent step): token_wait() runs after the rows are requested and
+// before the token is read, which waits for the previous layer's output;
+// otherwise the token is requested first.
+template <bool WAIT, typename TokenWait>
+__device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, double *s_red,
+                                       TokenWait token_wait) {
   const int H = a.H, E = a.E, n8 = H / 8;
   const int LPR = lanes_per_row(H);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, lg = lane % LPR;
@@ -1347,7 +1355,8 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
   // (indices clamped into the buffers: every load is unconditional, so the
   // waits before the norm cover the token and the gain only)
   const int tc = tid < n8 ? tid : n8 - 1;
-  uint4 x0 = reinterpret_cast<const uint4 *>(a.x)[tc], g0 = make_uint4(0, 0, 0, 0);
+  uint4 x0 = make_uint4(0, 0, 0, 0), g0 = make_uint4(0, 0, 0, 0);
+  if (!WAIT) x0 = reinterpret_cast<const uint4 *>(a.x)[tc];
   if (a.use_norm) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tc];
   uint4 w0[4];
 #pragma unroll
@@ -1357,6 +1366,10 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
     if (!(row < E && lg + i * LPR < n8)) w0[i] = make_uint4(0, 0, 0, 0);
   float bias = a.router_b ? a.router_b[row < E ? row : E - 1] : 0.f;
   if (row >= E) bias = 0.f;
+  if (WAIT) {
+    token_wait();
+    x0 = reinterpret_cast<const uint4 *>(a.x)[tc];
+  }
   stage_token(a, s_x, s_red, x0, g0);
   if (row >= E) return;
   float acc = 0.f;
@@ -1384,10 +1397,14 @@ __device__ inline void router_block_b1(const DecodeArgs &a, int rb, uint4 *s_x, 
   if (lg == 0) publish_tagged(a.ws.sync_l + row, __float_as_uint(v + bias), a.tag);
 }
 
-template <int WT>
+// PERSIST (the persistent step): the residual input of this thread's row
+// is xres (the row this block produced in the previous layer, or x in the
+// first), and the output row goes to xres and, unless `last`, out as tagged
+// words for the next layer's blocks; the last layer writes y.
+template <int WT, bool PERSIST = false>
 __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int xcc, Routing &R, uint32_t *s_mark,
                                               float (&s_part)[2][kMaxDownSlots][kRows], int &s_llead,
-                                              int &s_hlead) {
+                                              int &s_hlead, float *xres = nullptr, bool last = true) {
   const int H = a.H, K = a.I;  // experts present: Is is I or 0
   const int LPR = lanes_per_row(K), C = K / 32;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), lg = lane % LPR;
@@ -1465,7 +1482,18 @@ __device__ __forceinline__ void down_block_b1(const DecodeArgs &a, int dbid, int
       for (int s2 = 0; s2 < slots; ++s2) total += s_part[half][s2][ht];
     __syncthreads();
   }
-  if (ht < kRows) {
+  if constexpr (PERSIST) {
+    // every lane computes (lanes ht < 4 hold the rows), so that the pair
+    // exchange below reads active lanes
+    const int64_t o = r0 + (ht & (kRows - 1));
+    const uint32_t yb = f32_to_bf16(*xres + round_bf16(total));
+    const uint32_t other = xor_lane<1>(yb);
+    if (ht < kRows) {
+      *xres = bf16_to_f32(yb);
+      if (last) a.y[o] = (uint16_t)yb;
+      else if ((ht & 1) == 0) publish_tagged(a.ws.sync_y + o / 2, yb | (other << 16), a.tag);
+    }
+  } else if (ht < kRows) {
     const int64_t o = r0 + ht;
     float v = round_bf16(total);
     if (a.residual) v = bf16_to_f32(a.x[o]) + v;
@@ -1485,7 +1513,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
   __shared__ int s_llead, s_hlead;
   const int b = blockIdx.x;
   if (b < rt_blocks) {
-    router_block_b1(a, b, s_x, s_red);
+    router_block_b1<false>(a, b, s_x, s_red, [] {});
     return;
   }
   const int xcc = xcc_id();
@@ -1506,6 +1534,158 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_layer_b1(DecodeArgs a, 
   } else {
     down_block_b1<WT>(a, b - rt_blocks - gu_blocks, xcc, R, s_mark, s_part, s_llead, s_hlead);
   }
+}
+
+// ---------------------------------------------------------------------------
+// k_step_b1: the persistent one-token step, consecutive MoE layers of one
+// shape in one launch ("Day-0 Support for Flint on vLLM", section
+// "Optimizations": the low-latency path loads each kernel's weights while
+// the previous one still runs).  Every block keeps its k_layer_b1 role in
+// every layer.  Between layers the output, not a kernel boundary, is
+// handed over: the down blocks publish their rows as tagged words, and the
+// router and gate/up blocks of the next layer take them through their
+// XCD's stage like the logits and h.  So a router block has its next
+// layer's rows in flight while it waits for that layer's input, and no
+// launch separates the layers.  The down blocks keep their rows of the
+// residual stream in registers.  Every block must be resident at once (the
+// host checks the occupancy); each layer has its own stage set, so no block
+// reads a stage address twice in a launch; tickets and flags only grow, so
+// a block that is one layer behind cannot undo a later layer's hand-over.
+// ---------------------------------------------------------------------------
+
+// The previous layer's output (tagged with word_tag) into this XCD's copy
+// for this layer, by one leader per XCD; everyone else waits for the flag.
+// Ends with a barrier.
+__device__ inline void take_token(const DecodeArgs &a, int xcc, uint16_t *stage, uint32_t word_tag, int &s_lead) {
+  if (threadIdx.x == 0) s_lead = take_ticket(a, kLineYTicket, xcc);
+  __syncthreads();
+  if (s_lead) {
+    if (!copy_tagged(a.ws.sync_y, reinterpret_cast<uint32_t *>(stage), a.H / 2, word_tag))
+      report_giveup(a, kStatusYWait);
+    raise_flag(a, kLineYFlag, xcc);
+  } else {
+    wait_flag(a, kLineYFlag, xcc, kStatusYWait);
+  }
+  __syncthreads();
+}
+
+// Layer l's arguments: the first layer's, with layer l's weights, tag and
+// stage set.
+__device__ __forceinline__ DecodeArgs layer_args(const PersistArgs &p, int l) {
+  DecodeArgs a = p.a;
+  const PersistLayer &W = p.L[l];
+  a.router_w = W.router_w;
+  a.router_b = W.router_b;
+  a.w_gate = W.w_gate;
+  a.w_up = W.w_up;
+  a.w_down = W.w_down;
+  a.w_scale = W.w_scale;
+  a.sh_gate = W.sh_gate;
+  a.sh_up = W.sh_up;
+  a.sh_down = W.sh_down;
+  a.sh_scale = W.sh_scale;
+  a.norm_gain = W.norm_gain;
+  a.tag = p.a.tag + (uint32_t)l;
+  uint8_t *slot = p.stages + (int64_t)l * p.slot_bytes;
+  a.ws.xcd_l = reinterpret_cast<float *>(slot);
+  a.ws.xcd_h = reinterpret_cast<uint16_t *>(slot + p.off_h);
+  return a;
+}
+
+__device__ __forceinline__ uint16_t *token_stage(const PersistArgs &p, int l, int xcc) {
+  return reinterpret_cast<uint16_t *>(p.stages + (int64_t)l * p.slot_bytes + p.off_y) + (int64_t)xcc * p.a.H;
+}
+
+// Blocks [0, gu_blocks): gate/up; the rest: down blocks of 8 rows, of
+// which the first rt_blocks also compute k_layer_b1's router block rows
+// (the same function, so the same bits) at the start of every layer, while
+// they would otherwise wait for the routing.  Fewer blocks than k_layer_b1
+// (480 at the full shape), so that all are resident at two per CU.
+template <int WT>
+__global__ __launch_bounds__(kGateupWaves *kWave) void k_step_b1(PersistArgs p, int rt_blocks, int gu_blocks) {
+  extern __shared__ uint4 s_x[];  // [H / 8] the token (router rows and gate/up blocks)
+  __shared__ Routing R;
+  __shared__ uint32_t s_mark[1];
+  __shared__ float s_part[2][kMaxDownSlots][kRows];
+  __shared__ double s_red[kGateupWaves];
+  __shared__ int s_llead, s_hlead, s_ylead;
+  const int b = blockIdx.x;
+  const int xcc = xcc_id();
+  const int n = p.n_layers;
+  if (b < gu_blocks) {
+    for (int l = 0; l < n; ++l) {
+      DecodeArgs a = layer_args(p, l);
+      const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
+      if (l > 0) {
+        uint16_t *ystage = token_stage(p, l, xcc);
+        take_token(a, xcc, ystage, a.tag - 1, s_ylead);
+        a.x = ystage;
+      }
+      uint4 x0, g0;
+      first_pieces(a, x0, g0);
+      stage_token(a, s_x, s_red, x0, g0);
+      if (b * groups < a.max_routed * (a.I / kRows) || b == 0) take_routing(a, xcc, R, s_mark, s_llead);
+      gateup_block<WT, 1, true>(a, b, R, reinterpret_cast<const uint16_t *>(s_x));
+      __syncthreads();  // LDS is rewritten by the next layer
+    }
+  } else {
+    const int dbid = b - gu_blocks;
+    // this thread's row of the residual stream (threads ht < 4 of each
+    // half hold it), from x for the first layer
+    const int ht = threadIdx.x % kDnHalf, half = threadIdx.x / kDnHalf;
+    float xres = bf16_to_f32(p.a.x[dbid * (2 * kRows) + half * kRows + (ht & (kRows - 1))]);
+    for (int l = 0; l < n; ++l) {
+      DecodeArgs a = layer_args(p, l);
+      if (dbid < rt_blocks) {
+        if (l > 0) {
+          DecodeArgs ar = a;
+          uint16_t *ystage = token_stage(p, l, xcc);
+          ar.x = ystage;  // read once the hand-over has filled it
+          router_block_b1<true>(ar, dbid, s_x, s_red, [&] { take_token(ar, xcc, ystage, ar.tag - 1, s_ylead); });
+        } else {
+          router_block_b1<false>(a, dbid, s_x, s_red, [] {});
+        }
+      }
+      down_block_b1<WT, true>(a, dbid, xcc, R, s_mark, s_part, s_llead, s_hlead, &xres, l == n - 1);
+      __syncthreads();
+    }
+  }
+}
+
+static int rt_blocks_of(const DecodeArgs &a) {
+  const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
+  return (a.E + rows_per_block - 1) / rows_per_block;
+}
+static int gu_blocks_of(const DecodeArgs &a) {
+  const int groups = kGateupWaves * (kWave / lanes_per_row(a.H));
+  const int units = a.max_routed * (a.I / kRows) + a.Is / kRows;
+  return (units + groups - 1) / groups;
+}
+
+hipError_t persist_fits(const DecodeArgs &a, bool *fits) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = a.wtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step_b1<1>, kGateupWaves * kWave,
+                                                                 (size_t)a.H * 2)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step_b1<0>, kGateupWaves * kWave,
+                                                                 (size_t)a.H * 2);
+  if (e != hipSuccess) return e;
+  const int64_t grid = gu_blocks_of(a) + a.H / (2 * kRows);
+  *fits = (int64_t)per_cu * cus >= grid && rt_blocks_of(a) <= a.H / (2 * kRows);
+  return hipSuccess;
+}
+
+hipError_t launch_step_b1(const PersistArgs &p, hipStream_t stream) {
+  const DecodeArgs &a = p.a;
+  const int rt = rt_blocks_of(a), gu = gu_blocks_of(a);
+  const int grid = gu + a.H / (2 * kRows);
+  if (a.wtype == 1)
+    hipLaunchKernelGGL(k_step_b1<1>, dim3(grid), dim3(kGateupWaves * kWave), (size_t)a.H * 2, stream, p, rt, gu);
+  else
+    hipLaunchKernelGGL(k_step_b1<0>, dim3(grid), dim3(kGateupWaves * kWave), (size_t)a.H * 2, stream, p, rt, gu);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -21,14 +21,27 @@ constexpr int kPrefillTileRows = 128;       // rows of one prefill GEMM tile
 constexpr int32_t kMaxPrefillTokens = 1 << 22;
 constexpr size_t kWsAlign = 256;            // workspace pieces start on 256-byte lines
 
-// Lines of the decode sync region: per XCD, the logit ticket and flag,
-// then the h ticket and flag (256 bytes each, word 0 used).
-enum { kLineLTicket = 0, kLineLFlag = 1, kLineHTicket = 2, kLineHFlag = 3, kSyncLines = 4 };
+// Lines of the decode sync region: per XCD, the logit ticket and flag, the
+// h ticket and flag, and the layer-output ticket and flag of the persistent
+// step (256 bytes each, word 0 used).
+enum {
+  kLineLTicket = 0,
+  kLineLFlag = 1,
+  kLineHTicket = 2,
+  kLineHFlag = 3,
+  kLineYTicket = 4,
+  kLineYFlag = 5,
+  kSyncLines = 6
+};
+
+// Layers of one persistent step launch (their weight pointers travel as
+// kernel arguments).
+constexpr int kPersistMaxLayers = 24;
 
 // Bits of the status word: a bounded wait on another block of the same
 // kernel ran out of polls (the values it waited for never arrived); an
 // attention token's position was out of range (its output rows are zero).
-enum { kStatusLogitWait = 1, kStatusHWait = 2, kStatusRouteWait = 4, kStatusBadPos = 8 };
+enum { kStatusLogitWait = 1, kStatusHWait = 2, kStatusRouteWait = 4, kStatusBadPos = 8, kStatusYWait = 16 };
 
 // Decode attention: head_dim 128, tiles of 32 positions, one MFMA column
 // per query head of a GQA group (at most 16), blocks of 8 waves.

@@ -54,7 +54,8 @@ int max_routed_of(const moe_layer_desc &d, int B) {
 size_t sync_bytes_of(const moe_layer_desc &d, int B) {
   if (d.n_experts <= 0) return 0;
   const size_t words_h = (size_t)(max_routed_of(d, 1) + 1) * imax_of(d) / 2;
-  return kSyncLineBytes + up((size_t)B * d.n_experts * 8) + up(words_h * 8);
+  const size_t words_y = (size_t)d.hidden / 2;  // the persistent step's layer outputs
+  return kSyncLineBytes + up((size_t)B * d.n_experts * 8) + up(words_h * 8) + up(words_y * 8);
 }
 
 DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap) {
@@ -67,6 +68,7 @@ DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap) {
   L.sync_lines = kStatusLine;
   L.sync_l = kStatusLine + kSyncLineBytes;
   L.sync_h = L.sync_l + up(B * E * 8);
+  L.sync_y = L.sync_h + up((max_routed_of(d, 1) + 1) * Imax / 2 * 8);
   L.clear_bytes = kStatusLine + sync;
   size_t o = L.clear_bytes;
   L.logits = o; o += up(B * E * 4);
@@ -108,6 +110,41 @@ bool step_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, StepL
   L.act1 = L.act0 + act;
   L.bytes = L.act1 + act;
   return true;
+}
+
+bool persist_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, PersistLayout &L) {
+  if (!step_layout(descs, n_layers, B, L.step)) return false;
+  L.stage_l = 0;
+  L.stage_elems = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    const DecodeLayout d = decode_layout(descs[i], 1, L.step.sync_cap);
+    L.stage_l = d.stage_l > L.stage_l ? d.stage_l : L.stage_l;
+    L.stage_elems = d.stage_elems > L.stage_elems ? d.stage_elems : L.stage_elems;
+  }
+  const size_t H = descs[0].hidden;
+  L.off_h = up(kXcdSlots * (size_t)L.stage_l * 4);
+  L.off_y = L.off_h + up(kXcdSlots * (size_t)L.stage_elems * 2);
+  L.slot_bytes = L.off_y + up(kXcdSlots * H * 2);
+  L.stages = L.step.bytes;
+  L.bytes = L.stages + (size_t)kPersistMaxLayers * L.slot_bytes;
+  return true;
+}
+
+int32_t persist_run_end(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                        int32_t batch, int32_t i) {
+  const moe_layer_desc &d = descs[i];
+  if (batch != 1 || d.n_experts <= 0) return i + 1;
+  const bool norm = weights[i].norm_gain != nullptr;
+  int32_t j = i + 1;
+  while (j < n_layers && j - i < kPersistMaxLayers) {
+    const moe_layer_desc &e = descs[j];
+    if (e.n_experts != d.n_experts || e.hidden != d.hidden || e.inter != d.inter ||
+        e.shared_inter != d.shared_inter || e.top_k != d.top_k || e.wtype != d.wtype ||
+        (weights[j].norm_gain != nullptr) != norm || (norm && e.norm_eps != d.norm_eps))
+      break;
+    ++j;
+  }
+  return j;
 }
 
 PfLayout prefill_layout(const moe_layer_desc &d, int64_t T) {
@@ -235,6 +272,19 @@ moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights 
     if (st != MOE_OK) return st;
   }
   if (L) *L = S;
+  return MOE_OK;
+}
+
+moe_status check_step_persistent_call(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                     int32_t n_layers, const void *x, int32_t batch, const void *y, const void *ws,
+                                     size_t ws_bytes, PersistLayout *L) {
+  // every check of the step (the persistent workspace begins with the step's)
+  const moe_status st = check_step_call(descs, weights, n_layers, x, batch, y, ws, ws_bytes, nullptr);
+  if (st != MOE_OK) return st;
+  PersistLayout P;
+  if (!persist_layout(descs, n_layers, batch, P)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < P.bytes) return MOE_ERR_WORKSPACE;
+  if (L) *L = P;
   return MOE_OK;
 }
 
@@ -420,6 +470,18 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
 size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch) {
   StepLayout S;
   return step_layout(descs, n_layers, max_batch, S) ? S.bytes : 0;
+}
+
+size_t moe_decode_step_persistent_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch) {
+  PersistLayout P;
+  if (!descs || n_layers < 1 || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  return persist_layout(descs, n_layers, max_batch, P) ? P.bytes : 0;
+}
+
+moe_status moe_check_decode_step_persistent(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                            int32_t n_layers, const void *x, int32_t batch, const void *y,
+                                            const void *ws, size_t ws_bytes) {
+  return check_step_persistent_call(descs, weights, n_layers, x, batch, y, ws, ws_bytes, nullptr);
 }
 
 size_t moe_prefill_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens) {

@@ -14,7 +14,7 @@ namespace moe {
 // logit words [B][E] and the one-token h words); the call zeroes
 // [0, clear_bytes) before its kernels run.
 struct DecodeLayout {
-  size_t sync_lines, sync_l, sync_h, clear_bytes;
+  size_t sync_lines, sync_l, sync_h, sync_y, clear_bytes;
   size_t logits, xn, n_routed, entry_expert, entry_mask, entry_w, topk_idx, topk_w, h, xcd_l, xcd_h, bytes;
   int64_t stage_l, stage_elems;
 };
@@ -23,6 +23,16 @@ struct DecodeLayout {
 // status word and sync region), then two activation buffers.
 struct StepLayout {
   size_t sync_cap, layer_bytes, act0, act1, bytes;
+};
+
+// The persistent step's workspace: the step's, then per-layer stage sets
+// (the logits, h and layer-input copies of every XCD) for the layers of one
+// launch, so that no block reads a stage address twice in a launch.
+struct PersistLayout {
+  StepLayout step;
+  size_t stages, slot_bytes, bytes;
+  int64_t stage_l, stage_elems;  // per-XCD stage sizes (elements), as in DecodeLayout
+  size_t off_h, off_y;           // offsets of the h and input stages within a slot
 };
 
 // A prefill workspace, carved in this order.
@@ -35,6 +45,12 @@ int max_routed_of(const moe_layer_desc &d, int B);
 size_t sync_bytes_of(const moe_layer_desc &d, int B);
 DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0);
 bool step_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, StepLayout &L);
+bool persist_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, PersistLayout &L);
+// Layers i .. end - 1 that one persistent launch can run: batch 1, routed
+// experts, the shape of layer i, a pre-norm gain on all or none, at most
+// kPersistMaxLayers; end == i + 1 means none (the layer runs alone).
+int32_t persist_run_end(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
+                        int32_t batch, int32_t i);
 PfLayout prefill_layout(const moe_layer_desc &d, int64_t T);
 
 moe_status check_desc(const moe_layer_desc *d);
@@ -48,6 +64,9 @@ moe_status check_decode_call(const moe_layer_desc *desc, const moe_layer_weights
 moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights *weights, int32_t n_layers,
                            const void *x, int32_t batch, const void *y, const void *ws, size_t ws_bytes,
                            StepLayout *L);
+moe_status check_step_persistent_call(const moe_layer_desc *descs, const moe_layer_weights *weights,
+                                     int32_t n_layers, const void *x, int32_t batch, const void *y, const void *ws,
+                                     size_t ws_bytes, PersistLayout *L);
 moe_status check_prefill_call(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
                               int32_t n_tokens, const void *y, const int32_t *topk_idx, const float *topk_w,
                               const void *ws, size_t ws_bytes, PfLayout *L);
