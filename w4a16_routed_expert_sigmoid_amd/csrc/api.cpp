@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "attn.h"
 #include "common.h"
 #include "validate.h"
 

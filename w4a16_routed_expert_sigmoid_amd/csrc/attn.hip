@@ -30,7 +30,7 @@
 // values are stored by dimension within a tile, so the 8 positions a lane
 // feeds into P V are 16 contiguous bytes, and the probabilities leave the
 // score MFMA already in the lane order that P V takes (see k_attn_decode).
-#include "common.h"
+#include "attn.h"
 
 namespace moe {
 

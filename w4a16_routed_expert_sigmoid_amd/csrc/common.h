@@ -393,37 +393,6 @@ hipError_t launch_unpack(const void *src, void *dst, int64_t rows, int64_t cols,
                          hipStream_t stream);
 hipError_t launch_dequant(const void *src, float *dst, int64_t rows, int64_t cols, int64_t n_mats,
                           const float *tensor_scale, hipStream_t stream);
-// Attention kernels (attn.hip).
-struct AttnPrepArgs {
-  const uint16_t *qkv, *q_gain, *k_gain;
-  const int64_t *pos;
-  uint16_t *q_out, *k_cache, *v_cache;
-  int n_q, n_kv, slots, window, rope;
-  double log2_theta, eps;
-};
-
-struct AttnDecodeArgs {
-  const uint16_t *q, *k_cache, *v_cache;
-  const int64_t *pos;
-  const float *sinks;
-  uint16_t *out;
-  float *part;        // [B][n_kv][chunks] FP32 partials (split plans; attn_part_floats each)
-  uint32_t *status;   // the call's status word
-  int n_q, n_kv, G, slots, window, B;
-  int64_t span;       // most positions a token may attend
-  int tpc, chunks;
-};
-
-struct AttnKvWriteArgs {
-  const uint16_t *k_rows, *v_rows;  // [B][n][n_kv][128]
-  const int64_t *pos;               // [B][n]
-  uint16_t *k_cache, *v_cache;
-  int n, n_kv, slots, window;
-};
-
-hipError_t launch_attn_prep(const AttnPrepArgs &a, int B, hipStream_t stream);
-hipError_t launch_attn_kv_write(const AttnKvWriteArgs &a, int B, hipStream_t stream);
-hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *sink, hipStream_t stream);
 
 }  // namespace moe

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "../../include/moe.h"
+#include "attn_shapes.h"
 #include "shapes.h"
 
 namespace moe {
