@@ -481,6 +481,8 @@ def run(args, dev):
                     "layers, RMSNorm before each, independent seeded weights, one HIP graph")
     if any(v.get("status") for v in configs.get("attn_step_100k", {}).values()):
         warn.append("attention status non-zero: outputs invalid")
+    if any(v.get("fused_equals_prep_decode") is False for v in configs.get("attn_step_100k", {}).values()):
+        warn.append("the fused attention layer differs from prep + decode")
     if any(v.get("nonfinite") for k in ("dense_gemv_nvfp4", "mid_batch_nvfp4_zipf", "attn_step_100k")
            for v in configs.get(k, {}).values()):
         warn.append("non-finite outputs")
@@ -696,6 +698,28 @@ def run_attention(args, dev):
         e1.record()
         torch.cuda.synchronize()
         step_us = e0.elapsed_time(e1) * 1e3 / reps
+        outs = [L["o"].clone() for L in layers]
+        # the same step with each layer in one fused call (moe_attn_layer)
+        for L in layers:
+            moe.moe_attn_layer(L["desc"], L["qkv"], pos, B, L["qg"], L["kg"], L["kc"], L["vc"], L["o"], L["ws"],
+                               L["ws_bytes"], max_ctx=L["max_ctx"], sinks=L["sinks"])
+        torch.cuda.synchronize()
+        fused_same = all(torch.equal(L["o"], o) for L, o in zip(layers, outs))
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            for L in layers:
+                moe.moe_attn_layer(L["desc"], L["qkv"], pos, B, L["qg"], L["kg"], L["kc"], L["vc"], L["o"],
+                                   L["ws"], L["ws_bytes"], max_ctx=L["max_ctx"], sinks=L["sinks"])
+        for _ in range(3):
+            gf.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            gf.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        fused_us = e0.elapsed_time(e1) * 1e3 / reps
+        del gf
         # the full-context decode alone (split + combine kernels), per call
         fulls = [L for L in layers if L["full"]]
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3 * 14)]
@@ -720,13 +744,14 @@ def run_attention(args, dev):
         full_gbs = kv_bytes / (full_us * 1e-6) / 1e9
         out[f"b{B}"] = {
             "us_per_step": round(step_us, 2), "tokens_per_s": round(B * 1e6 / step_us, 1),
+            "us_per_step_fused_layer": round(fused_us, 2), "fused_equals_prep_decode": fused_same,
             "step_GBps": round(step_bytes / (step_us * 1e-6) / 1e9, 1), "step_kv_bytes": int(step_bytes),
             "full_decode_us": round(full_us, 2), "full_decode_GBps": round(full_gbs, 1),
             "full_decode_hbm_frac": round(full_gbs / HBM_PEAK_GBS, 4), "full_decode_kv_bytes": int(kv_bytes),
             "context_positions": span, "status": status, "nonfinite": nonfinite,
             "layers": "14 full-context (no RoPE) + 35 window-513 (RoPE), prep + decode each"}
-        log(f"attention B={B}: {step_us:.1f} us per 49-layer step, full-context decode {full_us:.1f} us "
-            f"({full_gbs:.0f} GB/s), status {status}")
+        log(f"attention B={B}: {step_us:.1f} us per 49-layer step (fused layer calls {fused_us:.1f} us, equal "
+            f"{fused_same}), full-context decode {full_us:.1f} us ({full_gbs:.0f} GB/s), status {status}")
         del layers, g
         torch.cuda.empty_cache()
     return out

@@ -438,14 +438,36 @@ moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void 
                            const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
                            void *ws, size_t ws_bytes, void *stream);
 
-/* Host-side validation alone of moe_attn_prep, moe_attn_kv_write and
- * moe_attn_decode, as for the calls above. */
+/* moe_attn_prep then moe_attn_decode in one kernel (plus the chunk merge
+ * when the context is split): the same outputs and cache writes, bit for
+ * bit, with no q buffer.  Each block of the decode forms the q heads of its
+ * group itself (norm and RoPE while its first cache tiles load), and the
+ * block whose share of the context holds the token's position also forms
+ * the new k and v, writes them to the cache and uses them from registers.
+ * One launch fewer per layer than prep + decode ("Day-0 Support for Flint
+ * on vLLM", section "Optimizations": the Q/K norm, RoPE and KV write fused;
+ * decode attention with sinks and sliding windows).
+ *  Arguments as for moe_attn_prep (qkv, pos, batch, gains, caches) and
+ *  moe_attn_decode (max_ctx, sinks, out, ws: ws_bytes >=
+ *  moe_attn_workspace_bytes(desc, batch, max_ctx)); status bit 8 as there.
+ * Errors: as the two calls; INVALID_ARG also when out, ws or a cache shares
+ * a byte with another argument. */
+moe_status moe_attn_layer(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                          int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks, void *k_cache,
+                          void *v_cache, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Host-side validation alone of moe_attn_prep, moe_attn_kv_write,
+ * moe_attn_decode and moe_attn_layer, as for the calls above. */
 moe_status moe_check_attn_prep(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
                                const void *q_gain, const void *k_gain, const void *q_out, const void *k_cache,
                                const void *v_cache);
 moe_status moe_check_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, const void *v_rows,
                                    const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
                                    const void *v_cache);
+moe_status moe_check_attn_layer(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks,
+                                const void *k_cache, const void *v_cache, const void *out, const void *ws,
+                                size_t ws_bytes);
 moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,
                                  const void *v_cache, const int64_t *pos, int32_t batch, int64_t max_ctx,
                                  const float *sinks, const void *out, const void *ws, size_t ws_bytes);

@@ -76,6 +76,8 @@ def _declare(lib):
     lib.moe_check_attn_kv_write.argtypes = [AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]
     lib.moe_attn_workspace_bytes.restype = _sz
     lib.moe_attn_workspace_bytes.argtypes = [AD, _i32, _i64]
+    lib.moe_check_attn_layer.restype = _i32
+    lib.moe_check_attn_layer.argtypes = [AD, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]
     return lib
 
 
@@ -146,7 +148,7 @@ def test_host_library_needs_no_hip_runtime():
               "moe_check_repack_nvfp4", "moe_decode_workspace_bytes", "moe_decode_step_workspace_bytes",
               "moe_prefill_workspace_bytes", "moe_nvfp4_matrix_bytes", "moe_status_string",
               "moe_check_attn_prep", "moe_check_attn_decode", "moe_attn_workspace_bytes",
-              "moe_check_attn_kv_write"):
+              "moe_check_attn_kv_write", "moe_check_attn_layer"):
         assert hasattr(lib, n), n
     with open("/proc/self/maps") as f:
         maps = f.read()
@@ -572,3 +574,36 @@ def test_persistent_step_workspace_and_checks():
     assert chk(ds, ww, 3, A(20), 9, A(21), A(22), pers) == UNSUPPORTED
     assert chk(ds, ww, 0, A(20), 1, A(21), A(22), pers) == INVALID
     assert chk(ds, ww, 3, A(20), 1, A(20), A(22), pers) == INVALID   # y == x
+
+
+def alayer(which, d=None, qkv=A(1), pos=A(2), B=1, max_ctx=0, qg=A(3), kg=A(4), sinks=A(6), kc=KC, vc=VC, out=A(7),
+           ws=A(8), ws_bytes=1 << 20):
+    d = d or adesc()
+    if which == "host":
+        return host().moe_check_attn_layer(ctypes.byref(d), qkv, pos, B, max_ctx, qg, kg, sinks, kc, vc, out, ws,
+                                           ws_bytes)
+    lib = hip()
+    lib.moe_attn_layer.argtypes = [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    return lib.moe_attn_layer(ctypes.byref(AttnDesc.from_buffer_copy(d)), qkv, pos, B, max_ctx, qg, kg, sinks, kc,
+                              vc, out, ws, ws_bytes, None)
+
+
+def test_attn_layer_valid_call_passes_validation():
+    assert alayer("host") == OK and alayer("host", sinks=None) == OK
+    full = adesc(window=0, rope=0, slots=100032)
+    assert alayer("host", d=full, B=8, max_ctx=100001, ws_bytes=attn_ws(full, 8, 100001)) == OK
+
+
+@pytest.mark.parametrize("which", LIBS)
+@pytest.mark.parametrize("kw,want", [
+    (dict(qkv=None), INVALID), (dict(pos=None), INVALID), (dict(qg=None), INVALID), (dict(kg=None), INVALID),
+    (dict(kc=None), INVALID), (dict(vc=None), INVALID), (dict(out=None), INVALID), (dict(ws=None), INVALID),
+    (dict(B=0), INVALID), (dict(B=257), INVALID), (dict(max_ctx=514), INVALID), (dict(ws=A(8) + 16), INVALID),
+    (dict(qkv=A(1) + 2), INVALID), (dict(d=adesc(head_dim=64)), UNSUPPORTED),
+    (dict(out=A(1)), INVALID),               # out == qkv
+    (dict(ws=KC + 4096), INVALID),           # workspace inside the key cache
+    (dict(kc=A(3)), INVALID),                # the key cache over a gain
+    (dict(ws_bytes=100), WORKSPACE),
+])
+def test_attn_layer_errors(which, kw, want):
+    assert alayer(which, **kw) == want

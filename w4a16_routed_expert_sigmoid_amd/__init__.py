@@ -132,6 +132,10 @@ _lib.moe_attn_kv_write.restype = _i32
 _lib.moe_attn_kv_write.argtypes = [_AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
 _lib.moe_check_attn_kv_write.restype = _i32
 _lib.moe_check_attn_kv_write.argtypes = [_AD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]
+_lib.moe_attn_layer.restype = _i32
+_lib.moe_attn_layer.argtypes = [_AD, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_check_attn_layer.restype = _i32
+_lib.moe_check_attn_layer.argtypes = [_AD, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]
 _lib.moe_check_attn_decode.restype = _i32
 _lib.moe_check_attn_decode.argtypes = [_AD, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz]
 
@@ -145,7 +149,7 @@ EXPORTS = ("moe_status_string", "moe_last_error_detail", "moe_nvfp4_matrix_bytes
            "moe_attn_prep", "moe_attn_workspace_bytes", "moe_attn_decode", "moe_check_attn_prep",
            "moe_check_attn_decode", "moe_attn_kv_write", "moe_check_attn_kv_write",
            "moe_decode_step_persistent", "moe_decode_step_persistent_workspace_bytes",
-           "moe_check_decode_step_persistent")
+           "moe_check_decode_step_persistent", "moe_attn_layer", "moe_check_attn_layer")
 
 
 def lib():
@@ -249,6 +253,14 @@ def moe_attn_prep(desc, qkv, pos, batch, q_gain, k_gain, q_out, k_cache, v_cache
     """Q/K norm + RoPE of `batch` tokens; q to q_out, k and v into the caches."""
     _check(_lib.moe_attn_prep(ctypes.byref(desc), _ptr(qkv), _ptr(pos), batch, _ptr(q_gain), _ptr(k_gain),
                               _ptr(q_out), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "moe_attn_prep")
+
+
+def moe_attn_layer(desc, qkv, pos, batch, q_gain, k_gain, k_cache, v_cache, out, ws, ws_bytes, max_ctx=0,
+                   sinks=None, stream=None):
+    """moe_attn_prep + moe_attn_decode in one kernel (no q buffer)."""
+    _check(_lib.moe_attn_layer(ctypes.byref(desc), _ptr(qkv), _ptr(pos), batch, max_ctx, _ptr(q_gain), _ptr(k_gain),
+                               _ptr(sinks), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(ws), ws_bytes,
+                               _stream(stream)), "moe_attn_layer")
 
 
 def moe_attn_kv_write(desc, k_rows, v_rows, pos, n, batch, k_cache, v_cache, stream=None):

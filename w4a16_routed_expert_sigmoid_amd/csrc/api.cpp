@@ -392,6 +392,41 @@ moe_status moe_attn_kv_write(const moe_attn_desc *desc, const void *k_rows, cons
   return hip_status(launch_attn_kv_write(a, batch, (hipStream_t)stream));
 }
 
+moe_status moe_attn_layer(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                          int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks, void *k_cache,
+                          void *v_cache, void *out, void *ws, size_t ws_bytes, void *stream) {
+  const moe_status st = check_attn_layer_call(desc, qkv, pos, batch, max_ctx, q_gain, k_gain, sinks, k_cache,
+                                              v_cache, out, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  const AttnPlan plan = attn_plan_of(*desc, batch, max_ctx);
+  AttnDecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.pos = pos;
+  a.sinks = sinks;
+  a.out = (uint16_t *)out;
+  a.status = (uint32_t *)ws;
+  a.part = plan.chunks > 1 ? (float *)((uint8_t *)ws + attn_partial_offset()) : nullptr;
+  a.n_q = desc->n_q;
+  a.n_kv = desc->n_kv;
+  a.G = desc->n_q / desc->n_kv;
+  a.slots = desc->slots;
+  a.window = desc->window;
+  a.B = batch;
+  a.span = plan.span;
+  a.tpc = plan.tpc;
+  a.chunks = plan.chunks;
+  a.fused = 1;
+  a.rope = desc->rope;
+  a.qkv = (const uint16_t *)qkv;
+  a.q_gain = (const uint16_t *)q_gain;
+  a.k_gain = (const uint16_t *)k_gain;
+  a.log2_theta = desc->rope ? log2(desc->rope_theta) : 0.0;
+  a.eps = (double)desc->norm_eps;
+  return hip_status(launch_attn_decode(a, (hipStream_t)stream));
+}
+
 moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                            const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks, void *out,
                            void *ws, size_t ws_bytes, void *stream) {
@@ -400,6 +435,7 @@ moe_status moe_attn_decode(const moe_attn_desc *desc, const void *q, const void 
   if (st != MOE_OK) return st;
   const AttnPlan plan = attn_plan_of(*desc, batch, max_ctx);
   AttnDecodeArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = (const uint16_t *)q;
   a.k_cache = (const uint16_t *)k_cache;
   a.v_cache = (const uint16_t *)v_cache;

@@ -25,6 +25,11 @@ struct AttnDecodeArgs {
   int n_q, n_kv, G, slots, window, B;
   int64_t span;       // most positions a token may attend
   int tpc, chunks;
+  // fused (moe_attn_layer): the Q/K norm, RoPE and KV write run in the
+  // decode kernel; q is then unused and the caches are written
+  int fused, rope;
+  const uint16_t *qkv, *q_gain, *k_gain;
+  double log2_theta, eps;
 };
 
 struct AttnKvWriteArgs {

@@ -47,13 +47,39 @@ __device__ __forceinline__ bool attn_range(int64_t pos, int window, int slots, i
   return pos - lo + 1 <= span;
 }
 
+// RoPE angle of the pair (lane, lane + 64) at position pos: its cosine and
+// sine, angle = pos * theta^(-2 lane / 128) in FP64.
+__device__ __forceinline__ void rope_angle(int64_t pos, int lane, double log2_theta, double &cs, double &sn) {
+  const double f = exp2(-(double)lane / 64.0 * log2_theta);
+  sincos((double)pos * f, &sn, &cs);
+}
+
+// One head (lane holds elements lane and lane + 64): y = BF16(x / sqrt(
+// mean(x^2) + eps) * gain) with an FP64 sum of squares (exact per term) and
+// scale, then with RoPE (a, b) -> (BF16(a cos - b sin), BF16(b cos + a sin)).
+__device__ __forceinline__ void norm_rope_head(uint32_t x0b, uint32_t x1b, const uint16_t *gain, int lane, double eps,
+                                               bool rope, double cs, double sn, uint32_t &y0, uint32_t &y1) {
+#pragma clang fp contract(off)
+  const double x0 = (double)bf16_to_f32(x0b), x1 = (double)bf16_to_f32(x1b);
+  double ss = x0 * x0 + x1 * x1;
+  ss = group_sum_f64(ss, kWave);
+  const double inv = 1.0 / sqrt(ss / (double)kAttnD + eps);
+  const double g0 = (double)bf16_to_f32(gain[lane]), g1 = (double)bf16_to_f32(gain[lane + 64]);
+  y0 = f64_to_bf16(x0 * inv * g0);
+  y1 = f64_to_bf16(x1 * inv * g1);
+  if (rope) {
+    const double ya = (double)bf16_to_f32(y0), yb = (double)bf16_to_f32(y1);
+    y0 = f64_to_bf16(ya * cs - yb * sn);
+    y1 = f64_to_bf16(yb * cs + ya * sn);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Q/K norm + RoPE + KV write.  Grid (ceil(units / 4), B), 4 waves; unit u of
 // a token: q heads 0..n_q-1, k heads, then v heads.  Lane l holds elements
 // l and l + 64, the RoPE pair.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
-#pragma clang fp contract(off)
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -85,23 +111,10 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnPrepArgs a) {
     }
     return;
   }
-  // RMSNorm of the head: squares of BF16 values are exact in FP64.
-  const double x0 = (double)bf16_to_f32(x0b), x1 = (double)bf16_to_f32(x1b);
-  double ss = x0 * x0 + x1 * x1;
-  ss = group_sum_f64(ss, kWave);
-  const double inv = 1.0 / sqrt(ss / (double)kAttnD + a.eps);
-  const uint16_t *gain = is_q ? a.q_gain : a.k_gain;
-  const double g0 = (double)bf16_to_f32(gain[lane]), g1 = (double)bf16_to_f32(gain[lane + 64]);
-  uint32_t y0 = f64_to_bf16(x0 * inv * g0), y1 = f64_to_bf16(x1 * inv * g1);
-  if (a.rope) {
-    // angle = pos * theta^(-2 lane / 128), in FP64
-    const double f = exp2(-(double)lane / 64.0 * a.log2_theta);
-    double sn, cs;
-    sincos((double)pos * f, &sn, &cs);
-    const double ya = (double)bf16_to_f32(y0), yb = (double)bf16_to_f32(y1);
-    y0 = f64_to_bf16(ya * cs - yb * sn);
-    y1 = f64_to_bf16(yb * cs + ya * sn);
-  }
+  double cs = 1.0, sn = 0.0;
+  if (a.rope) rope_angle(pos, lane, a.log2_theta, cs, sn);
+  uint32_t y0, y1;
+  norm_rope_head(x0b, x1b, is_q ? a.q_gain : a.k_gain, lane, a.eps, a.rope != 0, cs, sn, y0, y1);
   if (is_q) {
     uint16_t *dq = a.q_out + ((int64_t)b * a.n_q + u) * kAttnD;
     dq[lane] = (uint16_t)y0;
@@ -199,9 +212,43 @@ __device__ __forceinline__ float col_max(float v) {
 
 constexpr int kAccStride = kAttnD + 4;  // LDS row of one head's accumulator (floats)
 
+// moe_attn_layer: KV head kv's new k (normed, rotated) or v (u = 0 / 1) of
+// token b into the cache slot of pos, by one wave; the row also to `row`
+// when given.
+__device__ inline void fused_kv_unit(const AttnDecodeArgs &a, int b, int kv, int u, int64_t pos, int lane, double cs,
+                                     double sn, uint16_t *row) {
+  const int64_t slot = pos % a.slots;
+  const int o = (int)(slot % kAttnTile);
+  const int64_t tile_off = ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD + (slot / kAttnTile) * kAttnTileElems;
+  const uint16_t *src = a.qkv + ((int64_t)b * (a.n_q + 2 * a.n_kv) + a.n_q + (int64_t)u * a.n_kv + kv) * kAttnD;
+  uint32_t y0 = src[lane], y1 = src[lane + 64];
+  if (u == 0) {
+    norm_rope_head(y0, y1, a.k_gain, lane, a.eps, a.rope != 0, cs, sn, y0, y1);
+    uint16_t *kt = const_cast<uint16_t *>(a.k_cache) + tile_off;
+    kt[attn_k_index(o, lane)] = (uint16_t)y0;
+    kt[attn_k_index(o, lane + 64)] = (uint16_t)y1;
+  } else {
+    uint16_t *vt = const_cast<uint16_t *>(a.v_cache) + tile_off;
+    vt[attn_v_index(o, lane)] = (uint16_t)y0;
+    vt[attn_v_index(o, lane + 64)] = (uint16_t)y1;
+  }
+  if (row) {
+    row[lane] = (uint16_t)y0;
+    row[lane + 64] = (uint16_t)y1;
+  }
+}
+
+// FUSED (moe_attn_layer): before the tiles are used, the block computes its
+// group's q heads into LDS (norm and RoPE as k_attn_prep, the same bits),
+// and the block whose chunk holds the current position also the new k and
+// v, which it writes to the cache and patches into its registers when it
+// reaches that tile (its tiles were requested before the write).
+template <bool FUSED>
 __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float s_acc[kAttnWaves][kAttnMaxGroup][kAccStride];
   __shared__ float s_m[kAttnWaves][kAttnMaxGroup], s_l[kAttnWaves][kAttnMaxGroup];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[FUSED ? kAttnMaxGroup : 1][kAttnD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kv[FUSED ? 2 : 1][kAttnD];  // the position's k, v
 
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   // the wave index as a scalar: tile indices and the edge test stay in
@@ -229,26 +276,69 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
     if (a.chunks == 1)
       for (int i = threadIdx.x; i < G * kAttnD / 8; i += blockDim.x)
         reinterpret_cast<u32x4 *>(outb)[i] = u32x4{0, 0, 0, 0};
+    if constexpr (FUSED) {
+      // a position the cache holds, beyond the context bound: the new k and
+      // v are still written, as moe_attn_prep writes them (chunk 0's block)
+      int64_t lo2;
+      if (c == 0 && wave < 2 && attn_range(pos, a.window, a.slots, (int64_t)1 << 62, lo2)) {
+        double cs = 1.0, sn = 0.0;
+        if (a.rope) rope_angle(pos, lane, a.log2_theta, cs, sn);
+        fused_kv_unit(a, b, kv, wave, pos, lane, cs, sn, nullptr);
+      }
+    }
     return;
   }
   const int64_t ft = lo / kAttnTile, lt = pos / kAttnTile;
   const int64_t t0 = ft + (int64_t)c * a.tpc;
   if (t0 > lt) return;  // this token needs fewer chunks
   const int64_t t1 = t0 + a.tpc - 1 < lt ? t0 + a.tpc - 1 : lt;
+  const uint16_t *kb = a.k_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
+  const uint16_t *vb = a.v_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
+
+  // This wave's first tile, requested before anything else (cache tiles
+  // follow the tiles: st = t mod (slots / 32), advanced by addition).
+  int64_t t = t0 + wave;
+  const int nst = a.slots / kAttnTile;
+  int sa = 0;
+  AttnTileRegs ra, rb;
+  if (t <= t1) {
+    sa = (int)(t % nst);
+    attn_load_tile(ra, kb, vb, sa, lane);
+  }
+
+  if constexpr (FUSED) {
+    // units: the group's q heads, then (the block holding the position)
+    // KV head kv's k and v
+    const bool holds_pos = t0 <= lt && lt <= t1;
+    const int units = G + (holds_pos ? 2 : 0);
+    const uint16_t *row = a.qkv + (int64_t)b * (a.n_q + 2 * a.n_kv) * kAttnD;
+    double cs = 1.0, sn = 0.0;
+    if (a.rope) rope_angle(pos, lane, a.log2_theta, cs, sn);
+    for (int u = wave; u < units; u += kAttnWaves) {
+      if (u >= G) {
+        fused_kv_unit(a, b, kv, u - G, pos, lane, cs, sn, &s_kv[u - G][0]);
+      } else {
+        const uint16_t *src = row + (int64_t)(kv * G + u) * kAttnD;
+        uint32_t y0, y1;
+        norm_rope_head(src[lane], src[lane + 64], a.q_gain, lane, a.eps, a.rope != 0, cs, sn, y0, y1);
+        s_q[u][lane] = (uint16_t)y0;
+        s_q[u][lane + 64] = (uint16_t)y1;
+      }
+    }
+    __syncthreads();
+  }
 
   // q of head r of the group, dims 8 (4 s + g) .. + 8 for k-step s
   u32x4 qv[4];
   {
     const int hq = r < G ? r : 0;
-    const uint16_t *qh = a.q + ((int64_t)b * a.n_q + (int64_t)kv * G + hq) * kAttnD;
+    const uint16_t *qh = FUSED ? &s_q[hq][0] : a.q + ((int64_t)b * a.n_q + (int64_t)kv * G + hq) * kAttnD;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4 v = ld16(qh + (s * 4 + g) * 8);
       qv[s] = r < G ? v : u32x4{0, 0, 0, 0};
     }
   }
-  const uint16_t *kb = a.k_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
-  const uint16_t *vb = a.v_cache + ((int64_t)b * a.n_kv + kv) * a.slots * kAttnD;
   const float qscale = kLog2e / sqrtf((float)kAttnD);
 
   f32x4 acc[8];
@@ -260,7 +350,35 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
   // used in turn: the loads of the next tile are in flight while this one
   // is computed (a copy between the sets would wait for them).  Loads are
   // unconditional: past the end they reload the last tile, a cache hit.
-  auto tile_step = [&](const AttnTileRegs &cur, int64_t t) {
+  auto tile_step = [&](AttnTileRegs &cur, int64_t t) {
+    if constexpr (FUSED) {
+      if (t == lt) {
+        // the current position's new k and v, into the lanes that hold it
+        const int o = (int)(pos - t * kAttnTile);
+        const int r_o = ((o >> 3) << 2) | (o & 3);
+        if (r == r_o) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u32x4 nk = *reinterpret_cast<const u32x4 *>(&s_kv[0][(s * 4 + g) * 8]);
+            if ((o >> 2) & 1) cur.k[1][s] = nk;
+            else cur.k[0][s] = nk;
+          }
+        }
+        if (g == (o >> 3)) {
+          const int j = o & 7;
+          const uint32_t keep = (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t val = (uint32_t)s_kv[1][dt * 16 + r] << ((j & 1) * 16);
+            u32x4 &vv = cur.v[dt];
+            if ((j >> 1) == 0) vv.x = (vv.x & keep) | val;
+            else if ((j >> 1) == 1) vv.y = (vv.y & keep) | val;
+            else if ((j >> 1) == 2) vv.z = (vv.z & keep) | val;
+            else vv.w = (vv.w & keep) | val;
+          }
+        }
+      }
+    }
     f32x4 sc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -335,19 +453,12 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void k_attn_decode(AttnDecodeAr
       }
     }
   };
-  // Cache tiles follow the tiles: st = t mod (slots / 32), advanced by
-  // addition (no division per tile).
-  int64_t t = t0 + wave;
   if (t <= t1) {
-    const int nst = a.slots / kAttnTile;
     auto advance = [nst](int st) {
       st += kAttnWaves;
       while (st >= nst) st -= nst;
       return st;
     };
-    int sa = (int)(t % nst);
-    AttnTileRegs ra, rb;
-    attn_load_tile(ra, kb, vb, sa, lane);
     for (;;) {
       const int64_t tb = t + kAttnWaves;
       const int sb = advance(sa);
@@ -496,7 +607,10 @@ hipError_t launch_attn_kv_write(const AttnKvWriteArgs &a, int B, hipStream_t str
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_attn_decode, dim3(a.chunks, a.n_kv, a.B), dim3(kAttnWaves * kWave), 0, stream, a);
+  if (a.fused)
+    hipLaunchKernelGGL(k_attn_decode<true>, dim3(a.chunks, a.n_kv, a.B), dim3(kAttnWaves * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_attn_decode<false>, dim3(a.chunks, a.n_kv, a.B), dim3(kAttnWaves * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.chunks == 1) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(a.n_q, a.B), dim3(kCombineThreads), 0, stream, a);

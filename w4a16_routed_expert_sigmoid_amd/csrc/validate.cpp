@@ -411,6 +411,34 @@ moe_status check_attn_kv_write_call(const moe_attn_desc *desc, const void *k_row
   return outputs_disjoint(r, 5, 2) ? MOE_OK : MOE_ERR_INVALID_ARG;
 }
 
+moe_status check_attn_layer_call(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                 int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks,
+                                 const void *k_cache, const void *v_cache, const void *out, const void *ws,
+                                 size_t ws_bytes) {
+  const moe_status st = check_attn_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!qkv || !pos || !q_gain || !k_gain || !k_cache || !v_cache || !out || !ws) return MOE_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kAttnMaxBatch) return MOE_ERR_INVALID_ARG;
+  if (attn_span(*desc, max_ctx) < 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(qkv, 16) || !aligned(pos, 8) || !aligned(q_gain, 16) || !aligned(k_gain, 16) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(ws, kWsAlign) ||
+      (sinks && !aligned(sinks, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t cb = cache_bytes(*desc, batch);
+  const Range r[9] = {{out, (size_t)batch * desc->n_q * kAttnD * 2},
+                      {ws, ws_bytes},
+                      {k_cache, cb},
+                      {v_cache, cb},
+                      {qkv, (size_t)batch * (desc->n_q + 2 * desc->n_kv) * kAttnD * 2},
+                      {pos, (size_t)batch * 8},
+                      {q_gain, kAttnD * 2},
+                      {k_gain, kAttnD * 2},
+                      {sinks, sinks ? (size_t)desc->n_q * 4 : 0}};
+  if (!outputs_disjoint(r, 9, 4)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < attn_workspace_bytes(*desc, batch, max_ctx)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
 moe_status check_attn_decode_call(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                                   const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks,
                                   const void *out, const void *ws, size_t ws_bytes) {
@@ -526,6 +554,14 @@ moe_status moe_check_attn_kv_write(const moe_attn_desc *desc, const void *k_rows
                                    const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
                                    const void *v_cache) {
   return check_attn_kv_write_call(desc, k_rows, v_rows, pos, n, batch, k_cache, v_cache);
+}
+
+moe_status moe_check_attn_layer(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks,
+                                const void *k_cache, const void *v_cache, const void *out, const void *ws,
+                                size_t ws_bytes) {
+  return check_attn_layer_call(desc, qkv, pos, batch, max_ctx, q_gain, k_gain, sinks, k_cache, v_cache, out, ws,
+                               ws_bytes);
 }
 
 moe_status moe_check_attn_decode(const moe_attn_desc *desc, const void *q, const void *k_cache,

@@ -87,6 +87,10 @@ moe_status check_attn_prep_call(const moe_attn_desc *desc, const void *qkv, cons
 moe_status check_attn_kv_write_call(const moe_attn_desc *desc, const void *k_rows, const void *v_rows,
                                    const int64_t *pos, int32_t n, int32_t batch, const void *k_cache,
                                    const void *v_cache);
+moe_status check_attn_layer_call(const moe_attn_desc *desc, const void *qkv, const int64_t *pos, int32_t batch,
+                                 int64_t max_ctx, const void *q_gain, const void *k_gain, const float *sinks,
+                                 const void *k_cache, const void *v_cache, const void *out, const void *ws,
+                                 size_t ws_bytes);
 moe_status check_attn_decode_call(const moe_attn_desc *desc, const void *q, const void *k_cache, const void *v_cache,
                                   const int64_t *pos, int32_t batch, int64_t max_ctx, const float *sinks,
                                   const void *out, const void *ws, size_t ws_bytes);
