@@ -317,14 +317,32 @@ constexpr int kRouterWaves = 4;
 constexpr int kRouterThreads = kRouterWaves * kWave;
 constexpr int kRouteWaves = kMaxBatch;  // batches: one wave per token in the routing block
 
-template <int W>
+// MT: tokens a block handles.  kMaxBatch: the whole batch, staged in
+// kMaxBatch * 4096 / 8 16-byte pieces (B * H <= 32768).  1: one token of a
+// batch of two or more, the batch split over blockIdx.y; its stage takes
+// at most 16384 / 8 pieces (H <= 16384), and its per-token registers are a
+// batch's eighth, so that several blocks fit on a compute unit.
+template <int W, int MT = kMaxBatch>
 __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready, int route) {
   constexpr int kRouterWaves = W, kRouterThreads = W * kWave;
-  __shared__ uint4 s_x[kMaxBatch * 4096 / 8];  // [B][H] BF16, B * H <= 32768
-  __shared__ double s_ss[kRouterWaves][kMaxBatch];
+  constexpr int XCAP = MT == 1 ? 16384 / 8 : kMaxBatch * 4096 / 8;
+  static_assert(XCAP * 16 >= 32768, "the routing block keeps B * E <= 8192 logits in the stage");
+  __shared__ uint4 s_x[XCAP];  // [B][H] BF16
+  __shared__ double s_ss[kRouterWaves][MT];
   if (route && blockIdx.x == gridDim.x - 1) {
     route_block(a, s_x);
     return;
+  }
+  if (MT == 1) {
+    // the batch split over blockIdx.y, one token per block row: a block
+    // takes its token's dot products only (a row's 16 pieces per lane
+    // instead of 16 per token), the row weights are read once per token
+    // from the L2
+    const int t = blockIdx.y;
+    a.x += (int64_t)t * a.H;
+    a.ws.xn += (int64_t)t * a.H;
+    a.ws.logits += (int64_t)t * a.E;
+    a.B = 1;
   }
   const int H = a.H, E = a.E, B = a.B;
   const int LPR = lanes_per_row(H);
@@ -403,9 +421,9 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
     // which arrive from memory while the norm runs.
     // (indices clamped into the buffers: every load is unconditional)
     const int tc = tid < n8 ? tid : n8 - 1;
-    uint4 v0[kMaxBatch];
+    uint4 v0[MT];
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t)
+    for (int t = 0; t < MT; ++t)
       if (t < B) v0[t] = reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[tc];
     uint4 g0 = make_uint4(0, 0, 0, 0);
     if (norm_here) g0 = reinterpret_cast<const uint4 *>(a.norm_gain)[tc];
@@ -424,16 +442,16 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
     // 1. activations -> LDS; sums of squares (exact per term in FP64).  A
     // thread's pieces of every token are loaded before any is stored, so the
     // loads are in flight together.
-    double ss[kMaxBatch];
+    double ss[MT];
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) ss[t] = 0.0;
+    for (int t = 0; t < MT; ++t) ss[t] = 0.0;
     for (int i = tid; i < n8; i += kRouterThreads) {
-      uint4 v[kMaxBatch];
+      uint4 v[MT];
 #pragma unroll
-      for (int t = 0; t < kMaxBatch; ++t)
+      for (int t = 0; t < MT; ++t)
         if (t < B) v[t] = i == tid ? v0[t] : reinterpret_cast<const uint4 *>(src + (int64_t)t * H)[i];
 #pragma unroll
-      for (int t = 0; t < kMaxBatch; ++t) {
+      for (int t = 0; t < MT; ++t) {
         if (t >= B) break;
         s_x[t * n8 + i] = v[t];
         if (norm_here) {
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
     }
     if (norm_here) {
 #pragma unroll
-      for (int t = 0; t < kMaxBatch; ++t) {
+      for (int t = 0; t < MT; ++t) {
         if (t >= B) break;
         const double v = group_sum_f64(ss[t], kWave);
         if (lane == 0) s_ss[wave][t] = v;
@@ -466,14 +484,14 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
         s_ss[0][tid] = 1.0 / sqrt(tot / (double)H + (double)a.eps);
       }
       __syncthreads();
-      double inv[kMaxBatch];
+      double inv[MT];
 #pragma unroll
-      for (int t = 0; t < kMaxBatch; ++t) inv[t] = t < B ? s_ss[0][t] : 1.0;
+      for (int t = 0; t < MT; ++t) inv[t] = t < B ? s_ss[0][t] : 1.0;
       for (int i = tid; i < n8; i += kRouterThreads) {
         const uint4 gv = i == tid ? g0 : reinterpret_cast<const uint4 *>(a.norm_gain)[i];
         const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-        for (int t = 0; t < kMaxBatch; ++t) {
+        for (int t = 0; t < MT; ++t) {
           if (t >= B) break;
           const float inv_f = (float)inv[t];
           const uint4 o = norm_piece_bf16(s_x[t * n8 + i], gv, inv_f, inv[t]);
@@ -487,9 +505,9 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
 
   // 3. router row x every token
   if (row >= E) return;
-  float acc[kMaxBatch];
+  float acc[MT];
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) acc[t] = 0.f;
+  for (int t = 0; t < MT; ++t) acc[t] = 0.f;
   for (int j0 = lg; j0 < n8; j0 += 4 * LPR) {
     uint4 w[4];
 #pragma unroll
@@ -499,7 +517,7 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
       else w[i] = j < n8 ? reinterpret_cast<const uint4 *>(a.router_w + (int64_t)row * H)[j] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int t = 0; t < kMaxBatch; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t >= B) break;
       float s = acc[t];
 #pragma unroll
@@ -517,7 +535,7 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
     }
   }
 #pragma unroll
-  for (int t = 0; t < kMaxBatch; ++t) {
+  for (int t = 0; t < MT; ++t) {
     if (t >= B) break;
     const float v = group_sum(acc[t], LPR);
     if (lg == 0) {
@@ -1953,12 +1971,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
   // measurement, eager launches only).
   hipError_t e;
   if (a.B == 1 && a.E > 0) return a.wtype == 1 ? launch_layer_b1<1>(a, stream, ev) : launch_layer_b1<0>(a, stream, ev);
-  // NVFP4 batches with routed experts: three kernels.  The router blocks
-  // normalise the batch themselves (block 0 also stores xn) and store plain
-  // logits; the gate/up blocks derive the routing from them.
+  // NVFP4 batches with routed experts: three kernels.  The router has one
+  // row of blocks per token; each block normalises its token itself (the
+  // first block of a row also stores its xn) and stores plain logits; the
+  // gate/up blocks derive the routing from them.
   if (a.wtype == 1 && a.B > 1 && a.E > 0) {
     const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
-    if ((e = launch(k_router<kRouterWaves>, dim3((a.E + rows_per_block - 1) / rows_per_block),
+    if ((e = launch(k_router<kRouterWaves, 1>, dim3((a.E + rows_per_block - 1) / rows_per_block, a.B),
                     dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, a, 0, 0)) !=
         hipSuccess)
       return e;
@@ -1984,7 +2003,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
       return e;
   } else if (a.use_norm && !xn_ready) {
     // a dense layer of one token: the pre-norm only
-    if ((e = launch(k_router<kRouterWaves>, dim3(1), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
+    if ((e = launch(k_router<kRouterWaves, 1>, dim3(1), dim3(kRouterThreads), 0, stream, ev ? ev[0] : nullptr,
                     ev ? ev[1] : nullptr, a, xn_ready, 0)) != hipSuccess)
       return e;
   }
