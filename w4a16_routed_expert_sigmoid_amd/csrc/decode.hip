@@ -935,6 +935,40 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
   }
 }
 
+// Buffer resource of a device range of `bytes` bytes (< 4 GiB) for the
+// raw buffer loads: an offset at or past the range's end reads zeros and
+// touches no memory, so a lane with nothing to load takes kBufNone instead
+// of a branch around its load.  (Loads under branches, divergent or
+// uniform, leave the compiler unable to count the ones in flight, and it
+// then waits for all of them before the first use of any.)  Word 3 is the
+// gfx9 data format for raw 32-bit access.
+constexpr uint32_t kBufNone = 0x80000000u;
+
+// An offset chosen by a lane condition, passed through an empty asm
+// statement: the compiler cannot see the choice and so does not split the
+// load into two loads under branches.
+__device__ __forceinline__ uint32_t buf_off(bool ok, uint32_t off) {
+  uint32_t v = ok ? off : kBufNone;
+  asm("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // One piece (two 128-K super-steps of each K half) of one entry's down
 // weights and h, as one lane loads it.
 struct DnPiece {
@@ -942,6 +976,7 @@ struct DnPiece {
   uint32_t sp[2];
   float sd, w;  // the entry's FP32 tensor scale and this lane's token weight
 };
+constexpr int kDnRing = 4;
 
 // Down and combine: block = 8 output rows; the 8 waves take the entries
 // (selected experts, then the shared expert) in turn, each over the full K,
@@ -975,6 +1010,8 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
   const int n_routed = (a.E > 0) ? *a.ws.n_routed : 0;
   const int n_entries = n_routed + (a.Is > 0 ? 1 : 0);
   const int mine = wave < n_entries ? (n_entries - wave + kMmWaves - 1) / kMmWaves : 0;
+  const __amdgpu_buffer_rsrc_t hr = buf_rsrc(a.ws.h, (int64_t)(a.max_routed + 1) * B * Imax * 2);
+  const __amdgpu_buffer_rsrc_t ewr = buf_rsrc(a.ws.entry_w, (int64_t)a.max_routed * kMaxBatch * 4);
 
   for (int i0 = 0; i0 < mine; i0 += kWave) {
     // lane i holds the expert (-1: shared) and token mask of this wave's
@@ -991,32 +1028,38 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
       }
     }
     const int cnt = min(mine - i0, kWave), nu = cnt * NP;
+    // Units u >= nu in the ring's first pass load the last unit again (no
+    // load of that pass depends on a branch) and are not multiplied.
     auto load = [&](int u, DnPiece &L) __attribute__((always_inline)) {
-      const int ii = u / NP, pc = u - ii * NP;
+      const int uu = u < nu ? u : nu - 1;
+      const int ii = uu / NP, pc = uu - ii * NP;
       const int e = __builtin_amdgcn_readlane(e_l, ii);
       const uint32_t msk = (uint32_t)__builtin_amdgcn_readlane((int)m_l, ii);
       const int j = wave + (i0 + ii) * kMmWaves;
       const uint8_t *Wd = e >= 0 ? a.w_down + e * mbytes : a.sh_down;
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc(Wd, mbytes);
       const bool tok = r8 < B && ((msk >> r8) & 1u);  // B column m: token m & 7
-      const uint16_t *hrow = a.ws.h + ((int64_t)(e >= 0 ? j : a.max_routed) * B + r8) * Imax;
-      L.sd = e >= 0 ? a.w_scale[3 * e + 2] : a.sh_scale[2];
+      const uint32_t hrow = (uint32_t)(((e >= 0 ? j : a.max_routed) * B + r8) * Imax) * 2u;
+      L.sd = *(e >= 0 ? a.w_scale + 3 * e + 2 : a.sh_scale + 2);
       const int t = lane & 15;  // C column of this lane after the MFMAs: token t & 7
-      L.w = ((t & 7) < B && ((msk >> (t & 7)) & 1u)) ? (e >= 0 ? a.ws.entry_w[j * kMaxBatch + (t & 7)] : 1.0f) : 0.f;
+      const bool wt = (t & 7) < B && ((msk >> (t & 7)) & 1u);
+      const float ew = buf_load4f(ewr, (uint32_t)(j * kMaxBatch + (t & 7)) * 4u);
+      L.w = wt ? (e >= 0 ? ew : 1.0f) : 0.f;
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int cc = (pc * 2 + v) * 4 + p;  // chunk within this lane's K half
         const int c = kh * C2 + cc;
         const bool cok = cc < C2 && c < C;
-        L.q[v] = cok ? *reinterpret_cast<const uint4 *>(Wd + (int64_t)n * (K / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-        L.sp[v] = cok ? scale_pair(Wd, H, K, n, c) : 0u;
+        L.q[v] = buf_load16(wr, buf_off(cok, (uint32_t)(n * (K / 2) + c * 16)));
+        L.sp[v] = buf_load2(wr, buf_off(cok, (uint32_t)(H * K / 2 + ((n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2)));
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          L.hv[v][s] = (cok && tok) ? *reinterpret_cast<const uint4 *>(hrow + c * 32 + s * 8) : make_uint4(0, 0, 0, 0);
+          L.hv[v][s] = buf_load16(hr, buf_off(cok && tok, hrow + (uint32_t)(c * 32 + s * 8) * 2u));
       }
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     auto step = [&](int u, const DnPiece &L) __attribute__((always_inline)) {
-      const int ii = u / NP, pc = u - ii * NP;
+      const int pc = u - (u / NP) * NP;
 #pragma unroll
       for (int v = 0; v < 2; ++v)
 #pragma unroll
@@ -1037,13 +1080,20 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    DnPiece P0, P1;
-    if (nu > 0) load(0, P0);
-    for (int u = 0; u < nu; u += 2) {
-      if (u + 1 < nu) load(u + 1, P1);
-      step(u, P0);
-      if (u + 2 < nu) load(u + 2, P0);
-      if (u + 1 < nu) step(u + 1, P1);
+    // A ring of kDnRing pieces: every unit's loads are issued kDnRing - 1
+    // units ahead of its math (a wave's entries at the full shape, about
+    // four, are then all in flight at once).  The first kDnRing units are
+    // loaded unconditionally (the math of the first pass then waits for
+    // exactly its own unit); later loads only for units that exist.
+    DnPiece P[kDnRing];
+#pragma unroll
+    for (int q = 0; q < kDnRing; ++q) load(q, P[q]);
+    for (int u0 = 0; u0 < nu; u0 += kDnRing) {
+#pragma unroll
+      for (int q = 0; q < kDnRing; ++q) {
+        if (u0 + q < nu) step(u0 + q, P[q]);
+        if (u0 + q + kDnRing < nu) load(u0 + q + kDnRing, P[q]);
+      }
     }
   }
 #pragma unroll
