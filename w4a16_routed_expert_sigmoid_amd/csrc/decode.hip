@@ -802,6 +802,40 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &q, int s) {
   return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
 }
 
+// Buffer resource of a device range of `bytes` bytes (< 4 GiB) for the
+// raw buffer loads: an offset at or past the range's end reads zeros and
+// touches no memory, so a lane with nothing to load takes kBufNone instead
+// of a branch around its load.  (Loads under branches, divergent or
+// uniform, leave the compiler unable to count the ones in flight, and it
+// then waits for all of them before the first use of any.)  Word 3 is the
+// gfx9 data format for raw 32-bit access.
+constexpr uint32_t kBufNone = 0x80000000u;
+
+// An offset chosen by a lane condition, passed through an empty asm
+// statement: the compiler cannot see the choice and so does not split the
+// load into two loads under branches.
+__device__ __forceinline__ uint32_t buf_off(bool ok, uint32_t off) {
+  uint32_t v = ok ? off : kBufNone;
+  asm("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // Scale pair (blocks 2c, 2c+1) of row n of an N x K NVFP4 matrix.
 __device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int64_t K, int n, int c) {
   return *reinterpret_cast<const uint16_t *>(m + N * K / 2 + ((int64_t)(n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2);
@@ -866,7 +900,11 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
     for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int SS = (C + 3) / 4;
     // Two super-steps per pass, all their loads issued before any math, in
-    // the order the math consumes them (tokens, then row group by row group).
+    // the order the math consumes them (tokens, then row group by row group;
+    // raw buffer loads, a lane out of range reading zeros).
+    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xs, (int64_t)B * H * 2);
+    const __amdgpu_buffer_rsrc_t gr = buf_rsrc(Wg, nvfp4_matrix_bytes(N, H));
+    const __amdgpu_buffer_rsrc_t ur = buf_rsrc(Wu, nvfp4_matrix_bytes(N, H));
     for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
       uint4 qg[2][4], qu[2][4], xv[2][4];
       uint32_t sg[2][4], su[2][4];
@@ -877,19 +915,22 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
         const bool cok = ss < SS && c < C;
         const bool tok = cok && r16 < B;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          xv[v][s] = tok ? *reinterpret_cast<const uint4 *>(xs + (int64_t)r16 * H + c * 32 + s * 8)
-                         : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < 4; ++s) xv[v][s] = buf_load16(xr, buf_off(tok, (uint32_t)(r16 * H + c * 32 + s * 8) * 2u));
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int n = row0 + rg * 16 + r16;
           const bool ok = cok && n < N;
-          qg[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wg + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-          sg[v][rg] = ok ? scale_pair(Wg, N, H, n, c) : 0u;
-          qu[v][rg] = ok ? *reinterpret_cast<const uint4 *>(Wu + (int64_t)n * (H / 2) + c * 16) : make_uint4(0, 0, 0, 0);
-          su[v][rg] = ok ? scale_pair(Wu, N, H, n, c) : 0u;
+          const uint32_t qo = buf_off(ok, (uint32_t)(n * (H / 2) + c * 16));
+          const uint32_t so = buf_off(ok, (uint32_t)(N * (H / 2) + ((n >> 3) * (H / 32) + c) * 16 + (n & 7) * 2));
+          qg[v][rg] = buf_load16(gr, qo);
+          sg[v][rg] = buf_load2(gr, so);
+          qu[v][rg] = buf_load16(ur, qo);
+          su[v][rg] = buf_load2(ur, so);
         }
       }
+      // all loads of both super-steps issued before any math: the math of
+      // the first waits for its own loads only, while the second's arrive
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int v = 0; v < 2; ++v)
 #pragma unroll
@@ -933,40 +974,6 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
       }
     }
   }
-}
-
-// Buffer resource of a device range of `bytes` bytes (< 4 GiB) for the
-// raw buffer loads: an offset at or past the range's end reads zeros and
-// touches no memory, so a lane with nothing to load takes kBufNone instead
-// of a branch around its load.  (Loads under branches, divergent or
-// uniform, leave the compiler unable to count the ones in flight, and it
-// then waits for all of them before the first use of any.)  Word 3 is the
-// gfx9 data format for raw 32-bit access.
-constexpr uint32_t kBufNone = 0x80000000u;
-
-// An offset chosen by a lane condition, passed through an empty asm
-// statement: the compiler cannot see the choice and so does not split the
-// load into two loads under branches.
-__device__ __forceinline__ uint32_t buf_off(bool ok, uint32_t off) {
-  uint32_t v = ok ? off : kBufNone;
-  asm("" : "+v"(v));
-  return v;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
 // One piece (two 128-K super-steps of each K half) of one entry's down
