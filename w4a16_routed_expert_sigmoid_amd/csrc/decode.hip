@@ -139,9 +139,69 @@ __device__ __forceinline__ void wave_topk(const float *lt, int E, int k, int (&s
   }
 }
 
+// The same selection for E <= 256 (four experts per lane), with each
+// lane's keys sorted once: every round is then the wave max of the lanes'
+// first keys, one ballot for the lowest lane holding it, and that lane
+// shifts its list by one.  The sort is odd-even transposition (adjacent
+// exchanges on a strict comparison), so equal keys keep their index order
+// and a lane's first key is its lowest-index expert among equals.
+__device__ __forceinline__ void wave_topk4(const float *lt, int E, int k, int (&sel)[kMaxTopK],
+                                           float (&selv)[kMaxTopK]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float lv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane * 4 + j;
+    lv[j] = lt[e < E ? e : E - 1];
+  }
+  uint32_t key[4];
+  int idx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // the empty asm keeps the four loads unconditional and in flight
+    // together (a load whose value only one side of the bound test uses
+    // would otherwise move under that test, one wait per load)
+    float l = lv[j];
+    asm volatile("" : "+v"(l));
+    key[j] = (lane * 4 + j < E) ? topk_key(l) : 0u;
+    idx[j] = j;
+  }
+  auto cx = [&](int p, int q) __attribute__((always_inline)) {
+    const bool sw = key[q] > key[p];
+    const uint32_t kp = key[p], kq = key[q];
+    const int ip = idx[p], iq = idx[q];
+    key[p] = sw ? kq : kp;
+    key[q] = sw ? kp : kq;
+    idx[p] = sw ? iq : ip;
+    idx[q] = sw ? ip : iq;
+  };
+  cx(0, 1); cx(2, 3);
+  cx(1, 2);
+  cx(0, 1); cx(2, 3);
+  cx(1, 2);
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    if (r < k) {
+      // k <= E, so an untaken real key (> 0) remains and some lane holds m
+      const uint32_t m = wave_max_u32(key[0]);
+      const int L = (int)__builtin_ctzll(__ballot(key[0] == m));
+      sel[r] = L * 4 + __builtin_amdgcn_readlane(idx[0], L);
+      selv[r] = topk_key_logit(m);
+      const bool mine = lane == L;
+      key[0] = mine ? key[1] : key[0];
+      key[1] = mine ? key[2] : key[1];
+      key[2] = mine ? key[3] : key[2];
+      key[3] = mine ? 0u : key[3];
+      idx[0] = mine ? idx[1] : idx[0];
+      idx[1] = mine ? idx[2] : idx[1];
+      idx[2] = mine ? idx[3] : idx[2];
+    }
+  }
+}
+
 __device__ __forceinline__ void wave_topk_any(const float *lt, int E, int k, int (&sel)[kMaxTopK],
                                               float (&selv)[kMaxTopK]) {
-  if (E <= 4 * kWave) wave_topk<4>(lt, E, k, sel, selv);
+  if (E <= 4 * kWave) wave_topk4(lt, E, k, sel, selv);
   else wave_topk<kMaxExperts / kWave>(lt, E, k, sel, selv);
 }
 
