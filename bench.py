@@ -417,7 +417,11 @@ def run(args, dev):
         configs["nvfp4_b1"] = summary(r1, len(pool), 1)
         r8 = time_stack(args, dev, pool, descs, 8, zipf, "NVFP4 batch 8 (Zipf)")
         configs["nvfp4_b8_zipf"] = summary(r8, len(pool), 8)
-        for r in (r1, r8):
+        # 16 tokens through the same decode kernels (the mid-batch leg below
+        # runs 16 tokens through the prefill entry)
+        r16 = time_stack(args, dev, pool, descs, 16, zipf, "NVFP4 batch 16 (Zipf)")
+        configs["nvfp4_b16_zipf"] = summary(r16, len(pool), 16)
+        for r in (r1, r8, r16):
             if r["nonfinite"]:
                 warn.append("non-finite outputs")
     if args.workload == "layer" and not args.no_mid:

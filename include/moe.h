@@ -119,12 +119,15 @@ moe_status moe_dequant_nvfp4(const void *src, float *dst, int64_t rows, int64_t 
                              const float *tensor_scale, void *stream);
 
 /* Workspace bytes moe_decode_layer needs for batches up to max_batch, or 0
- * if the description is invalid. */
+ * if the description is invalid or max_batch is outside the layer's batch
+ * range (1..16 with NVFP4 weights, 1..8 with BF16 weights). */
 size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch);
 
-/* One decode step of the layer for `batch` independent tokens, 1..8 (the
- * low-latency path the pages describe for up to eight requests: "Day-0
- * Support for Flint on vLLM", section "Optimizations").
+/* One decode step of the layer for `batch` independent tokens: 1..16 with
+ * NVFP4 weights, 1..8 with BF16 weights (the low-latency path the pages
+ * describe for up to eight requests: "Day-0 Support for Flint on vLLM",
+ * section "Optimizations"; batches of 9..16 run the same matrix-core
+ * kernels as 2..8, the tokens filling the 16 columns of their tiles).
  *  x [batch][H] BF16 in; y [batch][H] BF16 out.
  *  Per token: xn = x, or, when norm_gain is given, xn = BF16(x /
  *  sqrt(mean(x^2) + eps) * gain), rounded once from the exact value;
@@ -145,10 +148,11 @@ size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch)
  *  across calls and batch sizes.  Its first word reports waits that gave
  *  up (moe_decode_wait_status).
  *  Concurrent calls must not share a workspace.
- * Errors: UNSUPPORTED for batch outside 1..8 (use moe_prefill_layer) and
- * for shapes the kernels do not tile (H/32, I/32 and Is/32 must each be at
- * least 2 and either a power of two or at least 64; E at most 1024; Is == I
- * when both routed and shared experts exist; batch * H * 2 <= 64 KiB); INVALID_ARG for null required
+ * Errors: UNSUPPORTED for batch above the range (use moe_prefill_layer)
+ * and for shapes the kernels do not tile (H/32, I/32 and Is/32 must each
+ * be at least 2 and either a power of two or at least 64; E at most 1024;
+ * Is == I when both routed and shared experts exist; batch * H * 2 <= 64
+ * KiB; for batch >= 2 with routed experts, (batch + 1) * E <= 16384); INVALID_ARG for null required
  * pointers, misalignment, top_k outside 1..8 or above E, H or I not a
  * multiple of 32; WORKSPACE; HIP. */
 moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, const void *x,
@@ -160,7 +164,8 @@ moe_status moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights 
  * layers' hidden sizes differ. */
 size_t moe_decode_step_workspace_bytes(const moe_layer_desc *descs, int32_t n_layers, int32_t max_batch);
 
-/* One decode step of `batch` tokens (1..8) through a stack of pre-norm
+/* One decode step of `batch` tokens (1..16; 1..8 if a layer has BF16
+ * weights) through a stack of pre-norm
  * residual layers ("vLLM Flint" commentary, section "Only 14 of 49 layers
  * retain full-history KV": 49 pre-norm layers; "Day-0 Support for Flint on
  * vLLM", section "Model architecture": layers 0 and 1 use a dense MLP, the

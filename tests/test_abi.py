@@ -180,9 +180,13 @@ def test_workspace_bytes():
     lib = host()
     n1 = lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 1)
     n8 = lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 8)
-    assert 0 < n1 < n8
+    n16 = lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 16)
+    assert 0 < n1 < n8 < n16
     assert lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 0) == 0
-    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 9) == 0
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc()), 17) == 0
+    # BF16 weights: up to 8 tokens
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc(wtype=W_BF16)), 8) > 0
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(desc(wtype=W_BF16)), 9) == 0
     assert lib.moe_decode_workspace_bytes(ctypes.byref(desc(hidden=100)), 1) == 0
 
 
@@ -194,13 +198,16 @@ def test_a_valid_call_passes_validation():
     # call would launch (nothing is launched by the check).
     assert decode("host") == OK
     assert decode("host", batch=8, idx=TK, tw=TK + 4096) == OK
+    assert decode("host", batch=16, idx=TK, tw=TK + 4096) == OK
     assert prefill("host", idx=TK, tw=TK + 4096) == OK
 
 
 @pytest.mark.parametrize("which", LIBS)
 @pytest.mark.parametrize("kw,want", [
     (dict(batch=0), INVALID),
-    (dict(batch=9), UNSUPPORTED),
+    (dict(batch=17), UNSUPPORTED),
+    (dict(batch=9, d=desc(wtype=W_BF16)), UNSUPPORTED),                       # BF16 weights: 8 tokens
+    (dict(batch=16, d=desc(n_experts=1024, top_k=8)), UNSUPPORTED),          # 17 x 1024 > the routing stage
     (dict(x=None), INVALID),
     (dict(y=None), INVALID),
     (dict(ws=None), INVALID),
@@ -312,7 +319,9 @@ def test_step_validation(which):
     assert step_bytes([d, desc(hidden=1024)], 1) == 0
     G = 1 << 30
     assert step(which, dd, ww, 0, A(20), 1, A(21), A(22), G) == INVALID
-    assert step(which, dd, ww, 2, A(20), 9, A(21), A(22), G) == UNSUPPORTED
+    assert step(which, dd, ww, 2, A(20), 17, A(21), A(22), G) == UNSUPPORTED
+    bf = (Desc * 2)(desc(wtype=W_BF16), dd[1])
+    assert step(which, bf, ww, 2, A(20), 9, A(21), A(22), G) == UNSUPPORTED
     assert step(which, dd, ww, 2, A(20), 1, A(20), A(22), G) == INVALID
     assert step(which, dd, ww, 2, A(22) + 4096, 1, A(21), A(22), G) == INVALID   # x inside ws
     assert step(which, dd, ww, 2, A(20), 1, A(21), A(22), 64) == WORKSPACE
@@ -401,7 +410,7 @@ def test_noalloc_rejects_layers_beyond_its_array():
                                                      0, A(21), None, None, None)
     assert call(big, 8) == WORKSPACE
     assert call(desc(top_k=9), 1) == INVALID
-    assert call(desc(), 9) == UNSUPPORTED
+    assert call(desc(), 17) == UNSUPPORTED
     assert call(desc(), 0) == INVALID
 
 
@@ -571,7 +580,7 @@ def test_persistent_step_workspace_and_checks():
     chk = host().moe_check_decode_step_persistent
     assert chk(ds, ww, 3, A(20), 1, A(21), A(22), pers) == OK
     assert chk(ds, ww, 3, A(20), 1, A(21), A(22), pers - 1) == WORKSPACE
-    assert chk(ds, ww, 3, A(20), 9, A(21), A(22), pers) == UNSUPPORTED
+    assert chk(ds, ww, 3, A(20), 17, A(21), A(22), pers) == UNSUPPORTED
     assert chk(ds, ww, 0, A(20), 1, A(21), A(22), pers) == INVALID
     assert chk(ds, ww, 3, A(20), 1, A(20), A(22), pers) == INVALID   # y == x
 

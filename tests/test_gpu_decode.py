@@ -102,7 +102,19 @@ def test_decode_small(wtype, B):
     log(f"  {st}")
 
 
-@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("B", [9, 12, 16])
+def test_decode_small_sixteen_token_batches(B):
+    # NVFP4 batches of 9..16 tokens: the tokens fill the 16 columns of the
+    # gate/up tiles and two token groups of the down tiles.
+    log(f"test: decode small nvfp4 B={B}")
+    L = synth.make_layer(11, bias="zipf", **SMALL)
+    x = synth.tokens(B, 256, stream=100 + B)
+    out, idx, w = run(L, x)
+    _, st = compare(L, x, out, idx, w, what=f"small nvfp4 B={B}")
+    log(f"  {st}")
+
+
+@pytest.mark.parametrize("B", [1, 8, 16])
 def test_decode_small_norm_residual(B):
     log(f"test: decode small norm+residual B={B}")
     L = synth.make_layer(12, bias="zipf", norm=True, residual=True, **SMALL)
@@ -127,9 +139,10 @@ def test_decode_top1_no_shared():
     compare(L, x, out, idx, w, what="k=1, no shared")
 
 
-def test_decode_identical_tokens_share_experts():
+@pytest.mark.parametrize("B", [8, 16])
+def test_decode_identical_tokens_share_experts(B):
     L = synth.make_layer(15, **SMALL)
-    x = np.repeat(synth.tokens(1, 256, stream=7), 8, axis=0)
+    x = np.repeat(synth.tokens(1, 256, stream=7), B, axis=0)
     out, idx, w = run(L, x)
     assert len({tuple(sorted(r)) for r in idx.tolist()}) == 1
     assert np.all(out == out[0:1])
@@ -177,20 +190,22 @@ def test_decode_wide_hidden_multi_chunk_lanes(B, norm):
     compare(L, x, out, idx, w, what=f"H=4096 B={B} norm={norm}")
 
 
-@pytest.mark.parametrize("Is,norm", [(2112, True), (2112, False), (256, True)])
-def test_dense_layer_small(Is, norm):
-    # 2112 = 66 chunks of 32: two chunk steps per lane, the second ragged.
+@pytest.mark.parametrize("Is,norm,B", [(2112, True, 2), (2112, False, 2), (256, True, 2), (2112, True, 16),
+                                        (256, False, 11)])
+def test_dense_layer_small(Is, norm, B):
+    # 2112 = 66 chunks of 32: two chunk steps per lane, the second ragged
+    # (and five K pieces per entry in the batch down kernel).
     L = synth.make_layer(18, hidden=256, inter=0, shared_inter=Is, n_experts=0, norm=norm, residual=norm)
-    x = synth.tokens(2, 256, stream=10)
+    x = synth.tokens(B, 256, stream=10)
     out, _, _ = run(L, x)
-    compare(L, x, out, None, None, what="dense")
+    compare(L, x, out, None, None, what=f"dense B={B}")
 
 
 def test_workspace_reuse_across_batches_and_determinism():
     L = synth.make_layer(19, bias="zipf", **SMALL)
     dev = moe.DeviceLayer(L)
-    ws = dev.workspace(8)
-    for B in (8, 1, 3, 8):
+    ws = dev.workspace(16)
+    for B in (8, 1, 16, 3, 9, 8):
         x = synth.tokens(B, 256, stream=300 + B)
         a = run(L, x, dev, ws)
         b = run(L, x, dev, ws)
@@ -243,7 +258,7 @@ def full_layer(kind):
 
 
 @pytest.mark.parametrize("kind,B", [("bf16", 1), ("nvfp4", 1), ("zipf", 8), ("nvfp4", 8), ("norm", 1),
-                                    ("norm", 8), ("dense", 1)])
+                                    ("norm", 8), ("dense", 1), ("zipf", 16), ("nvfp4", 12), ("dense", 16)])
 def test_decode_full_shape(kind, B):
     log(f"test: full shape {kind} B={B}")
     L = full_layer(kind)

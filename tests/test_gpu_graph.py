@@ -27,7 +27,7 @@ def layers():
             synth.make_layer(142, norm=True, residual=True, **kw)]
 
 
-@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("B", [1, 3, 16])
 def test_graph_replays_match_eager_calls(B):
     log(f"test: graph replays B={B}")
     devs = [moe.DeviceLayer(L) for L in layers()]

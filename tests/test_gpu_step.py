@@ -47,7 +47,7 @@ def stack(kind):
 
 
 @pytest.mark.parametrize("kind,B", [("small", 1), ("small", 8), ("mixed", 1), ("mixed", 3), ("full", 1),
-                                    ("full", 8)])
+                                    ("full", 8), ("full", 16)])
 def test_step_matches_layers_and_oracle(kind, B):
     log(f"test: step {kind} B={B}")
     layers = stack(kind)

@@ -375,17 +375,17 @@ __device__ void route_block(const DecodeArgs &a, uint4 *lds);
 // ... of the row, so a wave's LDS and global accesses are contiguous.
 constexpr int kRouterWaves = 4;
 constexpr int kRouterThreads = kRouterWaves * kWave;
-constexpr int kRouteWaves = kMaxBatch;  // batches: one wave per token in the routing block
+constexpr int kRouteWaves = kMaxBatchBf16;  // BF16 batches: one wave per token in the routing block
 
-// MT: tokens a block handles.  kMaxBatch: the whole batch, staged in
-// kMaxBatch * 4096 / 8 16-byte pieces (B * H <= 32768).  1: one token of a
+// MT: tokens a block handles.  kMaxBatchBf16: the whole batch (BF16
+// weights), staged in 32768 / 8 16-byte pieces (B * H <= 32768).  1: one token of a
 // batch of two or more, the batch split over blockIdx.y; its stage takes
 // at most 16384 / 8 pieces (H <= 16384), and its per-token registers are a
 // batch's eighth, so that several blocks fit on a compute unit.
-template <int W, int MT = kMaxBatch>
+template <int W, int MT>
 __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready, int route) {
   constexpr int kRouterWaves = W, kRouterThreads = W * kWave;
-  constexpr int XCAP = MT == 1 ? 16384 / 8 : kMaxBatch * 4096 / 8;
+  constexpr int XCAP = MT == 1 ? 16384 / 8 : 32768 / 8;
   static_assert(XCAP * 16 >= 32768, "the routing block keeps B * E <= 8192 logits in the stage");
   __shared__ uint4 s_x[XCAP];  // [B][H] BF16
   __shared__ double s_ss[kRouterWaves][MT];
@@ -1038,24 +1038,31 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
 
 // One piece (two 128-K super-steps of each K half) of one entry's down
 // weights and h, as one lane loads it.
+template <int G>
 struct DnPiece {
-  uint4 q[2], hv[2][4];
+  uint4 q[2], hv[G][2][4];
   uint32_t sp[2];
-  float sd, w;  // the entry's FP32 tensor scale and this lane's token weight
+  float sd, w[G];  // the entry's FP32 tensor scale and this lane's token weight per token group
 };
-constexpr int kDnRing = 4;
 
 // Down and combine: block = 8 output rows; the 8 waves take the entries
 // (selected experts, then the shared expert) in turn, each over the full K,
-// loading the next piece while the current one is multiplied.
+// with the loads of the next units in flight.
 //   The 16x16 MFMA tile is split in two along K: A row m holds weight row
-//   m & 7 over K half m >> 3, B column n holds token n & 7 over K half
-//   n >> 3, so the C entries with m >> 3 == n >> 3 are the two half-K
-//   products of (row, token) and the rest are discarded; lane l and lane
-//   l ^ 40 hold the two halves.  8-row blocks put H/8 blocks on the GPU,
-//   each owning its rows outright (no cross-block combine).
+//   m & 7 over K half m >> 3, B column n holds token 8g + (n & 7) of token
+//   group g over K half n >> 3, so the C entries with m >> 3 == n >> 3 are
+//   the two half-K products of (row, token) and the rest are discarded;
+//   lane l and lane l ^ 40 hold the two halves.  G token groups (1 for up
+//   to 8 tokens, 2 for up to 16) share each dequantised A fragment.  8-row
+//   blocks put H/8 blocks on the GPU, each owning its rows outright (no
+//   cross-block combine).
+template <int G>
 __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
-  __shared__ float s_red[kMmWaves][4][kWave];
+  // A ring of RING pieces: every unit's loads are issued RING - 1 units
+  // ahead of its math (a wave's entries at the full batch-8 shape, about
+  // four, are then all in flight at once).
+  constexpr int RING = G == 1 ? 4 : 2;
+  __shared__ float s_red[kMmWaves][G][4][kWave];
   const int H = a.H, B = a.B;
   const int K = (a.E > 0) ? a.I : a.Is;  // Is == I when both exist
   const int C = K / 32, C2 = (C + 1) / 2, NP = (C2 + 7) / 8;  // chunks per K half; 8-chunk pieces
@@ -1065,7 +1072,9 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
   const int row0 = blockIdx.x * 8;
   const int n = row0 + r8;
   const int64_t mbytes = nvfp4_matrix_bytes(H, K);
-  float tot[4] = {0.f, 0.f, 0.f, 0.f};
+  float tot[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g) tot[g][0] = tot[g][1] = tot[g][2] = tot[g][3] = 0.f;
   // The entry arrays hold max_routed slots: the first 64 of this wave's
   // slots are read together with the count.
   int e_l = -1;
@@ -1097,7 +1106,7 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
     const int cnt = min(mine - i0, kWave), nu = cnt * NP;
     // Units u >= nu in the ring's first pass load the last unit again (no
     // load of that pass depends on a branch) and are not multiplied.
-    auto load = [&](int u, DnPiece &L) __attribute__((always_inline)) {
+    auto load = [&](int u, DnPiece<G> &L) __attribute__((always_inline)) {
       const int uu = u < nu ? u : nu - 1;
       const int ii = uu / NP, pc = uu - ii * NP;
       const int e = __builtin_amdgcn_readlane(e_l, ii);
@@ -1105,13 +1114,16 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
       const int j = wave + (i0 + ii) * kMmWaves;
       const uint8_t *Wd = e >= 0 ? a.w_down + e * mbytes : a.sh_down;
       const __amdgpu_buffer_rsrc_t wr = buf_rsrc(Wd, mbytes);
-      const bool tok = r8 < B && ((msk >> r8) & 1u);  // B column m: token m & 7
-      const uint32_t hrow = (uint32_t)(((e >= 0 ? j : a.max_routed) * B + r8) * Imax) * 2u;
+      const int slot = e >= 0 ? j : a.max_routed;
       L.sd = *(e >= 0 ? a.w_scale + 3 * e + 2 : a.sh_scale + 2);
-      const int t = lane & 15;  // C column of this lane after the MFMAs: token t & 7
-      const bool wt = (t & 7) < B && ((msk >> (t & 7)) & 1u);
-      const float ew = buf_load4f(ewr, (uint32_t)(j * kMaxBatch + (t & 7)) * 4u);
-      L.w = wt ? (e >= 0 ? ew : 1.0f) : 0.f;
+      const int t = lane & 15;  // C column of this lane after the MFMAs: token 8g + (t & 7)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int tc = 8 * g + (t & 7);
+        const bool wt = tc < B && ((msk >> tc) & 1u);
+        const float ew = buf_load4f(ewr, (uint32_t)(j * kMaxBatch + tc) * 4u);
+        L.w[g] = wt ? (e >= 0 ? ew : 1.0f) : 0.f;
+      }
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int cc = (pc * 2 + v) * 4 + p;  // chunk within this lane's K half
@@ -1120,60 +1132,75 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_down_mm(DecodeArgs a) {
         L.q[v] = buf_load16(wr, buf_off(cok, (uint32_t)(n * (K / 2) + c * 16)));
         L.sp[v] = buf_load2(wr, buf_off(cok, (uint32_t)(H * K / 2 + ((n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2)));
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          L.hv[v][s] = buf_load16(hr, buf_off(cok && tok, hrow + (uint32_t)(c * 32 + s * 8) * 2u));
+        for (int g = 0; g < G; ++g) {
+          const int tb = 8 * g + r8;  // B column m: token 8g + (m & 7)
+          const bool tok = tb < B && ((msk >> tb) & 1u);
+          const uint32_t hrow = (uint32_t)((slot * B + tb) * Imax) * 2u;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            L.hv[g][v][s] = buf_load16(hr, buf_off(cok && tok, hrow + (uint32_t)(c * 32 + s * 8) * 2u));
+        }
       }
     };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto step = [&](int u, const DnPiece &L) __attribute__((always_inline)) {
+    f32x4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int u, const DnPiece<G> &L) __attribute__((always_inline)) {
       const int pc = u - (u / NP) * NP;
 #pragma unroll
       for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const float sc = e4m3_to_f32((L.sp[v] >> (8 * (s >> 1))) & 0xffu);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              dq8(word_of(L.q[v], s), sc),
-              __builtin_bit_cast(bf16x8, u32x4{L.hv[v][s].x, L.hv[v][s].y, L.hv[v][s].z, L.hv[v][s].w}), acc, 0, 0, 0);
+          const bf16x8 af = dq8(word_of(L.q[v], s), sc);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af, __builtin_bit_cast(bf16x8, u32x4{L.hv[g][v][s].x, L.hv[g][v][s].y, L.hv[g][v][s].z, L.hv[g][v][s].w}),
+                acc[g], 0, 0, 0);
         }
       if (pc == NP - 1) {
         // entry done: lanes l < 32 with l & 8 == 0 add the other K half
-        // (lane l ^ 40) and hold rows (l/16)*4 + i of token l & 7
+        // (lane l ^ 40) and hold rows (l/16)*4 + i of token 8g + (l & 7)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float full = acc[i] + xor_lane<8>(xor_lane<32>(acc[i]));
-          tot[i] += L.w * round_bf16(full * L.sd);
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float full = acc[g][i] + xor_lane<8>(xor_lane<32>(acc[g][i]));
+            tot[g][i] += L.w[g] * round_bf16(full * L.sd);
+          }
+          acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    // A ring of kDnRing pieces: every unit's loads are issued kDnRing - 1
-    // units ahead of its math (a wave's entries at the full shape, about
-    // four, are then all in flight at once).  The first kDnRing units are
-    // loaded unconditionally (the math of the first pass then waits for
-    // exactly its own unit); later loads only for units that exist.
-    DnPiece P[kDnRing];
+    // The first RING units are loaded unconditionally (the math of the
+    // first pass then waits for exactly its own unit); later loads only for
+    // units that exist.
+    DnPiece<G> P[RING];
 #pragma unroll
-    for (int q = 0; q < kDnRing; ++q) load(q, P[q]);
-    for (int u0 = 0; u0 < nu; u0 += kDnRing) {
+    for (int q = 0; q < RING; ++q) load(q, P[q]);
+    for (int u0 = 0; u0 < nu; u0 += RING) {
 #pragma unroll
-      for (int q = 0; q < kDnRing; ++q) {
+      for (int q = 0; q < RING; ++q) {
         if (u0 + q < nu) step(u0 + q, P[q]);
-        if (u0 + q + kDnRing < nu) load(u0 + q + kDnRing, P[q]);
+        if (u0 + q + RING < nu) load(u0 + q + RING, P[q]);
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s_red[wave][i][lane] = tot[i];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][g][i][lane] = tot[g][i];
   __syncthreads();
-  const int t = lane & 7;
-  if (tid < 32 && (lane & 8) == 0 && t < B) {
+  // thread g * 32 + l (l < 32, l & 8 == 0): rows (l/16)*4 + i of token 8g + (l & 7)
+  const int g = tid >> 5, l = tid & 31, t = 8 * g + (l & 7);
+  if (g < G && (l & 8) == 0 && t < B) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kMmWaves; ++w) v += s_red[w][i][lane];
-      const int64_t o = (int64_t)t * H + row0 + (lane >> 4) * 4 + i;
+      for (int w = 0; w < kMmWaves; ++w) v += s_red[w][g][i][l];
+      const int64_t o = (int64_t)t * H + row0 + (l >> 4) * 4 + i;
       float r = round_bf16(v);
       if (a.residual) r = bf16_to_f32(a.x[o]) + r;
       a.y[o] = (uint16_t)f32_to_bf16(r);
@@ -2033,7 +2060,10 @@ static hipError_t launch_experts(const DecodeArgs &a, hipStream_t stream, hipEve
     if ((e = launch(k_gateup_mm, dim3(grid), dim3(kMmWaves * kWave), 0, stream,
                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, a)) != hipSuccess)
       return e;
-    return launch(k_down_mm, dim3(a.H / 8), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
+    if (a.B > 8)
+      return launch(k_down_mm<2>, dim3(a.H / 8), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
+                    ev ? ev[5] : nullptr, a);
+    return launch(k_down_mm<1>, dim3(a.H / 8), dim3(kMmWaves * kWave), 0, stream, ev ? ev[4] : nullptr,
                   ev ? ev[5] : nullptr, a);
   }
   {
@@ -2115,7 +2145,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t con
     // the routing from the others' logits
     const int rows_per_block = kRouteWaves * (kWave / lanes_per_row(a.H));
     const int grid = (a.E + rows_per_block - 1) / rows_per_block + 1;
-    if ((e = launch(k_router<kRouteWaves>, dim3(grid), dim3(kRouteWaves * kWave), 0, stream, ev ? ev[0] : nullptr,
+    if ((e = launch(k_router<kRouteWaves, kMaxBatchBf16>, dim3(grid), dim3(kRouteWaves * kWave), 0, stream, ev ? ev[0] : nullptr,
                     ev ? ev[1] : nullptr, a, xn_ready, 1)) != hipSuccess)
       return e;
   } else if (a.use_norm && !xn_ready) {

@@ -13,7 +13,9 @@
 namespace moe {
 
 constexpr int kWave = 64;
-constexpr int kMaxBatch = 8;   // decode path: up to eight tokens
+constexpr int kMaxBatch = 16;     // decode path: up to 16 tokens (NVFP4 weights)
+constexpr int kMaxBatchBf16 = 8;  // decode path with BF16 weights, and the dense projection
+constexpr int kMaxRouteStage = 16384;  // floats of a batch gate/up block's routing stage: B * E logits + E marks
 constexpr int kMaxTopK = 8;
 constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
 constexpr int kMaxExperts = 1024;

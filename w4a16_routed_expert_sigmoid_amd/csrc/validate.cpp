@@ -42,6 +42,11 @@ bool disjoint(const Range *r, int n) {
 
 }  // namespace
 
+// Largest decode batch of a layer: 16 tokens with NVFP4 weights (the
+// matrix-core kernels take the tokens as the 16 columns of their tiles),
+// 8 with BF16 weights (per-token dot products on the vector ALUs).
+int max_batch_of(const moe_layer_desc &d) { return d.wtype == 1 ? kMaxBatch : kMaxBatchBf16; }
+
 int max_routed_of(const moe_layer_desc &d, int B) {
   if (d.n_experts <= 0) return 0;
   const int m = B * d.top_k;
@@ -94,7 +99,8 @@ DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap) {
 bool step_layout(const moe_layer_desc *descs, int32_t n_layers, int32_t B, StepLayout &L) {
   if (!descs || n_layers < 1 || B < 1 || B > kMaxBatch) return false;
   for (int32_t i = 0; i < n_layers; ++i)
-    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden) return false;
+    if (check_desc(&descs[i]) != MOE_OK || descs[i].hidden != descs[0].hidden || B > max_batch_of(descs[i]))
+      return false;
   L.sync_cap = 0;
   for (int32_t i = 0; i < n_layers; ++i) {
     const size_t b = sync_bytes_of(descs[i], B);
@@ -221,9 +227,12 @@ moe_status check_decode_call(const moe_layer_desc *desc, const moe_layer_weights
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (batch < 1) return MOE_ERR_INVALID_ARG;
-  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
-  // The routing kernels stage the batch's activations through 64 KiB.
+  if (batch > max_batch_of(*desc)) return MOE_ERR_UNSUPPORTED;
+  // The routing kernels stage the batch's activations through 64 KiB, and
+  // a batch gate/up block its logits and expert marks through 64 KiB.
   if ((size_t)batch * desc->hidden * 2 > 65536) return MOE_ERR_UNSUPPORTED;
+  if (batch > 1 && desc->n_experts > 0 && (size_t)(batch + 1) * desc->n_experts > (size_t)kMaxRouteStage)
+    return MOE_ERR_UNSUPPORTED;
   st = check_weights(desc, w);
   if (st != MOE_OK) return st;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -251,7 +260,8 @@ moe_status check_step_call(const moe_layer_desc *descs, const moe_layer_weights 
     if (descs[i].hidden != descs[0].hidden) return MOE_ERR_INVALID_ARG;
   }
   if (batch < 1) return MOE_ERR_INVALID_ARG;
-  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  for (int32_t i = 0; i < n_layers; ++i)
+    if (batch > max_batch_of(descs[i])) return MOE_ERR_UNSUPPORTED;
   if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
   const size_t act = (size_t)batch * descs[0].hidden * 2;
@@ -316,7 +326,7 @@ moe_status check_gemv_call(const void *w, const float *tensor_scale, int64_t row
   if (rows <= 0 || cols <= 0 || rows % 8 || cols % 32) return MOE_ERR_INVALID_ARG;
   if (batch < 1) return MOE_ERR_INVALID_ARG;
   if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(tensor_scale, 4)) return MOE_ERR_INVALID_ARG;
-  if (batch > kMaxBatch) return MOE_ERR_UNSUPPORTED;
+  if (batch > kMaxBatchBf16) return MOE_ERR_UNSUPPORTED;
   // one token stages x in 64 KiB of LDS
   if (!k_tileable(cols) || rows > (int64_t)1 << 30 || (batch == 1 && cols > 32768)) return MOE_ERR_UNSUPPORTED;
   // the output may share no byte with an input
@@ -491,7 +501,7 @@ size_t moe_nvfp4_matrix_bytes(int64_t rows, int64_t cols) {
 }
 
 size_t moe_decode_workspace_bytes(const moe_layer_desc *desc, int32_t max_batch) {
-  if (check_desc(desc) != MOE_OK || max_batch < 1 || max_batch > kMaxBatch) return 0;
+  if (check_desc(desc) != MOE_OK || max_batch < 1 || max_batch > max_batch_of(*desc)) return 0;
   return decode_layout(*desc, max_batch).bytes;
 }
 

@@ -42,6 +42,7 @@ struct PfLayout {
   int64_t max_tiles;
 };
 
+int max_batch_of(const moe_layer_desc &d);
 int max_routed_of(const moe_layer_desc &d, int B);
 size_t sync_bytes_of(const moe_layer_desc &d, int B);
 DecodeLayout decode_layout(const moe_layer_desc &d, int B, size_t sync_cap = 0);
