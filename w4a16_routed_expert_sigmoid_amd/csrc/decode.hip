@@ -901,138 +901,159 @@ __device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int6
   return *reinterpret_cast<const uint16_t *>(m + N * K / 2 + ((int64_t)(n >> 3) * (K / 32) + c) * 16 + (n & 7) * 2);
 }
 
+// One gate/up work item: rows [row0, row0 + 16 RG) of one entry (a
+// selected expert, or the shared one) over the full K, split over the 8
+// waves and met in LDS.  RG: 16-row groups per item (4, or 2 when the
+// items of 64 rows outnumber the blocks).
+template <int RG>
+__device__ __forceinline__ void gateup_item(const DecodeArgs &a, const Routing &R, float (&s_red)[kMmWaves][32][kWave],
+                                            const uint16_t *xs, int item, int groups, int sh_groups) {
+  const int H = a.H, B = a.B, C = H / 32;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r16 = lane & 15, p = lane >> 4;
+  const bool shared = item < sh_groups;
+  const int slot = shared ? a.max_routed : (item - sh_groups) / groups;
+  const int row0 = (shared ? item : (item - sh_groups) % groups) * (16 * RG);
+  const uint8_t *Wg, *Wu;
+  float Sg, Su;
+  uint32_t mask;
+  int N;
+  if (!shared) {
+    const int e = R.expert[slot];
+    mask = R.mask[slot];
+    N = a.I;
+    const int64_t mb = nvfp4_matrix_bytes(a.I, H);
+    Wg = a.w_gate + e * mb;
+    Wu = a.w_up + e * mb;
+    Sg = a.w_scale[3 * e + 0];
+    Su = a.w_scale[3 * e + 1];
+  } else {
+    mask = (1u << B) - 1u;
+    N = a.Is;
+    Wg = a.sh_gate;
+    Wu = a.sh_up;
+    Sg = a.sh_scale[0];
+    Su = a.sh_scale[1];
+  }
+  if (row0 >= N) return;  // block-uniform
+
+  f32x4 acc[RG][2];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int SS = (C + 3) / 4;
+  // Two super-steps per pass, all their loads issued before any math, in
+  // the order the math consumes them (tokens, then row group by row group;
+  // raw buffer loads, a lane out of range reading zeros).
+  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xs, (int64_t)B * H * 2);
+  const __amdgpu_buffer_rsrc_t gr = buf_rsrc(Wg, nvfp4_matrix_bytes(N, H));
+  const __amdgpu_buffer_rsrc_t ur = buf_rsrc(Wu, nvfp4_matrix_bytes(N, H));
+  for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
+    uint4 qg[2][RG], qu[2][RG], xv[2][4];
+    uint32_t sg[2][RG], su[2][RG];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int ss = ss0 + v * kMmWaves;
+      const int c = ss * 4 + p;
+      const bool cok = ss < SS && c < C;
+      const bool tok = cok && r16 < B;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xv[v][s] = buf_load16(xr, buf_off(tok, (uint32_t)(r16 * H + c * 32 + s * 8) * 2u));
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const int n = row0 + rg * 16 + r16;
+        const bool ok = cok && n < N;
+        const uint32_t qo = buf_off(ok, (uint32_t)(n * (H / 2) + c * 16));
+        const uint32_t so = buf_off(ok, (uint32_t)(N * (H / 2) + ((n >> 3) * (H / 32) + c) * 16 + (n & 7) * 2));
+        qg[v][rg] = buf_load16(gr, qo);
+        sg[v][rg] = buf_load2(gr, so);
+        qu[v][rg] = buf_load16(ur, qo);
+        su[v][rg] = buf_load2(ur, so);
+      }
+    }
+    // all loads of both super-steps issued before any math: the math of
+    // the first waits for its own loads only, while the second's arrive
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
+          const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
+          const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
+          acc[rg][0] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
+          acc[rg][1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
+        }
+      }
+  }
+  // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
+  __syncthreads();  // the routing's logits, or the previous item's sums, are no longer read
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
+      s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < RG / 2; ++k) {
+    const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
+    const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMmWaves; ++w) {
+      g += s_red[w][rg * 8 + i][l];
+      u += s_red[w][rg * 8 + 4 + i][l];
+    }
+    const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
+    if (t < B && n < N && ((mask >> t) & 1u)) {
+      const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
+      a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
+    }
+  }
+}
+
 // Gate/up of a batch.  With routed experts every block first derives the
 // routing from the logits (one wave per token: the top-k, then the sorted
 // list of distinct experts), so no separate routing stage runs between the
 // router kernel and this one; block 0 also publishes the list, the combine
 // weights and the top-k outputs for the down kernel.  Work items are
-// (entry, 64-row group) pairs, the shared expert's first (they need no
+// (entry, row group) pairs, the shared expert's first (they need no
 // routing), then the distinct selected experts'; blocks take items in
-// turn.  Per item the 8 waves split K and meet in LDS.
+// turn.
 __global__ __launch_bounds__(kMmWaves *kWave) void k_gateup_mm(DecodeArgs a) {
   __shared__ float s_red[kMmWaves][32][kWave];  // before the first item: the logits and marks of the routing
   __shared__ Routing R;
-  const int H = a.H, B = a.B, C = H / 32;
+  const int B = a.B;
   const int Imax = a.I > a.Is ? a.I : a.Is;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int r16 = lane & 15, p = lane >> 4;
-  const int groups = (Imax + kMmRows - 1) / kMmRows;
-  const int sh_groups = a.Is > 0 ? (a.Is + kMmRows - 1) / kMmRows : 0;
-  int n_items = sh_groups;
+  const int tid = threadIdx.x;
+  int n_routed = 0;
   if (a.E > 0) {
-    float *s_l = &s_red[0][0][0];                                   // [B][E] <= 32 KiB
-    uint32_t *s_mark = reinterpret_cast<uint32_t *>(s_l + B * a.E);  // [E] <= 4 KiB
+    float *s_l = &s_red[0][0][0];                                   // [B][E]
+    uint32_t *s_mark = reinterpret_cast<uint32_t *>(s_l + B * a.E);  // [E]; (B + 1) E <= 16384 floats
     for (int i = tid; i < B * a.E; i += kMmWaves * kWave) s_l[i] = a.ws.logits[i];
     build_routing(a, s_l, R, s_mark, kMmWaves);  // ends with a barrier
     if (blockIdx.x == 0) publish_routing(a, R);
-    n_items += R.n * groups;
+    n_routed = R.n;
   }
   const uint16_t *xs = a.use_norm ? a.ws.xn : a.x;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const bool shared = item < sh_groups;
-    const int slot = shared ? a.max_routed : (item - sh_groups) / groups;
-    const int row0 = (shared ? item : (item - sh_groups) % groups) * kMmRows;
-    const uint8_t *Wg, *Wu;
-    float Sg, Su;
-    uint32_t mask;
-    int N;
-    if (!shared) {
-      const int e = R.expert[slot];
-      mask = R.mask[slot];
-      N = a.I;
-      const int64_t mb = nvfp4_matrix_bytes(a.I, H);
-      Wg = a.w_gate + e * mb;
-      Wu = a.w_up + e * mb;
-      Sg = a.w_scale[3 * e + 0];
-      Su = a.w_scale[3 * e + 1];
-    } else {
-      mask = (1u << B) - 1u;
-      N = a.Is;
-      Wg = a.sh_gate;
-      Wu = a.sh_up;
-      Sg = a.sh_scale[0];
-      Su = a.sh_scale[1];
-    }
-    if (row0 >= N) continue;  // block-uniform
-
-    f32x4 acc[4][2];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int SS = (C + 3) / 4;
-    // Two super-steps per pass, all their loads issued before any math, in
-    // the order the math consumes them (tokens, then row group by row group;
-    // raw buffer loads, a lane out of range reading zeros).
-    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xs, (int64_t)B * H * 2);
-    const __amdgpu_buffer_rsrc_t gr = buf_rsrc(Wg, nvfp4_matrix_bytes(N, H));
-    const __amdgpu_buffer_rsrc_t ur = buf_rsrc(Wu, nvfp4_matrix_bytes(N, H));
-    for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
-      uint4 qg[2][4], qu[2][4], xv[2][4];
-      uint32_t sg[2][4], su[2][4];
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int ss = ss0 + v * kMmWaves;
-        const int c = ss * 4 + p;
-        const bool cok = ss < SS && c < C;
-        const bool tok = cok && r16 < B;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) xv[v][s] = buf_load16(xr, buf_off(tok, (uint32_t)(r16 * H + c * 32 + s * 8) * 2u));
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = row0 + rg * 16 + r16;
-          const bool ok = cok && n < N;
-          const uint32_t qo = buf_off(ok, (uint32_t)(n * (H / 2) + c * 16));
-          const uint32_t so = buf_off(ok, (uint32_t)(N * (H / 2) + ((n >> 3) * (H / 32) + c) * 16 + (n & 7) * 2));
-          qg[v][rg] = buf_load16(gr, qo);
-          sg[v][rg] = buf_load2(gr, so);
-          qu[v][rg] = buf_load16(ur, qo);
-          su[v][rg] = buf_load2(ur, so);
-        }
-      }
-      // all loads of both super-steps issued before any math: the math of
-      // the first waits for its own loads only, while the second's arrive
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
-            const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
-            const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
-            acc[rg][0] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
-            acc[rg][1] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
-          }
-        }
-    }
-    // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
-    __syncthreads();  // the routing's logits, or the previous item's sums, are no longer read
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
-        s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
-      }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
-      const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-      float g = 0.f, u = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMmWaves; ++w) {
-        g += s_red[w][rg * 8 + i][l];
-        u += s_red[w][rg * 8 + 4 + i][l];
-      }
-      const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
-      if (t < B && n < N && ((mask >> t) & 1u)) {
-        const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
-        a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
-      }
-    }
+  // Items of 64 rows while they fit the grid; 32-row items when they would
+  // leave some blocks two 64-row items and others none (the routing, the
+  // same in every block, makes the choice the same everywhere).
+  const int groups = (Imax + 63) / 64, sh_groups = a.Is > 0 ? (a.Is + 63) / 64 : 0;
+  const int n_items = sh_groups + n_routed * groups;
+  if (n_items <= (int)gridDim.x) {
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) gateup_item<4>(a, R, s_red, xs, item, groups, sh_groups);
+  } else {
+    const int groups2 = (Imax + 31) / 32, sh_groups2 = a.Is > 0 ? (a.Is + 31) / 32 : 0;
+    const int n_items2 = sh_groups2 + n_routed * groups2;
+    for (int item = blockIdx.x; item < n_items2; item += gridDim.x)
+      gateup_item<2>(a, R, s_red, xs, item, groups2, sh_groups2);
   }
 }
 
