@@ -322,6 +322,7 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
   a.use_norm = w->norm_gain ? 1 : 0;
   a.P = a.T * a.k;
   a.max_tiles = (int)L.max_tiles;
+  a.tile_rows = prefill_tile_rows(n_tokens, desc->wtype);
   a.eps = desc->norm_eps;
   a.x = (const uint16_t *)x;
   a.y = (uint16_t *)y;

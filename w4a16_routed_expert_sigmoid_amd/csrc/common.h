@@ -314,6 +314,11 @@ struct DecodeArgs {
   int32_t *out_idx;
   float *out_w;
   DecodeWs ws;
+  // zero0[0, zero_n) and zero1[0, zero_n): words the router kernel zeroes
+  // for a later kernel of the same call (the small-tile prefill's expert
+  // counts and cursors); NULL otherwise
+  int32_t *zero0, *zero1;
+  int zero_n;
 };
 
 // Arguments of the prefill kernels (passed by value).  Row space of the
@@ -321,6 +326,7 @@ struct DecodeArgs {
 // by expert, rows [P, P + T) the shared expert's, in token order.
 struct PrefillArgs {
   int T, H, I, Is, E, k, wtype, residual, use_norm, P, max_tiles;
+  int tile_rows;  // rows per GEMM tile: kPrefillTileRows, or kPrefillSmallRows (small-tile kernels)
   float eps;
   const uint16_t *x;
   uint16_t *y;
@@ -358,6 +364,12 @@ hipError_t launch_gemv(const GemvArgs &g, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *stage_events);
+// The router of a batch of a.B tokens alone (one row of blocks per token):
+// the pre-norm into ws.xn when the layer has one, the logits into
+// ws.logits, and the zero0/zero1 words.  a.H <= kRouterTokenMaxHidden (a
+// block stages its token in LDS).
+constexpr int kRouterTokenMaxHidden = 16384;
+hipError_t launch_router_tokens(const DecodeArgs &a, hipStream_t stream);
 
 // The persistent one-token step: n_layers consecutive MoE layers of one
 // shape in one launch.  a: the shapes and workspace of the first layer, x

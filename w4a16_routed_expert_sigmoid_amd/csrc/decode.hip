@@ -39,6 +39,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "mm_rows.h"
 
 namespace moe {
 
@@ -385,7 +386,7 @@ constexpr int kRouteWaves = kMaxBatchBf16;  // BF16 batches: one wave per token 
 template <int W, int MT>
 __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready, int route) {
   constexpr int kRouterWaves = W, kRouterThreads = W * kWave;
-  constexpr int XCAP = MT == 1 ? 16384 / 8 : 32768 / 8;
+  constexpr int XCAP = MT == 1 ? kRouterTokenMaxHidden / 8 : 32768 / 8;
   static_assert(XCAP * 16 >= 32768, "the routing block keeps B * E <= 8192 logits in the stage");
   __shared__ uint4 s_x[XCAP];  // [B][H] BF16
   __shared__ double s_ss[kRouterWaves][MT];
@@ -393,6 +394,11 @@ __global__ __launch_bounds__(W *kWave) void k_router(DecodeArgs a, int xn_ready,
     route_block(a, s_x);
     return;
   }
+  if (a.zero0 && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += kRouterThreads) {
+      a.zero0[i] = 0;
+      a.zero1[i] = 0;
+    }
   if (MT == 1) {
     // the batch split over blockIdx.y, one token per block row: a block
     // takes its token's dot products only (a row's 16 pieces per lane
@@ -855,46 +861,7 @@ __global__ __launch_bounds__(kGateupWaves *kWave) void k_gateup(DecodeArgs a) {
 //   step s uses its elements s*8 .. +8, for A and B alike.
 // ---------------------------------------------------------------------------
 
-constexpr int kMmWaves = 8;
 constexpr int kMmRows = 64;  // gate/up weight rows per block (four 16-row groups)
-
-__device__ __forceinline__ uint32_t word_of(const uint4 &q, int s) {
-  return s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
-}
-
-// Buffer resource of a device range of `bytes` bytes (< 4 GiB) for the
-// raw buffer loads: an offset at or past the range's end reads zeros and
-// touches no memory, so a lane with nothing to load takes kBufNone instead
-// of a branch around its load.  (Loads under branches, divergent or
-// uniform, leave the compiler unable to count the ones in flight, and it
-// then waits for all of them before the first use of any.)  Word 3 is the
-// gfx9 data format for raw 32-bit access.
-constexpr uint32_t kBufNone = 0x80000000u;
-
-// An offset chosen by a lane condition, passed through an empty asm
-// statement: the compiler cannot see the choice and so does not split the
-// load into two loads under branches.
-__device__ __forceinline__ uint32_t buf_off(bool ok, uint32_t off) {
-  uint32_t v = ok ? off : kBufNone;
-  asm("" : "+v"(v));
-  return v;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
-}
 
 // Scale pair (blocks 2c, 2c+1) of row n of an N x K NVFP4 matrix.
 __device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int64_t K, int n, int c) {
@@ -902,16 +869,14 @@ __device__ __forceinline__ uint32_t scale_pair(const uint8_t *m, int64_t N, int6
 }
 
 // One gate/up work item: rows [row0, row0 + 16 RG) of one entry (a
-// selected expert, or the shared one) over the full K, split over the 8
-// waves and met in LDS.  RG: 16-row groups per item (4, or 2 when the
-// items of 64 rows outnumber the blocks).
+// selected expert, or the shared one) times the batch's tokens.  RG:
+// 16-row groups per item (4, or 2 when the items of 64 rows outnumber the
+// blocks).
 template <int RG>
 __device__ __forceinline__ void gateup_item(const DecodeArgs &a, const Routing &R, float (&s_red)[kMmWaves][32][kWave],
                                             const uint16_t *xs, int item, int groups, int sh_groups) {
-  const int H = a.H, B = a.B, C = H / 32;
+  const int H = a.H, B = a.B;
   const int Imax = a.I > a.Is ? a.I : a.Is;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int r16 = lane & 15, p = lane >> 4;
   const bool shared = item < sh_groups;
   const int slot = shared ? a.max_routed : (item - sh_groups) / groups;
   const int row0 = (shared ? item : (item - sh_groups) % groups) * (16 * RG);
@@ -937,85 +902,10 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs &a, const Routing &
     Su = a.sh_scale[1];
   }
   if (row0 >= N) return;  // block-uniform
-
-  f32x4 acc[RG][2];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) acc[rg][0] = acc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int SS = (C + 3) / 4;
-  // Two super-steps per pass, all their loads issued before any math, in
-  // the order the math consumes them (tokens, then row group by row group;
-  // raw buffer loads, a lane out of range reading zeros).
-  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xs, (int64_t)B * H * 2);
-  const __amdgpu_buffer_rsrc_t gr = buf_rsrc(Wg, nvfp4_matrix_bytes(N, H));
-  const __amdgpu_buffer_rsrc_t ur = buf_rsrc(Wu, nvfp4_matrix_bytes(N, H));
-  for (int ss0 = wave; ss0 < SS; ss0 += 2 * kMmWaves) {
-    uint4 qg[2][RG], qu[2][RG], xv[2][4];
-    uint32_t sg[2][RG], su[2][RG];
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int ss = ss0 + v * kMmWaves;
-      const int c = ss * 4 + p;
-      const bool cok = ss < SS && c < C;
-      const bool tok = cok && r16 < B;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xv[v][s] = buf_load16(xr, buf_off(tok, (uint32_t)(r16 * H + c * 32 + s * 8) * 2u));
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        const int n = row0 + rg * 16 + r16;
-        const bool ok = cok && n < N;
-        const uint32_t qo = buf_off(ok, (uint32_t)(n * (H / 2) + c * 16));
-        const uint32_t so = buf_off(ok, (uint32_t)(N * (H / 2) + ((n >> 3) * (H / 32) + c) * 16 + (n & 7) * 2));
-        qg[v][rg] = buf_load16(gr, qo);
-        sg[v][rg] = buf_load2(gr, so);
-        qu[v][rg] = buf_load16(ur, qo);
-        su[v][rg] = buf_load2(ur, so);
-      }
-    }
-    // all loads of both super-steps issued before any math: the math of
-    // the first waits for its own loads only, while the second's arrive
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 bx = __builtin_bit_cast(bf16x8, u32x4{xv[v][s].x, xv[v][s].y, xv[v][s].z, xv[v][s].w});
-          const float scg = e4m3_to_f32((sg[v][rg] >> (8 * (s >> 1))) & 0xffu);
-          const float scu = e4m3_to_f32((su[v][rg] >> (8 * (s >> 1))) & 0xffu);
-          acc[rg][0] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qg[v][rg], s), scg), bx, acc[rg][0], 0, 0, 0);
-          acc[rg][1] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8(word_of(qu[v][rg], s), scu), bx, acc[rg][1], 0, 0, 0);
-        }
-      }
-  }
-  // K-partial sums of the 8 waves, then h = BF16(SiLU(BF16(g Sg)) BF16(u Su)).
-  __syncthreads();  // the routing's logits, or the previous item's sums, are no longer read
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_red[wave][rg * 8 + i][lane] = acc[rg][0][i];
-      s_red[wave][rg * 8 + 4 + i][lane] = acc[rg][1][i];
-    }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < RG / 2; ++k) {
-    const int idx = tid + k * kMmWaves * kWave;  // (row group, value, lane)
-    const int rg = idx >> 8, i = (idx >> 6) & 3, l = idx & 63;
-    float g = 0.f, u = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMmWaves; ++w) {
-      g += s_red[w][rg * 8 + i][l];
-      u += s_red[w][rg * 8 + 4 + i][l];
-    }
-    const int t = l & 15, n = row0 + rg * 16 + (l >> 4) * 4 + i;
-    if (t < B && n < N && ((mask >> t) & 1u)) {
-      const float gg = round_bf16(g * Sg), uu = round_bf16(u * Su);
-      a.ws.h[((int64_t)slot * B + t) * Imax + n] = (uint16_t)f32_to_bf16(silu_mul(gg, uu));
-    }
-  }
+  const int col = threadIdx.x & 15;
+  uint16_t *h = a.ws.h + (int64_t)slot * B * Imax;
+  mm_rows<RG, true>(H, xs, B, H, col < B ? col : -1, Wg, Wu, Sg, Su, N, row0, mask, s_red,
+                    [&](int t, int n, uint32_t v) { h[(int64_t)t * Imax + n] = (uint16_t)v; });
 }
 
 // Gate/up of a batch.  With routed experts every block first derives the
@@ -2131,6 +2021,12 @@ hipError_t launch_sync_clear(uint32_t *region, int64_t words, hipStream_t stream
   const int blocks = (int)(blocks64 < 64 ? (blocks64 > 0 ? blocks64 : 1) : 64);
   hipLaunchKernelGGL(k_sync_clear, dim3(blocks), dim3(256), 0, stream, region, words);
   return hipGetLastError();
+}
+
+hipError_t launch_router_tokens(const DecodeArgs &a, hipStream_t stream) {
+  const int rows_per_block = kRouterWaves * (kWave / lanes_per_row(a.H));
+  return launch(k_router<kRouterWaves, 1>, dim3((a.E + rows_per_block - 1) / rows_per_block, a.B), dim3(kRouterThreads),
+                0, stream, nullptr, nullptr, a, 0, 0);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, hipEvent_t const *ev) {

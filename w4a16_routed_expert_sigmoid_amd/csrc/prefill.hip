@@ -22,7 +22,10 @@
 // Row space of the grouped GEMMs: rows [0, P) are the P = T*k (token,
 // expert) pairs sorted by expert; rows [P, P + T) are the shared expert's
 // (token order).  h and y are stored per row.
+#include <string.h>
+
 #include "common.h"
+#include "mm_rows.h"
 
 namespace moe {
 
@@ -265,13 +268,14 @@ __global__ __launch_bounds__(PThreads) void k_pf_place(PrefillArgs a) {
   __shared__ uint32_t s_cnt[kMaxExperts];
   __shared__ int s_base[kMaxExperts];
   const int tid = threadIdx.x;
+  const int TR = a.tile_rows;
   int c[kPlaceExp], rows = 0, tl = 0;
 #pragma unroll
   for (int j = 0; j < kPlaceExp; ++j) {
     const int e = tid * kPlaceExp + j;
     c[j] = e < a.E ? a.counts[e] : 0;
     rows += c[j];
-    tl += (c[j] + PBM - 1) / PBM;
+    tl += (c[j] + TR - 1) / TR;
   }
   s_rows[tid] = rows;
   s_tl[tid] = tl;
@@ -290,17 +294,17 @@ __global__ __launch_bounds__(PThreads) void k_pf_place(PrefillArgs a) {
     s_off[e] = off;
     if (blockIdx.x == 0 && e < a.E) {
       a.offsets[e] = off;
-      const int nt = (c[j] + PBM - 1) / PBM;
-      for (int i = 0; i < nt; ++i) a.tiles[toff + i] = PfTile{off + i * PBM, min(PBM, c[j] - i * PBM), e};
+      const int nt = (c[j] + TR - 1) / TR;
+      for (int i = 0; i < nt; ++i) a.tiles[toff + i] = PfTile{off + i * TR, min(TR, c[j] - i * TR), e};
     }
     off += c[j];
-    toff += (c[j] + PBM - 1) / PBM;
+    toff += (c[j] + TR - 1) / TR;
   }
   if (blockIdx.x == 0) {
     const int routed_tiles = s_tl[PThreads - 1];
-    const int shared_tiles = a.Is > 0 ? (a.T + PBM - 1) / PBM : 0;
+    const int shared_tiles = a.Is > 0 ? (a.T + TR - 1) / TR : 0;
     for (int i = tid; i < shared_tiles; i += PThreads)
-      a.tiles[routed_tiles + i] = PfTile{a.P + i * PBM, min(PBM, a.T - i * PBM), -1};
+      a.tiles[routed_tiles + i] = PfTile{a.P + i * TR, min(TR, a.T - i * TR), -1};
     if (tid == 0) {
       a.offsets[a.E] = s_rows[PThreads - 1];
       *a.n_tiles = routed_tiles + shared_tiles;
@@ -782,6 +786,66 @@ __global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nbl
   }
 }
 
+constexpr int64_t kPfSmallBlocks = 512;  // two rounds of one block per compute unit
+
+// ---------------------------------------------------------------------------
+// Small-tile prefill (NVFP4, up to kPrefillSmallMaxTokens tokens): tiles of
+// at most 16 rows, so that an expert's few rows do not fill a 128-row tile
+// with padding and one block does not stream a quarter of an expert's
+// weights alone.  Each (tile, row group) item runs on one block as in the
+// small-batch decode kernels: the tile's rows are the 16 token columns of
+// v_mfma_f32_16x16x32_bf16 tiles, K is split over the 8 waves.
+// ---------------------------------------------------------------------------
+
+// Gate/up: item (tile, 64 h columns); h rows as the large-tile kernel
+// writes them.
+__global__ __launch_bounds__(kMmWaves *kWave) void k_pf_small_gateup(PrefillArgs a) {
+  __shared__ float s_red[kMmWaves][32][kWave];
+  const int n_tiles = *a.n_tiles;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int groups = (Imax + 63) / 64;
+  const int64_t mb = nvfp4_matrix_bytes(a.I, a.H);
+  const uint16_t *xs = a.use_norm ? a.xn : a.x;
+  const int col = threadIdx.x & 15;
+  for (int item = blockIdx.x; item < n_tiles * groups; item += gridDim.x) {
+    const PfTile tile = a.tiles[item / groups];
+    const int row0 = (item % groups) * 64;
+    const bool shared = tile.e < 0;
+    const int N = shared ? a.Is : a.I;
+    if (row0 >= N) continue;  // block-uniform
+    const uint8_t *Wg = shared ? a.sh_gate : a.w_gate + tile.e * mb;
+    const uint8_t *Wu = shared ? a.sh_up : a.w_up + tile.e * mb;
+    const float Sg = shared ? a.sh_scale[0] : a.w_scale[3 * tile.e + 0];
+    const float Su = shared ? a.sh_scale[1] : a.w_scale[3 * tile.e + 1];
+    int xrow = -1;  // this lane's token row
+    if (col < tile.cnt) xrow = shared ? tile.p0 + col - a.P : a.sorted_tok[tile.p0 + col];
+    mm_rows<4, true>(a.H, xs, a.T, a.H, xrow, Wg, Wu, Sg, Su, N, row0, (1u << tile.cnt) - 1u, s_red,
+                     [&](int t, int n, uint32_t v) { a.h_rows[(int64_t)(tile.p0 + t) * Imax + n] = (uint16_t)v; });
+  }
+}
+
+// Down: item (tile, 128 output columns); y rows as the large-tile kernel
+// writes them, for the combine.
+__global__ __launch_bounds__(kMmWaves *kWave) void k_pf_small_down(PrefillArgs a) {
+  __shared__ float s_red[kMmWaves][32][kWave];
+  const int n_tiles = *a.n_tiles;
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int groups = (a.H + 127) / 128;
+  const int64_t mb = nvfp4_matrix_bytes(a.H, a.I);
+  const int col = threadIdx.x & 15;
+  for (int item = blockIdx.x; item < n_tiles * groups; item += gridDim.x) {
+    const PfTile tile = a.tiles[item / groups];
+    const int row0 = (item % groups) * 128;
+    const bool shared = tile.e < 0;
+    const int K = shared ? a.Is : a.I;
+    const uint8_t *Wd = shared ? a.sh_down : a.w_down + tile.e * mb;
+    const float Sd = shared ? a.sh_scale[2] : a.w_scale[3 * tile.e + 2];
+    const int hrow = col < tile.cnt ? tile.p0 + col : -1;
+    mm_rows<8, false>(K, a.h_rows, a.P + a.T, Imax, hrow, Wd, Wd, Sd, Sd, a.H, row0, (1u << tile.cnt) - 1u, s_red,
+                      [&](int t, int n, uint32_t v) { a.y_rows[(int64_t)(tile.p0 + t) * a.H + n] = (uint16_t)v; });
+  }
+}
+
 // out[t] = BF16(sum_j w_j y_row(t, j) + y_shared(t)) (+ residual); 8 columns
 // per thread, one block per token.
 __global__ __launch_bounds__(PThreads) void k_pf_combine(PrefillArgs a) {
@@ -834,13 +898,40 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
   hipError_t e;
 #define MOE_CK_LAUNCH() \
   if ((e = hipGetLastError()) != hipSuccess) return e
-  if (a.use_norm) {
+  // Small-tile calls with routed experts run the decode path's router (one
+  // row of blocks per token, the pre-norm in each block): its 64 blocks per
+  // token spread the router weights over the GPU, where the GEMM router's
+  // 64 x 64 tiles would put them on E/64 blocks.
+  const bool token_router = BT == 1 && a.tile_rows == kPrefillSmallRows && a.E > 0 && a.H <= kRouterTokenMaxHidden;
+  if (a.use_norm && !token_router) {
     hipLaunchKernelGGL(k_pf_norm, dim3((a.T + 3) / 4), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
   }
   if (a.E > 0) {
-    hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN), dim3(PThreads), 0, s, a);
-    MOE_CK_LAUNCH();
+    if (token_router) {
+      DecodeArgs d;
+      memset(&d, 0, sizeof(d));
+      d.H = a.H;
+      d.E = a.E;
+      d.B = a.T;
+      d.use_norm = a.use_norm;
+      d.eps = a.eps;
+      d.x = a.x;
+      d.router_w = a.router_w;
+      d.router_b = a.router_b;
+      d.norm_gain = a.norm_gain;
+      d.ws.xn = a.xn;
+      d.ws.logits = a.logits;
+      // the expert counts the top-k kernel accumulates, and the cursors the
+      // placement kernel advances, start at zero
+      d.zero0 = a.counts;
+      d.zero1 = a.cursors;
+      d.zero_n = a.E + 1;
+      if ((e = launch_router_tokens(d, s)) != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN), dim3(PThreads), 0, s, a);
+      MOE_CK_LAUNCH();
+    }
     const int waves = (a.T + kPfTokensPerWave - 1) / kPfTokensPerWave;
     const dim3 tg((waves + kPfTopkWaves - 1) / kPfTopkWaves), tb(kPfTopkWaves * kWave);
     if (a.E <= 4 * kWave) hipLaunchKernelGGL(k_pf_topk<4>, tg, tb, 0, s, a);
@@ -857,7 +948,16 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
     MOE_CK_LAUNCH();
   }
   const int nmax = a.I > a.Is ? a.I : a.Is;
-  if (BT == 1) {
+  if (BT == 1 && a.tile_rows == kPrefillSmallRows) {
+    // blocks: every item of the largest tile count, at most kPfSmallBlocks
+    const int64_t gu = (int64_t)a.max_tiles * ((nmax + 63) / 64), dn = (int64_t)a.max_tiles * ((a.H + 127) / 128);
+    hipLaunchKernelGGL(k_pf_small_gateup, dim3((unsigned)(gu < kPfSmallBlocks ? gu : kPfSmallBlocks)),
+                       dim3(kMmWaves * kWave), 0, s, a);
+    MOE_CK_LAUNCH();
+    hipLaunchKernelGGL(k_pf_small_down, dim3((unsigned)(dn < kPfSmallBlocks ? dn : kPfSmallBlocks)),
+                       dim3(kMmWaves * kWave), 0, s, a);
+    MOE_CK_LAUNCH();
+  } else if (BT == 1) {
     // grid: every (tile, n-block) item, rounded up to whole XCD chunks
     const int nb_gu = (nmax + GBN / 2 - 1) / (GBN / 2), nb_dn = (a.H + GBN - 1) / GBN;
     const int64_t round = 8 * GChunk;

@@ -20,6 +20,8 @@ constexpr int kMaxTopK = 8;
 constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
 constexpr int kMaxExperts = 1024;
 constexpr int kPrefillTileRows = 128;       // rows of one prefill GEMM tile
+constexpr int kPrefillSmallRows = 16;       // rows of a small-tile prefill tile (up to kPrefillSmallMaxTokens tokens)
+constexpr int kPrefillSmallMaxTokens = 64;
 constexpr int32_t kMaxPrefillTokens = 1 << 22;
 constexpr size_t kWsAlign = 256;            // workspace pieces start on 256-byte lines
 
@@ -59,17 +61,23 @@ constexpr bool k_tileable(int64_t k) {
   return k >= 64 && k % 32 == 0 && (k / 32 >= kWave || ((k / 32) & (k / 32 - 1)) == 0);
 }
 
-// Prefill: one GEMM tile of up to 128 rows of one expert's segment.
+// Prefill: one GEMM tile of up to 128 (or 16) rows of one expert's segment.
 struct PfTile {
-  int p0, cnt, e;  // first row, rows (<= 128), expert (-1: the shared expert)
+  int p0, cnt, e;  // first row, rows (<= the tile height), expert (-1: the shared expert)
 };
 
-// Upper bound of the 128-row tiles of a prefill call: the routed rows in
-// whole tiles plus one ragged tile per non-empty expert, and the shared
-// expert's rows.
-constexpr int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared) {
-  return (E > 0 ? (T * k + kPrefillTileRows - 1) / kPrefillTileRows + (E < T * k ? E : T * k) : 0) +
-         (shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
+// Upper bound of the tiles of `rows` rows of a prefill call: the routed
+// rows in whole tiles plus one ragged tile per non-empty expert, and the
+// shared expert's rows.
+constexpr int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared, int64_t rows = kPrefillTileRows) {
+  return (E > 0 ? (T * k + rows - 1) / rows + (E < T * k ? E : T * k) : 0) + (shared ? (T + rows - 1) / rows : 0);
+}
+
+// Rows per prefill tile: NVFP4 calls of up to kPrefillSmallMaxTokens tokens
+// take 16-row tiles (each expert's few rows as the 16 token columns of the
+// decode kernels' matrix-core tiles); the rest 128-row tiles.
+constexpr int prefill_tile_rows(int64_t T, int wtype) {
+  return (wtype == 1 && T <= kPrefillSmallMaxTokens) ? kPrefillSmallRows : kPrefillTileRows;
 }
 
 }  // namespace moe

@@ -158,7 +158,7 @@ PfLayout prefill_layout(const moe_layer_desc &d, int64_t T) {
   const int64_t E = d.n_experts > 0 ? d.n_experts : 0, H = d.hidden, k = E > 0 ? d.top_k : 0;
   const int64_t Imax = d.inter > d.shared_inter ? d.inter : d.shared_inter;
   const int64_t P = T * k, rows = P + (d.shared_inter > 0 ? T : 0);
-  L.max_tiles = prefill_max_tiles(T, k, E, d.shared_inter > 0);
+  L.max_tiles = prefill_max_tiles(T, k, E, d.shared_inter > 0, prefill_tile_rows(T, d.wtype));
   size_t o = 0;
   L.xn = o; o += up(T * H * 2);
   L.logits = o; o += up(T * E * 4);
