@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0                                # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0                       # MI355X dense BF16, published
 COUNTERS = os.path.join(ROOT, "profiles", "decode_hbm_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_routed_expert_sigmoid_amd", "csrc", f)
-                  for f in ("decode.hip", "common.h", "shapes.h")]
+                  for f in ("decode.hip", "mm_rows.h", "common.h", "shapes.h")]
 
 
 def selected_bytes(distinct, expert_bytes=EXPERT_BYTES, scales=12):
