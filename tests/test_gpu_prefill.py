@@ -169,6 +169,50 @@ def test_prefill_placement_second_pass():
     compare(L, x[s], out[s], idx[s], w[s], what=f"prefill second pass T={T}")
 
 
+# Calls of up to 64 NVFP4 tokens run 16-row tiles (the small-tile kernels)
+# and, with routed experts and H <= 16384, the per-token router that also
+# clears the expert counts and cursors.
+SMALL_TILE_CASES = {
+    # 64 identical tokens: each of the 4 selected experts and the shared one
+    # gets four full 16-row tiles
+    "identical": (dict(SMALL), 64, "same"),
+    # the last 64-column gate/up item holds 32 columns, the last 128-column
+    # down item 64, and neither depth is a multiple of 128
+    "ragged": (dict(hidden=2112, inter=2080, shared_inter=2080, n_experts=8, top_k=2, bias="zipf"), 40, None),
+    "k_equals_E": (dict(hidden=128, inter=64, shared_inter=64, n_experts=8, top_k=8), 60, None),
+    "top1_no_shared": (dict(hidden=128, inter=64, shared_inter=0, n_experts=16, top_k=1), 33, None),
+    # 1000 experts: 250 router blocks per token, 1001 count and cursor words
+    # cleared by the router's first block
+    "many_experts": (dict(hidden=256, inter=64, shared_inter=64, n_experts=1000, top_k=8, bias="zipf"), 50, None),
+    # no router: the pre-norm runs on its own, the shared expert in 16-row tiles
+    "dense": (dict(hidden=256, inter=0, shared_inter=512, n_experts=0, norm=True), 20, None),
+    # H = 16416 > 16384: the token does not fit the per-token router's LDS
+    # stage, so the norm and the GEMM router run instead
+    "wide_hidden": (dict(hidden=16416, inter=64, shared_inter=64, n_experts=4, top_k=2, norm=True, bias="zipf"), 3,
+                    None),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL_TILE_CASES))
+def test_prefill_small_tile_cases(case):
+    kw, T, mode = SMALL_TILE_CASES[case]
+    log(f"test: prefill small tiles {case} T={T}")
+    L = synth.make_layer(41, wtype="nvfp4", **kw)
+    H = kw["hidden"]
+    if mode == "same":
+        x = np.repeat(synth.tokens(1, H, stream=41), T, axis=0)
+    else:
+        x = synth.tokens(T, H, stream=41)
+    out, idx, w = run(L, x)
+    E = L["n_experts"]
+    if E:
+        check_routing_properties(L, idx, w)
+    if mode == "same":
+        assert len({tuple(sorted(r)) for r in idx.tolist()}) == 1
+        assert np.all(out == out[0:1])
+    compare(L, x, out, idx if E else None, w if E else None, what=f"small tiles {case}")
+
+
 def test_prefill_rejects_and_sizes():
     L = synth.make_layer(40, **SMALL)
     dev = moe.DeviceLayer(L)
