@@ -323,6 +323,7 @@ moe_status moe_prefill_layer(const moe_layer_desc *desc, const moe_layer_weights
   a.P = a.T * a.k;
   a.max_tiles = (int)L.max_tiles;
   a.tile_rows = prefill_tile_rows(n_tokens, desc->wtype);
+  a.rsplit = prefill_router_split(n_tokens, desc->n_experts > 0 ? desc->n_experts : 0, desc->hidden);
   a.eps = desc->norm_eps;
   a.x = (const uint16_t *)x;
   a.y = (uint16_t *)y;

@@ -327,6 +327,7 @@ struct DecodeArgs {
 struct PrefillArgs {
   int T, H, I, Is, E, k, wtype, residual, use_norm, P, max_tiles;
   int tile_rows;  // rows per GEMM tile: kPrefillTileRows, or kPrefillSmallRows (small-tile kernels)
+  int rsplit;     // K splits of the router GEMM: logits holds rsplit partial [T][E] arrays
   float eps;
   const uint16_t *x;
   uint16_t *y;

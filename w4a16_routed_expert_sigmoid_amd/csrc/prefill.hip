@@ -188,22 +188,63 @@ constexpr int kPfTopkWaves = 16;
 // round every lane notes the first slot of its own max and its keys and max
 // without that slot, beside the wave max; one ballot then names the lowest
 // lane holding the max, which drops its slot (ties to the lower index).
-template <int J>
-__global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a) {
+template <int J, int W>
+__global__ __launch_bounds__(W *kWave) void k_pf_topk(PrefillArgs a) {
   __shared__ uint32_t s_hist[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < a.E; e += kPfTopkWaves * kWave) s_hist[e] = 0u;
+  for (int e = threadIdx.x; e < a.E; e += W * kWave) s_hist[e] = 0u;
   __syncthreads();
-  const int t0 = (blockIdx.x * kPfTopkWaves + wave) * kPfTokensPerWave;
+  const int t0 = (blockIdx.x * W + wave) * kPfTokensPerWave;
+  const __amdgpu_buffer_rsrc_t lr = buf_rsrc(a.logits, a.rsplit > 1 ? (int64_t)a.rsplit * a.T * a.E * 4 : 0);
   for (int tt = 0; tt < kPfTokensPerWave; ++tt) {
     const int t = t0 + tt;
     if (t >= a.T) break;
-    const float *lt = a.logits + (int64_t)t * a.E;
     uint32_t key[J];
+    if (a.rsplit == 1) {
+      const float *lt = a.logits + (int64_t)t * a.E;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane * J + j;
-      key[j] = (e < a.E) ? pf_key(lt[e]) : 0u;
+      for (int j = 0; j < J; ++j) {
+        const int e = lane * J + j;
+        key[j] = (e < a.E) ? pf_key(lt[e]) : 0u;
+      }
+    } else {
+      // the router's K splits (a split call has under 128 router tiles,
+      // T E < 2^19, so its partial logits span under 16 MiB), summed in
+      // split order; the partials
+      // of four logits are loaded at once (splits past a.rsplit read zeros,
+      // and adding +0 changes no sum that pf_key sees)
+      const uint32_t lbase = (uint32_t)(t * a.E) * 4u, zstride = (uint32_t)(a.T * a.E) * 4u;
+#pragma unroll
+      for (int j0 = 0; j0 < J; j0 += 4) {
+        float part[4][kRouterMaxSplit];
+        const int e0 = lane * J + j0;
+        if ((a.E & 3) == 0) {
+          // E % 4 == 0: the four logits are one 16-byte piece of each split
+#pragma unroll
+          for (int z = 0; z < kRouterMaxSplit; ++z) {
+            const uint4 v = buf_load16(lr, buf_off(e0 < a.E && z < a.rsplit, lbase + z * zstride + (uint32_t)e0 * 4u));
+            part[0][z] = __uint_as_float(v.x);
+            part[1][z] = __uint_as_float(v.y);
+            part[2][z] = __uint_as_float(v.z);
+            part[3][z] = __uint_as_float(v.w);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int z = 0; z < kRouterMaxSplit; ++z)
+              part[j][z] =
+                  buf_load4f(lr, buf_off(e0 + j < a.E && z < a.rsplit, lbase + z * zstride + (uint32_t)(e0 + j) * 4u));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = lane * J + j0 + j;
+          float l = part[j][0];
+#pragma unroll
+          for (int z = 1; z < kRouterMaxSplit; ++z) l += part[j][z];
+          key[j0 + j] = (e < a.E) ? pf_key(l) : 0u;
+        }
+      }
     }
     uint32_t lmax = key[0];
 #pragma unroll
@@ -248,7 +289,7 @@ __global__ __launch_bounds__(kPfTopkWaves * kWave) void k_pf_topk(PrefillArgs a)
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += kPfTopkWaves * kWave)
+  for (int e = threadIdx.x; e < a.E; e += W * kWave)
     if (s_hist[e]) atomicAdd(&a.counts[e], (int)s_hist[e]);
 }
 
@@ -362,7 +403,7 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the expert counts the top-k kernel accumulates, and the cursors the
   // placement kernel advances, start at zero
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
     for (int i = tid; i < a.E + 1; i += PThreads) {
       a.counts[i] = 0;
       a.cursors[i] = 0;
@@ -387,7 +428,10 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   };
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc = {};
-  const int S = (a.H + RBK - 1) / RBK;  // H % 32 == 0; a ragged last stage reads zeros past H
+  // this block's stages [s0, s1) of the a.rsplit splits of the depth
+  // (H % 32 == 0; a ragged last stage reads zeros past H)
+  const int S_all = (a.H + RBK - 1) / RBK, per = (S_all + a.rsplit - 1) / a.rsplit;
+  const int s0 = blockIdx.z * per, S = min(S_all, s0 + per) - s0;
   auto load_k = [&](int k0) {
     // H % 32 == 0 and RPART is 16 or 32: a thread's part is wholly in or out
     if (k0 + part * RPART < a.H) {
@@ -397,10 +441,10 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
       for (int i = 0; i < RV; ++i) av[i] = bv[i] = make_uint4(0, 0, 0, 0);
     }
   };
-  load_k(0);
+  load_k(s0 * RBK);
   store(0);
   for (int st = 0; st < S; ++st) {
-    if (st + 1 < S) load_k((st + 1) * RBK);
+    if (st + 1 < S) load_k((s0 + st + 1) * RBK);
     __syncthreads();
     const uint16_t *A = &sA[st & 1][(wm * 32 + (lane & 31)) * RLD + (lane >> 5) * 8];
     const uint16_t *Bm = &sB[st & 1][(wn * 32 + (lane & 31)) * RLD + (lane >> 5) * 8];
@@ -412,11 +456,13 @@ __global__ __launch_bounds__(PThreads) void k_pf_router(PrefillArgs a) {
   }
   const int n = n0 + wn * 32 + (lane & 31);
   if (n >= a.E) return;
-  const float bias = a.router_b ? a.router_b[n] : 0.f;
+  // split z writes partial array z; the first carries the bias
+  const float bias = (a.router_b && blockIdx.z == 0) ? a.router_b[n] : 0.f;
+  float *out = a.logits + (int64_t)blockIdx.z * a.T * a.E;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int m = m0 + wm * 32 + (i / 4) * 8 + (lane >> 5) * 4 + (i % 4);
-    if (m < a.T) a.logits[(int64_t)m * a.E + n] = acc[i] + bias;
+    if (m < a.T) out[(int64_t)m * a.E + n] = acc[i] + bias;
   }
 }
 
@@ -894,15 +940,19 @@ __global__ __launch_bounds__(PThreads) void k_pf_combine(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int BT>
-static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
+static hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t s) {
   hipError_t e;
 #define MOE_CK_LAUNCH() \
   if ((e = hipGetLastError()) != hipSuccess) return e
   // Small-tile calls with routed experts run the decode path's router (one
   // row of blocks per token, the pre-norm in each block): its 64 blocks per
   // token spread the router weights over the GPU, where the GEMM router's
-  // 64 x 64 tiles would put them on E/64 blocks.
-  const bool token_router = BT == 1 && a.tile_rows == kPrefillSmallRows && a.E > 0 && a.H <= kRouterTokenMaxHidden;
+  // 64 x 64 tiles would put them on E/64 blocks.  It writes one [T][E]
+  // array of logits.
+  const bool token_router =
+      BT == 1 && args.tile_rows == kPrefillSmallRows && args.E > 0 && args.H <= kRouterTokenMaxHidden;
+  PrefillArgs a = args;
+  if (token_router) a.rsplit = 1;
   if (a.use_norm && !token_router) {
     hipLaunchKernelGGL(k_pf_norm, dim3((a.T + 3) / 4), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
@@ -929,13 +979,22 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t s) {
       d.zero_n = a.E + 1;
       if ((e = launch_router_tokens(d, s)) != hipSuccess) return e;
     } else {
-      hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN), dim3(PThreads), 0, s, a);
+      hipLaunchKernelGGL(k_pf_router, dim3((a.T + RBM - 1) / RBM, (a.E + RBN - 1) / RBN, a.rsplit), dim3(PThreads), 0, s,
+                         a);
       MOE_CK_LAUNCH();
     }
     const int waves = (a.T + kPfTokensPerWave - 1) / kPfTokensPerWave;
-    const dim3 tg((waves + kPfTopkWaves - 1) / kPfTopkWaves), tb(kPfTopkWaves * kWave);
-    if (a.E <= 4 * kWave) hipLaunchKernelGGL(k_pf_topk<4>, tg, tb, 0, s, a);
-    else hipLaunchKernelGGL(k_pf_topk<kMaxExperts / kWave>, tg, tb, 0, s, a);
+    // calls of up to 2048 tokens: blocks of 4 waves spread them over more
+    // compute units
+    if (a.T <= 2048) {
+      const dim3 tg((waves + 3) / 4), tb(4 * kWave);
+      if (a.E <= 4 * kWave) hipLaunchKernelGGL((k_pf_topk<4, 4>), tg, tb, 0, s, a);
+      else hipLaunchKernelGGL((k_pf_topk<kMaxExperts / kWave, 4>), tg, tb, 0, s, a);
+    } else {
+      const dim3 tg((waves + kPfTopkWaves - 1) / kPfTopkWaves), tb(kPfTopkWaves * kWave);
+      if (a.E <= 4 * kWave) hipLaunchKernelGGL((k_pf_topk<4, kPfTopkWaves>), tg, tb, 0, s, a);
+      else hipLaunchKernelGGL((k_pf_topk<kMaxExperts / kWave, kPfTopkWaves>), tg, tb, 0, s, a);
+    }
     MOE_CK_LAUNCH();
   }
   {

@@ -80,4 +80,32 @@ constexpr int prefill_tile_rows(int64_t T, int wtype) {
   return (wtype == 1 && T <= kPrefillSmallMaxTokens) ? kPrefillSmallRows : kPrefillTileRows;
 }
 
+// K splits of the prefill router GEMM (64 x 64 tiles, 128-K stages): calls
+// with fewer than kRouterMinBlocks tiles split the depth (at most
+// kRouterMaxSplit ways) so that about that many blocks run, each split
+// writing its own partial logits (the top-k sums them in split order).
+// Every split holds at least one stage.
+constexpr int kRouterMinBlocks = 128;
+constexpr int kRouterMaxSplit = 8;
+constexpr int prefill_router_split(int64_t T, int64_t E, int64_t H) {
+  const int64_t base = ((T + 63) / 64) * ((E + 63) / 64);
+  const int64_t stages = (H + 127) / 128;
+  if (E <= 0 || base >= kRouterMinBlocks) return 1;
+  int64_t split = (kRouterMinBlocks + base - 1) / base;
+  if (split > kRouterMaxSplit) split = kRouterMaxSplit;
+  if (split > stages) split = stages;
+  const int64_t per = (stages + split - 1) / split;
+  return (int)((stages + per - 1) / per);
+}
+
+// Rows of [E] logits the prefill workspace reserves: at least
+// prefill_router_split(T, E, H) * T, and non-decreasing in T (a workspace
+// sized for T tokens serves every smaller call).
+constexpr int64_t prefill_router_logit_rows(int64_t T, int64_t E, int64_t H) {
+  const int64_t stages = (H + 127) / 128;
+  const int64_t cap = T + 64 * kRouterMinBlocks / (E > 0 ? (E + 63) / 64 : 1) + 64;
+  const int64_t most = T * (stages < kRouterMaxSplit ? stages : kRouterMaxSplit);
+  return most < cap ? most : cap;
+}
+
 }  // namespace moe

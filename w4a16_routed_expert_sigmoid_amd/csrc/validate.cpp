@@ -161,7 +161,7 @@ PfLayout prefill_layout(const moe_layer_desc &d, int64_t T) {
   L.max_tiles = prefill_max_tiles(T, k, E, d.shared_inter > 0, prefill_tile_rows(T, d.wtype));
   size_t o = 0;
   L.xn = o; o += up(T * H * 2);
-  L.logits = o; o += up(T * E * 4);
+  L.logits = o; o += up((size_t)prefill_router_logit_rows(T, E, H) * E * 4);
   L.topk_idx = o; o += up(P * 4);
   L.topk_w = o; o += up(P * 4);
   L.counts = o; o += up((E + 1) * 4);
