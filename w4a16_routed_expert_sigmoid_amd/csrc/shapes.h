@@ -75,9 +75,16 @@ constexpr int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared
 
 // Rows per prefill tile: NVFP4 calls of up to kPrefillSmallMaxTokens tokens
 // take 16-row tiles (each expert's few rows as the 16 token columns of the
-// decode kernels' matrix-core tiles); the rest 128-row tiles.
+// decode kernels' matrix-core tiles); NVFP4 calls of up to
+// kPrefillMidMaxTokens tokens kPrefillMidRows-row tiles on the grouped GEMM
+// (an expert with many rows spreads over several blocks instead of one long
+// item); the rest 128-row tiles.
+constexpr int kPrefillMidRows = 32;
+constexpr int kPrefillMidMaxTokens = 512;
 constexpr int prefill_tile_rows(int64_t T, int wtype) {
-  return (wtype == 1 && T <= kPrefillSmallMaxTokens) ? kPrefillSmallRows : kPrefillTileRows;
+  return (wtype == 1 && T <= kPrefillSmallMaxTokens)  ? kPrefillSmallRows
+         : (wtype == 1 && T <= kPrefillMidMaxTokens) ? kPrefillMidRows
+                                                     : kPrefillTileRows;
 }
 
 // K splits of the prefill router GEMM (64 x 64 tiles, 128-K stages): calls
