@@ -169,21 +169,21 @@ def test_prefill_placement_second_pass():
     compare(L, x[s], out[s], idx[s], w[s], what=f"prefill second pass T={T}")
 
 
-# Calls of up to 64 NVFP4 tokens run 16-row tiles (the small-tile kernels)
+# Calls of up to 48 NVFP4 tokens run 16-row tiles (the small-tile kernels)
 # and, with routed experts and H <= 16384, the per-token router that also
 # clears the expert counts and cursors.
 SMALL_TILE_CASES = {
-    # 64 identical tokens: each of the 4 selected experts and the shared one
-    # gets four full 16-row tiles
-    "identical": (dict(SMALL), 64, "same"),
+    # 48 identical tokens: each of the 4 selected experts and the shared one
+    # gets three full 16-row tiles
+    "identical": (dict(SMALL), 48, "same"),
     # the last 64-column gate/up item holds 32 columns, the last 128-column
     # down item 64, and neither depth is a multiple of 128
     "ragged": (dict(hidden=2112, inter=2080, shared_inter=2080, n_experts=8, top_k=2, bias="zipf"), 40, None),
-    "k_equals_E": (dict(hidden=128, inter=64, shared_inter=64, n_experts=8, top_k=8), 60, None),
+    "k_equals_E": (dict(hidden=128, inter=64, shared_inter=64, n_experts=8, top_k=8), 45, None),
     "top1_no_shared": (dict(hidden=128, inter=64, shared_inter=0, n_experts=16, top_k=1), 33, None),
     # 1000 experts: 250 router blocks per token, 1001 count and cursor words
     # cleared by the router's first block
-    "many_experts": (dict(hidden=256, inter=64, shared_inter=64, n_experts=1000, top_k=8, bias="zipf"), 50, None),
+    "many_experts": (dict(hidden=256, inter=64, shared_inter=64, n_experts=1000, top_k=8, bias="zipf"), 44, None),
     # no router: the pre-norm runs on its own, the shared expert in 16-row tiles
     "dense": (dict(hidden=256, inter=0, shared_inter=512, n_experts=0, norm=True), 20, None),
     # H = 16416 > 16384: the token does not fit the per-token router's LDS

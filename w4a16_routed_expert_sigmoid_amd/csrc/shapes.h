@@ -21,7 +21,7 @@ constexpr int kXcdSlots = 16;  // XCC_ID is a 4-bit field
 constexpr int kMaxExperts = 1024;
 constexpr int kPrefillTileRows = 128;       // rows of one prefill GEMM tile
 constexpr int kPrefillSmallRows = 16;       // rows of a small-tile prefill tile (up to kPrefillSmallMaxTokens tokens)
-constexpr int kPrefillSmallMaxTokens = 64;
+constexpr int kPrefillSmallMaxTokens = 48;
 constexpr int32_t kMaxPrefillTokens = 1 << 22;
 constexpr size_t kWsAlign = 256;            // workspace pieces start on 256-byte lines
 
