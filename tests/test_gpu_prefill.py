@@ -213,6 +213,29 @@ def test_prefill_small_tile_cases(case):
     compare(L, x, out, idx if E else None, w if E else None, what=f"small tiles {case}")
 
 
+# Calls with fewer than 128 router tiles (64 tokens x 64 experts) split the
+# router GEMM's depth (up to 8 ways); the top-k sums the partial logits.
+# E % 4 != 0 takes the top-k's one-logit loads, E % 4 == 0 its 16-byte
+# loads; 2048 deep gives the full 8 splits, 256 deep 2.
+SPLIT_ROUTER_CASES = {
+    "odd_E_2way": (dict(hidden=256, inter=64, shared_inter=64, n_experts=6, top_k=2, bias="zipf"), 100),
+    "odd_E_8way": (dict(hidden=2048, inter=64, shared_inter=64, n_experts=6, top_k=2, bias="zipf"), 70),
+    "E_multiple_of_4_8way": (dict(hidden=2048, inter=64, shared_inter=0, n_experts=20, top_k=3, norm=True), 130),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_ROUTER_CASES))
+@pytest.mark.parametrize("wtype", ["nvfp4", "bf16"])
+def test_prefill_split_router(case, wtype):
+    kw, T = SPLIT_ROUTER_CASES[case]
+    log(f"test: prefill split router {case} {wtype} T={T}")
+    L = synth.make_layer(42, wtype=wtype, **kw)
+    x = synth.tokens(T, kw["hidden"], stream=42)
+    out, idx, w = run(L, x)
+    check_routing_properties(L, idx, w)
+    compare(L, x, out, idx, w, what=f"split router {case} {wtype}")
+
+
 def test_prefill_rejects_and_sizes():
     L = synth.make_layer(40, **SMALL)
     dev = moe.DeviceLayer(L)

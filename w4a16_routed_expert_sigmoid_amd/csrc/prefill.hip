@@ -896,13 +896,31 @@ __global__ __launch_bounds__(kMmWaves *kWave) void k_pf_small_down(PrefillArgs a
 // per thread, one block per token.
 __global__ __launch_bounds__(PThreads) void k_pf_combine(PrefillArgs a) {
   const int t = blockIdx.x;
+  // the token's pair rows and weights first, then every row's piece in
+  // flight together (selections past k read the first row and add nothing)
+  // (a layer without routed experts has no pairs: row 0 stands in)
+  int prow[kMaxTopK];
+  float pw[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) prow[j] = 0, pw[j] = 0.f;
+  if (a.k > 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int jj = j < a.k ? j : 0;
+      prow[j] = a.pair_pos[(int64_t)t * a.k + jj];
+      pw[j] = a.out_w[(int64_t)t * a.k + jj];
+    }
+  }
   for (int c = threadIdx.x * 8; c < a.H; c += PThreads * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < a.k; ++j) {
-      const int p = a.pair_pos[(int64_t)t * a.k + j];
-      const float w = a.out_w[(int64_t)t * a.k + j];
-      const uint4 v = *reinterpret_cast<const uint4 *>(a.y_rows + (int64_t)p * a.H + c);
-      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    uint4 yv[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) yv[j] = *reinterpret_cast<const uint4 *>(a.y_rows + (int64_t)prow[j] * a.H + c);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= a.k) break;
+      const float w = pw[j];
+      const uint32_t q[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = fmaf(w, bf16_to_f32(q[i] & 0xffffu), acc[2 * i]);
