@@ -147,6 +147,39 @@ __global__ __launch_bounds__(PThreads) void k_pf_norm(PrefillArgs a) {
   if (t >= a.T) return;
   const uint16_t *xr = a.x + (int64_t)t * a.H;
   double ss = 0.0;  // squares of BF16 values are exact in FP64
+  if (a.H <= 64 * 8 * 8) {
+    // up to 8 pieces per lane: the token and the gain loaded once, all in
+    // flight together, the token kept in registers for the second pass
+    // (pieces past H read as zeros and are not stored)
+    constexpr int NP = 8;
+    uint4 xv[NP], gv[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = lane * 8 + j * 64 * 8;
+      const int ic = i < a.H ? i : 0;
+      xv[j] = *reinterpret_cast<const uint4 *>(xr + ic);
+      gv[j] = *reinterpret_cast<const uint4 *>(a.norm_gain + ic);
+      if (i >= a.H) xv[j] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double lo = bf16_to_f32(w[q] & 0xffffu), hi = bf16_to_f32(w[q] >> 16);
+        ss = fma(lo, lo, fma(hi, hi, ss));
+      }
+    }
+    ss = group_sum_f64(ss, 64);
+    const double inv = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+    const float inv_f = (float)inv;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int i = lane * 8 + j * 64 * 8;
+      if (i < a.H) *reinterpret_cast<uint4 *>(a.xn + (int64_t)t * a.H + i) = norm_piece_bf16(xv[j], gv[j], inv_f, inv);
+    }
+    return;
+  }
   for (int i = lane * 8; i < a.H; i += 64 * 8) {
     const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
