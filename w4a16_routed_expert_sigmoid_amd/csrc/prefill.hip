@@ -698,28 +698,31 @@ __device__ __forceinline__ void gemm_stage(const uint16_t *sA, const BRaw (&b)[2
 }
 
 // K loop of one block: A stages through LDS (double-buffered), B stages
-// through registers (one stage ahead).
-template <int AMB>
-__device__ __forceinline__ void gemm_mainloop(uint16_t (*sA)[GBM * GLDA], const uint16_t *arow, int ar, int ap,
+// through registers (one stage ahead).  AMAX: 32-row blocks the tile rows
+// can fill (4, or 1 for 32-row tiles); thread (ar, ap) loads NV 16-byte
+// pieces of tile row ar per stage.
+template <int AMB, int AMAX>
+__device__ __forceinline__ void gemm_mainloop(uint16_t (*sA)[AMAX * 32 * GLDA], const uint16_t *arow, int ar, int ap,
                                               const uint8_t *const (&nib)[2], const uint8_t *const (&scl)[2],
                                               const int (&nrow)[2], const bool (&bok)[2], int K,
                                               f32x16 (&acc)[4][2]) {
+  constexpr int NV = AMAX;  // 16-byte pieces per thread and stage (GThreads threads cover AMAX * 32 rows x GBK)
   const int h = (threadIdx.x & 63) >> 5;
   const int S = (K + GBK - 1) / GBK;
-  uint4 av[4];
+  uint4 av[NV];
   auto load_a = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = make_uint4(0, 0, 0, 0);
-    if (arow && k0 + ap * 32 < K) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(arow + k0 + ap * 32);
+    for (int i = 0; i < NV; ++i) av[i] = make_uint4(0, 0, 0, 0);
+    if (arow && k0 + ap * NV * 8 < K) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(arow + k0 + ap * NV * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = p[i];
+      for (int i = 0; i < NV; ++i) av[i] = p[i];
     }
   };
   auto store_a = [&](int buf) {
-    uint4 *d = reinterpret_cast<uint4 *>(&sA[buf][ar * GLDA + ap * 32]);
+    uint4 *d = reinterpret_cast<uint4 *>(&sA[buf][ar * GLDA + ap * NV * 8]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = av[i];
+    for (int i = 0; i < NV; ++i) d[i] = av[i];
   };
   BRaw bcur[2], bnext[2];
   load_a(0);
@@ -749,9 +752,12 @@ __device__ __forceinline__ int gemm_item(int slot) {
 }
 
 // MODE 0: gate/up (K = H) -> h rows; MODE 1: down (K = I or Is) -> y rows.
-template <int MODE>
-__global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nblk) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][GBM * GLDA];
+// AMAX = 1: tiles of at most 32 rows (calls of 49..512 tokens): a quarter
+// of the A stage, and at most 128 registers, so that two blocks share a
+// compute unit and each hides the other's load waits.
+template <int MODE, int AMAX>
+__global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(PrefillArgs a, int nblk) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][AMAX * 32 * GLDA];
   const int w = gemm_item(blockIdx.x);
   if (w >= *a.n_tiles * nblk) return;
   const PfTile tile = a.tiles[w / nblk];
@@ -764,8 +770,9 @@ __global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nbl
   const int N = MODE == 0 ? Iw : a.H;
   const int64_t mat_bytes = nvfp4_matrix_bytes(MODE == 0 ? a.I : a.H, MODE == 0 ? a.H : a.I);
 
-  // A rows: thread (ar, ap) loads 32 K-elements of tile row ar per stage.
-  const int ar = tid >> 2, ap = tid & 3;
+  // A rows: thread (ar, ap) loads AMAX * 8 K-elements of tile row ar per stage.
+  constexpr int PARTS = GThreads / (AMAX * 32);  // threads per tile row in the A loads
+  const int ar = tid / PARTS, ap = tid % PARTS;
   const uint16_t *arow = nullptr;
   if (ar < tile.cnt) {
     const int p = tile.p0 + ar;
@@ -805,11 +812,15 @@ __global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nbl
   const int active_mb = (tile.cnt + 31) >> 5;
   f32x16 acc[4][2] = {};
   const uint8_t *const nibc[2] = {nib[0], nib[1]}, *const sclc[2] = {scl[0], scl[1]};
-  switch (active_mb) {
-    case 4: gemm_mainloop<4>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-    case 3: gemm_mainloop<3>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-    case 2: gemm_mainloop<2>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-    default: gemm_mainloop<1>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+  if (AMAX == 1) {
+    gemm_mainloop<1, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc);
+  } else {
+    switch (active_mb) {
+      case 4: gemm_mainloop<4, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      case 3: gemm_mainloop<3, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      case 2: gemm_mainloop<2, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      default: gemm_mainloop<1, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+    }
   }
 
   // Epilogue.  Value i of acc[mb][j] is tile row mb*32 + (i/4)*8 + h*4 + i%4
@@ -817,22 +828,25 @@ __global__ __launch_bounds__(GThreads) void k_pf_gemm_fp4(PrefillArgs a, int nbl
   // LDS (the A buffers, free now) and leave as whole 16-byte row pieces.
   constexpr int OC = MODE == 0 ? GBN / 2 : GBN;  // output columns of the block
   constexpr int OS = OC + 8;                     // staging row stride (elements)
-  constexpr int RPP = MODE == 0 ? 128 : 64;      // rows per pass
+  constexpr int RPP = (MODE == 0 ? 128 : 64) / (AMAX == 1 ? 4 : 1);  // rows per pass
   static_assert(RPP * OS * 2 <= (int)sizeof(sA), "a staging pass fits the A buffers");
+  static_assert(RPP % 8 == 0 && (AMAX * 32) % RPP == 0, "passes split the rows at 8-row groups");
   uint16_t *const stg = &sA[0][0];
   const int col0 = nb_i * OC;
   uint16_t *out = MODE == 0 ? a.h_rows : a.y_rows;
   const int64_t ostride = MODE == 0 ? Imax : a.H;
   constexpr int CPR = OC / 8;  // 16-byte pieces per row
 #pragma unroll
-  for (int pass = 0; pass < 128 / RPP; ++pass) {
+  for (int pass = 0; pass < AMAX * 32 / RPP; ++pass) {
     if (pass * RPP >= tile.cnt) break;
     __syncthreads();  // the A buffers (or the previous pass) are free
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb >= active_mb || mb * 32 / RPP != pass) continue;
+    for (int mb = 0; mb < AMAX; ++mb) {
+      if (mb >= active_mb) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        // the 8-row group of value i lies wholly in one pass (RPP is a multiple of 8)
+        if ((mb * 32 + (i >> 2) * 8) / RPP != pass) continue;
         const int r = mb * 32 - pass * RPP + (i >> 2) * 8 + h * 4 + (i & 3);
         if (MODE == 0) {
           const float g = round_bf16(acc[mb][0][i] * tscale[0]);
@@ -1073,10 +1087,17 @@ static hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t s) {
     const int64_t round = 8 * GChunk;
     const int64_t g_gu = ((int64_t)a.max_tiles * nb_gu + round - 1) / round * round;
     const int64_t g_dn = ((int64_t)a.max_tiles * nb_dn + round - 1) / round * round;
-    hipLaunchKernelGGL(k_pf_gemm_fp4<0>, dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
-    MOE_CK_LAUNCH();
-    hipLaunchKernelGGL(k_pf_gemm_fp4<1>, dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
-    MOE_CK_LAUNCH();
+    if (a.tile_rows <= 32) {
+      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 1>), dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
+      MOE_CK_LAUNCH();
+      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 1>), dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
+      MOE_CK_LAUNCH();
+    } else {
+      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 4>), dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
+      MOE_CK_LAUNCH();
+      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 4>), dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
+      MOE_CK_LAUNCH();
+    }
   } else {
     hipLaunchKernelGGL(k_pf_gateup<BT>, dim3(a.max_tiles, (nmax + 63) / 64), dim3(PThreads), 0, s, a);
     MOE_CK_LAUNCH();
