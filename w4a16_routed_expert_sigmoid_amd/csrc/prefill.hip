@@ -623,6 +623,7 @@ constexpr int GBK = 128;                // K per stage
 constexpr int GLDA = GBK + 8;           // LDS row stride, BF16 elements (272 B)
 constexpr int GBN = GWaves * 64;        // weight rows per block
 constexpr int GChunk = 8;               // consecutive work items per XCD chunk
+constexpr int kPfMidWaves = 4;          // waves per block on 32-row tiles (256 weight rows)
 
 // Raw NVFP4 data of one lane for one stage and one weight row: 64 FP4
 // (8 dwords) and the 4 block scales (two 16-bit scale pairs).
@@ -701,12 +702,11 @@ __device__ __forceinline__ void gemm_stage(const uint16_t *sA, const BRaw (&b)[2
 // through registers (one stage ahead).  AMAX: 32-row blocks the tile rows
 // can fill (4, or 1 for 32-row tiles); thread (ar, ap) loads NV 16-byte
 // pieces of tile row ar per stage.
-template <int AMB, int AMAX>
+template <int AMB, int AMAX, int NV>
 __device__ __forceinline__ void gemm_mainloop(uint16_t (*sA)[AMAX * 32 * GLDA], const uint16_t *arow, int ar, int ap,
                                               const uint8_t *const (&nib)[2], const uint8_t *const (&scl)[2],
                                               const int (&nrow)[2], const bool (&bok)[2], int K,
                                               f32x16 (&acc)[4][2]) {
-  constexpr int NV = AMAX;  // 16-byte pieces per thread and stage (GThreads threads cover AMAX * 32 rows x GBK)
   const int h = (threadIdx.x & 63) >> 5;
   const int S = (K + GBK - 1) / GBK;
   uint4 av[NV];
@@ -752,11 +752,18 @@ __device__ __forceinline__ int gemm_item(int slot) {
 }
 
 // MODE 0: gate/up (K = H) -> h rows; MODE 1: down (K = I or Is) -> y rows.
-// AMAX = 1: tiles of at most 32 rows (calls of 49..512 tokens): a quarter
-// of the A stage, and at most 128 registers, so that two blocks share a
-// compute unit and each hides the other's load waits.
-template <int MODE, int AMAX>
-__global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(PrefillArgs a, int nblk) {
+// WAVES waves per block, 64 weight rows each.  AMAX = 1: tiles of at most
+// 32 rows (calls of 49..512 tokens): a quarter of the A stage and the
+// accumulators, so that three blocks of 4 waves share a compute unit (at
+// most 168 registers) and hide each other's load waits; the small blocks
+// also give the few experts of such calls more items to spread over.
+template <int MODE, int AMAX, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave, AMAX == 1 ? 12 / WAVES : 8 / WAVES) void k_pf_gemm_fp4(PrefillArgs a,
+                                                                                                  int nblk) {
+  constexpr int NT = WAVES * kWave;  // threads
+  constexpr int BN = WAVES * 64;     // weight rows per block
+  constexpr int NV = AMAX * 32 * GBK / (8 * NT);  // A: 16-byte pieces per thread and stage
+  static_assert(NV >= 1 && NV * 8 * NT == AMAX * 32 * GBK, "the threads cover the A stage");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][AMAX * 32 * GLDA];
   const int w = gemm_item(blockIdx.x);
   if (w >= *a.n_tiles * nblk) return;
@@ -771,7 +778,7 @@ __global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(Pre
   const int64_t mat_bytes = nvfp4_matrix_bytes(MODE == 0 ? a.I : a.H, MODE == 0 ? a.H : a.I);
 
   // A rows: thread (ar, ap) loads AMAX * 8 K-elements of tile row ar per stage.
-  constexpr int PARTS = GThreads / (AMAX * 32);  // threads per tile row in the A loads
+  constexpr int PARTS = NT / (AMAX * 32);  // threads per tile row in the A loads
   const int ar = tid / PARTS, ap = tid % PARTS;
   const uint16_t *arow = nullptr;
   if (ar < tile.cnt) {
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(Pre
   int nrow[2];
   float tscale[2];
   if (MODE == 0) {
-    const int hc = nb_i * (GBN / 2) + wave * 32 + l32;
+    const int hc = nb_i * (BN / 2) + wave * 32 + l32;
     mats[0] = shared ? a.sh_gate : a.w_gate + tile.e * mat_bytes;
     mats[1] = shared ? a.sh_up : a.w_up + tile.e * mat_bytes;
     nrow[0] = nrow[1] = hc;
@@ -797,7 +804,7 @@ __global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(Pre
     tscale[1] = shared ? a.sh_scale[1] : a.w_scale[3 * tile.e + 1];
   } else {
     mats[0] = mats[1] = shared ? a.sh_down : a.w_down + tile.e * mat_bytes;
-    nrow[0] = nb_i * GBN + wave * 64 + l32;
+    nrow[0] = nb_i * BN + wave * 64 + l32;
     nrow[1] = nrow[0] + 32;
     tscale[0] = tscale[1] = shared ? a.sh_scale[2] : a.w_scale[3 * tile.e + 2];
   }
@@ -812,23 +819,25 @@ __global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(Pre
   const int active_mb = (tile.cnt + 31) >> 5;
   f32x16 acc[4][2] = {};
   const uint8_t *const nibc[2] = {nib[0], nib[1]}, *const sclc[2] = {scl[0], scl[1]};
-  if (AMAX == 1) {
-    gemm_mainloop<1, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc);
+  if constexpr (AMAX == 1) {
+    gemm_mainloop<1, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc);
   } else {
     switch (active_mb) {
-      case 4: gemm_mainloop<4, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-      case 3: gemm_mainloop<3, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-      case 2: gemm_mainloop<2, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
-      default: gemm_mainloop<1, AMAX>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      case 4: gemm_mainloop<4, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      case 3: gemm_mainloop<3, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      case 2: gemm_mainloop<2, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
+      default: gemm_mainloop<1, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
     }
   }
 
   // Epilogue.  Value i of acc[mb][j] is tile row mb*32 + (i/4)*8 + h*4 + i%4
   // and weight row nrow[j].  The BF16 results of RPP rows at a time go to
   // LDS (the A buffers, free now) and leave as whole 16-byte row pieces.
-  constexpr int OC = MODE == 0 ? GBN / 2 : GBN;  // output columns of the block
-  constexpr int OS = OC + 8;                     // staging row stride (elements)
-  constexpr int RPP = (MODE == 0 ? 128 : 64) / (AMAX == 1 ? 4 : 1);  // rows per pass
+  constexpr int OC = MODE == 0 ? BN / 2 : BN;  // output columns of the block
+  constexpr int OS = OC + 8;                   // staging row stride (elements)
+  // rows per pass: as many whole 8-row groups as the A buffers hold, dividing the tile rows
+  constexpr int RPP_FIT = (int)sizeof(sA) / (OS * 2) / 8 * 8;
+  constexpr int RPP = RPP_FIT >= AMAX * 32 ? AMAX * 32 : RPP_FIT >= 64 ? 64 : RPP_FIT >= 32 ? 32 : 16;
   static_assert(RPP * OS * 2 <= (int)sizeof(sA), "a staging pass fits the A buffers");
   static_assert(RPP % 8 == 0 && (AMAX * 32) % RPP == 0, "passes split the rows at 8-row groups");
   uint16_t *const stg = &sA[0][0];
@@ -860,7 +869,7 @@ __global__ __launch_bounds__(GThreads, AMAX == 1 ? 2 : 1) void k_pf_gemm_fp4(Pre
     }
     __syncthreads();
     const int rows = min(RPP, tile.cnt - pass * RPP);
-    for (int qi = tid; qi < rows * CPR; qi += GThreads) {
+    for (int qi = tid; qi < rows * CPR; qi += NT) {
       const int r = qi / CPR, c8 = qi % CPR;
       const int col = col0 + c8 * 8;
       if (col >= N) continue;
@@ -1083,19 +1092,22 @@ static hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t s) {
     MOE_CK_LAUNCH();
   } else if (BT == 1) {
     // grid: every (tile, n-block) item, rounded up to whole XCD chunks
-    const int nb_gu = (nmax + GBN / 2 - 1) / (GBN / 2), nb_dn = (a.H + GBN - 1) / GBN;
+    const int bn = a.tile_rows <= 32 ? kPfMidWaves * 64 : GBN;  // weight rows per block
+    const int nb_gu = (nmax + bn / 2 - 1) / (bn / 2), nb_dn = (a.H + bn - 1) / bn;
     const int64_t round = 8 * GChunk;
     const int64_t g_gu = ((int64_t)a.max_tiles * nb_gu + round - 1) / round * round;
     const int64_t g_dn = ((int64_t)a.max_tiles * nb_dn + round - 1) / round * round;
     if (a.tile_rows <= 32) {
-      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 1>), dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
+      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 1, kPfMidWaves>), dim3((unsigned)g_gu), dim3(kPfMidWaves * kWave), 0, s,
+                         a, nb_gu);
       MOE_CK_LAUNCH();
-      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 1>), dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
+      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 1, kPfMidWaves>), dim3((unsigned)g_dn), dim3(kPfMidWaves * kWave), 0, s,
+                         a, nb_dn);
       MOE_CK_LAUNCH();
     } else {
-      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 4>), dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
+      hipLaunchKernelGGL((k_pf_gemm_fp4<0, 4, GWaves>), dim3((unsigned)g_gu), dim3(GThreads), 0, s, a, nb_gu);
       MOE_CK_LAUNCH();
-      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 4>), dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
+      hipLaunchKernelGGL((k_pf_gemm_fp4<1, 4, GWaves>), dim3((unsigned)g_dn), dim3(GThreads), 0, s, a, nb_dn);
       MOE_CK_LAUNCH();
     }
   } else {
