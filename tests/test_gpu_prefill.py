@@ -38,11 +38,12 @@ SMALL = dict(hidden=256, inter=64, shared_inter=64, n_experts=16, top_k=4)
 
 
 @pytest.mark.parametrize("wtype", ["nvfp4", "bf16"])
-@pytest.mark.parametrize("T", [1, 37, 300, 1000])
+@pytest.mark.parametrize("T", [1, 37, 300, 1000, 1024, 1025])
 def test_prefill_small(wtype, T):
-    # zipf bias: the favoured experts get several 128-row tiles with a
-    # ragged last tile; T = 1000 gives the shared expert 8 tiles, the last
-    # one 104 rows.
+    # zipf bias: the favoured experts get several tiles with a ragged last
+    # tile.  NVFP4 calls of 49..1024 tokens run 32-row tiles (T = 1024 is
+    # the last), longer ones 128-row tiles (T = 1025 the first: the shared
+    # expert's 9th tile holds 1 row); BF16 calls always 128-row tiles.
     log(f"test: prefill small {wtype} T={T}")
     L = synth.make_layer(31, wtype=wtype, bias="zipf", **SMALL)
     x = synth.tokens(T, 256, stream=500 + T)

@@ -753,7 +753,7 @@ __device__ __forceinline__ int gemm_item(int slot) {
 
 // MODE 0: gate/up (K = H) -> h rows; MODE 1: down (K = I or Is) -> y rows.
 // WAVES waves per block, 64 weight rows each.  AMAX = 1: tiles of at most
-// 32 rows (calls of 49..512 tokens): a quarter of the A stage and the
+// 32 rows (calls of 49..1024 tokens): a quarter of the A stage and the
 // accumulators, so that three blocks of 4 waves share a compute unit (at
 // most 168 registers) and hide each other's load waits; the small blocks
 // also give the few experts of such calls more items to spread over.

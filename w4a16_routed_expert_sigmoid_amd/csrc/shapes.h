@@ -80,7 +80,7 @@ constexpr int64_t prefill_max_tiles(int64_t T, int64_t k, int64_t E, bool shared
 // (an expert with many rows spreads over several blocks instead of one long
 // item); the rest 128-row tiles.
 constexpr int kPrefillMidRows = 32;
-constexpr int kPrefillMidMaxTokens = 512;
+constexpr int kPrefillMidMaxTokens = 1024;
 constexpr int prefill_tile_rows(int64_t T, int wtype) {
   return (wtype == 1 && T <= kPrefillSmallMaxTokens)  ? kPrefillSmallRows
          : (wtype == 1 && T <= kPrefillMidMaxTokens) ? kPrefillMidRows
