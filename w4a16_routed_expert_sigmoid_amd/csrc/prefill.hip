@@ -743,6 +743,67 @@ __device__ __forceinline__ void gemm_mainloop(uint16_t (*sA)[AMAX * 32 * GLDA], 
   }
 }
 
+// K loop of a 32-row tile (one 32-row block).  Same stages as
+// gemm_mainloop, but every load is a branch-free buffer load (a lane or
+// stage with nothing to load reads zeros past the range's end) and the two
+// weight buffers take turns (b0 current while b1 fills, then the reverse)
+// instead of being copied: no exec-mask branches or register moves in the
+// loop, which matters where one weight fragment feeds a single 32-row block
+// and the loop's VALU work is mostly dequantisation.
+//   a_off: byte offset of this thread's A piece in its row (kBufNone for
+//     rows past the tile); nib_off / scl_off: byte offsets of the lane's
+//     first chunk and its scale pair at K = 0 (kBufNone for rows past N).
+template <int NV>
+__device__ __forceinline__ void gemm_mainloop_32(uint16_t (*sA)[32 * GLDA], __amdgpu_buffer_rsrc_t ar_rsrc,
+                                                 uint32_t a_off, int ar, int ap, const __amdgpu_buffer_rsrc_t (&br)[2],
+                                                 const uint32_t (&nib_off)[2], const uint32_t (&scl_off)[2], int K,
+                                                 f32x16 (&acc)[4][2]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const int S = (K + GBK - 1) / GBK, C = K >> 5;
+  uint4 av[NV];
+  BRaw b0[2], b1[2];
+  auto load_a = [&](int st) {
+    const int k0 = st * GBK;
+    const bool ok = st < S && k0 + ap * NV * 8 < K;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) av[i] = buf_load16(ar_rsrc, buf_off(ok, a_off + (uint32_t)k0 * 2 + i * 16));
+  };
+  auto store_a = [&](int buf) {
+    uint4 *d = reinterpret_cast<uint4 *>(&sA[buf][ar * GLDA + ap * NV * 8]);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) d[i] = av[i];
+  };
+  auto load_b = [&](int st, BRaw (&r)[2]) {
+    const int k0 = st * GBK, c = (k0 >> 5) + 2 * h;
+    const bool ok0 = st < S && c < C, ok1 = st < S && c + 1 < C;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t nb = nib_off[j] + (uint32_t)k0 / 2, sb = scl_off[j] + (uint32_t)k0 / 2;
+      r[j].q0 = buf_load16(br[j], buf_off(ok0, nb));
+      r[j].q1 = buf_load16(br[j], buf_off(ok1, nb + 16));
+      r[j].s0 = buf_load2(br[j], buf_off(ok0, sb));
+      r[j].s1 = buf_load2(br[j], buf_off(ok1, sb + 16));
+    }
+  };
+  // stage st: the operands of st + 1 go out, stage st computes, and the A
+  // rows of st + 1 move to LDS
+  auto step = [&](int st, const BRaw (&cur)[2], BRaw (&fill)[2]) {
+    load_a(st + 1);
+    load_b(st + 1, fill);
+    __syncthreads();
+    gemm_stage<1>(sA[st & 1], cur, acc);
+    store_a((st + 1) & 1);
+  };
+  load_a(0);
+  load_b(0, b0);
+  store_a(0);
+  for (int st = 0; st < S; st += 2) {
+    step(st, b0, b1);
+    if (st + 1 >= S) break;
+    step(st + 1, b1, b0);
+  }
+}
+
 // The (tile, n-block) item of grid slot `slot`: items are spread over the 8
 // XCDs in chunks of GChunk consecutive items (neighbouring items share A
 // rows or the expert's weights in that XCD's L2).
@@ -820,7 +881,33 @@ __global__ __launch_bounds__(WAVES * kWave, AMAX == 1 ? 12 / WAVES : 8 / WAVES) 
   f32x16 acc[4][2] = {};
   const uint8_t *const nibc[2] = {nib[0], nib[1]}, *const sclc[2] = {scl[0], scl[1]};
   if constexpr (AMAX == 1) {
-    gemm_mainloop<1, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc);
+    // 32-row tiles: the operands as buffer ranges and offsets when both fit
+    // below 2 GiB (any shape of the model's size; larger ones take the
+    // pointer loop)
+    const uint16_t *abase = MODE == 0 ? (a.use_norm ? a.xn : a.x) : a.h_rows;
+    const int64_t arow_elems = MODE == 0 ? a.H : Imax;
+    const int64_t abytes = (MODE == 0 ? (int64_t)a.T : (int64_t)(a.P + a.T)) * arow_elems * 2;
+    const int64_t wbytes = nvfp4_matrix_bytes(N, K);
+    if (abytes < (int64_t)kBufNone && wbytes < (int64_t)kBufNone) {
+      uint32_t a_off = kBufNone;
+      if (ar < tile.cnt) {
+        const int p = tile.p0 + ar;
+        const int64_t row = MODE == 0 ? (shared ? p - a.P : a.sorted_tok[p]) : p;
+        a_off = (uint32_t)(row * arow_elems * 2) + (uint32_t)(ap * NV * 16);
+      }
+      const __amdgpu_buffer_rsrc_t br[2] = {buf_rsrc(mats[0], wbytes), buf_rsrc(mats[1], wbytes)};
+      uint32_t nib_off[2], scl_off[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        nib_off[j] = bok[j] ? (uint32_t)(nrow[j] * (K / 2) + 32 * h) : kBufNone;
+        scl_off[j] = bok[j] ? (uint32_t)((int64_t)N * (K / 2) + (int64_t)(nrow[j] >> 3) * (K >> 5) * 16 +
+                                         (nrow[j] & 7) * 2 + 32 * h)
+                            : kBufNone;
+      }
+      gemm_mainloop_32<NV>(sA, buf_rsrc(abase, abytes), a_off, ar, ap, br, nib_off, scl_off, K, acc);
+    } else {
+      gemm_mainloop<1, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc);
+    }
   } else {
     switch (active_mb) {
       case 4: gemm_mainloop<4, AMAX, NV>(sA, arow, ar, ap, nibc, sclc, nrow, bok, K, acc); break;
